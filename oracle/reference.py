@@ -1,0 +1,252 @@
+"""Plain fp64 definitions of the hot path (TEST INFRASTRUCTURE ONLY).
+
+Citations name sections of the news page "CODA: New Research Optimizes
+Transformer Training with GEMM-Epilogue Programming" (KuCoin news flash).
+
+Everything is unfused and in float64 on the exact input values.  Weights are
+stored [N, K] (row n holds output feature n), so a linear layer is x @ W^T.
+Every block is row-independent: callers may pass a subset of token rows and get
+exactly the corresponding rows of the full result.  That is how full-size
+configurations are checked on sampled rows.
+"""
+
+import numpy as np
+
+
+# ---------------------------------------------------------------------------
+# building blocks
+# ---------------------------------------------------------------------------
+
+def gemm_nt(a, w):
+    """y = a @ w^T for a [M,K], w [N,K] (the blocked multiply the page calls
+    the GEMM mainloop, section "CODA: the secret in the epilogue").  float64
+    BLAS is used as the library matmul step."""
+    a = np.asarray(a, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    return a @ w.T
+
+
+def residual_add(y, res):
+    """h = res + y (elementwise residual add; section "Five building blocks
+    and a LEGO language", elementwise transform)."""
+    return np.asarray(res, dtype=np.float64) + np.asarray(y, dtype=np.float64)
+
+
+def rms_scale(h, eps):
+    """Per-row RMS scale r[m] = 1 / sqrt(mean_n h[m,n]^2 + eps).
+
+    The page (section "CODA: the secret in the epilogue") calls this the row
+    scale factor of RMS normalisation; it prints no formula.  Reading: eps
+    inside the square root, mean over the row's N features."""
+    h = np.asarray(h, dtype=np.float64)
+    ms = np.mean(h * h, axis=1)
+    return 1.0 / np.sqrt(ms + eps)
+
+
+def rmsnorm(h, gamma, eps):
+    """RMSNorm applied before the second GEMM (the unfused form):
+    n = diag(r) . h . diag(gamma)."""
+    r = rms_scale(h, eps)
+    return (r[:, None] * np.asarray(h, dtype=np.float64)) * np.asarray(gamma, dtype=np.float64)[None, :]
+
+
+def silu(z):
+    """silu(z) = z / (1 + exp(-z)) (the SiLU gate of SwiGLU)."""
+    z = np.asarray(z, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def swiglu(g, u):
+    """SwiGLU activation: silu(g) * u with g the gate projection and u the up
+    projection (named in sections "The cost of laziness..." and "CODA: the
+    secret in the epilogue"; reading: the LLaMA form)."""
+    return silu(g) * np.asarray(u, dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------
+# MLP block: GEMM -> residual -> RMSNorm -> GEMM (gate|up) -> SwiGLU
+# ---------------------------------------------------------------------------
+
+def mlp_block(x, res, wo, wg, wu, gamma, eps):
+    """GEMM-RMSNorm-GEMM with SwiGLU, unfused (section "CODA: the secret in
+    the epilogue": a matmul, a residual add, RMS normalisation, then a second
+    matmul; the SwiGLU step applies the same scheme).
+
+    x [M,K1], res [M,d], wo [d,K1], wg/wu [ffn,d], gamma [d] -> dict with
+      h   [M,d]   = res + x wo^T
+      r   [M]     = rms_scale(h)
+      g,u [M,ffn] = (diag(r) h diag(gamma)) wg^T, ... wu^T
+      out [M,ffn] = silu(g) * u
+    """
+    h = residual_add(gemm_nt(x, wo), res)
+    r = rms_scale(h, eps)
+    n = (r[:, None] * h) * np.asarray(gamma, dtype=np.float64)[None, :]
+    g = gemm_nt(n, wg)
+    u = gemm_nt(n, wu)
+    return {"h": h, "r": r, "g": g, "u": u, "out": swiglu(g, u)}
+
+
+def fp8_mlp_block(xq, sx, res, woq, swo, wgq, swg, wuq, swu, eps, h_scale=None):
+    """The same block with e4m3 operands (section "The cost of laziness in
+    large-model training" names FP8 as the regime where data movement
+    dominates).
+
+    xq [M,K1], woq [d,K1], wgq/wuq [ffn,d] are E4M3FN codes (uint8), each with
+    one fp32 per-tensor scale (value = decode(code) * scale); res [M,d] is the
+    residual's float64 value.  gamma was folded into wg/wu before they were
+    quantised, so it does not appear here.
+
+    The second GEMM reads h as e4m3 too.  That rounding is part of what an fp8
+    GEMM computes, so the oracle models it once:
+      s_h   = max|h| / 448 from the unrounded h (current scaling), unless a
+              scale is given,
+      h_hat = s_h * E4M3(h / s_h)   (round to nearest even, saturating)
+      g, u  = r * (h_hat Wg^T), r * (h_hat Wu^T);  out = silu(g) * u.
+    """
+    from .codecs import e4m3_decode, e4m3_encode_fast, E4M3_MAX
+
+    x = e4m3_decode(xq) * float(sx)
+    wo = e4m3_decode(woq) * float(swo)
+    h = residual_add(gemm_nt(x, wo), res)
+    r = rms_scale(h, eps)
+    amax = float(np.max(np.abs(h)))
+    s_h = amax / E4M3_MAX if h_scale is None else float(h_scale)
+    h_hat = e4m3_decode(e4m3_encode_fast(h / s_h)) * s_h
+    g = r[:, None] * gemm_nt(h_hat, e4m3_decode(wgq) * float(swg))
+    u = r[:, None] * gemm_nt(h_hat, e4m3_decode(wuq) * float(swu))
+    return {"h": h, "r": r, "amax": amax, "s_h": s_h, "h_hat": h_hat,
+            "g": g, "u": u, "out": swiglu(g, u)}
+
+
+# ---------------------------------------------------------------------------
+# attention-input block: GEMM -> residual -> RMSNorm -> QKV GEMM -> RoPE
+# ---------------------------------------------------------------------------
+
+def rope_tables(max_pos, head_dim, theta):
+    """cos/sin of the rotary angles, [max_pos, head_dim/2] float64.
+
+    Rotary position embedding is named (section "CODA: the secret in the
+    epilogue") without a formula.  Reading: angle(p, i) = p * theta^(-2i/hd)
+    for i = 0 .. hd/2-1, no frequency rescaling."""
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    inv_freq = theta ** (-2.0 * i / head_dim)
+    ang = np.arange(max_pos, dtype=np.float64)[:, None] * inv_freq[None, :]
+    return np.cos(ang), np.sin(ang)
+
+
+def apply_rope(y, pos, n_rot_heads, head_dim, cos, sin):
+    """Rotate the first n_rot_heads heads of y [M, heads*hd] by position.
+
+    Rotate-half pairing: within a head, feature i pairs with i + hd/2:
+      (a, b) -> (a cos - b sin, b cos + a sin).
+    Heads past n_rot_heads (the v heads) are returned unchanged."""
+    y = np.array(y, dtype=np.float64, copy=True)
+    half = head_dim // 2
+    c = cos[np.asarray(pos)]  # [M, half]
+    s = sin[np.asarray(pos)]
+    for hh in range(n_rot_heads):
+        lo = hh * head_dim
+        a = y[:, lo:lo + half].copy()
+        b = y[:, lo + half:lo + head_dim].copy()
+        y[:, lo:lo + half] = a * c - b * s
+        y[:, lo + half:lo + head_dim] = b * c + a * s
+    return y
+
+
+def attn_in_block(a, res, w1, wqkv, gamma, eps, pos, n_q, n_kv, head_dim, theta,
+                  max_pos):
+    """GEMM-RMSNorm-GEMM feeding attention, with RoPE on q and k.
+
+    a [M,K1], res [M,d], w1 [d,K1], wqkv [(n_q+2 n_kv) hd, d], gamma [d],
+    pos [M] -> dict(h, r, qkv [M, (n_q+2 n_kv) hd] laid out q | k | v)."""
+    h = residual_add(gemm_nt(a, w1), res)
+    r = rms_scale(h, eps)
+    n = (r[:, None] * h) * np.asarray(gamma, dtype=np.float64)[None, :]
+    y = gemm_nt(n, wqkv)
+    cos, sin = rope_tables(max_pos, head_dim, theta)
+    qkv = apply_rope(y, pos, n_q + n_kv, head_dim, cos, sin)
+    return {"h": h, "r": r, "qkv": qkv}
+
+
+# ---------------------------------------------------------------------------
+# LM head cross entropy via log-sum-exp
+# ---------------------------------------------------------------------------
+
+def logsumexp_rows(z):
+    """lse[m] = max_n z + ln sum_n exp(z - max) (natural log)."""
+    z = np.asarray(z, dtype=np.float64)
+    mx = np.max(z, axis=1)
+    return mx + np.log(np.sum(np.exp(z - mx[:, None]), axis=1))
+
+
+def lm_head_ce(x, wlm, labels, r=None, chunk=256):
+    """Per-row cross entropy of the LM head (section "CODA: the secret in the
+    epilogue" lists cross-entropy among the re-parameterised ops).
+
+    z = diag(r) x wlm^T (r optional), loss[m] = lse(z[m]) - z[m, label[m]].
+    Rows are processed in chunks so the float64 logits stay bounded."""
+    x = np.asarray(x, dtype=np.float64)
+    labels = np.asarray(labels)
+    M = x.shape[0]
+    lse = np.empty(M)
+    zl = np.empty(M)
+    for m0 in range(0, M, chunk):
+        z = gemm_nt(x[m0:m0 + chunk], wlm)
+        if r is not None:
+            z = np.asarray(r, dtype=np.float64)[m0:m0 + chunk, None] * z
+        lse[m0:m0 + chunk] = logsumexp_rows(z)
+        zl[m0:m0 + chunk] = z[np.arange(z.shape[0]), labels[m0:m0 + chunk]]
+    return {"lse": lse, "label_logit": zl, "loss": lse - zl}
+
+
+# ---------------------------------------------------------------------------
+# block-local quantities the epilogues emit (section "Five building blocks and
+# a LEGO language": block reduction -- local RMS, block log-sum-exp; stateful
+# transform -- running max and sum-exp)
+# ---------------------------------------------------------------------------
+
+def partial_sumsq(h, width):
+    """P[t, m] = sum over columns [t*width, (t+1)*width) of h[m, n]^2."""
+    h = np.asarray(h, dtype=np.float64)
+    M, N = h.shape
+    T = (N + width - 1) // width
+    P = np.zeros((T, M))
+    for t in range(T):
+        blk = h[:, t * width:(t + 1) * width]
+        P[t] = np.sum(blk * blk, axis=1)
+    return P
+
+
+def tile_lse(z, width):
+    """Per (tile, row) (max, sum exp(z - max)) over columns of width `width`.
+    Returns mx [T, M], se [T, M]."""
+    z = np.asarray(z, dtype=np.float64)
+    M, V = z.shape
+    T = (V + width - 1) // width
+    mx = np.empty((T, M))
+    se = np.empty((T, M))
+    for t in range(T):
+        blk = z[:, t * width:(t + 1) * width]
+        mx[t] = np.max(blk, axis=1)
+        se[t] = np.sum(np.exp(blk - mx[t][:, None]), axis=1)
+    return mx, se
+
+
+def lse_merge(mx, se, order=None):
+    """Combine per-tile (max, sum-exp) pairs into lse, one pair at a time in
+    the given tile order (the online-normalisation statistics).  The pair
+    (-inf, 0) is the identity of the merge."""
+    mx = np.asarray(mx, dtype=np.float64)
+    se = np.asarray(se, dtype=np.float64)
+    T = mx.shape[0]
+    order = range(T) if order is None else order
+    run_m = np.full(mx.shape[1], -np.inf)
+    run_s = np.zeros(mx.shape[1])
+    for t in order:
+        new_m = np.maximum(run_m, mx[t])
+        with np.errstate(invalid="ignore"):
+            a = np.where(run_s > 0, run_s * np.exp(run_m - new_m), 0.0)
+            b = np.where(se[t] > 0, se[t] * np.exp(mx[t] - new_m), 0.0)
+        run_m, run_s = new_m, a + b
+    return run_m + np.log(run_s)

@@ -1,0 +1,384 @@
+"""Checks that pin the CPU oracle to facts outside itself.
+
+Each `pin_*` function returns (ok: bool, detail: str).  They are run as plain
+tests (tests/test_oracle_pins.py) and again against deliberately broken copies
+of the oracle (tests/test_oracle_mutants.py) to show that a plausible mistake
+-- a dropped term, a wrong sign, index or eps placement, a transposed operand
+-- fails at least one of them.
+
+Kinds of pin used (none of them re-calls the oracle's own formula):
+  * brute force: pure-Python loops with math.fsum on tiny inputs;
+  * exact arithmetic: fractions.Fraction / decimal.Decimal on a hand-built
+    example (tests/golden/mlp_exact_example.json);
+  * library routines: torch CPU float64 rms_norm, silu, cross_entropy,
+    logsumexp, complex multiplication;
+  * closed forms and invariants of the mathematics (unit RMS after
+    normalisation, RoPE as a rotation, merge order independence, W = 0 gives
+    loss ln V).
+"""
+
+import json
+import math
+import os
+import random
+from decimal import Decimal, getcontext
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+import oracle
+from oracle import reference as R
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rel(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    den = max(float(np.max(np.abs(b))), 1e-300)
+    return float(np.max(np.abs(a - b))) / den
+
+
+def _ok(err, tol, what):
+    return (err <= tol, f"{what}: err {err:.3e} (tol {tol:.1e})")
+
+
+# ---------------------------------------------------------------------------
+# brute force, pure Python
+# ---------------------------------------------------------------------------
+
+def _bf_gemm_nt(a, w):
+    return [[math.fsum(a[i][k] * w[j][k] for k in range(len(a[i]))) for j in range(len(w))]
+            for i in range(len(a))]
+
+
+def _bf_silu(z):
+    return z / (1.0 + math.exp(-z))
+
+
+def _rand(rng, r, c, s=1.0):
+    return [[rng.gauss(0.0, s) for _ in range(c)] for _ in range(r)]
+
+
+def pin_mlp_bruteforce(seed=1):
+    rng = random.Random(seed)
+    M, K1, d, ffn, eps = 3, 5, 4, 6, 1e-5
+    x, res = _rand(rng, M, K1), _rand(rng, M, d)
+    wo, wg, wu = _rand(rng, d, K1, 0.5), _rand(rng, ffn, d, 0.5), _rand(rng, ffn, d, 0.5)
+    gamma = [1.0 + 0.1 * rng.gauss(0, 1) for _ in range(d)]
+    y = _bf_gemm_nt(x, wo)
+    h = [[res[m][n] + y[m][n] for n in range(d)] for m in range(M)]
+    r = [1.0 / math.sqrt(math.fsum(v * v for v in h[m]) / d + eps) for m in range(M)]
+    nrm = [[r[m] * h[m][n] * gamma[n] for n in range(d)] for m in range(M)]
+    g, u = _bf_gemm_nt(nrm, wg), _bf_gemm_nt(nrm, wu)
+    out = [[_bf_silu(g[m][j]) * u[m][j] for j in range(ffn)] for m in range(M)]
+    o = oracle.mlp_block(np.array(x), np.array(res), np.array(wo), np.array(wg), np.array(wu),
+                         np.array(gamma), eps)
+    err = max(_rel(o["h"], h), _rel(o["r"], r), _rel(o["g"], g), _rel(o["u"], u),
+              _rel(o["out"], out))
+    return _ok(err, 1e-12, "mlp brute force")
+
+
+def pin_mlp_exact_example():
+    """Hand-built example with exact rational values (eps = 0, rows chosen so
+    mean(h^2) is a perfect square); see tests/golden/mlp_exact_example.json."""
+    with open(os.path.join(GOLDEN, "mlp_exact_example.json")) as f:
+        ex = json.load(f)
+    arr = lambda k: np.array([[float(Fraction(v)) for v in row] for row in ex["inputs"][k]])
+    gamma = np.array([float(Fraction(v)) for v in ex["inputs"]["gamma"]])
+    o = oracle.mlp_block(arr("x"), arr("res"), arr("wo"), arr("wg"), arr("wu"), gamma,
+                         float(Fraction(ex["inputs"]["eps"])))
+    exp = ex["expected"]
+    errs = []
+    for k in ("h", "g", "u"):
+        ref = np.array([[float(Fraction(v)) for v in row] for row in exp[k]])
+        errs.append(_rel(o[k], ref))
+    errs.append(_rel(o["r"], [float(Fraction(v)) for v in exp["r"]]))
+    errs.append(_rel(o["out"], np.array([[float(Decimal(v)) for v in row] for row in exp["out"]])))
+    return _ok(max(errs), 1e-14, "mlp exact example")
+
+
+def pin_rmsnorm_torch(seed=2):
+    g = torch.Generator().manual_seed(seed)
+    h = torch.randn(7, 33, generator=g, dtype=torch.float64) * 3
+    gamma = 1 + 0.1 * torch.randn(33, generator=g, dtype=torch.float64)
+    eps = 1e-5
+    ref = torch.nn.functional.rms_norm(h, (33,), weight=gamma, eps=eps)
+    return _ok(_rel(R.rmsnorm(h.numpy(), gamma.numpy(), eps), ref.numpy()), 1e-13,
+               "rmsnorm vs torch")
+
+
+def pin_rms_closed_forms():
+    d, eps = 16, 1e-5
+    h = np.zeros((3, d))
+    h[0, :] = 2.5                       # constant row c: r = (c^2 + eps)^-1/2
+    h[1, 5] = -4.0                      # one non-zero c: r = (c^2/d + eps)^-1/2
+    h[2, :] = np.arange(d) - 7.5        # generic row: mean((r h)^2) = ms/(ms+eps)
+    r = R.rms_scale(h, eps)
+    e0 = abs(r[0] - (2.5 ** 2 + eps) ** -0.5)
+    e1 = abs(r[1] - (16.0 / d + eps) ** -0.5)
+    ms = sum((v - 7.5) ** 2 for v in range(d)) / d
+    e2 = abs(float(np.mean((r[2] * h[2]) ** 2)) - ms / (ms + eps))
+    return _ok(max(e0, e1, e2), 1e-12, "rms closed forms")
+
+
+def pin_unit_rms(seed=3):
+    """RMSNorm output rows have unit RMS before gamma (eps = 0)."""
+    rng = np.random.default_rng(seed)
+    h = rng.standard_normal((9, 40)) * rng.uniform(0.1, 10, size=(9, 1))
+    n = R.rmsnorm(h, np.ones(40), 0.0)
+    return _ok(float(np.max(np.abs(np.sqrt(np.mean(n * n, axis=1)) - 1.0))), 1e-13, "unit RMS")
+
+
+def pin_rowscale_commutes(seed=4):
+    """The page's identity: applying the row scale before GEMM2 equals
+    applying it after GEMM2, with gamma folded into W's columns."""
+    rng = np.random.default_rng(seed)
+    M, d, ffn, eps = 6, 24, 10, 1e-5
+    x, res = rng.standard_normal((M, d)), rng.standard_normal((M, d))
+    wo, wg, wu = (rng.standard_normal((d, d)) / 5, rng.standard_normal((ffn, d)) / 5,
+                  rng.standard_normal((ffn, d)) / 5)
+    gamma = 1 + 0.1 * rng.standard_normal(d)
+    o = oracle.mlp_block(x, res, wo, wg, wu, gamma, eps)
+    h = res + x @ wo.T
+    r_bf = [1.0 / math.sqrt(math.fsum(v * v for v in row) / d + eps) for row in h]
+    r_bf = np.array(r_bf)
+    g_after = r_bf[:, None] * (h @ (wg * gamma[None, :]).T)
+    u_after = r_bf[:, None] * (h @ (wu * gamma[None, :]).T)
+    return _ok(max(_rel(o["g"], g_after), _rel(o["u"], u_after)), 1e-12,
+               "row scale commutes with GEMM2")
+
+
+def pin_swiglu():
+    z = np.linspace(-30, 30, 601)
+    e0 = abs(float(R.silu(np.array([0.0]))[0]))
+    e1 = float(np.max(np.abs(R.silu(z) - R.silu(-z) - z)))
+    e2 = _rel(R.silu(z), torch.nn.functional.silu(torch.from_numpy(z)).numpy())
+    g = np.random.default_rng(5).standard_normal((4, 7))
+    e3 = _rel(R.swiglu(g, np.ones_like(g)), R.silu(g))
+    e4 = _rel(R.swiglu(g, 2 * np.ones_like(g)),
+              2 * torch.nn.functional.silu(torch.from_numpy(g)).numpy())
+    return _ok(max(e0, e1, e2, e3, e4), 1e-13, "silu/swiglu closed forms and torch")
+
+
+# ---------------------------------------------------------------------------
+# RoPE
+# ---------------------------------------------------------------------------
+
+def pin_rope_closed_forms():
+    hd, theta = 4, 10000.0
+    cos, sin = R.rope_tables(8, hd, theta)
+    # pair 0 turns by p radians, pair 1 by p / 100 (theta^(-2/4) = 1/100)
+    e = max(abs(cos[3, 0] - math.cos(3.0)), abs(sin[3, 0] - math.sin(3.0)),
+            abs(cos[5, 1] - math.cos(0.05)), abs(sin[5, 1] - math.sin(0.05)))
+    y = np.array([[1.0, 0.0, 0.0, 0.0]] * 2)  # a = 1, b = 0 in pair 0
+    out = R.apply_rope(y, np.array([0, 2]), 1, hd, cos, sin)
+    # position 0 is the identity; position 2 turns (1, 0) into (cos 2, sin 2)
+    e = max(e, float(np.max(np.abs(out[0] - y[0]))),
+            abs(out[1, 0] - math.cos(2.0)), abs(out[1, 2] - math.sin(2.0)))
+    return _ok(e, 1e-15, "rope closed forms")
+
+
+def pin_rope_torch_complex(seed=6):
+    """RoPE as complex multiplication: (a + ib) * e^{i angle}."""
+    rng = np.random.default_rng(seed)
+    M, hd, nh, theta = 11, 8, 3, 500000.0
+    y = rng.standard_normal((M, nh * hd))
+    pos = rng.integers(0, 50, size=M)
+    cos, sin = R.rope_tables(64, hd, theta)
+    out = R.apply_rope(y, pos, 2, hd, cos, sin)
+    yt = torch.from_numpy(y).view(M, nh, 2, hd // 2)
+    z = torch.complex(yt[:, :, 0], yt[:, :, 1])
+    inv = theta ** (-torch.arange(hd // 2, dtype=torch.float64) * 2 / hd)
+    ang = torch.from_numpy(pos).double()[:, None] * inv[None, :]
+    rot = z * torch.polar(torch.ones_like(ang), ang)[:, None, :]
+    ref = torch.stack([rot.real, rot.imag], dim=2).reshape(M, nh * hd).numpy()
+    ref[:, 2 * hd:] = y[:, 2 * hd:]  # third head not rotated
+    return _ok(_rel(out, ref), 1e-13, "rope vs torch complex")
+
+
+def pin_rope_relative(seed=7):
+    """<R_m q, R_n k> depends only on m - n; rotations keep pair norms."""
+    rng = np.random.default_rng(seed)
+    hd = 16
+    cos, sin = R.rope_tables(200, hd, 500000.0)
+    q = rng.standard_normal((1, hd))
+    k = rng.standard_normal((1, hd))
+    rq = lambda p: R.apply_rope(q, np.array([p]), 1, hd, cos, sin)[0]
+    rk = lambda p: R.apply_rope(k, np.array([p]), 1, hd, cos, sin)[0]
+    e1 = abs(np.dot(rq(30), rk(10)) - np.dot(rq(150), rk(130)))
+    a = rq(77)
+    e2 = float(np.max(np.abs(a[:hd // 2] ** 2 + a[hd // 2:] ** 2
+                             - (q[0, :hd // 2] ** 2 + q[0, hd // 2:] ** 2))))
+    return _ok(max(e1, e2), 1e-12, "rope relative position / norm")
+
+
+def pin_attn_bruteforce(seed=8):
+    rng = random.Random(seed)
+    M, K1, d, nq, nkv, hd, eps, theta = 3, 6, 8, 2, 1, 4, 1e-5, 500000.0
+    x, res = _rand(rng, M, K1), _rand(rng, M, d)
+    w1, wqkv = _rand(rng, d, K1, 0.4), _rand(rng, (nq + 2 * nkv) * hd, d, 0.4)
+    gamma = [1.0 + 0.1 * rng.gauss(0, 1) for _ in range(d)]
+    pos = [5, 0, 1234]
+    y1 = _bf_gemm_nt(x, w1)
+    h = [[res[m][n] + y1[m][n] for n in range(d)] for m in range(M)]
+    r = [1.0 / math.sqrt(math.fsum(v * v for v in h[m]) / d + eps) for m in range(M)]
+    nrm = [[r[m] * h[m][n] * gamma[n] for n in range(d)] for m in range(M)]
+    y = _bf_gemm_nt(nrm, wqkv)
+    out = [row[:] for row in y]
+    for m in range(M):
+        for head in range(nq + nkv):
+            for i in range(hd // 2):
+                ang = pos[m] * theta ** (-2.0 * i / hd)
+                a, b = y[m][head * hd + i], y[m][head * hd + i + hd // 2]
+                out[m][head * hd + i] = a * math.cos(ang) - b * math.sin(ang)
+                out[m][head * hd + i + hd // 2] = b * math.cos(ang) + a * math.sin(ang)
+    o = oracle.attn_in_block(np.array(x), np.array(res), np.array(w1), np.array(wqkv),
+                             np.array(gamma), eps, np.array(pos), nq, nkv, hd, theta, 2048)
+    return _ok(max(_rel(o["qkv"], out), _rel(o["r"], r), _rel(o["h"], h)), 1e-12,
+               "attn brute force")
+
+
+# ---------------------------------------------------------------------------
+# LSE / cross entropy
+# ---------------------------------------------------------------------------
+
+def pin_ce_bruteforce(seed=9):
+    rng = random.Random(seed)
+    M, d, V = 4, 5, 13
+    x, w = _rand(rng, M, d, 2.0), _rand(rng, V, d)
+    labels = [rng.randrange(V) for _ in range(M)]
+    z = _bf_gemm_nt(x, w)
+    loss = []
+    for m in range(M):
+        mx = max(z[m])
+        lse = mx + math.log(math.fsum(math.exp(v - mx) for v in z[m]))
+        loss.append(lse - z[m][labels[m]])
+    o = oracle.lm_head_ce(np.array(x), np.array(w), np.array(labels), chunk=3)
+    return _ok(_rel(o["loss"], loss), 1e-12, "ce brute force")
+
+
+def pin_ce_torch(seed=10):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(9, 16, generator=g, dtype=torch.float64) * 2
+    w = torch.randn(37, 16, generator=g, dtype=torch.float64)
+    lab = torch.randint(0, 37, (9,), generator=g)
+    r = torch.rand(9, generator=g, dtype=torch.float64) + 0.5
+    ref = torch.nn.functional.cross_entropy(r[:, None] * (x @ w.T), lab, reduction="none")
+    ref_lse = torch.logsumexp(r[:, None] * (x @ w.T), dim=1)
+    o = oracle.lm_head_ce(x.numpy(), w.numpy(), lab.numpy(), r=r.numpy(), chunk=4)
+    return _ok(max(_rel(o["loss"], ref.numpy()), _rel(o["lse"], ref_lse.numpy())), 1e-13,
+               "ce vs torch")
+
+
+def pin_ce_zero_weights():
+    """W = 0: every logit is 0, so loss = ln V for every row."""
+    V = 128256
+    o = oracle.lm_head_ce(np.ones((3, 4)), np.zeros((V, 4)), np.array([0, 5, V - 1]))
+    with open(os.path.join(GOLDEN, "closed_forms.json")) as f:
+        lnv = float(json.load(f)["ln_128256"])
+    return _ok(float(np.max(np.abs(o["loss"] - lnv))), 1e-12, "W = 0 gives ln V")
+
+
+def pin_lse_merge(seed=11):
+    rng = np.random.default_rng(seed)
+    z = rng.standard_normal((5, 300)) * 20
+    full = torch.logsumexp(torch.from_numpy(z), dim=1).numpy()
+    mx, se = R.tile_lse(z, 64)  # 5 tiles, the last one ragged (44 wide)
+    T = mx.shape[0]
+    e = _rel(R.lse_merge(mx, se), full)
+    e = max(e, _rel(R.lse_merge(mx, se, order=list(range(T))[::-1]), full))
+    perm = list(rng.permutation(T))
+    e = max(e, _rel(R.lse_merge(mx, se, order=perm), full))
+    # pairwise tree: merge (0,1), (2,3), then with 4
+    def pair(a, b):
+        m = np.maximum(a[0], b[0])
+        return m, a[1] * np.exp(a[0] - m) + b[1] * np.exp(b[0] - m)
+    p01 = pair((mx[0], se[0]), (mx[1], se[1]))
+    p23 = pair((mx[2], se[2]), (mx[3], se[3]))
+    t = pair(pair(p01, p23), (mx[4], se[4]))
+    e = max(e, _rel(t[0] + np.log(t[1]), full))
+    # each tile alone: mx_t + ln se_t is that tile's own logsumexp
+    for tt in range(T):
+        blk = torch.from_numpy(z[:, tt * 64:(tt + 1) * 64])
+        e = max(e, _rel(mx[tt] + np.log(se[tt]), torch.logsumexp(blk, dim=1).numpy()))
+    # a single tile is plain logsumexp; the identity pair changes nothing
+    m1, s1 = R.tile_lse(z, 300)
+    e = max(e, _rel(R.lse_merge(m1, s1), full))
+    mi = np.vstack([mx, np.full((1, 5), -np.inf)])
+    si = np.vstack([se, np.zeros((1, 5))])
+    e = max(e, _rel(R.lse_merge(mi, si), full))
+    return _ok(e, 1e-13, "lse merge order independence")
+
+
+def pin_partial_sumsq(seed=12):
+    rng = np.random.default_rng(seed)
+    h = rng.standard_normal((6, 200))
+    P = R.partial_sumsq(h, 64)  # 4 tiles, the last 8 wide
+    e = _rel(P.sum(axis=0), [math.fsum(v * v for v in row) for row in h])
+    e = max(e, _rel(P[3], [math.fsum(v * v for v in row[192:]) for row in h]))
+    return _ok(e, 1e-13, "partial sums of squares")
+
+
+# ---------------------------------------------------------------------------
+# fp8 block
+# ---------------------------------------------------------------------------
+
+def pin_fp8_block(seed=13):
+    """Brute force of the fp8 block on tiny inputs, with e4m3 codes picked at
+    random and values decoded from the format definition by hand here."""
+    rng = random.Random(seed)
+    M, K1, d, ffn, eps = 3, 4, 4, 5, 1e-5
+
+    def dec(c):  # E4M3FN value of a code, written out from the format
+        s = -1.0 if c & 0x80 else 1.0
+        e, m = (c >> 3) & 15, c & 7
+        return s * (m / 8 * 2.0 ** -6 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7))
+
+    finite = [c for c in range(256) if (c & 0x7F) != 0x7F and 0x30 <= (c & 0x7F) <= 0x48]
+    codes = lambda r, c: [[rng.choice(finite) for _ in range(c)] for _ in range(r)]
+    xq, woq, wgq, wuq = codes(M, K1), codes(d, K1), codes(ffn, d), codes(ffn, d)
+    sx, swo, swg, swu = 0.5, 0.25, 0.125, 0.375
+    res = _rand(rng, M, d)
+    val = lambda q, s: [[dec(c) * s for c in row] for row in q]
+    y = _bf_gemm_nt(val(xq, sx), val(woq, swo))
+    h = [[res[m][n] + y[m][n] for n in range(d)] for m in range(M)]
+    r = [1.0 / math.sqrt(math.fsum(v * v for v in h[m]) / d + eps) for m in range(M)]
+    amax = max(abs(v) for row in h for v in row)
+    s_h = amax / 448.0
+    # nearest E4M3 value (ties to even code) by search over all finite codes
+    grid = sorted({(dec(c), c) for c in range(256) if (c & 0x7F) != 0x7F})
+
+    def q8(v):
+        best = min(grid, key=lambda t: (abs(t[0] - v), t[1] & 1))
+        return best[0]
+    hh = [[q8(v / s_h) * s_h for v in row] for row in h]
+    g = _bf_gemm_nt(hh, val(wgq, swg))
+    u = _bf_gemm_nt(hh, val(wuq, swu))
+    out = [[_bf_silu(r[m] * g[m][j]) * r[m] * u[m][j] for j in range(ffn)] for m in range(M)]
+    o = oracle.fp8_mlp_block(np.array(xq, dtype=np.uint8), sx, np.array(res),
+                             np.array(woq, dtype=np.uint8), swo, np.array(wgq, dtype=np.uint8),
+                             swg, np.array(wuq, dtype=np.uint8), swu, eps)
+    return _ok(max(_rel(o["out"], out), _rel(o["h"], h), _rel(o["r"], r)), 1e-12,
+               "fp8 block brute force")
+
+
+ALL_PINS = [
+    pin_mlp_bruteforce, pin_mlp_exact_example, pin_rmsnorm_torch, pin_rms_closed_forms,
+    pin_unit_rms, pin_rowscale_commutes, pin_swiglu, pin_rope_closed_forms,
+    pin_rope_torch_complex, pin_rope_relative, pin_attn_bruteforce, pin_ce_bruteforce,
+    pin_ce_torch, pin_ce_zero_weights, pin_lse_merge, pin_partial_sumsq, pin_fp8_block,
+]
+
+
+def run_all():
+    """Run every pin; returns list of (name, ok, detail)."""
+    out = []
+    for p in ALL_PINS:
+        try:
+            ok, detail = p()
+        except Exception as e:  # a broken oracle may raise instead of erring
+            ok, detail = False, f"raised {type(e).__name__}: {e}"
+        out.append((p.__name__, ok, detail))
+    return out

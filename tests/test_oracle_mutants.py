@@ -1,0 +1,106 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that the pins
+catch every one of them.  Each mutant replaces one oracle function with a
+subtly wrong copy; at least one pin in tests/oracle_pins.py must then fail."""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import codecs, reference as R
+from tests import oracle_pins
+
+_ORIG_ROPE = R.apply_rope
+_ORIG_LM = R.lm_head_ce
+_ORIG_DEC = codecs.e4m3_decode
+
+
+def _mlp_block_no_gamma(x, res, wo, wg, wu, gamma, eps):
+    h = R.residual_add(R.gemm_nt(x, wo), res)
+    r = R.rms_scale(h, eps)
+    n = r[:, None] * h
+    g, u = R.gemm_nt(n, wg), R.gemm_nt(n, wu)
+    return {"h": h, "r": r, "g": g, "u": u, "out": R.swiglu(g, u)}
+
+
+def _mlp_block_swapped_gate(x, res, wo, wg, wu, gamma, eps):
+    h = R.residual_add(R.gemm_nt(x, wo), res)
+    r = R.rms_scale(h, eps)
+    n = (r[:, None] * h) * np.asarray(gamma)[None, :]
+    g, u = R.gemm_nt(n, wg), R.gemm_nt(n, wu)
+    return {"h": h, "r": r, "g": g, "u": u, "out": R.swiglu(u, g)}
+
+
+def _apply_rope_sign(y, pos, n_rot, hd, cos, sin):
+    return _ORIG_ROPE(y, pos, n_rot, hd, cos, -sin)
+
+
+def _apply_rope_interleaved(y, pos, n_rot, hd, cos, sin):
+    y = np.array(y, dtype=np.float64, copy=True)
+    c, s = cos[np.asarray(pos)], sin[np.asarray(pos)]
+    for hh in range(n_rot):
+        a = y[:, hh * hd:(hh + 1) * hd:2].copy()
+        b = y[:, hh * hd + 1:(hh + 1) * hd:2].copy()
+        y[:, hh * hd:(hh + 1) * hd:2] = a * c - b * s
+        y[:, hh * hd + 1:(hh + 1) * hd:2] = b * c + a * s
+    return y
+
+
+def _rope_tables_wrong_exponent(max_pos, hd, theta):
+    i = np.arange(hd // 2, dtype=np.float64)
+    ang = np.arange(max_pos, dtype=np.float64)[:, None] * (theta ** (-i / hd))[None, :]
+    return np.cos(ang), np.sin(ang)
+
+
+def _lse_merge_no_rescale(mx, se, order=None):
+    mx, se = np.asarray(mx), np.asarray(se)
+    M = np.max(mx, axis=0)
+    return M + np.log(np.sum(se, axis=0))
+
+
+def _lm_head_label_shift(x, wlm, labels, r=None, chunk=256):
+    V = np.asarray(wlm).shape[0]
+    return _ORIG_LM(x, wlm, (np.asarray(labels) + 1) % V, r=r, chunk=chunk)
+
+
+
+MUTANTS = {
+    "eps outside sqrt": ("rms_scale", lambda h, eps: 1.0 / np.sqrt(np.mean(np.asarray(h) ** 2, axis=1)) + eps),
+    "sum instead of mean": ("rms_scale", lambda h, eps: 1.0 / np.sqrt(np.sum(np.asarray(h) ** 2, axis=1) + eps)),
+    "residual dropped": ("residual_add", lambda y, res: np.asarray(y, dtype=np.float64)),
+    "residual subtracted": ("residual_add", lambda y, res: np.asarray(y) - np.asarray(res)),
+    "transposed weight": ("gemm_nt", lambda a, w: np.asarray(a, dtype=np.float64) @ np.asarray(w, dtype=np.float64)),
+    "silu sign": ("silu", lambda z: np.asarray(z) / (1.0 + np.exp(np.asarray(z)))),
+    "gamma dropped": ("mlp_block", _mlp_block_no_gamma),
+    "gate and up swapped": ("mlp_block", _mlp_block_swapped_gate),
+    "rope sign": ("apply_rope", _apply_rope_sign),
+    "rope interleaved pairs": ("apply_rope", _apply_rope_interleaved),
+    "rope exponent": ("rope_tables", _rope_tables_wrong_exponent),
+    "lse without max": ("logsumexp_rows", lambda z: np.log(np.sum(np.exp(np.asarray(z)), axis=1)) + 1e-3),
+    "merge without rescale": ("lse_merge", _lse_merge_no_rescale),
+    "label off by one": ("lm_head_ce", _lm_head_label_shift),
+    "abs instead of square": ("partial_sumsq", lambda h, w: np.stack([np.sum(np.abs(np.asarray(h)[:, t * w:(t + 1) * w]), axis=1) for t in range((np.asarray(h).shape[1] + w - 1) // w)])),
+}
+
+
+@pytest.mark.parametrize("name", list(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    fn_name, mutant = MUTANTS[name]
+    monkeypatch.setattr(R, fn_name, mutant)
+    if hasattr(oracle, fn_name):
+        monkeypatch.setattr(oracle, fn_name, mutant)
+    results = oracle_pins.run_all()
+    failed = [n for n, ok, _ in results if not ok]
+    assert failed, f"mutant '{name}' passed every pin"
+
+
+def test_e4m3_bias_mutant_is_caught(monkeypatch):
+    # exponent bias 8 instead of 7 halves every decoded value
+    wrong = lambda codes: _ORIG_DEC(codes) / 2.0
+    monkeypatch.setattr(codecs, "e4m3_decode", wrong)
+    results = oracle_pins.run_all()
+    assert any(not ok for _, ok, _ in results)
+
+
+def test_unmutated_oracle_passes_every_pin():
+    results = oracle_pins.run_all()
+    assert all(ok for _, ok, _ in results), [d for _, ok, d in results if not ok]
+
