@@ -1,0 +1,216 @@
+"""Benchmark of the fused GEMM-RMSNorm-GEMM + SwiGLU block on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+
+One step = one pass of the fused hot path over the LLaMA-3-1B-shaped MLP
+block (M = 8192 tokens, d = 2048, ffn = 8192, bf16, fp32 accumulate):
+GEMM1 (residual add + partial sums of squares) -> RMS reduce -> GEMM2 (row
+scale + SwiGLU).  Inputs are seeded synthetic tensors already resident in
+HBM; the RMSNorm gain is folded into the gate/up weights once, before timing
+(weight preparation, not per-token work).
+
+Prints ONE JSON line: fused-block TFLOP/s (the metric), the unfused GPU
+sequence timed the same way, the dominant kernel's roofline figure measured
+with HIP events on the launch stream, and the CPU oracle's throughput on a
+bounded row sample (a baseline only).
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA, 2.4 GHz
+WORKLOAD = "mlp_1b"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="approximate CPU time budget of the oracle baseline")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from gemm_epilogue_transformer_gemm1_amd import inputs, ops
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    w = inputs.make_workload(WORKLOAD)
+    M, d, K1, ffn = (w.sizes[k] for k in ("M", "d", "K1", "ffn"))
+    eps = 1e-5
+
+    def bf(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(
+            torch.bfloat16).to(dev)
+
+    x, res, w1 = bf(w.arrays["x"]), bf(w.arrays["res"]), bf(w.arrays["w1"])
+    wg, wu = bf(w.arrays["wg"]), bf(w.arrays["wu"])
+    gamma = torch.from_numpy(w.arrays["gamma"]).to(dev)
+    # weight preparation (untimed): fold gamma into gate / up weights
+    wg_f, wu_f = torch.empty_like(wg), torch.empty_like(wu)
+    ops.fold_gamma(wg, gamma, wg_f)
+    ops.fold_gamma(wu, gamma, wu_f)
+    wgu = torch.cat([wg, wu], 0).contiguous()  # unfused path: one GEMM for gate|up
+
+    T = ops.rms_tiles(d)
+    h = torch.empty(M, d, dtype=torch.bfloat16, device=dev)
+    P = torch.empty(T, M, dtype=torch.float32, device=dev)
+    r = torch.empty(M, dtype=torch.float32, device=dev)
+    out = torch.empty(M, ffn, dtype=torch.bfloat16, device=dev)
+    # unfused buffers
+    y_u, h_u, n_u = (torch.empty(M, d, dtype=torch.bfloat16, device=dev) for _ in range(3))
+    gu_u = torch.empty(M, 2 * ffn, dtype=torch.bfloat16, device=dev)
+    out_u = torch.empty(M, ffn, dtype=torch.bfloat16, device=dev)
+
+    stream = torch.cuda.current_stream()
+    flops_g1 = 2.0 * M * d * K1
+    flops_g2 = 2.0 * M * (2 * ffn) * d
+    flops = flops_g1 + flops_g2
+
+    def fused_step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        ops.gemm_residual_partialrms(x, w1, res, h, P)
+        if ev is not None:
+            ev[1].record(stream)
+        ops.rms_reduce(P, d, eps, r)
+        if ev is not None:
+            ev[2].record(stream)
+        ops.gemm_rowscale_swiglu(h, wg_f, wu_f, r, out)
+        if ev is not None:
+            ev[3].record(stream)
+
+    def unfused_step():
+        ops.gemm_bf16(x, w1, y_u)
+        ops.residual_add(y_u, res, h_u)
+        ops.rmsnorm(h_u, gamma, eps, n_u)
+        ops.gemm_bf16(n_u, wgu, gu_u)
+        ops.swiglu(gu_u, out_u)
+
+    def timed(step_fn, steps, per_kernel=False):
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start.record(stream)
+        for s in range(steps):
+            step_fn(evs[s]) if per_kernel else step_fn()
+        stop.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        total_ms = start.elapsed_time(stop)
+        per = None
+        if per_kernel:
+            per = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(3)] for e in evs])
+        return total_ms, wall, per
+
+    print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        fused_step()
+        unfused_step()
+    torch.cuda.synchronize()
+
+    print(f"[bench] timing {args.steps} fused steps", file=sys.stderr, flush=True)
+    # 1) whole-step throughput, no events between kernels
+    fused_ms, fused_wall, _ = timed(fused_step, args.steps)
+    # 2) per-kernel durations with events on the launch stream
+    _, _, per = timed(fused_step, args.steps, per_kernel=True)
+    print(f"[bench] timing {args.steps} unfused steps", file=sys.stderr, flush=True)
+    unfused_ms, _, _ = timed(unfused_step, args.steps)
+
+    ms_step = fused_ms / args.steps
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    unf_ms_step = unfused_ms / args.steps
+    unf_tflops = flops / (unf_ms_step * 1e-3) / 1e12
+    g1_ms, red_ms, g2_ms = (float(np.mean(per[:, i])) for i in range(3))
+    g2_tflops = flops_g2 / (g2_ms * 1e-3) / 1e12
+
+    cpu = None
+    if not args.no_cpu:
+        print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, eps, args.cpu_seconds)
+
+    line = {
+        "metric": "fused block TFLOP/s (GEMM1 residual+partial-RMS -> reduce -> GEMM2 "
+                  "row-scale+SwiGLU), LLaMA-1B-shaped MLP",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(0,1/d) weights, random init)",
+        "config": {"workload": "mlp_1b: M=8192 tokens (4x2048), d=2048, ffn=8192, "
+                               "gate/up with SwiGLU, eps=1e-5",
+                   "M": M, "d": d, "K1": K1, "ffn": ffn, "parallelism": "none (1 GPU)"},
+        "pct_of_mfma_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "unfused": {"ms_per_step": round(unf_ms_step, 4), "tflops": round(unf_tflops, 2),
+                    "speedup_fused_vs_unfused": round(unf_ms_step / ms_step, 3)},
+        "kernels_ms": {"gemm_residual_partialrms": round(g1_ms, 4),
+                       "rms_reduce": round(red_ms, 4),
+                       "gemm_rowscale_swiglu": round(g2_ms, 4)},
+        "roofline": {"kernel": "gemm_rowscale_swiglu", "bound": "mfma",
+                     "achieved": round(g2_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(g2_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(w, eps, budget_s):
+    """The CPU oracle (fp64, unfused) on a bounded row sample of the same
+    workload; TFLOP/s of the same algorithmic FLOP count."""
+    import oracle
+    from oracle import codecs
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"), default=1)
+    except Exception:  # pragma: no cover
+        threads = None
+    M, d, K1, ffn = (w.sizes[k] for k in ("M", "d", "K1", "ffn"))
+    W1 = codecs.bf16_decode(w.arrays["w1"])
+    Wg = codecs.bf16_decode(w.arrays["wg"])
+    Wu = codecs.bf16_decode(w.arrays["wu"])
+    g = w.arrays["gamma"].astype(np.float64)
+    rows = 128
+    elapsed, done = 0.0, 0
+    while True:
+        x = codecs.bf16_decode(w.arrays["x"][done:done + rows])
+        res = codecs.bf16_decode(w.arrays["res"][done:done + rows])
+        t0 = time.perf_counter()
+        oracle.mlp_block(x, res, W1, Wg, Wu, g, eps)
+        elapsed += time.perf_counter() - t0
+        done += x.shape[0]
+        if elapsed >= budget_s or done >= M:
+            break
+        rows = min(M - done, max(rows, int(rows * min(4.0, 0.5 * budget_s / max(elapsed, 1e-3)))))
+    flops = 2.0 * done * (d * K1 + 2 * ffn * d)
+    return {"value": round(flops / elapsed / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"first {done} of {M} token rows of mlp_1b (fp64 numpy, unfused), "
+                      f"{elapsed:.1f} s, host cores visible {len(os.sched_getaffinity(0))}"}
+
+
+if __name__ == "__main__":
+    main()

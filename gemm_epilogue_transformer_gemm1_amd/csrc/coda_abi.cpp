@@ -1,0 +1,237 @@
+// C ABI of libcoda (declared in include/coda.h): argument validation, the
+// gfx950 device check, and the launches.  Validation runs before any HIP
+// runtime call, so every argument error is reported without touching a GPU.
+// No C++ exception crosses the boundary.
+
+#include "../../include/coda.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "launch.hpp"
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+constexpr int kMaxDevices = 64;
+// 0 = unknown, 1 = gfx950, 2 = other / error
+std::atomic<int> g_arch_state[kMaxDevices];
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Elements of a matrix must stay below 2^30 so byte offsets fit the 32-bit
+// buffer addressing of the GEMM loads.
+bool small_enough(int64_t rows, int64_t cols) { return rows * cols < (int64_t(1) << 30); }
+
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return CODA_ERR_DEVICE;
+  if (dev >= kMaxDevices) return CODA_ERR_DEVICE;
+  int st = g_arch_state[dev].load(std::memory_order_acquire);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      st = 2;
+    } else {
+      st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    }
+    g_arch_state[dev].store(st, std::memory_order_release);
+  }
+  return st == 1 ? CODA_OK : CODA_ERR_DEVICE;
+}
+
+int launched(hipError_t e) { return e == hipSuccess ? CODA_OK : CODA_ERR_LAUNCH; }
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+int check_gemm_shape(int M, int N, int K, int kmul) {
+  if (M < 1 || N < 16 || K < 64) return CODA_ERR_SHAPE;
+  if (N % 16 != 0 || K % kmul != 0) return CODA_ERR_SHAPE;
+  if (!small_enough(M, K) || !small_enough(N, K) || !small_enough(M, N)) return CODA_ERR_SHAPE;
+  return CODA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int coda_abi_version(void) { return kAbiVersion; }
+
+const char* coda_status_string(int status) {
+  switch (status) {
+    case CODA_OK: return "ok";
+    case CODA_ERR_NULL: return "a required pointer is NULL";
+    case CODA_ERR_SHAPE: return "a size is out of range or not a required multiple";
+    case CODA_ERR_DTYPE: return "unknown or unsupported number format";
+    case CODA_ERR_ALIGN: return "a pointer is not aligned as required";
+    case CODA_ERR_DEVICE: return "current device is not gfx950 or cannot be queried";
+    case CODA_ERR_LAUNCH: return "the HIP runtime reported an error at launch";
+    default: return "unknown status";
+  }
+}
+
+int coda_rms_tile_width(void) { return coda::kRmsTileWidth; }
+int coda_rms_tiles(int N) { return N <= 0 ? 0 : (N + coda::kRmsTileWidth - 1) / coda::kRmsTileWidth; }
+int coda_lse_tile_width(void) { return coda::kLseTileWidth; }
+int coda_lse_tiles(int V) { return V <= 0 ? 0 : (V + coda::kLseTileWidth - 1) / coda::kLseTileWidth; }
+
+int coda_gemm_residual_partialrms(int dtype, const void* A, const void* W, const float* a_scale,
+                                  const float* w_scale, const void* residual, void* h,
+                                  float* partial_sumsq, const float* h8_scale, void* h8,
+                                  float* partial_amax, int M, int N, int K, void* stream) {
+  try {
+    if (dtype != CODA_BF16) return CODA_ERR_DTYPE;
+    if (!A || !W || !residual || !h || !partial_sumsq) return CODA_ERR_NULL;
+    if (a_scale || w_scale || h8_scale || h8 || partial_amax) return CODA_ERR_DTYPE;
+    if (int st = check_gemm_shape(M, N, K, 64)) return st;
+    if (!aligned(A, 16) || !aligned(W, 16) || !aligned(residual, 16) || !aligned(h, 16) ||
+        !aligned(partial_sumsq, 4))
+      return CODA_ERR_ALIGN;
+    if (int st = check_device()) return st;
+    return launched(coda::launch_residual_partialrms_bf16(
+        static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(W),
+        static_cast<const uint16_t*>(residual), static_cast<uint16_t*>(h), partial_sumsq, M, N, K,
+        as_stream(stream)));
+  } catch (...) {
+    return CODA_ERR_LAUNCH;
+  }
+}
+
+int coda_rms_reduce(const float* partial_sumsq, const float* partial_amax, int T, int M, int N,
+                    float eps, float* r, float* h_amax, float* h8_scale_out, void* stream) {
+  try {
+    if (!partial_sumsq || !r) return CODA_ERR_NULL;
+    if (partial_amax && (!h_amax || !h8_scale_out)) return CODA_ERR_NULL;
+    if (T < 1 || M < 1 || N < 1 || !(eps >= 0.f)) return CODA_ERR_SHAPE;
+    if (!small_enough(T, M)) return CODA_ERR_SHAPE;
+    if (!aligned(partial_sumsq, 4) || !aligned(r, 4) || (partial_amax && !aligned(partial_amax, 4)) ||
+        (h_amax && !aligned(h_amax, 4)) || (h8_scale_out && !aligned(h8_scale_out, 4)))
+      return CODA_ERR_ALIGN;
+    if (int st = check_device()) return st;
+    return launched(coda::launch_rms_reduce(partial_sumsq, partial_amax, T, M, N, eps, r,
+                                            partial_amax ? h_amax : nullptr,
+                                            partial_amax ? h8_scale_out : nullptr,
+                                            as_stream(stream)));
+  } catch (...) {
+    return CODA_ERR_LAUNCH;
+  }
+}
+
+int coda_gemm_rowscale_swiglu(int dtype, const void* X, const float* x_scale, const void* Wg,
+                              const void* Wu, const float* wg_scale, const float* wu_scale,
+                              const float* r, void* out, int M, int N, int K, void* stream) {
+  try {
+    if (dtype != CODA_BF16) return CODA_ERR_DTYPE;
+    if (!X || !Wg || !Wu || !r || !out) return CODA_ERR_NULL;
+    if (x_scale || wg_scale || wu_scale) return CODA_ERR_DTYPE;
+    if (int st = check_gemm_shape(M, N, K, 64)) return st;
+    if (!aligned(X, 16) || !aligned(Wg, 16) || !aligned(Wu, 16) || !aligned(out, 16) ||
+        !aligned(r, 4))
+      return CODA_ERR_ALIGN;
+    if (int st = check_device()) return st;
+    return launched(coda::launch_rowscale_swiglu_bf16(
+        static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(Wg),
+        static_cast<const uint16_t*>(Wu), r, static_cast<uint16_t*>(out), M, N, K,
+        as_stream(stream)));
+  } catch (...) {
+    return CODA_ERR_LAUNCH;
+  }
+}
+
+int coda_gemm_rope(const void* h, const void* Wqkv, const float* r, const float* rope_cos,
+                   const float* rope_sin, const int32_t* pos, int max_pos, void* qkv, int M, int K,
+                   int n_q_heads, int n_kv_heads, int head_dim, void* stream) {
+  (void)h; (void)Wqkv; (void)r; (void)rope_cos; (void)rope_sin; (void)pos; (void)max_pos;
+  (void)qkv; (void)M; (void)K; (void)n_q_heads; (void)n_kv_heads; (void)head_dim; (void)stream;
+  return CODA_ERR_DTYPE;
+}
+
+int coda_gemm_block_lse(const void* X, const void* W, const float* r, const int32_t* labels,
+                        float* tile_max, float* tile_sumexp, float* label_logit, float* lse,
+                        float* loss, int M, int V, int K, void* stream) {
+  (void)X; (void)W; (void)r; (void)labels; (void)tile_max; (void)tile_sumexp; (void)label_logit;
+  (void)lse; (void)loss; (void)M; (void)V; (void)K; (void)stream;
+  return CODA_ERR_DTYPE;
+}
+
+int coda_fold_gamma(const void* W, const float* gamma, void* W_out, int N, int K, void* stream) {
+  try {
+    if (!W || !gamma || !W_out) return CODA_ERR_NULL;
+    if (N < 1 || K < 8 || K % 8 != 0 || !small_enough(N, K)) return CODA_ERR_SHAPE;
+    if (!aligned(W, 16) || !aligned(W_out, 16) || !aligned(gamma, 4)) return CODA_ERR_ALIGN;
+    if (int st = check_device()) return st;
+    return launched(coda::launch_fold_gamma(static_cast<const uint16_t*>(W), gamma,
+                                            static_cast<uint16_t*>(W_out), N, K,
+                                            as_stream(stream)));
+  } catch (...) {
+    return CODA_ERR_LAUNCH;
+  }
+}
+
+int coda_rope_tables(double theta, int max_pos, int head_dim, float* rope_cos, float* rope_sin,
+                     void* stream) {
+  (void)theta; (void)max_pos; (void)head_dim; (void)rope_cos; (void)rope_sin; (void)stream;
+  return CODA_ERR_DTYPE;
+}
+
+int coda_gemm_bf16(const void* A, const void* W, void* C, int M, int N, int K, void* stream) {
+  try {
+    if (!A || !W || !C) return CODA_ERR_NULL;
+    if (int st = check_gemm_shape(M, N, K, 64)) return st;
+    if (!aligned(A, 16) || !aligned(W, 16) || !aligned(C, 16)) return CODA_ERR_ALIGN;
+    if (int st = check_device()) return st;
+    return launched(coda::launch_gemm_plain_bf16(static_cast<const uint16_t*>(A),
+                                                 static_cast<const uint16_t*>(W),
+                                                 static_cast<uint16_t*>(C), M, N, K,
+                                                 as_stream(stream)));
+  } catch (...) {
+    return CODA_ERR_LAUNCH;
+  }
+}
+
+int coda_residual_add(const void* y, const void* res, void* h, int64_t count, void* stream) {
+  try {
+    if (!y || !res || !h) return CODA_ERR_NULL;
+    if (count < 8 || count % 8 != 0) return CODA_ERR_SHAPE;
+    if (!aligned(y, 16) || !aligned(res, 16) || !aligned(h, 16)) return CODA_ERR_ALIGN;
+    if (int st = check_device()) return st;
+    return launched(coda::launch_residual_add(static_cast<const uint16_t*>(y),
+                                              static_cast<const uint16_t*>(res),
+                                              static_cast<uint16_t*>(h), count,
+                                              as_stream(stream)));
+  } catch (...) {
+    return CODA_ERR_LAUNCH;
+  }
+}
+
+int coda_rmsnorm(const void* h, const float* gamma, float eps, void* out, int M, int N,
+                 void* stream) {
+  try {
+    if (!h || !gamma || !out) return CODA_ERR_NULL;
+    if (M < 1 || N < 8 || N % 8 != 0 || N > 16384 || !(eps >= 0.f) || !small_enough(M, N))
+      return CODA_ERR_SHAPE;
+    if (!aligned(h, 16) || !aligned(out, 16) || !aligned(gamma, 4)) return CODA_ERR_ALIGN;
+    if (int st = check_device()) return st;
+    return launched(coda::launch_rmsnorm(static_cast<const uint16_t*>(h), gamma, eps,
+                                         static_cast<uint16_t*>(out), M, N, as_stream(stream)));
+  } catch (...) {
+    return CODA_ERR_LAUNCH;
+  }
+}
+
+int coda_swiglu(const void* gu, void* out, int M, int N, void* stream) {
+  try {
+    if (!gu || !out) return CODA_ERR_NULL;
+    if (M < 1 || N < 8 || N % 8 != 0 || !small_enough(M, 2 * (int64_t)N)) return CODA_ERR_SHAPE;
+    if (!aligned(gu, 16) || !aligned(out, 16)) return CODA_ERR_ALIGN;
+    if (int st = check_device()) return st;
+    return launched(coda::launch_swiglu(static_cast<const uint16_t*>(gu),
+                                        static_cast<uint16_t*>(out), M, N, as_stream(stream)));
+  } catch (...) {
+    return CODA_ERR_LAUNCH;
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,80 @@
+// Device helpers shared by the gfx950 kernels of libcoda.
+//
+// Citations name sections of the news page "CODA: New Research Optimizes
+// Transformer Training with GEMM-Epilogue Programming" (KuCoin news flash).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace coda {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Raw buffer resource over `bytes` bytes starting at `base` (gfx9 family
+// descriptor: stride 0, raw addressing).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// 16 bytes per lane from global memory straight into LDS.  The LDS
+// destination of lane L is lds_base + 16 * L (the wave writes 1 KiB
+// contiguously); the global source is rsrc + voffset + soffset.
+__device__ __forceinline__ void load16_to_lds(__amdgpu_buffer_rsrc_t rsrc, void* lds_base,
+                                              uint32_t voffset, uint32_t soffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)lds_base, 16, voffset, soffset, 0,
+                                           0);
+}
+
+__device__ __forceinline__ f32x4_t mfma16x16x32(const bf16x8_t& a, const bf16x8_t& b,
+                                                const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Round-to-nearest-even float -> bf16 bits for four values, packed in 8 bytes.
+__device__ __forceinline__ u32x2_t pack_bf16x4(float a, float b, float c, float d) {
+  bf16x4_t v = {(__bf16)a, (__bf16)b, (__bf16)c, (__bf16)d};
+  return __builtin_bit_cast(u32x2_t, v);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t bits) {
+  return __builtin_bit_cast(float, (uint32_t)bits << 16);
+}
+
+// Unpack 4 bf16 (8 bytes) to floats.
+__device__ __forceinline__ void unpack_bf16x4(u32x2_t v, float* f) {
+  f[0] = __builtin_bit_cast(float, v.x << 16);
+  f[1] = __builtin_bit_cast(float, v.x & 0xffff0000u);
+  f[2] = __builtin_bit_cast(float, v.y << 16);
+  f[3] = __builtin_bit_cast(float, v.y & 0xffff0000u);
+}
+
+// Sum over the four 16-lane groups of a wave (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float sum_over_lane_groups(float v) {
+  v += __shfl_xor(v, 16, 64);
+  v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+__device__ __forceinline__ float max_over_lane_groups(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16, 64));
+  v = fmaxf(v, __shfl_xor(v, 32, 64));
+  return v;
+}
+
+// silu(z) = z / (1 + e^-z), with the hardware exp and reciprocal; for very
+// negative z, e^-z = inf and the reciprocal gives 0.
+__device__ __forceinline__ float silu_f32(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
+
+}  // namespace coda

@@ -1,0 +1,171 @@
+// bf16 GEMM kernels with epilogue programs, on the mainloop of gemm_core.hpp.
+//
+// Citations name sections of the news page "CODA: New Research Optimizes
+// Transformer Training with GEMM-Epilogue Programming" (KuCoin news flash).
+//
+// Accumulator layout reminder (see gemm_core.hpp): lane L, register v of the
+// 16x16 tile (j, i) holds output feature  nbase + j*16 + 4*(L/16) + v  of
+// token  mbase + i*16 + L%16.  So each lane stores 4 consecutive features
+// (8 bytes of bf16) of one token, and a per-token sum over the wave's
+// features is a lane-local sum followed by one reduction over the 4 lane
+// groups.
+
+#include "gemm_core.hpp"
+#include "launch.hpp"
+
+namespace coda {
+
+// ---------------------------------------------------------------------------
+// GEMM1: residual add + partial sums of squares (section "CODA: the secret in
+// the epilogue": the first GEMM's epilogue computes only a partial RMS).
+// Output tile 256 tokens x 256 features; each wave's 128 features form one
+// partial tile, so T = ceil(N / 128).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads, 1) void k_residual_partialrms_bf16(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
+    const uint16_t* __restrict__ res, uint16_t* __restrict__ h, float* __restrict__ psum, int M,
+    int N, int K, int gm, int gn) {
+  __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
+  const TileCoord tc = map_tile(blockIdx.x, gm, gn, 8);
+  const int m0 = tc.tm * kBM, n0 = tc.tn * kBN;
+  MainloopSrc src{A, W, nullptr, M, N, K, m0, n0};
+  Acc acc;
+  mainloop_bf16<false>(acc, smem, src);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int nw0 = n0 + wn * 128;  // first feature of this wave = partial tile start
+  const int g4 = (lane >> 4) * 4;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int m = m0 + wm * 128 + i * 16 + (lane & 15);
+    const bool mv = m < M;
+    const size_t row = (size_t)min(m, M - 1) * (size_t)N;
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int n = nw0 + j * 16 + g4;
+      if (n < N) {
+        float rv[4];
+        unpack_bf16x4(*(const u32x2_t*)(res + row + n), rv);
+        float hv[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          hv[v] = acc.v[j][i][v] + rv[v];
+          ss += hv[v] * hv[v];
+        }
+        if (mv) *(u32x2_t*)(h + row + n) = pack_bf16x4(hv[0], hv[1], hv[2], hv[3]);
+      }
+    }
+    ss = sum_over_lane_groups(ss);
+    if (mv && lane < 16 && nw0 < N) psum[(size_t)(nw0 / kRmsTileWidth) * M + m] = ss;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// GEMM2: row scale + SwiGLU (section "CODA: the secret in the epilogue": the
+// row scale r commutes with the second GEMM and is applied at its end; SwiGLU
+// is re-parameterised the same way).  Output tile 256 tokens x 128 features:
+// the block's LDS weight tile holds 128 gate rows and the same 128 up rows.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads, 1) void k_rowscale_swiglu_bf16(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wg,
+    const uint16_t* __restrict__ Wu, const float* __restrict__ r, uint16_t* __restrict__ out,
+    int M, int N, int K, int gm, int gn) {
+  __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
+  const TileCoord tc = map_tile(blockIdx.x, gm, gn, 8);
+  const int m0 = tc.tm * kBM, n0 = tc.tn * (kBN / 2);
+  MainloopSrc src{X, Wg, Wu, M, N, K, m0, n0};
+  Acc acc;
+  mainloop_bf16<true>(acc, smem, src);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int nw0 = n0 + wn * 64;
+  const int g4 = (lane >> 4) * 4;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int m = m0 + wm * 128 + i * 16 + (lane & 15);
+    const bool mv = m < M;
+    const float rr = r[min(m, M - 1)];
+    const size_t row = (size_t)min(m, M - 1) * (size_t)N;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = nw0 + j * 16 + g4;
+      float o[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float g = acc.v[j][i][v] * rr;
+        const float u = acc.v[j + 4][i][v] * rr;
+        o[v] = silu_f32(g) * u;
+      }
+      if (mv && n < N) *(u32x2_t*)(out + row + n) = pack_bf16x4(o[0], o[1], o[2], o[3]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Plain GEMM (unfused baseline): the same mainloop, epilogue = convert + store.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads, 1) void k_gemm_plain_bf16(const uint16_t* __restrict__ A,
+                                                                 const uint16_t* __restrict__ W,
+                                                                 uint16_t* __restrict__ C, int M,
+                                                                 int N, int K, int gm, int gn) {
+  __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
+  const TileCoord tc = map_tile(blockIdx.x, gm, gn, 8);
+  const int m0 = tc.tm * kBM, n0 = tc.tn * kBN;
+  MainloopSrc src{A, W, nullptr, M, N, K, m0, n0};
+  Acc acc;
+  mainloop_bf16<false>(acc, smem, src);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int nw0 = n0 + wn * 128;
+  const int g4 = (lane >> 4) * 4;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int m = m0 + wm * 128 + i * 16 + (lane & 15);
+    if (m >= M) continue;
+    const size_t row = (size_t)m * (size_t)N;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int n = nw0 + j * 16 + g4;
+      if (n < N)
+        *(u32x2_t*)(C + row + n) =
+            pack_bf16x4(acc.v[j][i][0], acc.v[j][i][1], acc.v[j][i][2], acc.v[j][i][3]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+static inline int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+hipError_t launch_residual_partialrms_bf16(const uint16_t* A, const uint16_t* W,
+                                           const uint16_t* res, uint16_t* h, float* psum, int M,
+                                           int N, int K, hipStream_t stream) {
+  const int gm = cdiv(M, kBM), gn = cdiv(N, kBN);
+  hipLaunchKernelGGL(k_residual_partialrms_bf16, dim3(gm * gn), dim3(kThreads), 0, stream, A, W,
+                     res, h, psum, M, N, K, gm, gn);
+  return hipGetLastError();
+}
+
+hipError_t launch_rowscale_swiglu_bf16(const uint16_t* X, const uint16_t* Wg, const uint16_t* Wu,
+                                       const float* r, uint16_t* out, int M, int N, int K,
+                                       hipStream_t stream) {
+  const int gm = cdiv(M, kBM), gn = cdiv(N, kBN / 2);
+  hipLaunchKernelGGL(k_rowscale_swiglu_bf16, dim3(gm * gn), dim3(kThreads), 0, stream, X, Wg, Wu,
+                     r, out, M, N, K, gm, gn);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_plain_bf16(const uint16_t* A, const uint16_t* W, uint16_t* C, int M, int N,
+                                  int K, hipStream_t stream) {
+  const int gm = cdiv(M, kBM), gn = cdiv(N, kBN);
+  hipLaunchKernelGGL(k_gemm_plain_bf16, dim3(gm * gn), dim3(kThreads), 0, stream, A, W, C, M, N,
+                     K, gm, gn);
+  return hipGetLastError();
+}
+
+}  // namespace coda

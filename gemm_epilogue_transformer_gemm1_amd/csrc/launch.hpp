@@ -1,0 +1,33 @@
+// Internal launchers: called by the C ABI layer after it has validated every
+// argument.  Each enqueues its kernels on `stream` and returns the HIP status
+// of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace coda {
+
+constexpr int kRmsTileWidth = 128;  // features per partial sum-of-squares tile
+constexpr int kLseTileWidth = 128;  // vocabulary entries per log-sum-exp tile
+
+hipError_t launch_residual_partialrms_bf16(const uint16_t* A, const uint16_t* W,
+                                           const uint16_t* res, uint16_t* h, float* psum, int M,
+                                           int N, int K, hipStream_t stream);
+hipError_t launch_rowscale_swiglu_bf16(const uint16_t* X, const uint16_t* Wg, const uint16_t* Wu,
+                                       const float* r, uint16_t* out, int M, int N, int K,
+                                       hipStream_t stream);
+hipError_t launch_gemm_plain_bf16(const uint16_t* A, const uint16_t* W, uint16_t* C, int M, int N,
+                                  int K, hipStream_t stream);
+
+hipError_t launch_rms_reduce(const float* psum, const float* pamax, int T, int M, int N, float eps,
+                             float* r, float* h_amax, float* h8_scale_out, hipStream_t stream);
+hipError_t launch_fold_gamma(const uint16_t* W, const float* gamma, uint16_t* W_out, int N, int K,
+                             hipStream_t stream);
+hipError_t launch_residual_add(const uint16_t* y, const uint16_t* res, uint16_t* h, int64_t count,
+                               hipStream_t stream);
+hipError_t launch_rmsnorm(const uint16_t* h, const float* gamma, float eps, uint16_t* out, int M,
+                          int N, hipStream_t stream);
+hipError_t launch_swiglu(const uint16_t* gu, uint16_t* out, int M, int N, hipStream_t stream);
+
+}  // namespace coda

@@ -1,0 +1,200 @@
+// Light (bandwidth- or latency-bound) kernels: the RMS reduction between the
+// two GEMMs, weight preparation, and the unfused baseline's elementwise ops.
+//
+// Citations name sections of the news page "CODA: New Research Optimizes
+// Transformer Training with GEMM-Epilogue Programming" (KuCoin news flash).
+
+#include "coda_device.hpp"
+#include "launch.hpp"
+
+namespace coda {
+
+static inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+// ---------------------------------------------------------------------------
+// The light reduction (section "CODA: the secret in the epilogue": a light
+// reduction kernel aggregates the partial RMS values).  One thread per token
+// row; consecutive threads read consecutive rows of each partial tile, so
+// every load is coalesced.  Optionally a global amax over the partial amax
+// tiles (fp8 delayed scaling): one atomicMax per block on the non-negative
+// float's bit pattern, which orders like the float.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_rms_reduce(const float* __restrict__ psum,
+                                                    const float* __restrict__ pamax, int T, int M,
+                                                    float inv_n, float eps, float* __restrict__ r,
+                                                    unsigned int* __restrict__ amax_bits) {
+  const int m = blockIdx.x * 256 + threadIdx.x;
+  float mx = 0.f;
+  if (m < M) {
+    float s = 0.f;
+    for (int t = 0; t < T; ++t) s += psum[(size_t)t * M + m];
+    r[m] = 1.0f / sqrtf(s * inv_n + eps);
+    if (pamax)
+      for (int t = 0; t < T; ++t) mx = fmaxf(mx, pamax[(size_t)t * M + m]);
+  }
+  if (pamax) {
+    __shared__ float red[4];
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+      atomicMax(amax_bits, __float_as_uint(mx));
+    }
+  }
+}
+
+__global__ void k_zero_u32(unsigned int* p) { *p = 0u; }
+
+__global__ void k_amax_to_scale(const unsigned int* amax_bits, float* h_amax, float* scale_out) {
+  const float a = __uint_as_float(*amax_bits);
+  *h_amax = a;
+  *scale_out = a > 0.f ? a * (1.0f / 448.0f) : 1.0f;
+}
+
+hipError_t launch_rms_reduce(const float* psum, const float* pamax, int T, int M, int N, float eps,
+                             float* r, float* h_amax, float* h8_scale_out, hipStream_t stream) {
+  unsigned int* bits = reinterpret_cast<unsigned int*>(h_amax);
+  if (pamax) hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(1), 0, stream, bits);
+  hipLaunchKernelGGL(k_rms_reduce, dim3(cdiv(M, 256)), dim3(256), 0, stream, psum, pamax, T, M,
+                     1.0f / (float)N, eps, r, bits);
+  if (pamax)
+    hipLaunchKernelGGL(k_amax_to_scale, dim3(1), dim3(1), 0, stream, bits, h_amax, h8_scale_out);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Weight preparation: fold the RMSNorm gain (it lies along GEMM2's K axis)
+// into the weight columns, W'[n,k] = bf16(W[n,k] * gamma[k]).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_fold_gamma(const uint16_t* __restrict__ W,
+                                                    const float* __restrict__ gamma,
+                                                    uint16_t* __restrict__ out, int64_t total8,
+                                                    int K) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;  // group of 8 elements
+  if (idx >= total8) return;
+  const int64_t e = idx * 8;
+  const int k = (int)(e % K);
+  const i32x4_t raw = *(const i32x4_t*)(W + e);
+  const u32x2_t lo = {(unsigned)raw.x, (unsigned)raw.y}, hi = {(unsigned)raw.z, (unsigned)raw.w};
+  float f[8];
+  unpack_bf16x4(lo, f);
+  unpack_bf16x4(hi, f + 4);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) f[q] *= gamma[k + q];
+  const u32x2_t plo = pack_bf16x4(f[0], f[1], f[2], f[3]);
+  const u32x2_t phi = pack_bf16x4(f[4], f[5], f[6], f[7]);
+  *(i32x4_t*)(out + e) = i32x4_t{(int)plo.x, (int)plo.y, (int)phi.x, (int)phi.y};
+}
+
+hipError_t launch_fold_gamma(const uint16_t* W, const float* gamma, uint16_t* W_out, int N, int K,
+                             hipStream_t stream) {
+  const int64_t total8 = (int64_t)N * K / 8;
+  hipLaunchKernelGGL(k_fold_gamma, dim3(cdiv(total8, 256)), dim3(256), 0, stream, W, gamma, W_out,
+                     total8, K);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Unfused baseline ops: each reads its inputs from HBM and writes its output
+// back (section "The cost of laziness in large-model training": every
+// operator boundary is a write-back to GPU memory).  16 B per lane accesses.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void load8(const uint16_t* p, float* f) {
+  const i32x4_t raw = *(const i32x4_t*)p;
+  unpack_bf16x4(u32x2_t{(unsigned)raw.x, (unsigned)raw.y}, f);
+  unpack_bf16x4(u32x2_t{(unsigned)raw.z, (unsigned)raw.w}, f + 4);
+}
+
+__device__ __forceinline__ void store8(uint16_t* p, const float* f) {
+  const u32x2_t lo = pack_bf16x4(f[0], f[1], f[2], f[3]);
+  const u32x2_t hi = pack_bf16x4(f[4], f[5], f[6], f[7]);
+  *(i32x4_t*)p = i32x4_t{(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
+}
+
+__global__ __launch_bounds__(256) void k_residual_add(const uint16_t* __restrict__ y,
+                                                      const uint16_t* __restrict__ res,
+                                                      uint16_t* __restrict__ h, int64_t total8) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= total8) return;
+  float a[8], b[8];
+  load8(y + idx * 8, a);
+  load8(res + idx * 8, b);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) a[q] += b[q];
+  store8(h + idx * 8, a);
+}
+
+hipError_t launch_residual_add(const uint16_t* y, const uint16_t* res, uint16_t* h, int64_t count,
+                               hipStream_t stream) {
+  const int64_t total8 = count / 8;
+  hipLaunchKernelGGL(k_residual_add, dim3(cdiv(total8, 256)), dim3(256), 0, stream, y, res, h,
+                     total8);
+  return hipGetLastError();
+}
+
+// RMSNorm of one row per 256-thread block; each thread owns 8-element groups
+// strided by 256*8, kept in registers between the two passes (N <= 16384).
+constexpr int kNormMaxGroups = 8;
+__global__ __launch_bounds__(256) void k_rmsnorm(const uint16_t* __restrict__ h,
+                                                 const float* __restrict__ gamma, float eps,
+                                                 uint16_t* __restrict__ out, int N) {
+  const int m = blockIdx.x;
+  const uint16_t* row = h + (size_t)m * N;
+  float v[kNormMaxGroups][8];
+  float ss = 0.f;
+#pragma unroll
+  for (int g = 0; g < kNormMaxGroups; ++g) {
+    const int n = (g * 256 + threadIdx.x) * 8;
+    if (n < N) {
+      load8(row + n, v[g]);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) ss += v[g][q] * v[g][q];
+    }
+  }
+  __shared__ float red[4];
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = red[0] + red[1] + red[2] + red[3];
+  const float rr = 1.0f / sqrtf(tot / (float)N + eps);
+#pragma unroll
+  for (int g = 0; g < kNormMaxGroups; ++g) {
+    const int n = (g * 256 + threadIdx.x) * 8;
+    if (n < N) {
+      float o[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) o[q] = v[g][q] * rr * gamma[n + q];
+      store8(out + (size_t)m * N + n, o);
+    }
+  }
+}
+
+hipError_t launch_rmsnorm(const uint16_t* h, const float* gamma, float eps, uint16_t* out, int M,
+                          int N, hipStream_t stream) {
+  hipLaunchKernelGGL(k_rmsnorm, dim3(M), dim3(256), 0, stream, h, gamma, eps, out, N);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void k_swiglu(const uint16_t* __restrict__ gu,
+                                                uint16_t* __restrict__ out, int M, int N) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int n8 = N / 8;
+  if (idx >= (int64_t)M * n8) return;
+  const int64_t m = idx / n8;
+  const int n = (int)(idx - m * n8) * 8;
+  float g[8], u[8];
+  load8(gu + (size_t)m * 2 * N + n, g);
+  load8(gu + (size_t)m * 2 * N + N + n, u);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) g[q] = silu_f32(g[q]) * u[q];
+  store8(out + (size_t)m * N + n, g);
+}
+
+hipError_t launch_swiglu(const uint16_t* gu, uint16_t* out, int M, int N, hipStream_t stream) {
+  hipLaunchKernelGGL(k_swiglu, dim3(cdiv((int64_t)M * (N / 8), 256)), dim3(256), 0, stream, gu,
+                     out, M, N);
+  return hipGetLastError();
+}
+
+}  // namespace coda

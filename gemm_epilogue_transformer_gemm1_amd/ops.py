@@ -1,0 +1,220 @@
+"""Thin Python binding of libcoda's C ABI (include/coda.h).
+
+Argument marshalling only: each function takes torch device tensors, checks
+dtype / device / contiguity, and passes raw pointers plus the current torch
+stream to the C entry point of the same name.  Every computation runs in the
+library's HIP kernels; there is no fallback: if libcoda.so is missing or a
+call fails, a RuntimeError is raised.
+
+bf16 tensors are torch.bfloat16; e4m3 tensors are torch.uint8 (E4M3FN codes)
+or torch.float8_e4m3fn.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcoda.so")
+
+CODA_BF16 = 0
+CODA_FP8_E4M3 = 1
+
+_lib = None
+
+_c_int, _c_float, _c_double = ctypes.c_int, ctypes.c_float, ctypes.c_double
+_p, _i64 = ctypes.c_void_p, ctypes.c_int64
+
+_SIGNATURES = {
+    "coda_abi_version": ([], _c_int),
+    "coda_status_string": ([_c_int], ctypes.c_char_p),
+    "coda_rms_tile_width": ([], _c_int),
+    "coda_rms_tiles": ([_c_int], _c_int),
+    "coda_lse_tile_width": ([], _c_int),
+    "coda_lse_tiles": ([_c_int], _c_int),
+    "coda_gemm_residual_partialrms": ([_c_int, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
+                                       _c_int, _c_int, _c_int, _p], _c_int),
+    "coda_rms_reduce": ([_p, _p, _c_int, _c_int, _c_int, _c_float, _p, _p, _p, _p], _c_int),
+    "coda_gemm_rowscale_swiglu": ([_c_int, _p, _p, _p, _p, _p, _p, _p, _p, _c_int, _c_int,
+                                   _c_int, _p], _c_int),
+    "coda_gemm_rope": ([_p, _p, _p, _p, _p, _p, _c_int, _p, _c_int, _c_int, _c_int, _c_int,
+                        _c_int, _p], _c_int),
+    "coda_gemm_block_lse": ([_p, _p, _p, _p, _p, _p, _p, _p, _p, _c_int, _c_int, _c_int, _p],
+                            _c_int),
+    "coda_fold_gamma": ([_p, _p, _p, _c_int, _c_int, _p], _c_int),
+    "coda_rope_tables": ([_c_double, _c_int, _c_int, _p, _p, _p], _c_int),
+    "coda_gemm_bf16": ([_p, _p, _p, _c_int, _c_int, _c_int, _p], _c_int),
+    "coda_residual_add": ([_p, _p, _p, _i64, _p], _c_int),
+    "coda_rmsnorm": ([_p, _p, _c_float, _p, _c_int, _c_int, _p], _c_int),
+    "coda_swiglu": ([_p, _p, _c_int, _c_int, _p], _c_int),
+}
+
+
+class CodaError(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__(f"{fn} failed: {status} ({status_string(status)})")
+        self.status = status
+
+
+def lib():
+    """Load libcoda.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m gemm_epilogue_transformer_gemm1_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGNATURES.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = L
+    return _lib
+
+
+def status_string(status):
+    return lib().coda_status_string(status).decode()
+
+
+def _call(name, *args):
+    st = getattr(lib(), name)(*args)
+    if st != 0:
+        raise CodaError(name, st)
+
+
+def _ptr(t, dtype=None, what="tensor"):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{what} has dtype {t.dtype}, expected {dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+_BF16 = torch.bfloat16
+_F32 = torch.float32
+_I32 = torch.int32
+_E4M3 = (torch.uint8, torch.float8_e4m3fn)
+
+
+def rms_tile_width():
+    return lib().coda_rms_tile_width()
+
+
+def rms_tiles(N):
+    return lib().coda_rms_tiles(N)
+
+
+def lse_tile_width():
+    return lib().coda_lse_tile_width()
+
+
+def lse_tiles(V):
+    return lib().coda_lse_tiles(V)
+
+
+def gemm_residual_partialrms(A, W, residual, h, partial_sumsq, a_scale=None, w_scale=None,
+                             h8_scale=None, h8=None, partial_amax=None, stream=None):
+    """h = residual + A W^T (*scales); partial sums of squares of h per tile."""
+    fp8 = A.dtype in _E4M3
+    dt = CODA_FP8_E4M3 if fp8 else CODA_BF16
+    M, K = A.shape
+    N = W.shape[0]
+    _call("coda_gemm_residual_partialrms", dt,
+          _ptr(A, _E4M3 if fp8 else _BF16, "A"), _ptr(W, _E4M3 if fp8 else _BF16, "W"),
+          _ptr(a_scale, _F32, "a_scale"), _ptr(w_scale, _F32, "w_scale"),
+          _ptr(residual, _BF16, "residual"), _ptr(h, _BF16, "h"),
+          _ptr(partial_sumsq, _F32, "partial_sumsq"), _ptr(h8_scale, _F32, "h8_scale"),
+          _ptr(h8, _E4M3, "h8"), _ptr(partial_amax, _F32, "partial_amax"),
+          M, N, K, _stream(stream))
+
+
+def rms_reduce(partial_sumsq, N, eps, r, partial_amax=None, h_amax=None, h8_scale_out=None,
+               stream=None):
+    """r = 1/sqrt(sum_t partial / N + eps) per row (plus the fp8 amax)."""
+    T, M = partial_sumsq.shape
+    _call("coda_rms_reduce", _ptr(partial_sumsq, _F32, "partial_sumsq"),
+          _ptr(partial_amax, _F32, "partial_amax"), T, M, N, float(eps), _ptr(r, _F32, "r"),
+          _ptr(h_amax, _F32, "h_amax"), _ptr(h8_scale_out, _F32, "h8_scale_out"),
+          _stream(stream))
+
+
+def gemm_rowscale_swiglu(X, Wg, Wu, r, out, x_scale=None, wg_scale=None, wu_scale=None,
+                         stream=None):
+    """out = silu(r * X Wg^T) * (r * X Wu^T) (*scales)."""
+    fp8 = X.dtype in _E4M3
+    dt = CODA_FP8_E4M3 if fp8 else CODA_BF16
+    M, K = X.shape
+    N = Wg.shape[0]
+    wt = _E4M3 if fp8 else _BF16
+    _call("coda_gemm_rowscale_swiglu", dt, _ptr(X, wt, "X"), _ptr(x_scale, _F32, "x_scale"),
+          _ptr(Wg, wt, "Wg"), _ptr(Wu, wt, "Wu"), _ptr(wg_scale, _F32, "wg_scale"),
+          _ptr(wu_scale, _F32, "wu_scale"), _ptr(r, _F32, "r"), _ptr(out, _BF16, "out"),
+          M, N, K, _stream(stream))
+
+
+def gemm_rope(h, Wqkv, r, rope_cos, rope_sin, pos, qkv, n_q_heads, n_kv_heads, head_dim,
+              stream=None):
+    """qkv = RoPE(r * h Wqkv^T) on the q and k heads."""
+    M, K = h.shape
+    _call("coda_gemm_rope", _ptr(h, _BF16, "h"), _ptr(Wqkv, _BF16, "Wqkv"), _ptr(r, _F32, "r"),
+          _ptr(rope_cos, _F32, "rope_cos"), _ptr(rope_sin, _F32, "rope_sin"),
+          _ptr(pos, _I32, "pos"), rope_cos.shape[0], _ptr(qkv, _BF16, "qkv"), M, K,
+          n_q_heads, n_kv_heads, head_dim, _stream(stream))
+
+
+def gemm_block_lse(X, W, labels, tile_max, tile_sumexp, label_logit, loss, lse=None, r=None,
+                   stream=None):
+    """Per-row cross entropy of z = (r *) X W^T without storing z."""
+    M, K = X.shape
+    V = W.shape[0]
+    _call("coda_gemm_block_lse", _ptr(X, _BF16, "X"), _ptr(W, _BF16, "W"), _ptr(r, _F32, "r"),
+          _ptr(labels, _I32, "labels"), _ptr(tile_max, _F32, "tile_max"),
+          _ptr(tile_sumexp, _F32, "tile_sumexp"), _ptr(label_logit, _F32, "label_logit"),
+          _ptr(lse, _F32, "lse"), _ptr(loss, _F32, "loss"), M, V, K, _stream(stream))
+
+
+def fold_gamma(W, gamma, W_out, stream=None):
+    N, K = W.shape
+    _call("coda_fold_gamma", _ptr(W, _BF16, "W"), _ptr(gamma, _F32, "gamma"),
+          _ptr(W_out, _BF16, "W_out"), N, K, _stream(stream))
+
+
+def rope_tables(theta, max_pos, head_dim, rope_cos, rope_sin, stream=None):
+    _call("coda_rope_tables", float(theta), max_pos, head_dim, _ptr(rope_cos, _F32, "rope_cos"),
+          _ptr(rope_sin, _F32, "rope_sin"), _stream(stream))
+
+
+def gemm_bf16(A, W, C, stream=None):
+    M, K = A.shape
+    N = W.shape[0]
+    _call("coda_gemm_bf16", _ptr(A, _BF16, "A"), _ptr(W, _BF16, "W"), _ptr(C, _BF16, "C"),
+          M, N, K, _stream(stream))
+
+
+def residual_add(y, res, h, stream=None):
+    _call("coda_residual_add", _ptr(y, _BF16, "y"), _ptr(res, _BF16, "res"), _ptr(h, _BF16, "h"),
+          y.numel(), _stream(stream))
+
+
+def rmsnorm(h, gamma, eps, out, stream=None):
+    M, N = h.shape
+    _call("coda_rmsnorm", _ptr(h, _BF16, "h"), _ptr(gamma, _F32, "gamma"), float(eps),
+          _ptr(out, _BF16, "out"), M, N, _stream(stream))
+
+
+def swiglu(gu, out, stream=None):
+    M, N2 = gu.shape
+    _call("coda_swiglu", _ptr(gu, _BF16, "gu"), _ptr(out, _BF16, "out"), M, N2 // 2,
+          _stream(stream))

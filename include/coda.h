@@ -1,0 +1,210 @@
+/*
+ * coda.h -- C ABI of libcoda, the MI355X (gfx950) GEMM-epilogue hot path.
+ *
+ * Source of the method: the news page "CODA: New Research Optimizes
+ * Transformer Training with GEMM-Epilogue Programming" (KuCoin news flash,
+ * Vietnamese / Indonesian / Hindi editions).  Section "CODA: the secret in the
+ * epilogue" states the problem these calls solve: in the pattern GEMM ->
+ * residual add -> RMSNorm -> GEMM, the RMS row scale r is one scalar per row,
+ * so it commutes with the second GEMM and can be applied at the end of it; the
+ * first GEMM's epilogue then only needs partial RMS statistics, which a light
+ * reduction kernel combines, and the separate RMSNorm pass disappears.  The
+ * same re-parameterisation covers SwiGLU, RoPE and the cross-entropy loss.
+ * Section "Five building blocks and a LEGO language" lists the epilogue
+ * primitives used here: elementwise transforms (residual add, activation,
+ * RoPE), vector loads (per-row / per-column broadcasts), block reductions
+ * (local RMS, block log-sum-exp) and stateful max / sum-exp statistics.
+ *
+ * Conventions for every call below
+ *   - Matrices are row-major.  Weights are stored [N, K] (row n = output
+ *     feature n, K contiguous), so a linear layer computes X . W^T.
+ *   - bf16 tensors are passed as raw 16-bit patterns; e4m3 tensors are OCP
+ *     E4M3FN byte codes.  Accumulation is fp32.  Stores round to nearest even.
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *     library never allocates, frees or synchronises; each call enqueues its
+ *     kernels on `stream` (a hipStream_t; NULL = the default stream) and
+ *     returns.  Results are visible after the caller synchronises the stream.
+ *   - Return value: CODA_OK (0) or a negative coda_status.  Arguments are
+ *     validated BEFORE any HIP runtime call, so a bad argument never launches
+ *     anything.  Data-dependent problems (NaN / Inf inputs, labels outside
+ *     [0, V)) are not detected: they propagate as NaN / garbage into the
+ *     affected rows only.
+ *   - Matrix pointers must be 16-byte aligned, float / int vectors 4-byte
+ *     aligned.  Outputs must not alias inputs.
+ *   - Calls keep no global mutable state and are thread-safe; calls on
+ *     different streams may overlap.
+ */
+#ifndef CODA_H
+#define CODA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CODA_OK = 0,
+  CODA_ERR_NULL = -1,    /* a required pointer is NULL */
+  CODA_ERR_SHAPE = -2,   /* a size is out of range or not a required multiple */
+  CODA_ERR_DTYPE = -3,   /* unknown or unsupported number format */
+  CODA_ERR_ALIGN = -4,   /* a pointer is not aligned as required */
+  CODA_ERR_DEVICE = -5,  /* current device is not gfx950 or cannot be queried */
+  CODA_ERR_LAUNCH = -6   /* the HIP runtime reported an error at launch */
+} coda_status;
+
+typedef enum {
+  CODA_BF16 = 0,     /* bfloat16 operands */
+  CODA_FP8_E4M3 = 1  /* OCP E4M3FN operands with one fp32 scale per tensor */
+} coda_dtype;
+
+/* Library version of this ABI (increases on incompatible change). */
+int coda_abi_version(void);
+
+/* Static description of a status code (never NULL). */
+const char* coda_status_string(int status);
+
+/* Width, in output features, of one partial sum-of-squares tile. */
+int coda_rms_tile_width(void);
+/* T = number of partial sum-of-squares tiles per row for N features. */
+int coda_rms_tiles(int N);
+/* Width, in vocabulary entries, of one log-sum-exp tile. */
+int coda_lse_tile_width(void);
+/* T_v = number of log-sum-exp tiles per row for a vocabulary of V. */
+int coda_lse_tiles(int V);
+
+/*
+ * GEMM1 with the residual / partial-RMS epilogue.
+ * Page section "CODA: the secret in the epilogue" (first GEMM of
+ * GEMM-RMSNorm-GEMM computes only a partial RMS in its epilogue) and section
+ * "Five building blocks and a LEGO language" (elementwise residual add; block
+ * reduction "local RMS").
+ *
+ *   h[m,n]            = residual[m,n] + (A[m,:] . W[n,:]) * sa * sw   (stored bf16)
+ *   partial_sumsq[t*M+m] = sum over n in tile t of h[m,n]^2, from the fp32
+ *                        value before rounding; tile t covers features
+ *                        [t*w, t*w+w), w = coda_rms_tile_width()
+ * bf16:  A [M,K] bf16, W [N,K] bf16; a_scale, w_scale, h8_scale, h8 and
+ *        partial_amax must be NULL (sa = sw = 1).
+ * fp8:   A [M,K] e4m3, W [N,K] e4m3, *a_scale / *w_scale their fp32 scales
+ *        (device scalars).  Additionally, if h8 != NULL:
+ *          h8[m,n] = E4M3(h[m,n] / *h8_scale), rounded to nearest even and
+ *                    saturated to +-448 (h8_scale: device scalar, typically the
+ *                    h8_scale_out of the previous coda_rms_reduce -- delayed
+ *                    scaling), and, if partial_amax != NULL,
+ *          partial_amax[t*M+m] = max over n in tile t of |h[m,n]|.
+ * residual, h: [M,N] bf16.  partial_sumsq: [T,M] fp32, T = coda_rms_tiles(N).
+ * Sizes: M >= 1; N >= 16, N % 16 == 0; K >= 64, K % 64 == 0 (fp8: K % 128);
+ *        M*K, N*K, M*N element counts below 2^30.
+ */
+int coda_gemm_residual_partialrms(int dtype, const void* A, const void* W,
+                                  const float* a_scale, const float* w_scale,
+                                  const void* residual, void* h, float* partial_sumsq,
+                                  const float* h8_scale, void* h8, float* partial_amax,
+                                  int M, int N, int K, void* stream);
+
+/*
+ * The light reduction kernel that combines the partial RMS statistics
+ * (page section "CODA: the secret in the epilogue").
+ *   r[m] = 1 / sqrt( (sum_t partial_sumsq[t*M+m]) / N + eps )
+ * If partial_amax != NULL (fp8 path), also
+ *   *h_amax       = max over all t, m of partial_amax[t*M+m]
+ *   *h8_scale_out = *h_amax / 448            (both device scalars; required)
+ * partial_sumsq: [T,M] fp32 as written by coda_gemm_residual_partialrms.
+ * Sizes: T >= 1, M >= 1, N >= 1; eps >= 0.
+ */
+int coda_rms_reduce(const float* partial_sumsq, const float* partial_amax, int T, int M, int N,
+                    float eps, float* r, float* h_amax, float* h8_scale_out, void* stream);
+
+/*
+ * GEMM2 with the row-scale + SwiGLU epilogue (page section "CODA: the secret
+ * in the epilogue": r moved from before the second GEMM to its end; SwiGLU
+ * re-parameterised the same way).  The RMSNorm gain gamma is folded into the
+ * weights' columns beforehand (coda_fold_gamma), since it lies along K.
+ *   g[m,n] = r[m] * (X[m,:] . Wg[n,:]) * sx * sg
+ *   u[m,n] = r[m] * (X[m,:] . Wu[n,:]) * sx * su
+ *   out[m,n] = silu(g) * u,  silu(z) = z / (1 + e^-z)      (stored bf16)
+ * g and u are never stored.
+ * bf16: X [M,K] bf16 (the stored h), Wg, Wu [N,K] bf16; scales NULL.
+ * fp8:  X [M,K] e4m3 (h8), Wg, Wu e4m3; x_scale, wg_scale, wu_scale device
+ *       fp32 scalars (x_scale = the h8_scale used to write X).
+ * r: [M] fp32.  out: [M,N] bf16.
+ * Sizes: M >= 1; N >= 16, N % 16 == 0; K >= 64, K % 64 == 0 (fp8: K % 128).
+ */
+int coda_gemm_rowscale_swiglu(int dtype, const void* X, const float* x_scale, const void* Wg,
+                              const void* Wu, const float* wg_scale, const float* wu_scale,
+                              const float* r, void* out, int M, int N, int K, void* stream);
+
+/*
+ * QKV GEMM with the row-scale + RoPE epilogue (page section "CODA: the
+ * secret in the epilogue": RoPE re-parameterised into the epilogue; section
+ * "Five building blocks and a LEGO language": RoPE as an elementwise
+ * transform).
+ *   y[m,c]   = r[m] * (h[m,:] . Wqkv[c,:]),  c in [0, (nq + 2 nkv) * hd)
+ *   columns are q heads | k heads | v heads, hd columns per head;
+ *   for every q and k head and i < hd/2 (rotate-half pairs (i, i + hd/2)),
+ *   with p = pos[m], c = rope_cos[p*(hd/2) + i], s = rope_sin[p*(hd/2) + i]:
+ *     qkv[.., i]        = y_i c - y_{i+hd/2} s
+ *     qkv[.., i + hd/2] = y_{i+hd/2} c + y_i s
+ *   v heads are stored unrotated.                           (stored bf16)
+ * h [M,K] bf16, Wqkv [(nq+2nkv)hd, K] bf16 (gamma folded in), r [M] fp32,
+ * rope_cos / rope_sin [max_pos, hd/2] fp32 (coda_rope_tables), pos [M] int32
+ * in [0, max_pos) (not checked), qkv [M, (nq+2nkv)hd] bf16.
+ * Sizes: head_dim == 64; nq, nkv >= 1; K % 64 == 0; M >= 1.
+ */
+int coda_gemm_rope(const void* h, const void* Wqkv, const float* r, const float* rope_cos,
+                   const float* rope_sin, const int32_t* pos, int max_pos, void* qkv, int M,
+                   int K, int n_q_heads, int n_kv_heads, int head_dim, void* stream);
+
+/*
+ * LM-head GEMM with the block log-sum-exp epilogue and the merge (page
+ * section "CODA: the secret in the epilogue": cross-entropy re-parameterised;
+ * section "Five building blocks and a LEGO language": block log-sum-exp
+ * reduction and the running max / sum-exp statistics).
+ *   z[m,v] = r[m] * (X[m,:] . W[v,:])   (r == NULL means r = 1); z never stored
+ *   per tile t of w = coda_lse_tile_width() vocabulary entries:
+ *     tile_max[t*M+m]    = max over v in tile of z[m,v]
+ *     tile_sumexp[t*M+m] = sum over v in tile of exp(z[m,v] - tile_max)
+ *   label_logit[m] = z[m, labels[m]], from the fp32 accumulator
+ *   lse[m]  = M_m + ln sum_t tile_sumexp * exp(tile_max - M_m), M_m = max_t tile_max
+ *   loss[m] = lse[m] - label_logit[m]        (natural log, one value per row)
+ * X [M,K] bf16, W [V,K] bf16, labels [M] int32 in [0,V) (not checked),
+ * tile_max, tile_sumexp [T_v, M] fp32 workspace (T_v = coda_lse_tiles(V)),
+ * label_logit, loss [M] fp32, lse [M] fp32 or NULL.
+ * Sizes: M >= 1; V >= 16, V % 16 == 0; K % 64 == 0.
+ */
+int coda_gemm_block_lse(const void* X, const void* W, const float* r, const int32_t* labels,
+                        float* tile_max, float* tile_sumexp, float* label_logit, float* lse,
+                        float* loss, int M, int V, int K, void* stream);
+
+/* ---- weight preparation (run once per weight update, not per token) ---- */
+
+/* W_out[n,k] = bf16( W[n,k] * gamma[k] ): folds the RMSNorm gain, which lies
+ * along GEMM2's K axis, into the weight columns.  W, W_out [N,K] bf16,
+ * gamma [K] fp32.  Sizes: N, K >= 1, K % 8 == 0. */
+int coda_fold_gamma(const void* W, const float* gamma, void* W_out, int N, int K, void* stream);
+
+/* rope_cos/rope_sin[p*(hd/2)+i] = cos/sin(p * theta^(-2i/hd)), angles and
+ * trigonometry in fp64, stored fp32.  Sizes: max_pos >= 1, head_dim even. */
+int coda_rope_tables(double theta, int max_pos, int head_dim, float* rope_cos, float* rope_sin,
+                     void* stream);
+
+/* ---- the unfused sequence: one HBM round trip per op (speed baseline) ---- */
+
+/* C[m,n] = bf16( A[m,:] . W[n,:] ) -- the same mainloop, plain store.
+ * Sizes as coda_gemm_residual_partialrms (bf16). */
+int coda_gemm_bf16(const void* A, const void* W, void* C, int M, int N, int K, void* stream);
+/* h = bf16(y + res), all [count] bf16; count % 8 == 0. */
+int coda_residual_add(const void* y, const void* res, void* h, int64_t count, void* stream);
+/* out[m,n] = bf16( h[m,n] * r_m * gamma[n] ), r_m = 1/sqrt(mean_n h^2 + eps).
+ * h, out [M,N] bf16; gamma [N] fp32; N % 8 == 0. */
+int coda_rmsnorm(const void* h, const float* gamma, float eps, void* out, int M, int N,
+                 void* stream);
+/* out[m,n] = bf16( silu(gu[m,n]) * gu[m,N+n] ); gu [M,2N], out [M,N] bf16; N % 8 == 0. */
+int coda_swiglu(const void* gu, void* out, int M, int N, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CODA_H */

@@ -1,0 +1,99 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/coda.h declares, and rejects bad arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from gemm_epilogue_transformer_gemm1_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "coda.h")
+
+ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_ALIGN, ERR_DEVICE = -1, -2, -3, -4, -5
+A16 = 0x10000  # a fake 16-byte-aligned address, never dereferenced by these calls
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(coda_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(ops.LIB_PATH):
+        pytest.skip("libcoda.so not built")
+    return ops.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert len(names) >= 17
+    raw = ctypes.CDLL(ops.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+        assert n in ops._SIGNATURES, f"binding lacks {n}"
+
+
+def test_version_status_and_tiles(L):
+    assert L.coda_abi_version() >= 1
+    for s in (0, -1, -2, -3, -4, -5, -6, -99):
+        assert len(ops.status_string(s)) > 0
+    w = L.coda_rms_tile_width()
+    assert w in (64, 128, 256)
+    assert L.coda_rms_tiles(2048) == 2048 // w
+    assert L.coda_rms_tiles(2048 + 16) == 2048 // w + 1
+    assert L.coda_rms_tiles(0) == 0
+    v = L.coda_lse_tile_width()
+    assert L.coda_lse_tiles(128256) == (128256 + v - 1) // v
+
+
+def test_gemm1_validation(L):
+    f = L.coda_gemm_residual_partialrms
+    ok = dict(dtype=0, A=A16, W=A16, sa=None, sw=None, res=A16, h=A16, P=A16, s8=None,
+              h8=None, am=None, M=64, N=256, K=256, st=None)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["dtype"], a["A"], a["W"], a["sa"], a["sw"], a["res"], a["h"], a["P"],
+                 a["s8"], a["h8"], a["am"], a["M"], a["N"], a["K"], a["st"])
+    assert call(A=None) == ERR_NULL
+    assert call(P=None) == ERR_NULL
+    assert call(dtype=7) == ERR_DTYPE
+    assert call(sa=A16) == ERR_DTYPE          # scales only belong to the fp8 form
+    assert call(M=0) == ERR_SHAPE
+    assert call(N=8) == ERR_SHAPE
+    assert call(N=264) == ERR_SHAPE            # N % 16
+    assert call(K=96) == ERR_SHAPE             # K % 64
+    assert call(K=32) == ERR_SHAPE
+    assert call(M=1 << 20, K=2048) == ERR_SHAPE  # element count limit
+    assert call(A=A16 + 8) == ERR_ALIGN
+    assert call(P=A16 + 2) == ERR_ALIGN
+
+
+def test_other_validation(L):
+    assert L.coda_rms_reduce(None, None, 2, 8, 8, 1e-5, A16, None, None, None) == ERR_NULL
+    assert L.coda_rms_reduce(A16, None, 0, 8, 8, 1e-5, A16, None, None, None) == ERR_SHAPE
+    assert L.coda_rms_reduce(A16, None, 2, 8, 8, -1.0, A16, None, None, None) == ERR_SHAPE
+    assert L.coda_rms_reduce(A16, A16, 2, 8, 8, 1e-5, A16, None, None, None) == ERR_NULL
+    f = L.coda_gemm_rowscale_swiglu
+    assert f(0, A16, None, A16, None, None, None, A16, A16, 64, 64, 64, None) == ERR_NULL
+    assert f(0, A16, None, A16, A16, None, None, A16, A16, 64, 65, 64, None) == ERR_SHAPE
+    assert f(0, A16, A16, A16, A16, None, None, A16, A16, 64, 64, 64, None) == ERR_DTYPE
+    assert f(0, A16, None, A16, A16 + 4, None, None, A16, A16, 64, 64, 64, None) == ERR_ALIGN
+    assert L.coda_fold_gamma(A16, A16, A16, 4, 12, None) == ERR_SHAPE
+    assert L.coda_gemm_bf16(A16, A16, None, 64, 64, 64, None) == ERR_NULL
+    assert L.coda_residual_add(A16, A16, A16, 12, None) == ERR_SHAPE
+    assert L.coda_rmsnorm(A16, A16, 1e-5, A16, 4, 32768, None) == ERR_SHAPE
+    assert L.coda_swiglu(A16, A16 + 8, 4, 64, None) == ERR_ALIGN
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="would launch on fake pointers")
+def test_valid_arguments_without_gpu_report_device_error(L):
+    # With every argument valid, the next step is the device check, which
+    # fails cleanly on a machine without a gfx950 GPU.
+    st = L.coda_gemm_bf16(A16, A16, A16, 64, 64, 64, None)
+    assert st == ERR_DEVICE
