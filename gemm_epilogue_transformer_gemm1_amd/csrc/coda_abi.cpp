@@ -3,7 +3,7 @@
 // runtime call, so every argument error is reported without touching a GPU.
 // No C++ exception crosses the boundary.
 
-#include "../../include/coda.h"
+#include "coda.h"
 
 #include <hip/hip_runtime.h>
 

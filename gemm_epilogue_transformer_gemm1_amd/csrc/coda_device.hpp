@@ -40,6 +40,13 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(const bf16x8_t& a, const bf16x8_
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// In-place accumulate with the accumulator pinned to AGPRs (tied operand), so
+// the register allocator cannot rename accumulators across loop iterations.
+__device__ __forceinline__ void mfma16x16x32_acc(f32x4_t& c, const bf16x8_t& a,
+                                                 const bf16x8_t& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+
 // Round-to-nearest-even float -> bf16 bits for four values, packed in 8 bytes.
 __device__ __forceinline__ u32x2_t pack_bf16x4(float a, float b, float c, float d) {
   bf16x4_t v = {(__bf16)a, (__bf16)b, (__bf16)c, (__bf16)d};

@@ -20,6 +20,8 @@
 //     256 fp32 accumulators per lane.
 #pragma once
 
+#include <type_traits>
+
 #include "coda_device.hpp"
 
 namespace coda {
@@ -119,7 +121,7 @@ __device__ __forceinline__ void mfma_rows(Acc& acc, const Frags& f) {
 
 // Scheduling masks of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedMfma = 0x008;
-constexpr int kSchedVmemRead = 0x020;
+constexpr int kSchedVmem = 0x010;
 constexpr int kSchedDsRead = 0x100;
 
 template <bool kGated>
@@ -150,7 +152,7 @@ __device__ __forceinline__ void mainloop_bf16(Acc& acc, char* smem, const Mainlo
   char* x_lds_wave = smem + wave * 64 * kRowBytes;
   char* w_lds_wave = smem + kXBytes + wave * 64 * kRowBytes;
 
-  auto issue_stage = [&](int stage, int kt) {
+  auto issue_stage = [&](int stage, int kt) {  // prologue only
     const uint32_t soff = (uint32_t)kt * kRowBytes;
     char* xs = x_lds_wave + stage * kStageBytes;
     char* ws = w_lds_wave + stage * kStageBytes;
@@ -178,61 +180,113 @@ __device__ __forceinline__ void mainloop_bf16(Acc& acc, char* smem, const Mainlo
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc.v[j][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // Software pipeline, per stage kt (two k32 steps, fragment sets fa / fb):
-  //   [fa = step 0 of kt already in registers]
-  //   R1: loads of stage kt+1 -> LDS, fb <- step 1 of kt, MFMAs on fa
-  //   R2: first half of the MFMAs on fb
-  //   wait for this wave's loads, barrier (stage kt+1 complete everywhere and
-  //   nobody reads stage kt any more)
-  //   R3: fa <- step 0 of kt+1, second half of the MFMAs on fb
+  // Software pipeline over stages kt (two k32 steps each; fragment register
+  // sets fa / fb; LDS stages alternate, stage kt lives in slot kt & 1):
+  //   [fa = step 0 of kt already in registers; slot kt&1 holds kt, the other
+  //    slot is receiving kt+1]
+  //   R1: 16 x {one fb fragment read (step 1 of kt), 4 MFMAs on fa}
+  //   B1: barrier -- every wave has its step-1 fragments, so slot kt&1 is free
+  //   R2: 16 x {one 1 KiB load of stage kt+2 into slot kt&1, 2 MFMAs on fb}
+  //   B2: wait for this wave's stage kt+1 loads only (those of kt+2 stay in
+  //       flight), barrier (stage kt+1 complete everywhere)
+  //   R3: 16 x {one fa fragment read (step 0 of kt+1), 2 MFMAs on fb}
+  // A stage's loads are therefore issued about one and a half stages of MFMA
+  // work before they are needed.  Every group is fenced with
+  // sched_barrier(0) so the compiler keeps this interleaving; the barriers are
+  // plain s_barrier (no release fence, which would also drain the loads still
+  // in flight) after the explicit LDS-read wait they need.
   const int nk = s.K / kBK;
   Frags fa, fb;
   issue_stage(0, 0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  if (nk > 1) {
+    issue_stage(1, 1);
+    __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt(16): stage 0 landed
+  } else {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  }
   __syncthreads();
   read_frags<kGated>(fa, smem, xfrag[0], wfrag[0]);
 
-  for (int kt = 0; kt < nk - 1; ++kt) {
+  auto stage = [&](int kt, auto load_tag, auto next_tag) {
+    constexpr bool load2 = decltype(load_tag)::value;  // stage kt+2 exists
+    constexpr bool next = decltype(next_tag)::value;   // stage kt+1 exists
     const int cur = kt & 1;
     const char* base = smem + cur * kStageBytes;
+    const char* nbase = smem + (cur ^ 1) * kStageBytes;
+    const uint32_t soff = (uint32_t)(kt + 2) * kRowBytes;
+    char* xs = x_lds_wave + cur * kStageBytes;
+    char* ws = w_lds_wave + cur * kStageBytes;
     __builtin_amdgcn_sched_barrier(0);
-    issue_stage(cur ^ 1, kt + 1);
-    read_frags<kGated>(fb, base, xfrag[1], wfrag[1]);
-    mfma_rows<0, 8>(acc, fa);
+    // R1
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
-      __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
+      if (q < 8)
+        fb.a[q] = *(const bf16x8_t*)(base + xfrag[1] + q * 16 * kRowBytes);
+      else
+        fb.b[q - 8] =
+            *(const bf16x8_t*)(base + wfrag[1] + wrow_of_subtile<kGated>(q - 8) * kRowBytes);
+      const int j = q >> 1, i0 = (q & 1) * 4;
+#pragma unroll
+      for (int i = i0; i < i0 + 4; ++i) mfma16x16x32_acc(acc.v[j][i], fa.b[j], fa.a[i]);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_rows<0, 4>(acc, fb);
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stage kt+1 loads landed
-    __syncthreads();
-    __builtin_amdgcn_sched_barrier(0);
-    read_frags<kGated>(fa, smem + (cur ^ 1) * kStageBytes, xfrag[0], wfrag[0]);
-    mfma_rows<4, 8>(acc, fb);
+    // B1
+    if constexpr (load2) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): own step-1 reads done
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_s_barrier();
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // R2
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+      if constexpr (load2) {
+        if (q < 8)
+          load16_to_lds(xr, xs + q * 8 * kRowBytes, xoff[q], soff);
+        else
+          load16_to_lds(wr, ws + (q - 8) * 8 * kRowBytes, woff[q - 8], soff);
+      }
+      const int j = q >> 2, i0 = (q & 3) * 2;
+#pragma unroll
+      for (int i = i0; i < i0 + 2; ++i) mfma16x16x32_acc(acc.v[j][i], fb.b[j], fb.a[i]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // B2
+    if constexpr (next) {
+      if constexpr (load2)
+        __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt(16): stage kt+1 landed, kt+2 in flight
+      else
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_s_barrier();
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
     }
     __builtin_amdgcn_sched_barrier(0);
-  }
-  {  // last stage: no further loads
-    const char* base = smem + ((nk - 1) & 1) * kStageBytes;
-    read_frags<kGated>(fb, base, xfrag[1], wfrag[1]);
-    mfma_rows<0, 8>(acc, fa);
+    // R3
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
+      if constexpr (next) {
+        if (q < 8)
+          fa.a[q] = *(const bf16x8_t*)(nbase + xfrag[0] + q * 16 * kRowBytes);
+        else
+          fa.b[q - 8] =
+              *(const bf16x8_t*)(nbase + wfrag[0] + wrow_of_subtile<kGated>(q - 8) * kRowBytes);
+      }
+      const int j = 4 + (q >> 2), i0 = (q & 3) * 2;
+#pragma unroll
+      for (int i = i0; i < i0 + 2; ++i) mfma16x16x32_acc(acc.v[j][i], fb.b[j], fb.a[i]);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_rows<0, 8>(acc, fb);
-    __builtin_amdgcn_sched_barrier(0);
-  }
+  };
+  for (int kt = 0; kt < nk - 2; ++kt) stage(kt, std::true_type{}, std::true_type{});
+  if (nk >= 2) stage(nk - 2, std::false_type{}, std::true_type{});
+  stage(nk - 1, std::false_type{}, std::false_type{});
+  // The MFMAs are inline asm, so the compiler's hazard recognizer does not
+  // see their accumulator writes: give the last ones time to retire before
+  // the epilogue reads the accumulators with VALU instructions.
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 }  // namespace coda
