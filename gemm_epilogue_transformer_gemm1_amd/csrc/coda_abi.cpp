@@ -143,17 +143,47 @@ int coda_gemm_rowscale_swiglu(int dtype, const void* X, const float* x_scale, co
 int coda_gemm_rope(const void* h, const void* Wqkv, const float* r, const float* rope_cos,
                    const float* rope_sin, const int32_t* pos, int max_pos, void* qkv, int M, int K,
                    int n_q_heads, int n_kv_heads, int head_dim, void* stream) {
-  (void)h; (void)Wqkv; (void)r; (void)rope_cos; (void)rope_sin; (void)pos; (void)max_pos;
-  (void)qkv; (void)M; (void)K; (void)n_q_heads; (void)n_kv_heads; (void)head_dim; (void)stream;
-  return CODA_ERR_DTYPE;
+  try {
+    if (!h || !Wqkv || !r || !rope_cos || !rope_sin || !pos || !qkv) return CODA_ERR_NULL;
+    if (head_dim != 64 || n_q_heads < 1 || n_kv_heads < 1 || max_pos < 1) return CODA_ERR_SHAPE;
+    const int64_t N = (int64_t)(n_q_heads + 2 * n_kv_heads) * head_dim;
+    if (N > (int64_t(1) << 24)) return CODA_ERR_SHAPE;
+    if (int st = check_gemm_shape(M, (int)N, K, 64)) return st;
+    if (!aligned(h, 16) || !aligned(Wqkv, 16) || !aligned(qkv, 16) || !aligned(r, 4) ||
+        !aligned(rope_cos, 16) || !aligned(rope_sin, 16) || !aligned(pos, 4))
+      return CODA_ERR_ALIGN;
+    if (int st = check_device()) return st;
+    return launched(coda::launch_rope_bf16(
+        static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(Wqkv), r, rope_cos,
+        rope_sin, pos, max_pos, static_cast<uint16_t*>(qkv), M, K, n_q_heads, n_kv_heads,
+        as_stream(stream)));
+  } catch (...) {
+    return CODA_ERR_LAUNCH;
+  }
 }
 
 int coda_gemm_block_lse(const void* X, const void* W, const float* r, const int32_t* labels,
                         float* tile_max, float* tile_sumexp, float* label_logit, float* lse,
                         float* loss, int M, int V, int K, void* stream) {
-  (void)X; (void)W; (void)r; (void)labels; (void)tile_max; (void)tile_sumexp; (void)label_logit;
-  (void)lse; (void)loss; (void)M; (void)V; (void)K; (void)stream;
-  return CODA_ERR_DTYPE;
+  try {
+    if (!X || !W || !labels || !tile_max || !tile_sumexp || !label_logit || !loss)
+      return CODA_ERR_NULL;
+    if (int st = check_gemm_shape(M, V, K, 64)) return st;
+    if (!aligned(X, 16) || !aligned(W, 16) || !aligned(labels, 4) || !aligned(tile_max, 4) ||
+        !aligned(tile_sumexp, 4) || !aligned(label_logit, 4) || !aligned(loss, 4) ||
+        (r && !aligned(r, 4)) || (lse && !aligned(lse, 4)))
+      return CODA_ERR_ALIGN;
+    if (int st = check_device()) return st;
+    hipStream_t s = as_stream(stream);
+    if (hipError_t e = coda::launch_block_lse_bf16(static_cast<const uint16_t*>(X),
+                                                   static_cast<const uint16_t*>(W), r, labels,
+                                                   tile_max, tile_sumexp, label_logit, M, V, K, s))
+      return launched(e);
+    return launched(coda::launch_lse_merge(tile_max, tile_sumexp, label_logit,
+                                           coda_lse_tiles(V), M, lse, loss, s));
+  } catch (...) {
+    return CODA_ERR_LAUNCH;
+  }
 }
 
 int coda_fold_gamma(const void* W, const float* gamma, void* W_out, int N, int K, void* stream) {
@@ -172,8 +202,18 @@ int coda_fold_gamma(const void* W, const float* gamma, void* W_out, int N, int K
 
 int coda_rope_tables(double theta, int max_pos, int head_dim, float* rope_cos, float* rope_sin,
                      void* stream) {
-  (void)theta; (void)max_pos; (void)head_dim; (void)rope_cos; (void)rope_sin; (void)stream;
-  return CODA_ERR_DTYPE;
+  try {
+    if (!rope_cos || !rope_sin) return CODA_ERR_NULL;
+    if (!(theta > 0.0) || max_pos < 1 || head_dim < 2 || head_dim % 2 != 0 ||
+        !small_enough(max_pos, head_dim))
+      return CODA_ERR_SHAPE;
+    if (!aligned(rope_cos, 4) || !aligned(rope_sin, 4)) return CODA_ERR_ALIGN;
+    if (int st = check_device()) return st;
+    return launched(coda::launch_rope_tables(theta, max_pos, head_dim, rope_cos, rope_sin,
+                                             as_stream(stream)));
+  } catch (...) {
+    return CODA_ERR_LAUNCH;
+  }
 }
 
 int coda_gemm_bf16(const void* A, const void* W, void* C, int M, int N, int K, void* stream) {

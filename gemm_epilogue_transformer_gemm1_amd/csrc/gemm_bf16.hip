@@ -105,6 +105,138 @@ __global__ __launch_bounds__(kThreads, 1) void k_rowscale_swiglu_bf16(
 }
 
 // ---------------------------------------------------------------------------
+// QKV GEMM: row scale + rotary position embedding (section "CODA: the secret
+// in the epilogue": RoPE re-parameterised into the epilogue; section "Five
+// building blocks and a LEGO language": RoPE is an elementwise transform and
+// the cos/sin rows are vector loads).  Output tile 256 tokens x 256 features;
+// a wave's 128 features are two whole 64-wide heads, and the rotate-half
+// partner of feature c (< 32) of a head, c + 32, is subtile j + 2 in the same
+// lane and register, so the rotation needs no data exchange.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads, 1) void k_rope_bf16(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, const float* __restrict__ r,
+    const float* __restrict__ rcos, const float* __restrict__ rsin, const int* __restrict__ pos,
+    int max_pos, uint16_t* __restrict__ out, int M, int N, int K, int rot_features, int gm,
+    int gn) {
+  __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
+  const TileCoord tc = map_tile(blockIdx.x, gm, gn, 8);
+  const int m0 = tc.tm * kBM, n0 = tc.tn * kBN;
+  MainloopSrc src{X, W, nullptr, M, N, K, m0, n0};
+  Acc acc;
+  mainloop_bf16<false>(acc, smem, src);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int nw0 = n0 + wn * 128;  // multiple of 128: two whole heads of 64
+  const int g4 = (lane >> 4) * 4;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int m = m0 + wm * 128 + i * 16 + (lane & 15);
+    const bool mv = m < M;
+    const int mc = min(m, M - 1);
+    const float rr = r[mc];
+    // positions outside the table are clamped into it (memory safety)
+    const int p = min(max(pos[mc], 0), max_pos - 1);
+    // angle index of subtile jj (0, 1) of a head: 16*jj + g4 + v
+    const f32x4_t c0 = *(const f32x4_t*)(rcos + (size_t)p * 32 + g4);
+    const f32x4_t c1 = *(const f32x4_t*)(rcos + (size_t)p * 32 + 16 + g4);
+    const f32x4_t s0 = *(const f32x4_t*)(rsin + (size_t)p * 32 + g4);
+    const f32x4_t s1 = *(const f32x4_t*)(rsin + (size_t)p * 32 + 16 + g4);
+    const size_t row = (size_t)mc * (size_t)N;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int hbase = nw0 + hh * 64;
+      if (hbase >= N) continue;
+      const bool rot = hbase < rot_features;
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int ja = hh * 4 + jj, jb = ja + 2;
+        const f32x4_t cs = jj ? c1 : c0, sn = jj ? s1 : s0;
+        float lo[4], hi[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float a = acc.v[ja][i][v] * rr, b = acc.v[jb][i][v] * rr;
+          lo[v] = rot ? a * cs[v] - b * sn[v] : a;
+          hi[v] = rot ? b * cs[v] + a * sn[v] : b;
+        }
+        if (mv) {
+          const int na = hbase + jj * 16 + g4;
+          *(u32x2_t*)(out + row + na) = pack_bf16x4(lo[0], lo[1], lo[2], lo[3]);
+          *(u32x2_t*)(out + row + na + 32) = pack_bf16x4(hi[0], hi[1], hi[2], hi[3]);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// LM head: block log-sum-exp (section "Five building blocks and a LEGO
+// language": block reduction "block log-sum-exp" and the stateful max /
+// sum-exp statistics of online normalisation; section "CODA: the secret in the
+// epilogue": cross-entropy re-parameterised into the epilogue).  The logits
+// z = r * X W^T never leave registers: each wave reduces its 128 vocabulary
+// entries per token to (max, sum exp(z - max)) and the lane that holds the
+// label's logit writes it, taken from the fp32 accumulator.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads, 1) void k_block_lse_bf16(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, const float* __restrict__ r,
+    const int* __restrict__ labels, float* __restrict__ tmax, float* __restrict__ tsum,
+    float* __restrict__ label_logit, int M, int V, int K, int gm, int gn) {
+  __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
+  const TileCoord tc = map_tile(blockIdx.x, gm, gn, 8);
+  const int m0 = tc.tm * kBM, n0 = tc.tn * kBN;
+  MainloopSrc src{X, W, nullptr, M, V, K, m0, n0};
+  Acc acc;
+  mainloop_bf16<false>(acc, smem, src);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int nw0 = n0 + wn * kLseTileWidth;
+  const int g4 = (lane >> 4) * 4;
+  const float kLog2e = 1.4426950408889634f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int m = m0 + wm * 128 + i * 16 + (lane & 15);
+    const bool mv = m < M;
+    const int mc = min(m, M - 1);
+    const float rr = r ? r[mc] : 1.0f;
+    const int lab = labels[mc];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int n = nw0 + j * 16 + g4;
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        if (n + v < V) mx = fmaxf(mx, acc.v[j][i][v] * rr);
+    }
+    mx = max_over_lane_groups(mx);
+    const float mx2 = mx * kLog2e;
+    float se = 0.f, zl = 0.f;
+    bool has = false;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int n = nw0 + j * 16 + g4;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float z = acc.v[j][i][v] * rr;
+        if (n + v < V) se += __builtin_amdgcn_exp2f(z * kLog2e - mx2);
+        if (n + v == lab) {
+          zl = z;
+          has = true;
+        }
+      }
+    }
+    se = sum_over_lane_groups(se);
+    if (mv && has) label_logit[m] = zl;
+    if (mv && lane < 16 && nw0 < V) {
+      const size_t t = (size_t)(nw0 / kLseTileWidth);
+      tmax[t * M + m] = mx;
+      tsum[t * M + m] = se;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Plain GEMM (unfused baseline): the same mainloop, epilogue = convert + store.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_plain_bf16(const uint16_t* __restrict__ A,
@@ -157,6 +289,25 @@ hipError_t launch_rowscale_swiglu_bf16(const uint16_t* X, const uint16_t* Wg, co
   const int gm = cdiv(M, kBM), gn = cdiv(N, kBN / 2);
   hipLaunchKernelGGL(k_rowscale_swiglu_bf16, dim3(gm * gn), dim3(kThreads), 0, stream, X, Wg, Wu,
                      r, out, M, N, K, gm, gn);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_bf16(const uint16_t* X, const uint16_t* W, const float* r,
+                            const float* rcos, const float* rsin, const int* pos, int max_pos,
+                            uint16_t* out, int M, int K, int n_q, int n_kv, hipStream_t stream) {
+  const int N = (n_q + 2 * n_kv) * 64;
+  const int gm = cdiv(M, kBM), gn = cdiv(N, kBN);
+  hipLaunchKernelGGL(k_rope_bf16, dim3(gm * gn), dim3(kThreads), 0, stream, X, W, r, rcos, rsin,
+                     pos, max_pos, out, M, N, K, (n_q + n_kv) * 64, gm, gn);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_lse_bf16(const uint16_t* X, const uint16_t* W, const float* r,
+                                 const int* labels, float* tmax, float* tsum, float* label_logit,
+                                 int M, int V, int K, hipStream_t stream) {
+  const int gm = cdiv(M, kBM), gn = cdiv(V, kBN);
+  hipLaunchKernelGGL(k_block_lse_bf16, dim3(gm * gn), dim3(kThreads), 0, stream, X, W, r, labels,
+                     tmax, tsum, label_logit, M, V, K, gm, gn);
   return hipGetLastError();
 }
 

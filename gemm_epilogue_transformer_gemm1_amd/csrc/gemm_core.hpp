@@ -283,9 +283,15 @@ __device__ __forceinline__ void mainloop_bf16(Acc& acc, char* smem, const Mainlo
   if (nk >= 2) stage(nk - 2, std::false_type{}, std::true_type{});
   stage(nk - 1, std::false_type{}, std::false_type{});
   // The MFMAs are inline asm, so the compiler's hazard recognizer does not
-  // see their accumulator writes: give the last ones time to retire before
-  // the epilogue reads the accumulators with VALU instructions.
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  // see their accumulator writes and would happily read an accumulator right
+  // after the MFMA that writes it.  Give the last MFMAs time to retire, then
+  // re-define every accumulator with an empty asm statement ordered after the
+  // wait states: every epilogue read depends on it and so comes later.
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) asm volatile("" : "+a"(acc.v[j][i]));
   __builtin_amdgcn_sched_barrier(0);
 }
 

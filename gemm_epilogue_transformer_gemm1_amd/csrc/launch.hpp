@@ -17,6 +17,16 @@ hipError_t launch_residual_partialrms_bf16(const uint16_t* A, const uint16_t* W,
 hipError_t launch_rowscale_swiglu_bf16(const uint16_t* X, const uint16_t* Wg, const uint16_t* Wu,
                                        const float* r, uint16_t* out, int M, int N, int K,
                                        hipStream_t stream);
+hipError_t launch_rope_bf16(const uint16_t* X, const uint16_t* W, const float* r,
+                            const float* rcos, const float* rsin, const int* pos, int max_pos,
+                            uint16_t* out, int M, int K, int n_q, int n_kv, hipStream_t stream);
+hipError_t launch_rope_tables(double theta, int max_pos, int head_dim, float* rcos, float* rsin,
+                              hipStream_t stream);
+hipError_t launch_block_lse_bf16(const uint16_t* X, const uint16_t* W, const float* r,
+                                 const int* labels, float* tmax, float* tsum, float* label_logit,
+                                 int M, int V, int K, hipStream_t stream);
+hipError_t launch_lse_merge(const float* tmax, const float* tsum, const float* label_logit, int T,
+                            int M, float* lse, float* loss, hipStream_t stream);
 hipError_t launch_gemm_plain_bf16(const uint16_t* A, const uint16_t* W, uint16_t* C, int M, int N,
                                   int K, hipStream_t stream);
 

@@ -96,6 +96,86 @@ hipError_t launch_fold_gamma(const uint16_t* W, const float* gamma, uint16_t* W_
 }
 
 // ---------------------------------------------------------------------------
+// Log-sum-exp merge of the per-tile (max, sum-exp) pairs (section "Five
+// building blocks and a LEGO language": the running max / sum-exp statistics
+// of online normalisation).  A 256-thread block owns 64 token rows: lane l of
+// wave w merges tiles w, w+4, w+8, ... of row 64*block + l (coalesced 256 B
+// reads per wave), then the four partial pairs are merged through LDS.
+//   lse = Mx + ln sum_t s_t e^(m_t - Mx);  loss = lse - label_logit.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void lse_combine(float& m, float& s, float m2, float s2) {
+  const float nm = fmaxf(m, m2);
+  if (nm == -INFINITY) return;  // both empty
+  const float k = 1.4426950408889634f;
+  s = s * __builtin_amdgcn_exp2f((m - nm) * k) + s2 * __builtin_amdgcn_exp2f((m2 - nm) * k);
+  m = nm;
+}
+
+__global__ __launch_bounds__(256) void k_lse_merge(const float* __restrict__ tmax,
+                                                   const float* __restrict__ tsum,
+                                                   const float* __restrict__ label_logit, int T,
+                                                   int M, float* __restrict__ lse,
+                                                   float* __restrict__ loss) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int m = blockIdx.x * 64 + lane;
+  const int mc = min(m, M - 1);
+  float rm = -INFINITY, rs = 0.f;
+  int t = wave;
+  for (; t + 12 < T; t += 16) {  // four tiles in flight per lane
+    float a[4], b[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      a[q] = tmax[(size_t)(t + 4 * q) * M + mc];
+      b[q] = tsum[(size_t)(t + 4 * q) * M + mc];
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) lse_combine(rm, rs, a[q], b[q]);
+  }
+  for (; t < T; t += 4) lse_combine(rm, rs, tmax[(size_t)t * M + mc], tsum[(size_t)t * M + mc]);
+  __shared__ float pm[4][64], ps[4][64];
+  pm[wave][lane] = rm;
+  ps[wave][lane] = rs;
+  __syncthreads();
+  if (wave == 0 && m < M) {
+#pragma unroll
+    for (int w = 1; w < 4; ++w) lse_combine(rm, rs, pm[w][lane], ps[w][lane]);
+    const float l = rm + logf(rs);
+    if (lse) lse[m] = l;
+    loss[m] = l - label_logit[m];
+  }
+}
+
+hipError_t launch_lse_merge(const float* tmax, const float* tsum, const float* label_logit, int T,
+                            int M, float* lse, float* loss, hipStream_t stream) {
+  hipLaunchKernelGGL(k_lse_merge, dim3(cdiv(M, 64)), dim3(256), 0, stream, tmax, tsum,
+                     label_logit, T, M, lse, loss);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Rotary tables: cos / sin of p * theta^(-2i/hd), angles and trigonometry in
+// fp64, stored fp32, [max_pos, hd/2].
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_rope_tables(double theta, int max_pos, int half,
+                                                     float* __restrict__ rcos,
+                                                     float* __restrict__ rsin) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)max_pos * half) return;
+  const int p = (int)(idx / half), i = (int)(idx % half);
+  const double ang = (double)p * pow(theta, -2.0 * (double)i / (double)(2 * half));
+  rcos[idx] = (float)cos(ang);
+  rsin[idx] = (float)sin(ang);
+}
+
+hipError_t launch_rope_tables(double theta, int max_pos, int head_dim, float* rcos, float* rsin,
+                              hipStream_t stream) {
+  const int half = head_dim / 2;
+  hipLaunchKernelGGL(k_rope_tables, dim3(cdiv((int64_t)max_pos * half, 256)), dim3(256), 0, stream,
+                     theta, max_pos, half, rcos, rsin);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Unfused baseline ops: each reads its inputs from HBM and writes its output
 // back (section "The cost of laziness in large-model training": every
 // operator boundary is a write-back to GPU memory).  16 B per lane accesses.

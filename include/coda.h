@@ -148,8 +148,9 @@ int coda_gemm_rowscale_swiglu(int dtype, const void* X, const float* x_scale, co
  *     qkv[.., i + hd/2] = y_{i+hd/2} c + y_i s
  *   v heads are stored unrotated.                           (stored bf16)
  * h [M,K] bf16, Wqkv [(nq+2nkv)hd, K] bf16 (gamma folded in), r [M] fp32,
- * rope_cos / rope_sin [max_pos, hd/2] fp32 (coda_rope_tables), pos [M] int32
- * in [0, max_pos) (not checked), qkv [M, (nq+2nkv)hd] bf16.
+ * rope_cos / rope_sin [max_pos, hd/2] fp32 (coda_rope_tables; 16-byte aligned),
+ * pos [M] int32 in [0, max_pos) (a position outside is clamped into the table),
+ * qkv [M, (nq+2nkv)hd] bf16.
  * Sizes: head_dim == 64; nq, nkv >= 1; K % 64 == 0; M >= 1.
  */
 int coda_gemm_rope(const void* h, const void* Wqkv, const float* r, const float* rope_cos,

@@ -1,0 +1,102 @@
+"""GPU parity of the LM-head cross entropy (GEMM with block log-sum-exp
+epilogue + merge) against the CPU oracle."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gemm_epilogue_transformer_gemm1_amd import inputs, ops
+from tests.gpu_util import (DEV, TOL_ROW, bf16_dev, dec_bf16, f32_dev, f32_host, i32_dev,
+                            row_rel_err, sample_rows, say)
+
+pytestmark = pytest.mark.gpu
+
+
+def run_lse(w, r=None, W=None):
+    M, d, V = w.sizes["M"], w.sizes["d"], w.sizes["V"]
+    x = bf16_dev(w.arrays["x"])
+    wl = W if W is not None else bf16_dev(w.arrays["wlm"])
+    lab = i32_dev(w.arrays["labels"])
+    T = ops.lse_tiles(V)
+    tmax = torch.empty(T, M, dtype=torch.float32, device=DEV)
+    tsum = torch.empty_like(tmax)
+    zl = torch.empty(M, dtype=torch.float32, device=DEV)
+    lse = torch.empty(M, dtype=torch.float32, device=DEV)
+    loss = torch.empty(M, dtype=torch.float32, device=DEV)
+    ops.gemm_block_lse(x, wl, lab, tmax, tsum, zl, loss, lse=lse,
+                       r=None if r is None else f32_dev(r))
+    torch.cuda.synchronize()
+    return {"tmax": f32_host(tmax), "tsum": f32_host(tsum), "zl": f32_host(zl),
+            "lse": f32_host(lse), "loss": f32_host(loss)}
+
+
+def oracle_rows(w, rows=None, r=None):
+    sel = (lambda a: a) if rows is None else (lambda a: a[rows])
+    rr = None if r is None else sel(r).astype(np.float64)
+    return oracle.lm_head_ce(dec_bf16(sel(w.arrays["x"])), dec_bf16(w.arrays["wlm"]),
+                             sel(w.arrays["labels"]), r=rr)
+
+
+def check_partials(w, got, rows):
+    """(max, sum-exp) pairs are not unique, so check what is: each tile's
+    mx + ln(se) is that tile's own log-sum-exp, and re-merging the GPU's
+    pairs on the host in several orders gives the row's lse."""
+    wt = ops.lse_tile_width()
+    x = dec_bf16(w.arrays["x"][rows])
+    z = oracle.gemm_nt(x, dec_bf16(w.arrays["wlm"]))
+    T = got["tmax"].shape[0]
+    tl = got["tmax"][:, rows] + np.log(got["tsum"][:, rows])
+    for t in range(T):
+        ref = oracle.logsumexp_rows(z[:, t * wt:(t + 1) * wt])
+        assert float(np.max(np.abs(tl[t] - ref))) <= 2e-5, t
+    full = oracle.logsumexp_rows(z)
+    mx, se = got["tmax"][:, rows], got["tsum"][:, rows]
+    rng = np.random.default_rng(0)
+    for order in (None, list(range(T))[::-1], list(rng.permutation(T))):
+        assert float(np.max(np.abs(oracle.lse_merge(mx, se, order) - full))) <= 2e-5
+
+
+def test_lse_ragged_small():
+    w = inputs.make_lm(seed=11, M=300, d=192, V=1008)
+    say("block lse M=300 d=192 V=1008 (last tile 112 wide)")
+    got = run_lse(w)
+    ref = oracle_rows(w)
+    assert row_rel_err(got["loss"], ref["loss"]) <= TOL_ROW
+    assert row_rel_err(got["lse"], ref["lse"]) <= TOL_ROW
+    assert float(np.max(np.abs(got["zl"] - ref["label_logit"]))) <= 1e-4
+    check_partials(w, got, np.arange(300))
+
+
+def test_lse_with_row_scale():
+    w = inputs.make_lm(seed=12, M=257, d=128, V=512)
+    r = np.random.default_rng(3).uniform(0.5, 2.0, size=257).astype(np.float32)
+    say("block lse with row scale M=257 d=128 V=512")
+    got = run_lse(w, r=r)
+    ref = oracle_rows(w, r=r)
+    assert row_rel_err(got["loss"], ref["loss"]) <= TOL_ROW
+
+
+def test_lse_zero_weights_gives_ln_v():
+    """W = 0: all logits are 0, so every row's loss is ln V exactly."""
+    w = inputs.make_lm(seed=13, M=130, d=64, V=1008)
+    say("block lse with zero weights")
+    W0 = torch.zeros(1008, 64, dtype=torch.bfloat16, device=DEV)
+    got = run_lse(w, W=W0)
+    assert float(np.max(np.abs(got["loss"] - math.log(1008)))) <= 1e-5
+    assert float(np.max(np.abs(got["zl"]))) == 0.0
+
+
+def test_lm_head_full_sampled_rows():
+    """Full LM-head shape (M=8192, d=2048, V=128256); the oracle checks
+    sampled rows, the merge invariants run on a few of them."""
+    w = inputs.make_workload("lm_head")
+    say("lm_head full size, sampled rows")
+    got = run_lse(w)
+    rows = sample_rows(w.sizes["M"], n=24)
+    ref = oracle_rows(w, rows)
+    assert row_rel_err(got["loss"][rows], ref["loss"]) <= TOL_ROW
+    assert row_rel_err(got["lse"][rows], ref["lse"]) <= TOL_ROW
+    assert np.all(np.isfinite(got["loss"]))
+    check_partials(w, got, rows[:4])

@@ -1,0 +1,104 @@
+"""GPU parity of the attention-input block (GEMM1 residual/partial-RMS ->
+reduce -> QKV GEMM with row-scale + RoPE epilogue) against the CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gemm_epilogue_transformer_gemm1_amd import inputs, ops
+from tests.gpu_util import (DEV, TOL_BF16, TOL_ROW, bf16_dev, bf16_host, dec_bf16, f32_dev,
+                            f32_host, i32_dev, norm_err, row_rel_err, sample_rows, say)
+
+pytestmark = pytest.mark.gpu
+EPS = 1e-5
+
+
+def run_fused(w, eps=EPS, max_pos=None):
+    sz = w.sizes
+    M, d, K1 = sz["M"], sz["d"], sz["K1"]
+    nq, nkv, hd = sz["n_q"], sz["n_kv"], sz["head_dim"]
+    max_pos = max_pos or sz["seq_len"]
+    x, res, w1 = bf16_dev(w.arrays["x"]), bf16_dev(w.arrays["res"]), bf16_dev(w.arrays["w1"])
+    wqkv = bf16_dev(w.arrays["wqkv"])
+    gamma = f32_dev(w.arrays["gamma"])
+    wqkv_f = torch.empty_like(wqkv)
+    ops.fold_gamma(wqkv, gamma, wqkv_f)
+    cos = torch.empty(max_pos, hd // 2, dtype=torch.float32, device=DEV)
+    sin = torch.empty_like(cos)
+    ops.rope_tables(sz["theta"], max_pos, hd, cos, sin)
+    pos = i32_dev(w.arrays["pos"])
+    h = torch.empty(M, d, dtype=torch.bfloat16, device=DEV)
+    P = torch.empty(ops.rms_tiles(d), M, dtype=torch.float32, device=DEV)
+    r = torch.empty(M, dtype=torch.float32, device=DEV)
+    qkv = torch.empty(M, (nq + 2 * nkv) * hd, dtype=torch.bfloat16, device=DEV)
+    ops.gemm_residual_partialrms(x, w1, res, h, P)
+    ops.rms_reduce(P, d, eps, r)
+    ops.gemm_rope(h, wqkv_f, r, cos, sin, pos, qkv, nq, nkv, hd)
+    torch.cuda.synchronize()
+    return {"h": h, "r": r, "qkv": qkv, "cos": cos, "sin": sin}
+
+
+def oracle_rows(w, rows=None, eps=EPS, max_pos=None):
+    sz = w.sizes
+    sel = (lambda a: a) if rows is None else (lambda a: a[rows])
+    return oracle.attn_in_block(dec_bf16(sel(w.arrays["x"])), dec_bf16(sel(w.arrays["res"])),
+                                dec_bf16(w.arrays["w1"]), dec_bf16(w.arrays["wqkv"]),
+                                w.arrays["gamma"].astype(np.float64), eps, sel(w.arrays["pos"]),
+                                sz["n_q"], sz["n_kv"], sz["head_dim"], sz["theta"],
+                                max_pos or sz["seq_len"])
+
+
+def test_rope_tables_match_oracle():
+    say("rope tables theta=5e5 max_pos=2048 hd=64")
+    cos = torch.empty(2048, 32, dtype=torch.float32, device=DEV)
+    sin = torch.empty_like(cos)
+    ops.rope_tables(500000.0, 2048, 64, cos, sin)
+    torch.cuda.synchronize()
+    rc, rs = oracle.rope_tables(2048, 64, 500000.0)
+    # fp64 angles rounded once to fp32
+    assert float(np.max(np.abs(f32_host(cos) - rc))) <= 6e-8
+    assert float(np.max(np.abs(f32_host(sin) - rs))) <= 6e-8
+
+
+@pytest.mark.parametrize("M,d,K1,nq,nkv,seq", [
+    (300, 256, 192, 4, 2, 100),    # ragged M, many positions
+    (200, 384, 128, 3, 1, 64),     # 5 heads: the last wave tile holds one head
+])
+def test_rope_block_ragged(M, d, K1, nq, nkv, seq):
+    w = inputs.make_attn(seed=7, M=M, d=d, K1=K1, n_q=nq, n_kv=nkv, head_dim=64, seq_len=seq)
+    say(f"rope block M={M} d={d} K1={K1} nq={nq} nkv={nkv} seq={seq}")
+    got = run_fused(w)
+    ref = oracle_rows(w)
+    assert norm_err(bf16_host(got["h"]), ref["h"]) <= TOL_BF16
+    assert row_rel_err(f32_host(got["r"]), ref["r"]) <= TOL_ROW
+    q = bf16_host(got["qkv"])
+    assert norm_err(q, ref["qkv"]) <= TOL_BF16
+    # the v heads are the plain row-scaled projection: check them separately
+    vlo = (nq + nkv) * 64
+    assert norm_err(q[:, vlo:], ref["qkv"][:, vlo:]) <= TOL_BF16
+
+
+def test_rope_position_zero_is_identity_on_gpu():
+    """With every position 0 the rotation is the identity, so q|k|v equal the
+    plain row-scaled projection (checked against the oracle with RoPE off)."""
+    w = inputs.make_attn(seed=8, M=128, d=256, K1=128, n_q=2, n_kv=1, head_dim=64, seq_len=1)
+    say("rope block, all positions 0")
+    got = run_fused(w)
+    ref = oracle_rows(w)
+    n = oracle.rmsnorm(ref["h"], w.arrays["gamma"].astype(np.float64), EPS)
+    plain = oracle.gemm_nt(n, dec_bf16(w.arrays["wqkv"]))
+    assert norm_err(bf16_host(got["qkv"]), plain) <= TOL_BF16
+
+
+def test_attn_rope_full_sampled_rows():
+    """Full attention-input shape (M=8192, d=2048, GEMM1 K=8192, 32 q / 8 kv
+    heads of 64, theta=5e5, positions m mod 2048); sampled rows vs the oracle."""
+    w = inputs.make_workload("attn_rope")
+    say("attn_rope full size, sampled rows")
+    got = run_fused(w)
+    rows = sample_rows(w.sizes["M"], n=32)
+    ref = oracle_rows(w, rows)
+    assert norm_err(bf16_host(got["h"][rows.tolist()]), ref["h"]) <= TOL_BF16
+    assert row_rel_err(f32_host(got["r"])[rows], ref["r"]) <= TOL_ROW
+    assert norm_err(bf16_host(got["qkv"][rows.tolist()]), ref["qkv"]) <= TOL_BF16
+    assert bool(torch.isfinite(got["qkv"].float()).all())
