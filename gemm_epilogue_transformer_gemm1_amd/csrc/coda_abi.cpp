@@ -82,14 +82,26 @@ int coda_gemm_residual_partialrms(int dtype, const void* A, const void* W, const
                                   float* partial_sumsq, const float* h8_scale, void* h8,
                                   float* partial_amax, int M, int N, int K, void* stream) {
   try {
-    if (dtype != CODA_BF16) return CODA_ERR_DTYPE;
+    if (dtype != CODA_BF16 && dtype != CODA_FP8_E4M3) return CODA_ERR_DTYPE;
     if (!A || !W || !residual || !h || !partial_sumsq) return CODA_ERR_NULL;
-    if (a_scale || w_scale || h8_scale || h8 || partial_amax) return CODA_ERR_DTYPE;
-    if (int st = check_gemm_shape(M, N, K, 64)) return st;
+    const bool fp8 = dtype == CODA_FP8_E4M3;
+    if (fp8) {
+      if (!a_scale || !w_scale || (h8 && !h8_scale)) return CODA_ERR_NULL;
+    } else if (a_scale || w_scale || h8_scale || h8 || partial_amax) {
+      return CODA_ERR_DTYPE;
+    }
+    if (int st = check_gemm_shape(M, N, K, fp8 ? 128 : 64)) return st;
     if (!aligned(A, 16) || !aligned(W, 16) || !aligned(residual, 16) || !aligned(h, 16) ||
-        !aligned(partial_sumsq, 4))
+        !aligned(partial_sumsq, 4) || (h8 && !aligned(h8, 16)) ||
+        (partial_amax && !aligned(partial_amax, 4)) || (a_scale && !aligned(a_scale, 4)) ||
+        (w_scale && !aligned(w_scale, 4)) || (h8_scale && !aligned(h8_scale, 4)))
       return CODA_ERR_ALIGN;
     if (int st = check_device()) return st;
+    if (fp8)
+      return launched(coda::launch_residual_partialrms_fp8(
+          static_cast<const uint8_t*>(A), static_cast<const uint8_t*>(W), a_scale, w_scale,
+          static_cast<const uint16_t*>(residual), static_cast<uint16_t*>(h), partial_sumsq,
+          h8_scale, static_cast<uint8_t*>(h8), partial_amax, M, N, K, as_stream(stream)));
     return launched(coda::launch_residual_partialrms_bf16(
         static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(W),
         static_cast<const uint16_t*>(residual), static_cast<uint16_t*>(h), partial_sumsq, M, N, K,
@@ -123,14 +135,25 @@ int coda_gemm_rowscale_swiglu(int dtype, const void* X, const float* x_scale, co
                               const void* Wu, const float* wg_scale, const float* wu_scale,
                               const float* r, void* out, int M, int N, int K, void* stream) {
   try {
-    if (dtype != CODA_BF16) return CODA_ERR_DTYPE;
+    if (dtype != CODA_BF16 && dtype != CODA_FP8_E4M3) return CODA_ERR_DTYPE;
     if (!X || !Wg || !Wu || !r || !out) return CODA_ERR_NULL;
-    if (x_scale || wg_scale || wu_scale) return CODA_ERR_DTYPE;
-    if (int st = check_gemm_shape(M, N, K, 64)) return st;
+    const bool fp8 = dtype == CODA_FP8_E4M3;
+    if (fp8) {
+      if (!x_scale || !wg_scale || !wu_scale) return CODA_ERR_NULL;
+    } else if (x_scale || wg_scale || wu_scale) {
+      return CODA_ERR_DTYPE;
+    }
+    if (int st = check_gemm_shape(M, N, K, fp8 ? 128 : 64)) return st;
     if (!aligned(X, 16) || !aligned(Wg, 16) || !aligned(Wu, 16) || !aligned(out, 16) ||
-        !aligned(r, 4))
+        !aligned(r, 4) || (x_scale && !aligned(x_scale, 4)) ||
+        (wg_scale && !aligned(wg_scale, 4)) || (wu_scale && !aligned(wu_scale, 4)))
       return CODA_ERR_ALIGN;
     if (int st = check_device()) return st;
+    if (fp8)
+      return launched(coda::launch_rowscale_swiglu_fp8(
+          static_cast<const uint8_t*>(X), x_scale, static_cast<const uint8_t*>(Wg),
+          static_cast<const uint8_t*>(Wu), wg_scale, wu_scale, r, static_cast<uint16_t*>(out), M,
+          N, K, as_stream(stream)));
     return launched(coda::launch_rowscale_swiglu_bf16(
         static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(Wg),
         static_cast<const uint16_t*>(Wu), r, static_cast<uint16_t*>(out), M, N, K,

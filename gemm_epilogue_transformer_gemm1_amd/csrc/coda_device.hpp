@@ -47,10 +47,30 @@ __device__ __forceinline__ void mfma16x16x32_acc(f32x4_t& c, const bf16x8_t& a,
   asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
 }
 
+// Same for the e4m3 MFMA: 32x32 output tile, 64-deep reduction, both
+// operands OCP E4M3FN (32 bytes per lane each).
+__device__ __forceinline__ void mfma32x32x64_f8_acc(f32x16_t& c, const i32x8_t& a,
+                                                   const i32x8_t& b) {
+  asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+
 // Round-to-nearest-even float -> bf16 bits for four values, packed in 8 bytes.
 __device__ __forceinline__ u32x2_t pack_bf16x4(float a, float b, float c, float d) {
   bf16x4_t v = {(__bf16)a, (__bf16)b, (__bf16)c, (__bf16)d};
   return __builtin_bit_cast(u32x2_t, v);
+}
+
+// Four floats -> four OCP E4M3FN codes (round to nearest even), saturating:
+// magnitudes above 448 are clamped to 448 first; NaN stays NaN.
+__device__ __forceinline__ uint32_t pack_e4m3x4_sat(float a, float b, float c, float d) {
+  const float lim = 448.0f;
+  a = __builtin_fminf(__builtin_fmaxf(a, -lim), lim);
+  b = __builtin_fminf(__builtin_fmaxf(b, -lim), lim);
+  c = __builtin_fminf(__builtin_fmaxf(c, -lim), lim);
+  d = __builtin_fminf(__builtin_fmaxf(d, -lim), lim);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t bits) {

@@ -1,23 +1,28 @@
-// The fixed GEMM mainloop every epilogue program runs on (page section
+// The fixed GEMM mainloops every epilogue program runs on (page section
 // "CODA: the secret in the epilogue": a GEMM is a blocked multiply-accumulate
 // mainloop followed by an epilogue that still holds the output tile in
 // registers; section "Five building blocks and a LEGO language": the mainloop
 // stays fixed and epilogue primitives are composed on top of it).
 //
 // gfx950 design (one 256-thread workgroup per CU, 4 waves in a 2x2 grid):
-//   * block tile 256 token rows x 256 weight rows, reduction depth 64 per
-//     stage; two LDS stages of 64 KiB (token tile 32 KiB + weight tile 32 KiB);
+//   * block tile 256 token rows x 256 weight rows; each stage covers 128 bytes
+//     of reduction per row (64 bf16 or 128 e4m3 values); two LDS stages of
+//     64 KiB (token tile 32 KiB + weight tile 32 KiB);
 //   * global -> LDS with buffer_load ... lds (16 B per lane, no VGPR staging);
-//     each LDS row holds 64 bf16 (128 B) as 8 chunks of 16 B, chunk c of row r
-//     stored at chunk slot c ^ (r & 7) so that the 16 lanes reading one MFMA
-//     fragment hit distinct banks;
-//   * v_mfma_f32_16x16x32_bf16 with the WEIGHT fragment as the first operand
-//     and the TOKEN fragment as the second, so the accumulator is C^T: lane L,
-//     register v of a 16x16 tile holds output feature 4*(L/16)+v of token L%16.
-//     A lane therefore owns 4 consecutive features of one token, which makes
-//     per-token reductions (RMS partials, log-sum-exp) mostly lane-local;
-//   * each wave owns a 128-token x 128-weight-row quarter: 8x8 tiles of 16x16,
-//     256 fp32 accumulators per lane.
+//     each 128 B LDS row is 8 chunks of 16 B, chunk c of row r stored at slot
+//     c ^ (r & 7), so the lanes reading one MFMA fragment hit distinct banks;
+//   * the WEIGHT fragment is the MFMA's first operand and the TOKEN fragment
+//     its second, so the accumulator is C^T and a lane holds runs of 4
+//     consecutive output features of one token: per-token reductions (RMS
+//     partials, log-sum-exp) are mostly lane-local;
+//   * each wave owns a 128-token x 128-weight-row quarter, 256 fp32
+//     accumulators per lane, pinned to AGPRs;
+//   * bf16: v_mfma_f32_16x16x32_bf16, 8x8 tiles of 16x16 per wave;
+//     e4m3: v_mfma_f32_32x32x64_f8f6f4, 4x4 tiles of 32x32 per wave;
+//   * pipeline: the reduction of a stage is two MFMA steps with fragment sets
+//     fa / fb; a stage's LDS slot is refilled as soon as every wave holds its
+//     second step's fragments, so each stage's loads are issued about one and
+//     a half stages of MFMA work before they are needed.
 #pragma once
 
 #include <type_traits>
@@ -29,17 +34,24 @@ namespace coda {
 constexpr int kThreads = 256;
 constexpr int kBM = 256;                      // token rows per block
 constexpr int kBN = 256;                      // weight rows per block
-constexpr int kBK = 64;                       // bf16 reduction depth per stage
-constexpr int kRowBytes = kBK * 2;            // 128 B per LDS row
+constexpr int kRowBytes = 128;                // reduction bytes per row per stage
 constexpr int kXBytes = kBM * kRowBytes;      // 32 KiB token tile
 constexpr int kWBytes = kBN * kRowBytes;      // 32 KiB weight tile
 constexpr int kStageBytes = kXBytes + kWBytes;
 constexpr int kSmemBytes = 2 * kStageBytes;   // 128 KiB
 
-// Accumulators of one wave: acc[j][i] is the 16x16 tile of weight-row
-// subtile j and token subtile i.
+// bf16 accumulators of one wave: v[j][i] is the 16x16 tile of weight subtile
+// j and token subtile i.  Lane L, register r holds feature 16j + 4(L/16) + r
+// of token 16i + L%16 (relative to the wave's corner).
 struct Acc {
   f32x4_t v[8][8];
+};
+
+// e4m3 accumulators: v[j][i] is the 32x32 tile of weight subtile j and token
+// subtile i.  Lane L, register r holds feature 32j + 8(r/4) + 4(L/32) + r%4
+// of token 32i + L%32.
+struct Acc8 {
+  f32x16_t v[4][4];
 };
 
 struct TileCoord {
@@ -67,62 +79,135 @@ __device__ __forceinline__ TileCoord map_tile(int b, int gm, int gn, int group_m
   return c;
 }
 
-// Weight-tile row (within the 256-row LDS weight tile) of this wave's
-// n-subtile j.  Plain GEMMs: the wave owns rows [wn*128, wn*128+128).  Gated
-// (SwiGLU) GEMMs: LDS rows [0,128) hold gate rows and [128,256) the matching
-// up rows, and the wave owns gate rows [wn*64, +64) (subtiles 0..3) and the
-// same up rows (subtiles 4..7), so gate and up values of one output element
-// sit in the same lane and register.
-template <bool kGated>
-__device__ __forceinline__ constexpr int wrow_of_subtile(int j) {
-  return kGated ? (j < 4 ? j * 16 : 128 + (j - 4) * 16) : j * 16;
-}
+// Operand sources of one block.
+struct MainloopSrc {
+  const void* X;   // token operand [M, K]
+  const void* W0;  // weight rows for LDS rows [0,256) (plain) or [0,128) (gated)
+  const void* W1;  // gated only: weight rows for LDS rows [128,256)
+  int M;           // token rows of X
+  int Nw;          // rows of each weight matrix
+  int K;           // reduction length in elements
+  int m0;          // first token row of the block
+  int n0;          // first weight row of the block (per weight matrix)
+};
 
+// Gated (SwiGLU) blocks: LDS weight rows [0,128) hold gate rows n0.. and
+// [128,256) the same up rows, and a wave owns gate rows [wn*64, +64) and the
+// matching up rows, so gate and up values of one output element sit in the
+// same lane and register.  Plain blocks: the wave owns rows [wn*128, +128).
 template <bool kGated>
 __device__ __forceinline__ int wave_wrow_base(int wn) {
   return kGated ? wn * 64 : wn * 128;
 }
 
-// Operand sources of one block.
-struct MainloopSrc {
-  const uint16_t* X;   // token operand [M, K] bf16
-  const uint16_t* W0;  // weight rows for LDS rows [0,256) (plain) or [0,128) (gated)
-  const uint16_t* W1;  // gated only: weight rows for LDS rows [128,256)
-  int M;               // token rows of X
-  int Nw;              // rows of each weight matrix
-  int K;               // reduction length, multiple of 64
-  int m0;              // first token row of the block
-  int n0;              // first weight row of the block (per weight matrix)
+// Global -> LDS load plan: wave w fills LDS rows [w*64, w*64+64) of both
+// tiles with 8 instructions each (8 rows x 128 B per instruction).  Rows past
+// the matrix are clamped to its last row (their results are never stored).
+template <bool kGated>
+struct LoadPlan {
+  __amdgpu_buffer_rsrc_t xr, wr;
+  uint32_t xoff[8], woff[8];
+  char* x_lds;
+  char* w_lds;
+
+  __device__ __forceinline__ LoadPlan(const MainloopSrc& s, char* smem, int wave, int lane,
+                                      int esize) {
+    const uint32_t row_bytes = (uint32_t)s.K * (uint32_t)esize;
+    xr = make_rsrc(s.X, (uint32_t)s.M * row_bytes);
+    const void* wsrc = (kGated && wave >= 2) ? s.W1 : s.W0;
+    wr = make_rsrc(wsrc, (uint32_t)s.Nw * row_bytes);
+    const int wrow_shift = (kGated && wave >= 2) ? 128 : 0;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int lr = wave * 64 + q * 8 + (lane >> 3);
+      const int lc = (lane & 7) ^ (lr & 7);
+      const int gx = min(s.m0 + lr, s.M - 1);
+      const int gw = min(s.n0 + lr - wrow_shift, s.Nw - 1);
+      xoff[q] = (uint32_t)gx * row_bytes + (uint32_t)lc * 16u;
+      woff[q] = (uint32_t)gw * row_bytes + (uint32_t)lc * 16u;
+    }
+    x_lds = smem + wave * 64 * kRowBytes;
+    w_lds = smem + kXBytes + wave * 64 * kRowBytes;
+  }
+
+  // q in [0,16): instruction q of stage kt into LDS slot `slot`
+  __device__ __forceinline__ void issue(int slot, int kt, int q) const {
+    const uint32_t soff = (uint32_t)kt * kRowBytes;
+    if (q < 8)
+      load16_to_lds(xr, x_lds + slot * kStageBytes + q * 8 * kRowBytes, xoff[q], soff);
+    else
+      load16_to_lds(wr, w_lds + slot * kStageBytes + (q - 8) * 8 * kRowBytes, woff[q - 8], soff);
+  }
+
+  __device__ __forceinline__ void issue_all(int slot, int kt) const {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) issue(slot, kt, q);
+  }
 };
 
-// One k32 step's MFMA operands for a wave: 8 token fragments and 8 weight
-// fragments (16 B per lane each).
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+__device__ __forceinline__ void wait_vm16() { __builtin_amdgcn_s_waitcnt(0x4F70); }  // vmcnt(16)
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }  // lgkmcnt(0)
+
+// Barrier without the release fence of __syncthreads (which would also drain
+// the loads still in flight).  The signal fences keep the compiler from
+// moving LDS accesses across it.
+__device__ __forceinline__ void bare_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Prologue: stages 0 and 1 in flight, wait for stage 0.
+template <bool kGated>
+__device__ __forceinline__ void prologue(const LoadPlan<kGated>& lp, int nk) {
+  lp.issue_all(0, 0);
+  if (nk > 1) {
+    lp.issue_all(1, 1);
+    wait_vm16();
+  } else {
+    wait_vm0();
+  }
+  __syncthreads();
+}
+
+// The MFMAs are inline asm, so the compiler's hazard recognizer does not see
+// their accumulator writes and could read an accumulator right after the MFMA
+// that writes it.  Give the last MFMAs time to retire, then re-define every
+// accumulator with an empty asm statement ordered after the wait states: every
+// epilogue read depends on it and so comes later.
+template <class AccT, int NJ, int NI>
+__device__ __forceinline__ void settle_accumulators(AccT& acc) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+#pragma unroll
+    for (int i = 0; i < NI; ++i) asm volatile("" : "+a"(acc.v[j][i]));
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// ===========================================================================
+// bf16 mainloop: v_mfma_f32_16x16x32_bf16, two k32 steps per stage.
+// ===========================================================================
 struct Frags {
   bf16x8_t a[8];  // token subtiles i = 0..7
   bf16x8_t b[8];  // weight subtiles j = 0..7
 };
 
 template <bool kGated>
-__device__ __forceinline__ void read_frags(Frags& f, const char* stage, uint32_t xo, uint32_t wo) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) f.a[i] = *(const bf16x8_t*)(stage + xo + i * 16 * kRowBytes);
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-    f.b[j] = *(const bf16x8_t*)(stage + wo + wrow_of_subtile<kGated>(j) * kRowBytes);
+__device__ __forceinline__ constexpr int wrow_of_subtile(int j) {
+  return kGated ? (j < 4 ? j * 16 : 128 + (j - 4) * 16) : j * 16;
 }
 
-template <int J0, int J1>
-__device__ __forceinline__ void mfma_rows(Acc& acc, const Frags& f) {
-#pragma unroll
-  for (int j = J0; j < J1; ++j)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc.v[j][i] = mfma16x16x32(f.b[j], f.a[i], acc.v[j][i]);
+// fragment q (0..7 token, 8..15 weight) of one step
+template <bool kGated>
+__device__ __forceinline__ void read_frag(Frags& f, int q, const char* stage, uint32_t xo,
+                                          uint32_t wo) {
+  if (q < 8)
+    f.a[q] = *(const bf16x8_t*)(stage + xo + q * 16 * kRowBytes);
+  else
+    f.b[q - 8] = *(const bf16x8_t*)(stage + wo + wrow_of_subtile<kGated>(q - 8) * kRowBytes);
 }
-
-// Scheduling masks of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSchedMfma = 0x008;
-constexpr int kSchedVmem = 0x010;
-constexpr int kSchedDsRead = 0x100;
 
 template <bool kGated>
 __device__ __forceinline__ void mainloop_bf16(Acc& acc, char* smem, const MainloopSrc& s) {
@@ -130,42 +215,10 @@ __device__ __forceinline__ void mainloop_bf16(Acc& acc, char* smem, const Mainlo
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = wave >> 1, wn = wave & 1;
+  const LoadPlan<kGated> lp(s, smem, wave, lane, 2);
 
-  // ---- global -> LDS load plan: wave w fills LDS rows [w*64, w*64+64) of
-  // both tiles with 8 instructions each (8 rows x 128 B per instruction).
-  const uint32_t xbytes = (uint32_t)s.M * (uint32_t)s.K * 2u;
-  const uint32_t wbytes = (uint32_t)s.Nw * (uint32_t)s.K * 2u;
-  const __amdgpu_buffer_rsrc_t xr = make_rsrc(s.X, xbytes);
-  const uint16_t* wsrc = (kGated && wave >= 2) ? s.W1 : s.W0;
-  const __amdgpu_buffer_rsrc_t wr = make_rsrc(wsrc, wbytes);
-  const int wrow_shift = (kGated && wave >= 2) ? 128 : 0;
-  uint32_t xoff[8], woff[8];
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int lr = wave * 64 + q * 8 + (lane >> 3);
-    const int lc = (lane & 7) ^ (lr & 7);
-    const int gx = min(s.m0 + lr, s.M - 1);
-    const int gw = min(s.n0 + lr - wrow_shift, s.Nw - 1);
-    xoff[q] = (uint32_t)gx * (uint32_t)s.K * 2u + (uint32_t)lc * 16u;
-    woff[q] = (uint32_t)gw * (uint32_t)s.K * 2u + (uint32_t)lc * 16u;
-  }
-  char* x_lds_wave = smem + wave * 64 * kRowBytes;
-  char* w_lds_wave = smem + kXBytes + wave * 64 * kRowBytes;
-
-  auto issue_stage = [&](int stage, int kt) {  // prologue only
-    const uint32_t soff = (uint32_t)kt * kRowBytes;
-    char* xs = x_lds_wave + stage * kStageBytes;
-    char* ws = w_lds_wave + stage * kStageBytes;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      load16_to_lds(xr, xs + q * 8 * kRowBytes, xoff[q], soff);
-      load16_to_lds(wr, ws + q * 8 * kRowBytes, woff[q], soff);
-    }
-  };
-
-  // ---- LDS -> register fragment plan.  Lane reads row (base + lane%16),
-  // logical chunk 4*step + lane/16, stored at slot chunk ^ (row & 7) where
-  // row & 7 == lane & 7 because every fragment base is a multiple of 16.
+  // LDS -> register plan: lane reads row (base + lane%16), logical chunk
+  // 4*step + lane/16, stored at slot chunk ^ (row & 7) with row & 7 == lane & 7.
   const int r16 = lane & 15;
   uint32_t xfrag[2], wfrag[2];
 #pragma unroll
@@ -180,32 +233,19 @@ __device__ __forceinline__ void mainloop_bf16(Acc& acc, char* smem, const Mainlo
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc.v[j][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // Software pipeline over stages kt (two k32 steps each; fragment register
-  // sets fa / fb; LDS stages alternate, stage kt lives in slot kt & 1):
-  //   [fa = step 0 of kt already in registers; slot kt&1 holds kt, the other
-  //    slot is receiving kt+1]
+  // Per stage kt (slot kt & 1), with fa = step 0 of kt already in registers:
   //   R1: 16 x {one fb fragment read (step 1 of kt), 4 MFMAs on fa}
-  //   B1: barrier -- every wave has its step-1 fragments, so slot kt&1 is free
+  //   B1: LDS reads drained + barrier: slot kt&1 is free everywhere
   //   R2: 16 x {one 1 KiB load of stage kt+2 into slot kt&1, 2 MFMAs on fb}
-  //   B2: wait for this wave's stage kt+1 loads only (those of kt+2 stay in
-  //       flight), barrier (stage kt+1 complete everywhere)
+  //   B2: this wave's stage kt+1 loads landed (kt+2 stays in flight), barrier
   //   R3: 16 x {one fa fragment read (step 0 of kt+1), 2 MFMAs on fb}
-  // A stage's loads are therefore issued about one and a half stages of MFMA
-  // work before they are needed.  Every group is fenced with
-  // sched_barrier(0) so the compiler keeps this interleaving; the barriers are
-  // plain s_barrier (no release fence, which would also drain the loads still
-  // in flight) after the explicit LDS-read wait they need.
-  const int nk = s.K / kBK;
+  // Every group is fenced with sched_barrier(0) so the compiler keeps this
+  // interleaving; it still inserts the exact waitcnts the reads need.
+  const int nk = s.K / 64;
   Frags fa, fb;
-  issue_stage(0, 0);
-  if (nk > 1) {
-    issue_stage(1, 1);
-    __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt(16): stage 0 landed
-  } else {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  }
-  __syncthreads();
-  read_frags<kGated>(fa, smem, xfrag[0], wfrag[0]);
+  prologue(lp, nk);
+#pragma unroll
+  for (int q = 0; q < 16; ++q) read_frag<kGated>(fa, q, smem, xfrag[0], wfrag[0]);
 
   auto stage = [&](int kt, auto load_tag, auto next_tag) {
     constexpr bool load2 = decltype(load_tag)::value;  // stage kt+2 exists
@@ -213,66 +253,39 @@ __device__ __forceinline__ void mainloop_bf16(Acc& acc, char* smem, const Mainlo
     const int cur = kt & 1;
     const char* base = smem + cur * kStageBytes;
     const char* nbase = smem + (cur ^ 1) * kStageBytes;
-    const uint32_t soff = (uint32_t)(kt + 2) * kRowBytes;
-    char* xs = x_lds_wave + cur * kStageBytes;
-    char* ws = w_lds_wave + cur * kStageBytes;
     __builtin_amdgcn_sched_barrier(0);
-    // R1
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      if (q < 8)
-        fb.a[q] = *(const bf16x8_t*)(base + xfrag[1] + q * 16 * kRowBytes);
-      else
-        fb.b[q - 8] =
-            *(const bf16x8_t*)(base + wfrag[1] + wrow_of_subtile<kGated>(q - 8) * kRowBytes);
+    for (int q = 0; q < 16; ++q) {  // R1
+      read_frag<kGated>(fb, q, base, xfrag[1], wfrag[1]);
       const int j = q >> 1, i0 = (q & 1) * 4;
 #pragma unroll
       for (int i = i0; i < i0 + 4; ++i) mfma16x16x32_acc(acc.v[j][i], fa.b[j], fa.a[i]);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // B1
-    if constexpr (load2) {
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): own step-1 reads done
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      __builtin_amdgcn_s_barrier();
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if constexpr (load2) {  // B1
+      wait_lgkm0();
+      bare_barrier();
       __builtin_amdgcn_sched_barrier(0);
     }
-    // R2
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      if constexpr (load2) {
-        if (q < 8)
-          load16_to_lds(xr, xs + q * 8 * kRowBytes, xoff[q], soff);
-        else
-          load16_to_lds(wr, ws + (q - 8) * 8 * kRowBytes, woff[q - 8], soff);
-      }
+    for (int q = 0; q < 16; ++q) {  // R2
+      if constexpr (load2) lp.issue(cur, kt + 2, q);
       const int j = q >> 2, i0 = (q & 3) * 2;
 #pragma unroll
       for (int i = i0; i < i0 + 2; ++i) mfma16x16x32_acc(acc.v[j][i], fb.b[j], fb.a[i]);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // B2
-    if constexpr (next) {
+    if constexpr (next) {  // B2
       if constexpr (load2)
-        __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt(16): stage kt+1 landed, kt+2 in flight
+        wait_vm16();
       else
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      __builtin_amdgcn_s_barrier();
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        wait_vm0();
+      bare_barrier();
     }
     __builtin_amdgcn_sched_barrier(0);
-    // R3
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      if constexpr (next) {
-        if (q < 8)
-          fa.a[q] = *(const bf16x8_t*)(nbase + xfrag[0] + q * 16 * kRowBytes);
-        else
-          fa.b[q - 8] =
-              *(const bf16x8_t*)(nbase + wfrag[0] + wrow_of_subtile<kGated>(q - 8) * kRowBytes);
-      }
+    for (int q = 0; q < 16; ++q) {  // R3
+      if constexpr (next) read_frag<kGated>(fa, q, nbase, xfrag[0], wfrag[0]);
       const int j = 4 + (q >> 2), i0 = (q & 3) * 2;
 #pragma unroll
       for (int i = i0; i < i0 + 2; ++i) mfma16x16x32_acc(acc.v[j][i], fb.b[j], fb.a[i]);
@@ -282,17 +295,132 @@ __device__ __forceinline__ void mainloop_bf16(Acc& acc, char* smem, const Mainlo
   for (int kt = 0; kt < nk - 2; ++kt) stage(kt, std::true_type{}, std::true_type{});
   if (nk >= 2) stage(nk - 2, std::false_type{}, std::true_type{});
   stage(nk - 1, std::false_type{}, std::false_type{});
-  // The MFMAs are inline asm, so the compiler's hazard recognizer does not
-  // see their accumulator writes and would happily read an accumulator right
-  // after the MFMA that writes it.  Give the last MFMAs time to retire, then
-  // re-define every accumulator with an empty asm statement ordered after the
-  // wait states: every epilogue read depends on it and so comes later.
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  settle_accumulators<Acc, 8, 8>(acc);
+}
+
+// ===========================================================================
+// e4m3 mainloop: v_mfma_f32_32x32x64_f8f6f4 (OCP E4M3FN operands, fp32
+// accumulate), two k64 steps per stage.  A fragment is 32 reduction bytes of
+// one row: two 16 B chunks.
+// ===========================================================================
+struct Frags8 {
+  i32x8_t a[4];  // token subtiles i = 0..3 (32 rows each)
+  i32x8_t b[4];  // weight subtiles j = 0..3
+};
+
+template <bool kGated>
+__device__ __forceinline__ constexpr int wrow_of_subtile8(int j) {
+  return kGated ? (j < 2 ? j * 32 : 128 + (j - 2) * 32) : j * 32;
+}
+
+// fragment q (0..3 token, 4..7 weight) of one step: two 16 B chunk reads
+template <bool kGated>
+__device__ __forceinline__ void read_frag8(Frags8& f, int q, const char* stage, uint32_t xo0,
+                                           uint32_t xo1, uint32_t wo0, uint32_t wo1) {
+  i32x4_t lo, hi;
+  if (q < 4) {
+    lo = *(const i32x4_t*)(stage + xo0 + q * 32 * kRowBytes);
+    hi = *(const i32x4_t*)(stage + xo1 + q * 32 * kRowBytes);
+    f.a[q] = i32x8_t{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  } else {
+    const int off = wrow_of_subtile8<kGated>(q - 4) * kRowBytes;
+    lo = *(const i32x4_t*)(stage + wo0 + off);
+    hi = *(const i32x4_t*)(stage + wo1 + off);
+    f.b[q - 4] = i32x8_t{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  }
+}
+
+template <bool kGated>
+__device__ __forceinline__ void mainloop_fp8(Acc8& acc, char* smem, const MainloopSrc& s) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const LoadPlan<kGated> lp(s, smem, wave, lane, 1);
+
+  // Lane reads row (base + lane%32), logical chunks 4*step + 2*(lane/32) + {0,1};
+  // row & 7 == lane & 7 because every fragment base is a multiple of 32.
+  const int r32 = lane & 31;
+  uint32_t xo[2][2], wo[2][2];
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
+  for (int st = 0; st < 2; ++st)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) asm volatile("" : "+a"(acc.v[j][i]));
-  __builtin_amdgcn_sched_barrier(0);
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t slot = (uint32_t)((st * 4 + 2 * (lane >> 5) + h) ^ (lane & 7)) * 16u;
+      xo[st][h] = (uint32_t)(wm * 128 + r32) * kRowBytes + slot;
+      wo[st][h] =
+          (uint32_t)kXBytes + (uint32_t)(wave_wrow_base<kGated>(wn) + r32) * kRowBytes + slot;
+    }
+
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc.v[j][i][e] = 0.f;
+
+  // Same schedule as the bf16 loop, with 16 MFMAs (of 4x the work) per step:
+  //   R1: 8 x {two fb chunk reads, 2 MFMAs on fa}
+  //   B1; R2: 8 x {two stage kt+2 loads, 1 MFMA on fb (weight subtiles 0,1)}
+  //   B2; R3: 8 x {two fa chunk reads, 1 MFMA on fb (weight subtiles 2,3)}
+  const int nk = s.K / 128;
+  Frags8 fa, fb;
+  prologue(lp, nk);
+#pragma unroll
+  for (int q = 0; q < 8; ++q)
+    read_frag8<kGated>(fa, q, smem, xo[0][0], xo[0][1], wo[0][0], wo[0][1]);
+
+  auto stage = [&](int kt, auto load_tag, auto next_tag) {
+    constexpr bool load2 = decltype(load_tag)::value;
+    constexpr bool next = decltype(next_tag)::value;
+    const int cur = kt & 1;
+    const char* base = smem + cur * kStageBytes;
+    const char* nbase = smem + (cur ^ 1) * kStageBytes;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {  // R1
+      read_frag8<kGated>(fb, q, base, xo[1][0], xo[1][1], wo[1][0], wo[1][1]);
+      const int j = q >> 1, i0 = (q & 1) * 2;
+#pragma unroll
+      for (int i = i0; i < i0 + 2; ++i) mfma32x32x64_f8_acc(acc.v[j][i], fa.b[j], fa.a[i]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (load2) {  // B1
+      wait_lgkm0();
+      bare_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {  // R2
+      if constexpr (load2) {
+        lp.issue(cur, kt + 2, 2 * q);
+        lp.issue(cur, kt + 2, 2 * q + 1);
+      }
+      const int j = q >> 2, i = q & 3;
+      mfma32x32x64_f8_acc(acc.v[j][i], fb.b[j], fb.a[i]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (next) {  // B2
+      if constexpr (load2)
+        wait_vm16();
+      else
+        wait_vm0();
+      bare_barrier();
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {  // R3
+      if constexpr (next)
+        read_frag8<kGated>(fa, q, nbase, xo[0][0], xo[0][1], wo[0][0], wo[0][1]);
+      const int j = 2 + (q >> 2), i = q & 3;
+      mfma32x32x64_f8_acc(acc.v[j][i], fb.b[j], fb.a[i]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  for (int kt = 0; kt < nk - 2; ++kt) stage(kt, std::true_type{}, std::true_type{});
+  if (nk >= 2) stage(nk - 2, std::false_type{}, std::true_type{});
+  stage(nk - 1, std::false_type{}, std::false_type{});
+  settle_accumulators<Acc8, 4, 4>(acc);
 }
 
 }  // namespace coda

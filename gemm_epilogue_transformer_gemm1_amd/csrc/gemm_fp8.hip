@@ -1,0 +1,152 @@
+// e4m3 (OCP E4M3FN) GEMM kernels with epilogue programs, on the fp8 mainloop
+// of gemm_core.hpp.
+//
+// Citations name sections of the news page "CODA: New Research Optimizes
+// Transformer Training with GEMM-Epilogue Programming" (KuCoin news flash).
+// Section "The cost of laziness in large-model training" notes that FP8 makes
+// the matrix products faster while the data movement around them does not
+// shrink, which is what fusing the epilogues removes.
+//
+// Accumulator layout (32x32 tiles): lane L, register r of tile (j, i) holds
+// feature nbase + 32j + 8(r/4) + 4(L/32) + r%4 of token mbase + 32i + L%32.
+// Each group g = r/4 is a run of 4 consecutive features (8 bytes of bf16, 4
+// bytes of e4m3), and a per-token sum over the wave's features is a
+// lane-local sum plus one exchange between lanes L and L^32.
+
+#include "gemm_core.hpp"
+#include "launch.hpp"
+
+namespace coda {
+
+// ---------------------------------------------------------------------------
+// GEMM1 (fp8 operands): h = residual + acc * sa * sw, stored bf16; partial
+// sums of squares and partial amax of the unrounded h; optionally
+// h8 = E4M3(h / s_h) for the fp8 second GEMM (delayed scaling: s_h is a
+// device scalar written by the previous reduction).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads, 1) void k_residual_partialrms_fp8(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ W, const float* __restrict__ a_scale,
+    const float* __restrict__ w_scale, const uint16_t* __restrict__ res, uint16_t* __restrict__ h,
+    float* __restrict__ psum, const float* __restrict__ h8_scale, uint8_t* __restrict__ h8,
+    float* __restrict__ pamax, int M, int N, int K, int gm, int gn) {
+  __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
+  const TileCoord tc = map_tile(blockIdx.x, gm, gn, 8);
+  const int m0 = tc.tm * kBM, n0 = tc.tn * kBN;
+  MainloopSrc src{A, W, nullptr, M, N, K, m0, n0};
+  Acc8 acc;
+  mainloop_fp8<false>(acc, smem, src);
+
+  const float scale = a_scale[0] * w_scale[0];
+  const float s8 = h8 ? h8_scale[0] : 1.0f;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int nw0 = n0 + wn * 128;
+  const int g4 = (lane >> 5) * 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + wm * 128 + i * 32 + (lane & 31);
+    const bool mv = m < M;
+    const size_t row = (size_t)min(m, M - 1) * (size_t)N;
+    float ss = 0.f, amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = nw0 + j * 32 + g * 8 + g4;
+        if (n < N) {
+          float rv[4], hv[4];
+          unpack_bf16x4(*(const u32x2_t*)(res + row + n), rv);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            hv[v] = rv[v] + acc.v[j][i][g * 4 + v] * scale;
+            ss += hv[v] * hv[v];
+            amax = fmaxf(amax, fabsf(hv[v]));
+          }
+          if (mv) {
+            *(u32x2_t*)(h + row + n) = pack_bf16x4(hv[0], hv[1], hv[2], hv[3]);
+            if (h8)
+              *(uint32_t*)(h8 + row + n) =
+                  pack_e4m3x4_sat(hv[0] / s8, hv[1] / s8, hv[2] / s8, hv[3] / s8);
+          }
+        }
+      }
+    }
+    ss += __shfl_xor(ss, 32, 64);
+    amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+    if (mv && lane < 32 && nw0 < N) {
+      const size_t t = (size_t)(nw0 / kRmsTileWidth);
+      psum[t * M + m] = ss;
+      if (pamax) pamax[t * M + m] = amax;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// GEMM2 (fp8 operands): g = r * acc_g * sx * sg, u = r * acc_u * sx * su,
+// out = silu(g) * u (stored bf16).  Output tile 256 tokens x 128 features.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads, 1) void k_rowscale_swiglu_fp8(
+    const uint8_t* __restrict__ X, const float* __restrict__ x_scale,
+    const uint8_t* __restrict__ Wg, const uint8_t* __restrict__ Wu,
+    const float* __restrict__ wg_scale, const float* __restrict__ wu_scale,
+    const float* __restrict__ r, uint16_t* __restrict__ out, int M, int N, int K, int gm, int gn) {
+  __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
+  const TileCoord tc = map_tile(blockIdx.x, gm, gn, 8);
+  const int m0 = tc.tm * kBM, n0 = tc.tn * (kBN / 2);
+  MainloopSrc src{X, Wg, Wu, M, N, K, m0, n0};
+  Acc8 acc;
+  mainloop_fp8<true>(acc, smem, src);
+
+  const float sg = x_scale[0] * wg_scale[0];
+  const float su = x_scale[0] * wu_scale[0];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int nw0 = n0 + wn * 64;
+  const int g4 = (lane >> 5) * 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + wm * 128 + i * 32 + (lane & 31);
+    const bool mv = m < M;
+    const float rr = r[min(m, M - 1)];
+    const size_t row = (size_t)min(m, M - 1) * (size_t)N;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = nw0 + j * 32 + g * 8 + g4;
+        float o[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float gv = acc.v[j][i][g * 4 + v] * sg * rr;
+          const float uv = acc.v[j + 2][i][g * 4 + v] * su * rr;
+          o[v] = silu_f32(gv) * uv;
+        }
+        if (mv && n < N) *(u32x2_t*)(out + row + n) = pack_bf16x4(o[0], o[1], o[2], o[3]);
+      }
+    }
+  }
+}
+
+static inline int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+hipError_t launch_residual_partialrms_fp8(const uint8_t* A, const uint8_t* W, const float* a_scale,
+                                          const float* w_scale, const uint16_t* res, uint16_t* h,
+                                          float* psum, const float* h8_scale, uint8_t* h8,
+                                          float* pamax, int M, int N, int K, hipStream_t stream) {
+  const int gm = cdiv(M, kBM), gn = cdiv(N, kBN);
+  hipLaunchKernelGGL(k_residual_partialrms_fp8, dim3(gm * gn), dim3(kThreads), 0, stream, A, W,
+                     a_scale, w_scale, res, h, psum, h8_scale, h8, pamax, M, N, K, gm, gn);
+  return hipGetLastError();
+}
+
+hipError_t launch_rowscale_swiglu_fp8(const uint8_t* X, const float* x_scale, const uint8_t* Wg,
+                                      const uint8_t* Wu, const float* wg_scale,
+                                      const float* wu_scale, const float* r, uint16_t* out, int M,
+                                      int N, int K, hipStream_t stream) {
+  const int gm = cdiv(M, kBM), gn = cdiv(N, kBN / 2);
+  hipLaunchKernelGGL(k_rowscale_swiglu_fp8, dim3(gm * gn), dim3(kThreads), 0, stream, X, x_scale,
+                     Wg, Wu, wg_scale, wu_scale, r, out, M, N, K, gm, gn);
+  return hipGetLastError();
+}
+
+}  // namespace coda

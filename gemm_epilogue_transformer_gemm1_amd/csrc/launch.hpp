@@ -30,6 +30,15 @@ hipError_t launch_lse_merge(const float* tmax, const float* tsum, const float* l
 hipError_t launch_gemm_plain_bf16(const uint16_t* A, const uint16_t* W, uint16_t* C, int M, int N,
                                   int K, hipStream_t stream);
 
+hipError_t launch_residual_partialrms_fp8(const uint8_t* A, const uint8_t* W, const float* a_scale,
+                                          const float* w_scale, const uint16_t* res, uint16_t* h,
+                                          float* psum, const float* h8_scale, uint8_t* h8,
+                                          float* pamax, int M, int N, int K, hipStream_t stream);
+hipError_t launch_rowscale_swiglu_fp8(const uint8_t* X, const float* x_scale, const uint8_t* Wg,
+                                      const uint8_t* Wu, const float* wg_scale,
+                                      const float* wu_scale, const float* r, uint16_t* out, int M,
+                                      int N, int K, hipStream_t stream);
+
 hipError_t launch_rms_reduce(const float* psum, const float* pamax, int T, int M, int N, float eps,
                              float* r, float* h_amax, float* h8_scale_out, hipStream_t stream);
 hipError_t launch_fold_gamma(const uint16_t* W, const float* gamma, uint16_t* W_out, int N, int K,

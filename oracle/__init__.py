@@ -40,6 +40,7 @@ from .reference import (  # noqa: F401
     swiglu,
     mlp_block,
     fp8_mlp_block,
+    fp8_h_amax,
     rope_tables,
     apply_rope,
     attn_in_block,

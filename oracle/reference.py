@@ -119,6 +119,21 @@ def fp8_mlp_block(xq, sx, res, woq, swo, wgq, swg, wuq, swu, eps, h_scale=None):
             "g": g, "u": u, "out": swiglu(g, u)}
 
 
+def fp8_h_amax(xq, sx, res_bits, woq, swo, chunk=1024):
+    """max |h| over every row of h = res + x W1^T for the fp8 block, in row
+    chunks (the per-tensor scale of h is chosen from it: s_h = amax / 448).
+    res_bits are the residual's bf16 bit patterns."""
+    from .codecs import e4m3_decode, bf16_decode
+
+    wo = e4m3_decode(woq) * float(swo)
+    amax = 0.0
+    for m0 in range(0, xq.shape[0], chunk):
+        x = e4m3_decode(xq[m0:m0 + chunk]) * float(sx)
+        h = residual_add(gemm_nt(x, wo), bf16_decode(res_bits[m0:m0 + chunk]))
+        amax = max(amax, float(np.max(np.abs(h))))
+    return amax
+
+
 # ---------------------------------------------------------------------------
 # attention-input block: GEMM -> residual -> RMSNorm -> QKV GEMM -> RoPE
 # ---------------------------------------------------------------------------

@@ -360,8 +360,16 @@ def pin_fp8_block(seed=13):
     o = oracle.fp8_mlp_block(np.array(xq, dtype=np.uint8), sx, np.array(res),
                              np.array(woq, dtype=np.uint8), swo, np.array(wgq, dtype=np.uint8),
                              swg, np.array(wuq, dtype=np.uint8), swu, eps)
-    return _ok(max(_rel(o["out"], out), _rel(o["h"], h), _rel(o["r"], r)), 1e-12,
-               "fp8 block brute force")
+    # the chunked full-tensor amax reads the residual as bf16 bit patterns, so
+    # the brute force rounds its residual to bf16 for this check
+    res_bits = oracle.codecs.bf16_encode(np.array(res))
+    res_b = oracle.codecs.bf16_decode(res_bits)
+    hb = [[res_b[m][n] + y[m][n] for n in range(d)] for m in range(M)]
+    am_ref = max(abs(v) for row in hb for v in row)
+    am = oracle.fp8_h_amax(np.array(xq, dtype=np.uint8), sx, res_bits,
+                           np.array(woq, dtype=np.uint8), swo, chunk=2)
+    return _ok(max(_rel(o["out"], out), _rel(o["h"], h), _rel(o["r"], r),
+                   abs(am - am_ref) / am_ref), 1e-12, "fp8 block brute force")
 
 
 ALL_PINS = [
