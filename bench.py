@@ -33,6 +33,11 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--no-rows", action="store_true",
+                   help="skip timing the attention-input, LM-head and fp8 workloads")
+    p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                   help="before timing, copy a buffer of this many MiB three times (a plain "
+                        "copy kernel of known size, to scale HBM byte counters)")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="approximate CPU time budget of the oracle baseline")
     return p.parse_args()
@@ -119,6 +124,16 @@ def main():
             per = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(3)] for e in evs])
         return total_ms, wall, per
 
+    if args.calibrate_copy:
+        n = args.calibrate_copy * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] copied {args.calibrate_copy} MiB x3", file=sys.stderr, flush=True)
+        del src, dst
+
     print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         fused_step()
@@ -139,6 +154,10 @@ def main():
     unf_tflops = flops / (unf_ms_step * 1e-3) / 1e12
     g1_ms, red_ms, g2_ms = (float(np.mean(per[:, i])) for i in range(3))
     g2_tflops = flops_g2 / (g2_ms * 1e-3) / 1e12
+
+    rows = {}
+    if not args.no_rows:
+        rows = time_other_rows(torch, ops, inputs, stream, min(args.steps, 10), 3)
 
     cpu = None
     if not args.no_cpu:
@@ -171,10 +190,145 @@ def main():
         "roofline": {"kernel": "gemm_rowscale_swiglu", "bound": "mfma",
                      "achieved": round(g2_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(g2_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": measured_traffic("gemm_rowscale_swiglu"),
+                     "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE, "
+                                     "copy-calibrated)"},
         "cpu_baseline": cpu,
+        "other_rows": rows,
     }
     print(json.dumps(line), flush=True)
+
+
+PEAK_FP8_TFLOPS = 5033.2  # MI355X dense OCP fp8 MFMA, 2.4 GHz
+
+
+def _events_time(torch, stream, fn, steps, warmup):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def time_other_rows(torch, ops, inputs, stream, steps, warmup):
+    """Fused-path step time of the other hot-path workloads (same timing
+    policy: inputs resident in HBM, one stream, HIP events)."""
+    dev = "cuda:0"
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
+        torch.bfloat16).to(dev)
+    u8 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    out = {}
+    eps = 1e-5
+
+    # attention-input block: GEMM1 (K=8192) -> reduce -> QKV GEMM + RoPE
+    print("[bench] attn_rope", file=sys.stderr, flush=True)
+    w = inputs.make_workload("attn_rope")
+    sz = w.sizes
+    M, d, K1 = sz["M"], sz["d"], sz["K1"]
+    nq, nkv, hd = sz["n_q"], sz["n_kv"], sz["head_dim"]
+    x, res, w1, wqkv = (bf(w.arrays[k]) for k in ("x", "res", "w1", "wqkv"))
+    gamma = torch.from_numpy(w.arrays["gamma"]).to(dev)
+    wqkv_f = torch.empty_like(wqkv)
+    ops.fold_gamma(wqkv, gamma, wqkv_f)
+    cos = torch.empty(sz["seq_len"], hd // 2, dtype=torch.float32, device=dev)
+    sin = torch.empty_like(cos)
+    ops.rope_tables(sz["theta"], sz["seq_len"], hd, cos, sin)
+    pos = torch.from_numpy(w.arrays["pos"]).to(dev)
+    h = torch.empty(M, d, dtype=torch.bfloat16, device=dev)
+    P = torch.empty(ops.rms_tiles(d), M, dtype=torch.float32, device=dev)
+    r = torch.empty(M, dtype=torch.float32, device=dev)
+    qkv = torch.empty(M, (nq + 2 * nkv) * hd, dtype=torch.bfloat16, device=dev)
+
+    def attn_step():
+        ops.gemm_residual_partialrms(x, w1, res, h, P)
+        ops.rms_reduce(P, d, eps, r)
+        ops.gemm_rope(h, wqkv_f, r, cos, sin, pos, qkv, nq, nkv, hd)
+    ms = _events_time(torch, stream, attn_step, steps, warmup)
+    fl = 2.0 * M * d * K1 + 2.0 * M * (nq + 2 * nkv) * hd * d
+    out["attn_rope"] = {"workload": "M=8192, d=2048, GEMM1 K=8192, 32 q / 8 kv heads of 64, "
+                                    "RoPE theta=5e5", "ms_per_step": round(ms, 4),
+                        "tflops": round(fl / ms / 1e9, 1),
+                        "pct_of_bf16_peak": round(100 * fl / ms / 1e9 / PEAK_BF16_TFLOPS, 2)}
+    del x, res, w1, wqkv, wqkv_f, h, P, r, qkv, w
+
+    # LM head: block log-sum-exp GEMM + merge
+    print("[bench] lm_head", file=sys.stderr, flush=True)
+    w = inputs.make_workload("lm_head")
+    M, d, V = w.sizes["M"], w.sizes["d"], w.sizes["V"]
+    x, wl = bf(w.arrays["x"]), bf(w.arrays["wlm"])
+    lab = torch.from_numpy(w.arrays["labels"]).to(dev)
+    T = ops.lse_tiles(V)
+    tmax = torch.empty(T, M, dtype=torch.float32, device=dev)
+    tsum = torch.empty_like(tmax)
+    zl, loss = (torch.empty(M, dtype=torch.float32, device=dev) for _ in range(2))
+    ms = _events_time(torch, stream, lambda: ops.gemm_block_lse(x, wl, lab, tmax, tsum, zl, loss),
+                      steps, warmup)
+    fl = 2.0 * M * V * d
+    out["lm_head"] = {"workload": "M=8192, d=2048, V=128256, per-row CE via block LSE",
+                      "ms_per_step": round(ms, 4), "tflops": round(fl / ms / 1e9, 1),
+                      "pct_of_bf16_peak": round(100 * fl / ms / 1e9 / PEAK_BF16_TFLOPS, 2)}
+    del x, wl, tmax, tsum, w
+
+    # fp8 8B-shaped MLP block (delayed scaling: the previous step's scale)
+    print("[bench] mlp_8b_fp8", file=sys.stderr, flush=True)
+    w = inputs.make_workload("mlp_8b_fp8")
+    M, d, K1, ffn = (w.sizes[k] for k in ("M", "d", "K1", "ffn"))
+    x, w1, wg, wu = (u8(w.arrays[k]) for k in ("x", "w1", "wg", "wu"))
+    res = bf(w.arrays["res"])
+    sc = {k: torch.tensor([w.scales[k]], dtype=torch.float32, device=dev)
+          for k in ("x", "w1", "wg", "wu")}
+    h = torch.empty(M, d, dtype=torch.bfloat16, device=dev)
+    h8 = torch.empty(M, d, dtype=torch.uint8, device=dev)
+    T = ops.rms_tiles(d)
+    P, PA = (torch.empty(T, M, dtype=torch.float32, device=dev) for _ in range(2))
+    r = torch.empty(M, dtype=torch.float32, device=dev)
+    amax = torch.empty(1, dtype=torch.float32, device=dev)
+    scales = [torch.ones(1, dtype=torch.float32, device=dev) for _ in range(2)]
+    o = torch.empty(M, ffn, dtype=torch.bfloat16, device=dev)
+    flip = [0]
+
+    def fp8_step():
+        s_in, s_out = scales[flip[0]], scales[1 - flip[0]]
+        ops.gemm_residual_partialrms(x, w1, res, h, P, a_scale=sc["x"], w_scale=sc["w1"],
+                                     h8_scale=s_in, h8=h8, partial_amax=PA)
+        ops.rms_reduce(P, d, eps, r, partial_amax=PA, h_amax=amax, h8_scale_out=s_out)
+        ops.gemm_rowscale_swiglu(h8, wg, wu, r, o, x_scale=s_in, wg_scale=sc["wg"],
+                                 wu_scale=sc["wu"])
+        flip[0] = 1 - flip[0]
+    ms = _events_time(torch, stream, fp8_step, steps, warmup)
+    fl = 2.0 * M * d * K1 + 2.0 * M * 2 * ffn * d
+    out["mlp_8b_fp8"] = {"workload": "M=16384, d=4096, ffn=14336, e4m3 operands, "
+                                     "delayed per-tensor scale of h",
+                         "ms_per_step": round(ms, 4), "tflops": round(fl / ms / 1e9, 1),
+                         "pct_of_fp8_peak": round(100 * fl / ms / 1e9 / PEAK_FP8_TFLOPS, 2)}
+    return out
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, or None when the kernel sources changed since it was taken."""
+    import glob
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    try:
+        with open(os.path.join(root, "profiles", "traffic.json")) as f:
+            rec = json.load(f)[kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(root, "gemm_epilogue_transformer_gemm1_amd", "csrc",
+                                           "*"))):
+        h.update(os.path.basename(p).encode())
+        with open(p, "rb") as f:
+            h.update(f.read())
+    if h.hexdigest() != rec.get("csrc_sha256"):
+        return None
+    return int(rec["fetch_bytes"] + rec["write_bytes"])
 
 
 def cpu_baseline(w, eps, budget_s):
@@ -193,23 +347,27 @@ def cpu_baseline(w, eps, budget_s):
     Wg = codecs.bf16_decode(w.arrays["wg"])
     Wu = codecs.bf16_decode(w.arrays["wu"])
     g = w.arrays["gamma"].astype(np.float64)
-    rows = 128
+    # row chunks of the workload, in order, wrapping around, until the time
+    # budget is spent (at least one chunk)
+    rows = 512
     elapsed, done = 0.0, 0
     while True:
-        x = codecs.bf16_decode(w.arrays["x"][done:done + rows])
-        res = codecs.bf16_decode(w.arrays["res"][done:done + rows])
+        m0 = done % M
+        m1 = min(M, m0 + rows)
+        x = codecs.bf16_decode(w.arrays["x"][m0:m1])
+        res = codecs.bf16_decode(w.arrays["res"][m0:m1])
         t0 = time.perf_counter()
         oracle.mlp_block(x, res, W1, Wg, Wu, g, eps)
         elapsed += time.perf_counter() - t0
-        done += x.shape[0]
-        if elapsed >= budget_s or done >= M:
+        done += m1 - m0
+        if elapsed >= budget_s:
             break
-        rows = min(M - done, max(rows, int(rows * min(4.0, 0.5 * budget_s / max(elapsed, 1e-3)))))
     flops = 2.0 * done * (d * K1 + 2 * ffn * d)
     return {"value": round(flops / elapsed / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"first {done} of {M} token rows of mlp_1b (fp64 numpy, unfused), "
-                      f"{elapsed:.1f} s, host cores visible {len(os.sched_getaffinity(0))}"}
+            "sample": f"{done} token rows of mlp_1b ({done / M:.2f} passes over its {M} rows, "
+                      f"chunks of 512; fp64 numpy, unfused) in {elapsed:.1f} s; "
+                      f"host cores visible {len(os.sched_getaffinity(0))}"}
 
 
 if __name__ == "__main__":
