@@ -19,6 +19,8 @@ BUILD_DIR = os.path.join(HERE, "_build")
 ARCH = "gfx950"
 
 SOURCES = ["coda_abi.cpp", "gemm_bf16.hip", "gemm_fp8.hip", "light_kernels.hip"]
+# sources whose kernels run inline-asm MFMAs: their assembly is hazard-checked
+MFMA_SOURCES = ["gemm_bf16.hip", "gemm_fp8.hip"]
 
 # Packed fp32 VALU forms are kept out of generated code on purpose.
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
@@ -47,10 +49,19 @@ def _compile(src):
     return obj, errs
 
 
+def _check(src):
+    from gemm_epilogue_transformer_gemm1_amd import isa_check
+    flags = [f for f in HIP_FLAGS if f != "-fPIC"] + ["-I", os.path.join(HERE, "..", "include")]
+    return isa_check.check_source(hipcc(), os.path.join(CSRC, src), flags)
+
+
 def build(verbose=False):
     os.makedirs(BUILD_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES) + len(MFMA_SOURCES))) as ex:
+        checks = [ex.submit(_check, s) for s in MFMA_SOURCES]
         results = list(ex.map(_compile, SOURCES))
+        for c in checks:
+            c.result()  # raises if an accumulator access sits too close to an MFMA
     if verbose:
         for (obj, errs) in results:
             if errs.strip():

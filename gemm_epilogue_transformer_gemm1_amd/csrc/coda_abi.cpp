@@ -18,6 +18,7 @@ constexpr int kAbiVersion = 1;
 constexpr int kMaxDevices = 64;
 // 0 = unknown, 1 = gfx950, 2 = other / error
 std::atomic<int> g_arch_state[kMaxDevices];
+std::atomic<int> g_cu_count[kMaxDevices];
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -36,6 +37,8 @@ int check_device() {
       st = 2;
     } else {
       st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+      g_cu_count[dev].store(prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 1,
+                            std::memory_order_release);
     }
     g_arch_state[dev].store(st, std::memory_order_release);
   }
@@ -54,6 +57,16 @@ int check_gemm_shape(int M, int N, int K, int kmul) {
 }
 
 }  // namespace
+
+namespace coda {
+// Only called after check_device() succeeded on the current device.
+int cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  const int n = g_cu_count[dev].load(std::memory_order_acquire);
+  return n > 0 ? n : 256;
+}
+}  // namespace coda
 
 extern "C" {
 

@@ -26,39 +26,64 @@ __global__ __launch_bounds__(kThreads, 1) void k_residual_partialrms_bf16(
     const uint16_t* __restrict__ res, uint16_t* __restrict__ h, float* __restrict__ psum, int M,
     int N, int K, int gm, int gn) {
   __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
-  const TileCoord tc = map_tile(blockIdx.x, gm, gn, 8);
-  const int m0 = tc.tm * kBM, n0 = tc.tn * kBN;
-  MainloopSrc src{A, W, nullptr, M, N, K, m0, n0};
-  Acc acc;
-  mainloop_bf16<false>(acc, smem, src);
-
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int nw0 = n0 + wn * 128;  // first feature of this wave = partial tile start
   const int g4 = (lane >> 4) * 4;
+  const int nt = gm * gn;
+  bool prefetched = false;
+  for (int t = blockIdx.x; t < nt; t += gridDim.x) {
+    const TileCoord tc = map_tile(t, gm, gn, 8);
+    const int m0 = tc.tm * kBM, n0 = tc.tn * kBN;
+    TileChain ch;
+    ch.prefetched = prefetched;
+    const bool has_next = t + (int)gridDim.x < nt;
+    const TileCoord nc = has_next ? map_tile(t + gridDim.x, gm, gn, 8) : tc;
+    ch.next = MainloopSrc{A, W, nullptr, M, N, K, nc.tm * kBM, nc.tn * kBN};
+    const int nw0 = n0 + wn * 128;  // first feature of this wave = partial tile start
+    // the residual of the first four token subtiles (4 features x 8 x 4 per
+    // lane) is loaded during the last stage, ahead of the next tile's loads;
+    // the rest is loaded in the epilogue
+    constexpr int kPre = 1;
+    u32x2_t rv[kPre > 0 ? kPre : 1][8];
+    auto pre = [&]() {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int m = m0 + wm * 128 + i * 16 + (lane & 15);
-    const bool mv = m < M;
-    const size_t row = (size_t)min(m, M - 1) * (size_t)N;
-    float ss = 0.f;
+      for (int i = 0; i < kPre; ++i) {
+        const size_t row = (size_t)min(m0 + wm * 128 + i * 16 + (lane & 15), M - 1) * (size_t)N;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int n = nw0 + j * 16 + g4;
-      if (n < N) {
-        float rv[4];
-        unpack_bf16x4(*(const u32x2_t*)(res + row + n), rv);
-        float hv[4];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          hv[v] = acc.v[j][i][v] + rv[v];
-          ss += hv[v] * hv[v];
+        for (int j = 0; j < 8; ++j) {
+          const int n = min(nw0 + j * 16 + g4, N - 4);
+          rv[i][j] = *(const u32x2_t*)(res + row + n);
         }
-        if (mv) *(u32x2_t*)(h + row + n) = pack_bf16x4(hv[0], hv[1], hv[2], hv[3]);
       }
+    };
+    Acc acc;
+    mainloop_bf16<false>(acc, smem, MainloopSrc{A, W, nullptr, M, N, K, m0, n0}, ch, pre);
+
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int m = m0 + wm * 128 + i * 16 + (lane & 15);
+      const bool mv = m < M;
+      const size_t row = (size_t)min(m, M - 1) * (size_t)N;
+      float ss = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int n = nw0 + j * 16 + g4;
+        if (n < N) {
+          float r4[4];
+          unpack_bf16x4(i < kPre ? rv[i < kPre ? i : 0][j] : *(const u32x2_t*)(res + row + n), r4);
+          float hv[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            hv[v] = acc.v[j][i][v] + r4[v];
+            ss += hv[v] * hv[v];
+          }
+          if (mv) *(u32x2_t*)(h + row + n) = pack_bf16x4(hv[0], hv[1], hv[2], hv[3]);
+        }
+      }
+      ss = sum_over_lane_groups(ss);
+      if (mv && lane < 16 && nw0 < N) psum[(size_t)(nw0 / kRmsTileWidth) * M + m] = ss;
     }
-    ss = sum_over_lane_groups(ss);
-    if (mv && lane < 16 && nw0 < N) psum[(size_t)(nw0 / kRmsTileWidth) * M + m] = ss;
+    prefetched = has_next;
   }
 }
 
@@ -73,34 +98,50 @@ __global__ __launch_bounds__(kThreads, 1) void k_rowscale_swiglu_bf16(
     const uint16_t* __restrict__ Wu, const float* __restrict__ r, uint16_t* __restrict__ out,
     int M, int N, int K, int gm, int gn) {
   __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
-  const TileCoord tc = map_tile(blockIdx.x, gm, gn, 8);
-  const int m0 = tc.tm * kBM, n0 = tc.tn * (kBN / 2);
-  MainloopSrc src{X, Wg, Wu, M, N, K, m0, n0};
-  Acc acc;
-  mainloop_bf16<true>(acc, smem, src);
-
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int nw0 = n0 + wn * 64;
   const int g4 = (lane >> 4) * 4;
+  const int nt = gm * gn;
+  bool prefetched = false;
+  for (int t = blockIdx.x; t < nt; t += gridDim.x) {
+    const TileCoord tc = map_tile(t, gm, gn, 8);
+    const int m0 = tc.tm * kBM, n0 = tc.tn * (kBN / 2);
+    TileChain ch;
+    ch.prefetched = prefetched;
+    const bool has_next = t + (int)gridDim.x < nt;
+    const TileCoord nc = has_next ? map_tile(t + gridDim.x, gm, gn, 8) : tc;
+    ch.next = MainloopSrc{X, Wg, Wu, M, N, K, nc.tm * kBM, nc.tn * (kBN / 2)};
+    float rr[8];
+    auto pre = [&]() {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int m = m0 + wm * 128 + i * 16 + (lane & 15);
-    const bool mv = m < M;
-    const float rr = r[min(m, M - 1)];
-    const size_t row = (size_t)min(m, M - 1) * (size_t)N;
+      for (int i = 0; i < 8; ++i) rr[i] = r[min(m0 + wm * 128 + i * 16 + (lane & 15), M - 1)];
+    };
+    Acc acc;
+    mainloop_bf16<true>(acc, smem, MainloopSrc{X, Wg, Wu, M, N, K, m0, n0}, ch, pre);
+
+    const int nw0 = n0 + wn * 64;
+    const float kNegLog2e = -1.4426950408889634f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = nw0 + j * 16 + g4;
-      float o[4];
+    for (int i = 0; i < 8; ++i) {
+      const int m = m0 + wm * 128 + i * 16 + (lane & 15);
+      const bool mv = m < M;
+      // silu(g) u with g = r a, u = r b:  (a r^2) b / (1 + 2^(-log2e r a))
+      const float r2 = rr[i] * rr[i], c1 = rr[i] * kNegLog2e;
+      const size_t row = (size_t)min(m, M - 1) * (size_t)N;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float g = acc.v[j][i][v] * rr;
-        const float u = acc.v[j + 4][i][v] * rr;
-        o[v] = silu_f32(g) * u;
+      for (int j = 0; j < 4; ++j) {
+        const int n = nw0 + j * 16 + g4;
+        float o[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float a = acc.v[j][i][v], b = acc.v[j + 4][i][v];
+          const float e = __builtin_amdgcn_exp2f(a * c1);
+          o[v] = (a * r2) * b * __builtin_amdgcn_rcpf(1.0f + e);
+        }
+        if (mv && n < N) *(u32x2_t*)(out + row + n) = pack_bf16x4(o[0], o[1], o[2], o[3]);
       }
-      if (mv && n < N) *(u32x2_t*)(out + row + n) = pack_bf16x4(o[0], o[1], o[2], o[3]);
     }
+    prefetched = has_next;
   }
 }
 
@@ -119,53 +160,72 @@ __global__ __launch_bounds__(kThreads, 1) void k_rope_bf16(
     int max_pos, uint16_t* __restrict__ out, int M, int N, int K, int rot_features, int gm,
     int gn) {
   __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
-  const TileCoord tc = map_tile(blockIdx.x, gm, gn, 8);
-  const int m0 = tc.tm * kBM, n0 = tc.tn * kBN;
-  MainloopSrc src{X, W, nullptr, M, N, K, m0, n0};
-  Acc acc;
-  mainloop_bf16<false>(acc, smem, src);
-
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int nw0 = n0 + wn * 128;  // multiple of 128: two whole heads of 64
   const int g4 = (lane >> 4) * 4;
+  const int nt = gm * gn;
+  bool prefetched = false;
+  for (int t = blockIdx.x; t < nt; t += gridDim.x) {
+    const TileCoord tc = map_tile(t, gm, gn, 8);
+    const int m0 = tc.tm * kBM, n0 = tc.tn * kBN;
+    TileChain ch;
+    ch.prefetched = prefetched;
+    const bool has_next = t + (int)gridDim.x < nt;
+    const TileCoord nc = has_next ? map_tile(t + gridDim.x, gm, gn, 8) : tc;
+    ch.next = MainloopSrc{X, W, nullptr, M, N, K, nc.tm * kBM, nc.tn * kBN};
+    float rr[8];
+    int pp[8];
+    auto pre = [&]() {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int m = m0 + wm * 128 + i * 16 + (lane & 15);
-    const bool mv = m < M;
-    const int mc = min(m, M - 1);
-    const float rr = r[mc];
-    // positions outside the table are clamped into it (memory safety)
-    const int p = min(max(pos[mc], 0), max_pos - 1);
-    // angle index of subtile jj (0, 1) of a head: 16*jj + g4 + v
-    const f32x4_t c0 = *(const f32x4_t*)(rcos + (size_t)p * 32 + g4);
-    const f32x4_t c1 = *(const f32x4_t*)(rcos + (size_t)p * 32 + 16 + g4);
-    const f32x4_t s0 = *(const f32x4_t*)(rsin + (size_t)p * 32 + g4);
-    const f32x4_t s1 = *(const f32x4_t*)(rsin + (size_t)p * 32 + 16 + g4);
-    const size_t row = (size_t)mc * (size_t)N;
+      for (int i = 0; i < 8; ++i) {
+        const int mc = min(m0 + wm * 128 + i * 16 + (lane & 15), M - 1);
+        rr[i] = r[mc];
+        pp[i] = pos[mc];
+      }
+    };
+    Acc acc;
+    mainloop_bf16<false>(acc, smem, MainloopSrc{X, W, nullptr, M, N, K, m0, n0}, ch, pre);
+
+    const int nw0 = n0 + wn * 128;  // multiple of 128: two whole heads of 64
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const int hbase = nw0 + hh * 64;
-      if (hbase >= N) continue;
-      const bool rot = hbase < rot_features;
+    for (int i = 0; i < 8; ++i) {
+      const int m = m0 + wm * 128 + i * 16 + (lane & 15);
+      const bool mv = m < M;
+      const int mc = min(m, M - 1);
+      const float rr_i = rr[i];
+      // positions outside the table are clamped into it (memory safety)
+      const int p = min(max(pp[i], 0), max_pos - 1);
+      // angle index of subtile jj (0, 1) of a head: 16*jj + g4 + v
+      const f32x4_t c0 = *(const f32x4_t*)(rcos + (size_t)p * 32 + g4);
+      const f32x4_t c1 = *(const f32x4_t*)(rcos + (size_t)p * 32 + 16 + g4);
+      const f32x4_t s0 = *(const f32x4_t*)(rsin + (size_t)p * 32 + g4);
+      const f32x4_t s1 = *(const f32x4_t*)(rsin + (size_t)p * 32 + 16 + g4);
+      const size_t row = (size_t)mc * (size_t)N;
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const int ja = hh * 4 + jj, jb = ja + 2;
-        const f32x4_t cs = jj ? c1 : c0, sn = jj ? s1 : s0;
-        float lo[4], hi[4];
+      for (int hh = 0; hh < 2; ++hh) {
+        const int hbase = nw0 + hh * 64;
+        if (hbase >= N) continue;
+        const bool rot = hbase < rot_features;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float a = acc.v[ja][i][v] * rr, b = acc.v[jb][i][v] * rr;
-          lo[v] = rot ? a * cs[v] - b * sn[v] : a;
-          hi[v] = rot ? b * cs[v] + a * sn[v] : b;
-        }
-        if (mv) {
-          const int na = hbase + jj * 16 + g4;
-          *(u32x2_t*)(out + row + na) = pack_bf16x4(lo[0], lo[1], lo[2], lo[3]);
-          *(u32x2_t*)(out + row + na + 32) = pack_bf16x4(hi[0], hi[1], hi[2], hi[3]);
+        for (int jj = 0; jj < 2; ++jj) {
+          const int ja = hh * 4 + jj, jb = ja + 2;
+          const f32x4_t cs = jj ? c1 : c0, sn = jj ? s1 : s0;
+          float lo[4], hi[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const float a = acc.v[ja][i][v] * rr_i, b = acc.v[jb][i][v] * rr_i;
+            lo[v] = rot ? a * cs[v] - b * sn[v] : a;
+            hi[v] = rot ? b * cs[v] + a * sn[v] : b;
+          }
+          if (mv) {
+            const int na = hbase + jj * 16 + g4;
+            *(u32x2_t*)(out + row + na) = pack_bf16x4(lo[0], lo[1], lo[2], lo[3]);
+            *(u32x2_t*)(out + row + na + 32) = pack_bf16x4(hi[0], hi[1], hi[2], hi[3]);
+          }
         }
       }
     }
+    prefetched = has_next;
   }
 }
 
@@ -183,56 +243,72 @@ __global__ __launch_bounds__(kThreads, 1) void k_block_lse_bf16(
     const int* __restrict__ labels, float* __restrict__ tmax, float* __restrict__ tsum,
     float* __restrict__ label_logit, int M, int V, int K, int gm, int gn) {
   __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
-  const TileCoord tc = map_tile(blockIdx.x, gm, gn, 8);
-  const int m0 = tc.tm * kBM, n0 = tc.tn * kBN;
-  MainloopSrc src{X, W, nullptr, M, V, K, m0, n0};
-  Acc acc;
-  mainloop_bf16<false>(acc, smem, src);
-
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int nw0 = n0 + wn * kLseTileWidth;
   const int g4 = (lane >> 4) * 4;
   const float kLog2e = 1.4426950408889634f;
+  const int nt = gm * gn;
+  bool prefetched = false;
+  for (int t = blockIdx.x; t < nt; t += gridDim.x) {
+    const TileCoord tc = map_tile(t, gm, gn, 8);
+    const int m0 = tc.tm * kBM, n0 = tc.tn * kBN;
+    TileChain ch;
+    ch.prefetched = prefetched;
+    const bool has_next = t + (int)gridDim.x < nt;
+    const TileCoord nc = has_next ? map_tile(t + gridDim.x, gm, gn, 8) : tc;
+    ch.next = MainloopSrc{X, W, nullptr, M, V, K, nc.tm * kBM, nc.tn * kBN};
+    float rr[8];
+    int lab[8];
+    auto pre = [&]() {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int m = m0 + wm * 128 + i * 16 + (lane & 15);
-    const bool mv = m < M;
-    const int mc = min(m, M - 1);
-    const float rr = r ? r[mc] : 1.0f;
-    const int lab = labels[mc];
-    float mx = -INFINITY;
+      for (int i = 0; i < 8; ++i) {
+        const int mc = min(m0 + wm * 128 + i * 16 + (lane & 15), M - 1);
+        rr[i] = r ? r[mc] : 1.0f;
+        lab[i] = labels[mc];
+      }
+    };
+    Acc acc;
+    mainloop_bf16<false>(acc, smem, MainloopSrc{X, W, nullptr, M, V, K, m0, n0}, ch, pre);
+
+    const int nw0 = n0 + wn * kLseTileWidth;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int n = nw0 + j * 16 + g4;
+    for (int i = 0; i < 8; ++i) {
+      const int m = m0 + wm * 128 + i * 16 + (lane & 15);
+      const bool mv = m < M;
+      const float rr2 = rr[i] * kLog2e;
+      float mx = -INFINITY;
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
-        if (n + v < V) mx = fmaxf(mx, acc.v[j][i][v] * rr);
-    }
-    mx = max_over_lane_groups(mx);
-    const float mx2 = mx * kLog2e;
-    float se = 0.f, zl = 0.f;
-    bool has = false;
+      for (int j = 0; j < 8; ++j) {
+        const int n = nw0 + j * 16 + g4;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int n = nw0 + j * 16 + g4;
+        for (int v = 0; v < 4; ++v)
+          if (n + v < V) mx = fmaxf(mx, acc.v[j][i][v] * rr[i]);
+      }
+      mx = max_over_lane_groups(mx);
+      const float mx2 = mx * kLog2e;
+      float se = 0.f, zl = 0.f;
+      bool has = false;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float z = acc.v[j][i][v] * rr;
-        if (n + v < V) se += __builtin_amdgcn_exp2f(z * kLog2e - mx2);
-        if (n + v == lab) {
-          zl = z;
-          has = true;
+      for (int j = 0; j < 8; ++j) {
+        const int n = nw0 + j * 16 + g4;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          if (n + v < V) se += __builtin_amdgcn_exp2f(acc.v[j][i][v] * rr2 - mx2);
+          if (n + v == lab[i]) {
+            zl = acc.v[j][i][v] * rr[i];
+            has = true;
+          }
         }
       }
+      se = sum_over_lane_groups(se);
+      if (mv && has) label_logit[m] = zl;
+      if (mv && lane < 16 && nw0 < V) {
+        const size_t tt = (size_t)(nw0 / kLseTileWidth);
+        tmax[tt * M + m] = mx;
+        tsum[tt * M + m] = se;
+      }
     }
-    se = sum_over_lane_groups(se);
-    if (mv && has) label_logit[m] = zl;
-    if (mv && lane < 16 && nw0 < V) {
-      const size_t t = (size_t)(nw0 / kLseTileWidth);
-      tmax[t * M + m] = mx;
-      tsum[t * M + m] = se;
-    }
+    prefetched = has_next;
   }
 }
 
@@ -244,28 +320,37 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_plain_bf16(const uint16_t*
                                                                  uint16_t* __restrict__ C, int M,
                                                                  int N, int K, int gm, int gn) {
   __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
-  const TileCoord tc = map_tile(blockIdx.x, gm, gn, 8);
-  const int m0 = tc.tm * kBM, n0 = tc.tn * kBN;
-  MainloopSrc src{A, W, nullptr, M, N, K, m0, n0};
-  Acc acc;
-  mainloop_bf16<false>(acc, smem, src);
-
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int nw0 = n0 + wn * 128;
   const int g4 = (lane >> 4) * 4;
+  const int nt = gm * gn;
+  bool prefetched = false;
+  for (int t = blockIdx.x; t < nt; t += gridDim.x) {
+    const TileCoord tc = map_tile(t, gm, gn, 8);
+    const int m0 = tc.tm * kBM, n0 = tc.tn * kBN;
+    TileChain ch;
+    ch.prefetched = prefetched;
+    const bool has_next = t + (int)gridDim.x < nt;
+    const TileCoord nc = has_next ? map_tile(t + gridDim.x, gm, gn, 8) : tc;
+    ch.next = MainloopSrc{A, W, nullptr, M, N, K, nc.tm * kBM, nc.tn * kBN};
+    Acc acc;
+    mainloop_bf16<false>(acc, smem, MainloopSrc{A, W, nullptr, M, N, K, m0, n0}, ch, [] {});
+
+    const int nw0 = n0 + wn * 128;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int m = m0 + wm * 128 + i * 16 + (lane & 15);
-    if (m >= M) continue;
-    const size_t row = (size_t)m * (size_t)N;
+    for (int i = 0; i < 8; ++i) {
+      const int m = m0 + wm * 128 + i * 16 + (lane & 15);
+      if (m >= M) continue;
+      const size_t row = (size_t)m * (size_t)N;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int n = nw0 + j * 16 + g4;
-      if (n < N)
-        *(u32x2_t*)(C + row + n) =
-            pack_bf16x4(acc.v[j][i][0], acc.v[j][i][1], acc.v[j][i][2], acc.v[j][i][3]);
+      for (int j = 0; j < 8; ++j) {
+        const int n = nw0 + j * 16 + g4;
+        if (n < N)
+          *(u32x2_t*)(C + row + n) =
+              pack_bf16x4(acc.v[j][i][0], acc.v[j][i][1], acc.v[j][i][2], acc.v[j][i][3]);
+      }
     }
+    prefetched = has_next;
   }
 }
 
@@ -278,7 +363,7 @@ hipError_t launch_residual_partialrms_bf16(const uint16_t* A, const uint16_t* W,
                                            const uint16_t* res, uint16_t* h, float* psum, int M,
                                            int N, int K, hipStream_t stream) {
   const int gm = cdiv(M, kBM), gn = cdiv(N, kBN);
-  hipLaunchKernelGGL(k_residual_partialrms_bf16, dim3(gm * gn), dim3(kThreads), 0, stream, A, W,
+  hipLaunchKernelGGL(k_residual_partialrms_bf16, dim3(min(gm * gn, cu_count())), dim3(kThreads), 0, stream, A, W,
                      res, h, psum, M, N, K, gm, gn);
   return hipGetLastError();
 }
@@ -287,7 +372,7 @@ hipError_t launch_rowscale_swiglu_bf16(const uint16_t* X, const uint16_t* Wg, co
                                        const float* r, uint16_t* out, int M, int N, int K,
                                        hipStream_t stream) {
   const int gm = cdiv(M, kBM), gn = cdiv(N, kBN / 2);
-  hipLaunchKernelGGL(k_rowscale_swiglu_bf16, dim3(gm * gn), dim3(kThreads), 0, stream, X, Wg, Wu,
+  hipLaunchKernelGGL(k_rowscale_swiglu_bf16, dim3(min(gm * gn, cu_count())), dim3(kThreads), 0, stream, X, Wg, Wu,
                      r, out, M, N, K, gm, gn);
   return hipGetLastError();
 }
@@ -297,7 +382,7 @@ hipError_t launch_rope_bf16(const uint16_t* X, const uint16_t* W, const float* r
                             uint16_t* out, int M, int K, int n_q, int n_kv, hipStream_t stream) {
   const int N = (n_q + 2 * n_kv) * 64;
   const int gm = cdiv(M, kBM), gn = cdiv(N, kBN);
-  hipLaunchKernelGGL(k_rope_bf16, dim3(gm * gn), dim3(kThreads), 0, stream, X, W, r, rcos, rsin,
+  hipLaunchKernelGGL(k_rope_bf16, dim3(min(gm * gn, cu_count())), dim3(kThreads), 0, stream, X, W, r, rcos, rsin,
                      pos, max_pos, out, M, N, K, (n_q + n_kv) * 64, gm, gn);
   return hipGetLastError();
 }
@@ -306,7 +391,7 @@ hipError_t launch_block_lse_bf16(const uint16_t* X, const uint16_t* W, const flo
                                  const int* labels, float* tmax, float* tsum, float* label_logit,
                                  int M, int V, int K, hipStream_t stream) {
   const int gm = cdiv(M, kBM), gn = cdiv(V, kBN);
-  hipLaunchKernelGGL(k_block_lse_bf16, dim3(gm * gn), dim3(kThreads), 0, stream, X, W, r, labels,
+  hipLaunchKernelGGL(k_block_lse_bf16, dim3(min(gm * gn, cu_count())), dim3(kThreads), 0, stream, X, W, r, labels,
                      tmax, tsum, label_logit, M, V, K, gm, gn);
   return hipGetLastError();
 }
@@ -314,7 +399,7 @@ hipError_t launch_block_lse_bf16(const uint16_t* X, const uint16_t* W, const flo
 hipError_t launch_gemm_plain_bf16(const uint16_t* A, const uint16_t* W, uint16_t* C, int M, int N,
                                   int K, hipStream_t stream) {
   const int gm = cdiv(M, kBM), gn = cdiv(N, kBN);
-  hipLaunchKernelGGL(k_gemm_plain_bf16, dim3(gm * gn), dim3(kThreads), 0, stream, A, W, C, M, N,
+  hipLaunchKernelGGL(k_gemm_plain_bf16, dim3(min(gm * gn, cu_count())), dim3(kThreads), 0, stream, A, W, C, M, N,
                      K, gm, gn);
   return hipGetLastError();
 }

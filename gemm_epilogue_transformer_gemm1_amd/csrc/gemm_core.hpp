@@ -91,6 +91,18 @@ struct MainloopSrc {
   int n0;          // first weight row of the block (per weight matrix)
 };
 
+// Persistent kernels walk several tiles per workgroup.  While a tile's last
+// stage runs, both LDS slots are refilled with the first two stages of the
+// workgroup's next tile, so that tile's loads are in flight during this
+// tile's epilogue and its stores drain while the next tile computes.  The
+// last tile of a workgroup names itself as `next`: the loads are then
+// harmless re-reads that nobody consumes, and the MFMA code has no branch
+// (a branch there makes the register allocator copy accumulators).
+struct TileChain {
+  bool prefetched;   // stages 0 and 1 of this tile are already in flight
+  MainloopSrc next;  // the workgroup's next tile, or this tile if none
+};
+
 // Gated (SwiGLU) blocks: LDS weight rows [0,128) hold gate rows n0.. and
 // [128,256) the same up rows, and a wave owns gate rows [wn*64, +64) and the
 // matching up rows, so gate and up values of one output element sit in the
@@ -209,8 +221,12 @@ __device__ __forceinline__ void read_frag(Frags& f, int q, const char* stage, ui
     f.b[q - 8] = *(const bf16x8_t*)(stage + wo + wrow_of_subtile<kGated>(q - 8) * kRowBytes);
 }
 
-template <bool kGated>
-__device__ __forceinline__ void mainloop_bf16(Acc& acc, char* smem, const MainloopSrc& s) {
+// `pre` runs once, in the last stage, before the next tile's loads are
+// issued: epilogue operands loaded there are not queued behind those loads
+// (vector memory operations complete in order).
+template <bool kGated, class Pre>
+__device__ __forceinline__ void mainloop_bf16(Acc& acc, char* smem, const MainloopSrc& s,
+                                              const TileChain& chain, Pre&& pre) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -228,52 +244,102 @@ __device__ __forceinline__ void mainloop_bf16(Acc& acc, char* smem, const Mainlo
     wfrag[st] = (uint32_t)kXBytes + (uint32_t)(wave_wrow_base<kGated>(wn) + r16) * kRowBytes + slot;
   }
 
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc.v[j][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
   // Per stage kt (slot kt & 1), with fa = step 0 of kt already in registers:
-  //   R1: 16 x {one fb fragment read (step 1 of kt), 4 MFMAs on fa}
-  //   B1: LDS reads drained + barrier: slot kt&1 is free everywhere
-  //   R2: 16 x {one 1 KiB load of stage kt+2 into slot kt&1, 2 MFMAs on fb}
+  //   R1: the 16 fb fragment reads (step 1 of kt) in the first 4 groups of 4
+  //       MFMAs on fa, 2 more groups, then B1 (reads drained + barrier: slot
+  //       kt&1 is free everywhere), then fa's last 10 groups with the first
+  //       10 loads of stage kt+2 into slot kt&1
+  //   R2: 16 x {2 MFMAs on fb}, the last 6 loads in its first groups
   //   B2: this wave's stage kt+1 loads landed (kt+2 stays in flight), barrier
   //   R3: 16 x {one fa fragment read (step 0 of kt+1), 2 MFMAs on fb}
   // Every group is fenced with sched_barrier(0) so the compiler keeps this
   // interleaving; it still inserts the exact waitcnts the reads need.
   const int nk = s.K / 64;
   Frags fa, fb;
-  prologue(lp, nk);
+  if (!chain.prefetched) {
+    prologue(lp, nk);
+  } else {
+    wait_vm0();  // stages 0 / 1 (issued during the previous tile) and its stores
+    __syncthreads();
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc.v[j][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int q = 0; q < 16; ++q) read_frag<kGated>(fa, q, smem, xfrag[0], wfrag[0]);
 
   auto stage = [&](int kt, auto load_tag, auto next_tag) {
     constexpr bool load2 = decltype(load_tag)::value;  // stage kt+2 exists
     constexpr bool next = decltype(next_tag)::value;   // stage kt+1 exists
+    constexpr bool last = !load2 && !next;             // last stage of the tile
     const int cur = kt & 1;
     const char* base = smem + cur * kStageBytes;
     const char* nbase = smem + (cur ^ 1) * kStageBytes;
     __builtin_amdgcn_sched_barrier(0);
+    // R1a: all 16 step-1 fragment reads up front (4 per group of 4 MFMAs on fa)
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {  // R1
-      read_frag<kGated>(fb, q, base, xfrag[1], wfrag[1]);
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) read_frag<kGated>(fb, 4 * q + r, base, xfrag[1], wfrag[1]);
       const int j = q >> 1, i0 = (q & 1) * 4;
 #pragma unroll
       for (int i = i0; i < i0 + 4; ++i) mfma16x16x32_acc(acc.v[j][i], fa.b[j], fa.a[i]);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (load2) {  // B1
+    // R1b: two more groups while the reads drain
+#pragma unroll
+    for (int q = 4; q < 6; ++q) {
+      const int j = q >> 1, i0 = (q & 1) * 4;
+#pragma unroll
+      for (int i = i0; i < i0 + 4; ++i) mfma16x16x32_acc(acc.v[j][i], fa.b[j], fa.a[i]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (load2) {  // B1: slot kt&1 fully read by every wave
       wait_lgkm0();
       bare_barrier();
       __builtin_amdgcn_sched_barrier(0);
     }
+    // R1c: rest of fa's MFMAs, with the first 10 loads of stage kt+2
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {  // R2
-      if constexpr (load2) lp.issue(cur, kt + 2, q);
-      const int j = q >> 2, i0 = (q & 3) * 2;
+    for (int q = 6; q < 16; ++q) {
+      if constexpr (load2) lp.issue(cur, kt + 2, q - 6);
+      const int j = q >> 1, i0 = (q & 1) * 4;
 #pragma unroll
-      for (int i = i0; i < i0 + 2; ++i) mfma16x16x32_acc(acc.v[j][i], fb.b[j], fb.a[i]);
+      for (int i = i0; i < i0 + 4; ++i) mfma16x16x32_acc(acc.v[j][i], fa.b[j], fa.a[i]);
       __builtin_amdgcn_sched_barrier(0);
+    }
+    // R2: first half of fb's MFMAs, with the last 6 loads
+    auto r2 = [&](auto chain_tag) {
+      constexpr bool chained = decltype(chain_tag)::value;
+      if constexpr (chained) {
+        // every wave holds its step-1 fragments, so both slots are free
+        wait_lgkm0();
+        bare_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const LoadPlan<kGated> nlp(chain.next, smem, wave, lane, 2);
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        if constexpr (load2) {
+          if (q < 6) lp.issue(cur, kt + 2, 10 + q);
+        }
+        if constexpr (chained) {
+          nlp.issue(0, 0, q);
+          if (nk > 1) nlp.issue(1, 1, q);
+        }
+        const int j = q >> 2, i0 = (q & 3) * 2;
+#pragma unroll
+        for (int i = i0; i < i0 + 2; ++i) mfma16x16x32_acc(acc.v[j][i], fb.b[j], fb.a[i]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    if constexpr (last) {
+      pre();
+      __builtin_amdgcn_sched_barrier(0);
+      r2(std::true_type{});
+    } else {
+      r2(std::false_type{});
     }
     if constexpr (next) {  // B2
       if constexpr (load2)

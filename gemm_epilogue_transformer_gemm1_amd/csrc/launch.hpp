@@ -11,6 +11,10 @@ namespace coda {
 constexpr int kRmsTileWidth = 128;  // features per partial sum-of-squares tile
 constexpr int kLseTileWidth = 128;  // vocabulary entries per log-sum-exp tile
 
+// Compute units of the current device (persistent GEMM grids launch one
+// workgroup per compute unit); queried once per device.
+int cu_count();
+
 hipError_t launch_residual_partialrms_bf16(const uint16_t* A, const uint16_t* W,
                                            const uint16_t* res, uint16_t* h, float* psum, int M,
                                            int N, int K, hipStream_t stream);
