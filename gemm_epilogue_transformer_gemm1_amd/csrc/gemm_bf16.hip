@@ -40,14 +40,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_residual_partialrms_bf16(
     const TileCoord nc = has_next ? map_tile(t + gridDim.x, gm, gn, 8) : tc;
     ch.next = MainloopSrc{A, W, nullptr, M, N, K, nc.tm * kBM, nc.tn * kBN};
     const int nw0 = n0 + wn * 128;  // first feature of this wave = partial tile start
-    // the residual of the first four token subtiles (4 features x 8 x 4 per
-    // lane) is loaded during the last stage, ahead of the next tile's loads;
-    // the rest is loaded in the epilogue
-    constexpr int kPre = 1;
-    u32x2_t rv[kPre > 0 ? kPre : 1][8];
-    auto pre = [&]() {
+    // the residual tile (4 features x 8 x 8 token subtiles per lane) is
+    // loaded during the last two stages, ahead of the next tile's loads:
+    // token subtiles 0..3 in stage nk-2, 4..7 in the last stage
+    u32x2_t rv[8][8];
+    auto load_res = [&](int i0) {
 #pragma unroll
-      for (int i = 0; i < kPre; ++i) {
+      for (int i = i0; i < i0 + 4; ++i) {
         const size_t row = (size_t)min(m0 + wm * 128 + i * 16 + (lane & 15), M - 1) * (size_t)N;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -57,7 +56,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_residual_partialrms_bf16(
       }
     };
     Acc acc;
-    mainloop_bf16<false>(acc, smem, MainloopSrc{A, W, nullptr, M, N, K, m0, n0}, ch, pre);
+    mainloop_bf16<false>(acc, smem, MainloopSrc{A, W, nullptr, M, N, K, m0, n0}, ch,
+                         [&] { load_res(0); }, [&] { load_res(4); });
 
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -70,7 +70,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_residual_partialrms_bf16(
         const int n = nw0 + j * 16 + g4;
         if (n < N) {
           float r4[4];
-          unpack_bf16x4(i < kPre ? rv[i < kPre ? i : 0][j] : *(const u32x2_t*)(res + row + n), r4);
+          unpack_bf16x4(rv[i][j], r4);
           float hv[4];
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
@@ -117,7 +117,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_rowscale_swiglu_bf16(
       for (int i = 0; i < 8; ++i) rr[i] = r[min(m0 + wm * 128 + i * 16 + (lane & 15), M - 1)];
     };
     Acc acc;
-    mainloop_bf16<true>(acc, smem, MainloopSrc{X, Wg, Wu, M, N, K, m0, n0}, ch, pre);
+    mainloop_bf16<true>(acc, smem, MainloopSrc{X, Wg, Wu, M, N, K, m0, n0}, ch, pre, [] {});
 
     const int nw0 = n0 + wn * 64;
     const float kNegLog2e = -1.4426950408889634f;
@@ -184,7 +184,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_rope_bf16(
       }
     };
     Acc acc;
-    mainloop_bf16<false>(acc, smem, MainloopSrc{X, W, nullptr, M, N, K, m0, n0}, ch, pre);
+    mainloop_bf16<false>(acc, smem, MainloopSrc{X, W, nullptr, M, N, K, m0, n0}, ch, pre, [] {});
 
     const int nw0 = n0 + wn * 128;  // multiple of 128: two whole heads of 64
 #pragma unroll
@@ -268,7 +268,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_block_lse_bf16(
       }
     };
     Acc acc;
-    mainloop_bf16<false>(acc, smem, MainloopSrc{X, W, nullptr, M, V, K, m0, n0}, ch, pre);
+    mainloop_bf16<false>(acc, smem, MainloopSrc{X, W, nullptr, M, V, K, m0, n0}, ch, pre, [] {});
 
     const int nw0 = n0 + wn * kLseTileWidth;
 #pragma unroll
@@ -334,7 +334,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_plain_bf16(const uint16_t*
     const TileCoord nc = has_next ? map_tile(t + gridDim.x, gm, gn, 8) : tc;
     ch.next = MainloopSrc{A, W, nullptr, M, N, K, nc.tm * kBM, nc.tn * kBN};
     Acc acc;
-    mainloop_bf16<false>(acc, smem, MainloopSrc{A, W, nullptr, M, N, K, m0, n0}, ch, [] {});
+    mainloop_bf16<false>(acc, smem, MainloopSrc{A, W, nullptr, M, N, K, m0, n0}, ch, [] {}, [] {});
 
     const int nw0 = n0 + wn * 128;
 #pragma unroll

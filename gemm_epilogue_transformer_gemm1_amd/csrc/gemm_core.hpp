@@ -221,12 +221,15 @@ __device__ __forceinline__ void read_frag(Frags& f, int q, const char* stage, ui
     f.b[q - 8] = *(const bf16x8_t*)(stage + wo + wrow_of_subtile<kGated>(q - 8) * kRowBytes);
 }
 
-// `pre` runs once, in the last stage, before the next tile's loads are
-// issued: epilogue operands loaded there are not queued behind those loads
-// (vector memory operations complete in order).
-template <bool kGated, class Pre>
+// `pre` runs once, in the second-to-last stage (the last one if there is only
+// one), and `pre_last` in the last stage, both before the next tile's loads
+// are issued: epilogue operands loaded there arrive during the last stages
+// and are not queued behind those loads (vector memory operations complete in
+// order).
+template <bool kGated, class Pre, class PreLast>
 __device__ __forceinline__ void mainloop_bf16(Acc& acc, char* smem, const MainloopSrc& s,
-                                              const TileChain& chain, Pre&& pre) {
+                                              const TileChain& chain, Pre&& pre,
+                                              PreLast&& pre_last) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -335,9 +338,14 @@ __device__ __forceinline__ void mainloop_bf16(Acc& acc, char* smem, const Mainlo
       }
     };
     if constexpr (last) {
-      pre();
+      if (nk == 1) pre();  // otherwise already issued in stage nk-2
+      pre_last();
       __builtin_amdgcn_sched_barrier(0);
       r2(std::true_type{});
+    } else if constexpr (!load2) {  // stage nk-2: no stage loads of its own
+      pre();
+      __builtin_amdgcn_sched_barrier(0);
+      r2(std::false_type{});
     } else {
       r2(std::false_type{});
     }
