@@ -35,6 +35,17 @@ __device__ __forceinline__ void load16_to_lds(__amdgpu_buffer_rsrc_t rsrc, void*
                                            0);
 }
 
+// Offset that is out of range of every buffer built by make_rsrc (all are
+// smaller than 2 GiB): a raw-buffer store at this offset is dropped by the
+// hardware range check, so masked lanes can issue the same store
+// instructions as the others.
+constexpr uint32_t kOobOffset = 0x80000000u;
+
+// 8 bytes per lane to rsrc + voffset (dropped if voffset + 8 > the range).
+__device__ __forceinline__ void store8(__amdgpu_buffer_rsrc_t rsrc, u32x2_t v, uint32_t voffset) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, rsrc, voffset, 0, 0);
+}
+
 __device__ __forceinline__ f32x4_t mfma16x16x32(const bf16x8_t& a, const bf16x8_t& b,
                                                 const f32x4_t& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);

@@ -93,6 +93,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_residual_partialrms_bf16(
 // is re-parameterised the same way).  Output tile 256 tokens x 128 features:
 // the block's LDS weight tile holds 128 gate rows and the same 128 up rows.
 // ---------------------------------------------------------------------------
+constexpr int kSwigluStores = 32;  // 8-byte stores per lane per tile
+
 __global__ __launch_bounds__(kThreads, 1) void k_rowscale_swiglu_bf16(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wg,
     const uint16_t* __restrict__ Wu, const float* __restrict__ r, uint16_t* __restrict__ out,
@@ -117,17 +119,22 @@ __global__ __launch_bounds__(kThreads, 1) void k_rowscale_swiglu_bf16(
       for (int i = 0; i < 8; ++i) rr[i] = r[min(m0 + wm * 128 + i * 16 + (lane & 15), M - 1)];
     };
     Acc acc;
-    mainloop_bf16<true>(acc, smem, MainloopSrc{X, Wg, Wu, M, N, K, m0, n0}, ch, pre, [] {});
+    mainloop_bf16<true, kSwigluStores>(acc, smem, MainloopSrc{X, Wg, Wu, M, N, K, m0, n0}, ch,
+                                       pre, [] {});
 
+    // Every lane issues the same 32 stores (masked ones at an out-of-range
+    // offset), which the next tile's first wait counts on.  The buffer starts
+    // at the tile's first row, so offsets stay below 256 * N * 2 bytes.
+    const __amdgpu_buffer_rsrc_t orsrc =
+        make_rsrc(out + (size_t)m0 * N, (uint32_t)min(kBM, M - m0) * (uint32_t)N * 2u);
     const int nw0 = n0 + wn * 64;
     const float kNegLog2e = -1.4426950408889634f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int m = m0 + wm * 128 + i * 16 + (lane & 15);
-      const bool mv = m < M;
+      const int ml = wm * 128 + i * 16 + (lane & 15);  // row within the tile
+      const bool mv = m0 + ml < M;
       // silu(g) u with g = r a, u = r b:  (a r^2) b / (1 + 2^(-log2e r a))
       const float r2 = rr[i] * rr[i], c1 = rr[i] * kNegLog2e;
-      const size_t row = (size_t)min(m, M - 1) * (size_t)N;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int n = nw0 + j * 16 + g4;
@@ -138,7 +145,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_rowscale_swiglu_bf16(
           const float e = __builtin_amdgcn_exp2f(a * c1);
           o[v] = (a * r2) * b * __builtin_amdgcn_rcpf(1.0f + e);
         }
-        if (mv && n < N) *(u32x2_t*)(out + row + n) = pack_bf16x4(o[0], o[1], o[2], o[3]);
+        const uint32_t off = (mv && n < N) ? ((uint32_t)ml * (uint32_t)N + (uint32_t)n) * 2u
+                                           : kOobOffset;
+        store8(orsrc, pack_bf16x4(o[0], o[1], o[2], o[3]), off);
       }
     }
     prefetched = has_next;

@@ -98,6 +98,12 @@ struct MainloopSrc {
 // last tile of a workgroup names itself as `next`: the loads are then
 // harmless re-reads that nobody consumes, and the MFMA code has no branch
 // (a branch there makes the register allocator copy accumulators).
+//
+// The next tile's stage-0 loads are issued first, then its stage-1 loads, then
+// the epilogue's own vector memory operations.  Those retire in issue order,
+// so an epilogue that issues exactly E of them per wave (kEpiVmem = E) lets
+// the next tile wait for stage 0 alone with vmcnt(16 + E) instead of draining
+// its stores first; kEpiVmem < 0 means "not a fixed count" and waits for all.
 struct TileChain {
   bool prefetched;   // stages 0 and 1 of this tile are already in flight
   MainloopSrc next;  // the workgroup's next tile, or this tile if none
@@ -157,8 +163,14 @@ struct LoadPlan {
   }
 };
 
-__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
-__device__ __forceinline__ void wait_vm16() { __builtin_amdgcn_s_waitcnt(0x4F70); }  // vmcnt(16)
+// s_waitcnt vmcnt(n) (n < 64; expcnt and lgkmcnt not waited for)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void wait_vm0() { wait_vm<0>(); }
+__device__ __forceinline__ void wait_vm16() { wait_vm<16>(); }
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }  // lgkmcnt(0)
 
 // Barrier without the release fence of __syncthreads (which would also drain
@@ -226,7 +238,7 @@ __device__ __forceinline__ void read_frag(Frags& f, int q, const char* stage, ui
 // are issued: epilogue operands loaded there arrive during the last stages
 // and are not queued behind those loads (vector memory operations complete in
 // order).
-template <bool kGated, class Pre, class PreLast>
+template <bool kGated, int kEpiVmem = -1, class Pre, class PreLast>
 __device__ __forceinline__ void mainloop_bf16(Acc& acc, char* smem, const MainloopSrc& s,
                                               const TileChain& chain, Pre&& pre,
                                               PreLast&& pre_last) {
@@ -262,7 +274,12 @@ __device__ __forceinline__ void mainloop_bf16(Acc& acc, char* smem, const Mainlo
   if (!chain.prefetched) {
     prologue(lp, nk);
   } else {
-    wait_vm0();  // stages 0 / 1 (issued during the previous tile) and its stores
+    // stage 0, issued during the previous tile before stage 1 and that
+    // tile's epilogue stores
+    if constexpr (kEpiVmem >= 0 && kEpiVmem + 16 < 64)
+      wait_vm<kEpiVmem + 16>();
+    else
+      wait_vm0();
     __syncthreads();
   }
 #pragma unroll
@@ -328,8 +345,18 @@ __device__ __forceinline__ void mainloop_bf16(Acc& acc, char* smem, const Mainlo
           if (q < 6) lp.issue(cur, kt + 2, 10 + q);
         }
         if constexpr (chained) {
-          nlp.issue(0, 0, q);
-          if (nk > 1) nlp.issue(1, 1, q);
+          // all of stage 0, then all of stage 1.  Stage 1 is loaded even
+          // when K has one stage (slot 1 is then never read; past the end of
+          // the buffer the loads return zeros), so the count of operations
+          // in flight behind the epilogue's operand loads is the same on
+          // every path and the compiler's waits for them do not stall.
+          if (q < 8) {
+            nlp.issue(0, 0, 2 * q);
+            nlp.issue(0, 0, 2 * q + 1);
+          } else {
+            nlp.issue(1, 1, 2 * q - 16);
+            nlp.issue(1, 1, 2 * q - 15);
+          }
         }
         const int j = q >> 2, i0 = (q & 3) * 2;
 #pragma unroll

@@ -13,25 +13,40 @@ static inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
 // ---------------------------------------------------------------------------
 // The light reduction (section "CODA: the secret in the epilogue": a light
-// reduction kernel aggregates the partial RMS values).  One thread per token
-// row; consecutive threads read consecutive rows of each partial tile, so
-// every load is coalesced.  Optionally a global amax over the partial amax
-// tiles (fp8 delayed scaling): one atomicMax per block on the non-negative
-// float's bit pattern, which orders like the float.
+// reduction kernel aggregates the partial RMS values).  Four lanes per token
+// row: lane = 16 * g + (row % 16) sums tiles g, g + 4, g + 8, ... with all of
+// its loads issued before the first add (the kernel is latency-bound: a row
+// has only T values), then the four partial sums meet through two lane
+// exchanges.  The 16 lanes of one tile read 16 consecutive rows, so loads are
+// coalesced.  Optionally a global amax over the partial amax tiles (fp8
+// delayed scaling): one atomicMax per block on the non-negative float's bit
+// pattern, which orders like the float.
 // ---------------------------------------------------------------------------
+constexpr int kReduceRowsPerBlock = 64;  // 4 waves x 16 rows
+
 __global__ __launch_bounds__(256) void k_rms_reduce(const float* __restrict__ psum,
                                                     const float* __restrict__ pamax, int T, int M,
                                                     float inv_n, float eps, float* __restrict__ r,
                                                     unsigned int* __restrict__ amax_bits) {
-  const int m = blockIdx.x * 256 + threadIdx.x;
-  float mx = 0.f;
-  if (m < M) {
-    float s = 0.f;
-    for (int t = 0; t < T; ++t) s += psum[(size_t)t * M + m];
-    r[m] = 1.0f / sqrtf(s * inv_n + eps);
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4;
+  const int m = blockIdx.x * kReduceRowsPerBlock + (threadIdx.x >> 6) * 16 + (lane & 15);
+  const bool row_ok = m < M;
+  float s = 0.f, mx = 0.f;
+  if (row_ok) {
+    int t = g;
+    for (; t + 12 < T; t += 16) {  // four tiles per round, loads first
+      const float a0 = psum[(size_t)t * M + m], a1 = psum[(size_t)(t + 4) * M + m];
+      const float a2 = psum[(size_t)(t + 8) * M + m], a3 = psum[(size_t)(t + 12) * M + m];
+      s += (a0 + a1) + (a2 + a3);
+    }
+    for (; t < T; t += 4) s += psum[(size_t)t * M + m];
     if (pamax)
-      for (int t = 0; t < T; ++t) mx = fmaxf(mx, pamax[(size_t)t * M + m]);
+      for (int u = g; u < T; u += 4) mx = fmaxf(mx, pamax[(size_t)u * M + m]);
   }
+  s += __shfl_xor(s, 16, 64);
+  s += __shfl_xor(s, 32, 64);
+  if (row_ok && g == 0) r[m] = 1.0f / sqrtf(s * inv_n + eps);
   if (pamax) {
     __shared__ float red[4];
     for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
@@ -56,8 +71,8 @@ hipError_t launch_rms_reduce(const float* psum, const float* pamax, int T, int M
                              float* r, float* h_amax, float* h8_scale_out, hipStream_t stream) {
   unsigned int* bits = reinterpret_cast<unsigned int*>(h_amax);
   if (pamax) hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(1), 0, stream, bits);
-  hipLaunchKernelGGL(k_rms_reduce, dim3(cdiv(M, 256)), dim3(256), 0, stream, psum, pamax, T, M,
-                     1.0f / (float)N, eps, r, bits);
+  hipLaunchKernelGGL(k_rms_reduce, dim3(cdiv(M, kReduceRowsPerBlock)), dim3(256), 0, stream, psum,
+                     pamax, T, M, 1.0f / (float)N, eps, r, bits);
   if (pamax)
     hipLaunchKernelGGL(k_amax_to_scale, dim3(1), dim3(1), 0, stream, bits, h_amax, h8_scale_out);
   return hipGetLastError();

@@ -43,6 +43,12 @@ def test_gemm1_and_plain_exact(M, N, K):
     assert np.array_equal(bf16_host(C), y)
     assert np.array_equal(bf16_host(h), hh)
     assert np.array_equal(f32_host(P), oracle.partial_sumsq(hh, ops.rms_tile_width()))
+    # the light reduction over T = ceil(N / 128) tiles (T = 1, 3, 32, 64: the
+    # four-lane split of the tiles meets every remainder)
+    r = torch.empty(M, dtype=torch.float32, device=DEV)
+    ops.rms_reduce(P, N, 1e-5, r)
+    torch.cuda.synchronize()
+    assert row_rel_err(f32_host(r), oracle.rms_scale(hh, 1e-5)) <= TOL_ROW
 
 
 @pytest.mark.parametrize("M,N,K", [(8192, 2048, 64), (4096, 4096, 128), (300, 48, 64)])
