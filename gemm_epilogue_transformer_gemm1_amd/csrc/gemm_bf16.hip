@@ -133,8 +133,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_rowscale_swiglu_bf16(
     for (int i = 0; i < 8; ++i) {
       const int ml = wm * 128 + i * 16 + (lane & 15);  // row within the tile
       const bool mv = m0 + ml < M;
-      // silu(g) u with g = r a, u = r b:  (a r^2) b / (1 + 2^(-log2e r a))
-      const float r2 = rr[i] * rr[i], c1 = rr[i] * kNegLog2e;
+      // silu(g) u with g = r a, u = r b:  a b / ((1 + 2^(-log2e r a)) / r^2),
+      // the denominator one fma with 1/r^2 = mean(h^2) + eps (finite)
+      const float s2 = __builtin_amdgcn_rcpf(rr[i] * rr[i]), c1 = rr[i] * kNegLog2e;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int n = nw0 + j * 16 + g4;
@@ -143,7 +144,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_rowscale_swiglu_bf16(
         for (int v = 0; v < 4; ++v) {
           const float a = acc.v[j][i][v], b = acc.v[j + 4][i][v];
           const float e = __builtin_amdgcn_exp2f(a * c1);
-          o[v] = (a * r2) * b * __builtin_amdgcn_rcpf(1.0f + e);
+          o[v] = (a * b) * __builtin_amdgcn_rcpf(__builtin_fmaf(e, s2, s2));
         }
         const uint32_t off = (mv && n < N) ? ((uint32_t)ml * (uint32_t)N + (uint32_t)n) * 2u
                                            : kOobOffset;

@@ -431,8 +431,10 @@ __device__ __forceinline__ void read_frag8(Frags8& f, int q, const char* stage, 
   }
 }
 
-template <bool kGated>
-__device__ __forceinline__ void mainloop_fp8(Acc8& acc, char* smem, const MainloopSrc& s) {
+template <bool kGated, int kEpiVmem = -1, class Pre, class PreLast>
+__device__ __forceinline__ void mainloop_fp8(Acc8& acc, char* smem, const MainloopSrc& s,
+                                             const TileChain& chain, Pre&& pre,
+                                             PreLast&& pre_last) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -453,20 +455,29 @@ __device__ __forceinline__ void mainloop_fp8(Acc8& acc, char* smem, const Mainlo
           (uint32_t)kXBytes + (uint32_t)(wave_wrow_base<kGated>(wn) + r32) * kRowBytes + slot;
     }
 
+  // Same schedule as the bf16 loop, with 16 MFMAs (of 4x the work) per step:
+  //   R1: 8 x {two fb chunk reads, 2 MFMAs on fa}
+  //   B1; R2: 8 x {two stage kt+2 loads, 1 MFMA on fb (weight subtiles 0,1)}
+  //   B2; R3: 8 x {two fa chunk reads, 1 MFMA on fb (weight subtiles 2,3)}
+  // In a tile's last stage R2 starts with a barrier and carries the next
+  // tile's 32 loads (stage 0 in its first four groups, stage 1 in the rest).
+  const int nk = s.K / 128;
+  Frags8 fa, fb;
+  if (!chain.prefetched) {
+    prologue(lp, nk);
+  } else {
+    if constexpr (kEpiVmem >= 0 && kEpiVmem + 16 < 64)
+      wait_vm<kEpiVmem + 16>();
+    else
+      wait_vm0();
+    __syncthreads();
+  }
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc.v[j][i][e] = 0.f;
-
-  // Same schedule as the bf16 loop, with 16 MFMAs (of 4x the work) per step:
-  //   R1: 8 x {two fb chunk reads, 2 MFMAs on fa}
-  //   B1; R2: 8 x {two stage kt+2 loads, 1 MFMA on fb (weight subtiles 0,1)}
-  //   B2; R3: 8 x {two fa chunk reads, 1 MFMA on fb (weight subtiles 2,3)}
-  const int nk = s.K / 128;
-  Frags8 fa, fb;
-  prologue(lp, nk);
 #pragma unroll
   for (int q = 0; q < 8; ++q)
     read_frag8<kGated>(fa, q, smem, xo[0][0], xo[0][1], wo[0][0], wo[0][1]);
@@ -474,6 +485,7 @@ __device__ __forceinline__ void mainloop_fp8(Acc8& acc, char* smem, const Mainlo
   auto stage = [&](int kt, auto load_tag, auto next_tag) {
     constexpr bool load2 = decltype(load_tag)::value;
     constexpr bool next = decltype(next_tag)::value;
+    constexpr bool last = !load2 && !next;
     const int cur = kt & 1;
     const char* base = smem + cur * kStageBytes;
     const char* nbase = smem + (cur ^ 1) * kStageBytes;
@@ -491,15 +503,41 @@ __device__ __forceinline__ void mainloop_fp8(Acc8& acc, char* smem, const Mainlo
       bare_barrier();
       __builtin_amdgcn_sched_barrier(0);
     }
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {  // R2
-      if constexpr (load2) {
-        lp.issue(cur, kt + 2, 2 * q);
-        lp.issue(cur, kt + 2, 2 * q + 1);
+    auto r2 = [&](auto chain_tag) {
+      constexpr bool chained = decltype(chain_tag)::value;
+      if constexpr (chained) {
+        wait_lgkm0();
+        bare_barrier();
+        __builtin_amdgcn_sched_barrier(0);
       }
-      const int j = q >> 2, i = q & 3;
-      mfma32x32x64_f8_acc(acc.v[j][i], fb.b[j], fb.a[i]);
+      const LoadPlan<kGated> nlp(chain.next, smem, wave, lane, 1);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if constexpr (load2) {
+          lp.issue(cur, kt + 2, 2 * q);
+          lp.issue(cur, kt + 2, 2 * q + 1);
+        }
+        if constexpr (chained) {  // see mainloop_bf16: stage 1 is always loaded
+          const int st = q >> 2, q0 = (q & 3) * 4;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) nlp.issue(st, st, q0 + u);
+        }
+        const int j = q >> 2, i = q & 3;
+        mfma32x32x64_f8_acc(acc.v[j][i], fb.b[j], fb.a[i]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    if constexpr (last) {
+      if (nk == 1) pre();
+      pre_last();
       __builtin_amdgcn_sched_barrier(0);
+      r2(std::true_type{});
+    } else if constexpr (!load2) {
+      pre();
+      __builtin_amdgcn_sched_barrier(0);
+      r2(std::false_type{});
+    } else {
+      r2(std::false_type{});
     }
     if constexpr (next) {  // B2
       if constexpr (load2)

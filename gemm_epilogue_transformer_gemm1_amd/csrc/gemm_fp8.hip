@@ -30,54 +30,63 @@ __global__ __launch_bounds__(kThreads, 1) void k_residual_partialrms_fp8(
     float* __restrict__ psum, const float* __restrict__ h8_scale, uint8_t* __restrict__ h8,
     float* __restrict__ pamax, int M, int N, int K, int gm, int gn) {
   __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
-  const TileCoord tc = map_tile(blockIdx.x, gm, gn, 8);
-  const int m0 = tc.tm * kBM, n0 = tc.tn * kBN;
-  MainloopSrc src{A, W, nullptr, M, N, K, m0, n0};
-  Acc8 acc;
-  mainloop_fp8<false>(acc, smem, src);
-
   const float scale = a_scale[0] * w_scale[0];
-  const float s8 = h8 ? h8_scale[0] : 1.0f;
+  const float inv_s8 = h8 ? 1.0f / h8_scale[0] : 1.0f;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int nw0 = n0 + wn * 128;
   const int g4 = (lane >> 5) * 4;
+  const int nt = gm * gn;
+  bool prefetched = false;
+  for (int t = blockIdx.x; t < nt; t += gridDim.x) {
+    const TileCoord tc = map_tile(t, gm, gn, 8);
+    const int m0 = tc.tm * kBM, n0 = tc.tn * kBN;
+    TileChain ch;
+    ch.prefetched = prefetched;
+    const bool has_next = t + (int)gridDim.x < nt;
+    const TileCoord nc = has_next ? map_tile(t + gridDim.x, gm, gn, 8) : tc;
+    ch.next = MainloopSrc{A, W, nullptr, M, N, K, nc.tm * kBM, nc.tn * kBN};
+    Acc8 acc;
+    mainloop_fp8<false>(acc, smem, MainloopSrc{A, W, nullptr, M, N, K, m0, n0}, ch, [] {}, [] {});
+
+    const int nw0 = n0 + wn * 128;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = m0 + wm * 128 + i * 32 + (lane & 31);
-    const bool mv = m < M;
-    const size_t row = (size_t)min(m, M - 1) * (size_t)N;
-    float ss = 0.f, amax = 0.f;
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + wm * 128 + i * 32 + (lane & 31);
+      const bool mv = m < M;
+      const size_t row = (size_t)min(m, M - 1) * (size_t)N;
+      float ss = 0.f, amax = 0.f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < 4; ++j) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = nw0 + j * 32 + g * 8 + g4;
-        if (n < N) {
-          float rv[4], hv[4];
-          unpack_bf16x4(*(const u32x2_t*)(res + row + n), rv);
+        for (int g = 0; g < 4; ++g) {
+          const int n = nw0 + j * 32 + g * 8 + g4;
+          if (n < N) {
+            float rv[4], hv[4];
+            unpack_bf16x4(*(const u32x2_t*)(res + row + n), rv);
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            hv[v] = rv[v] + acc.v[j][i][g * 4 + v] * scale;
-            ss += hv[v] * hv[v];
-            amax = fmaxf(amax, fabsf(hv[v]));
-          }
-          if (mv) {
-            *(u32x2_t*)(h + row + n) = pack_bf16x4(hv[0], hv[1], hv[2], hv[3]);
-            if (h8)
-              *(uint32_t*)(h8 + row + n) =
-                  pack_e4m3x4_sat(hv[0] / s8, hv[1] / s8, hv[2] / s8, hv[3] / s8);
+            for (int v = 0; v < 4; ++v) {
+              hv[v] = rv[v] + acc.v[j][i][g * 4 + v] * scale;
+              ss += hv[v] * hv[v];
+              amax = fmaxf(amax, fabsf(hv[v]));
+            }
+            if (mv) {
+              *(u32x2_t*)(h + row + n) = pack_bf16x4(hv[0], hv[1], hv[2], hv[3]);
+              if (h8)
+                *(uint32_t*)(h8 + row + n) = pack_e4m3x4_sat(hv[0] * inv_s8, hv[1] * inv_s8,
+                                                             hv[2] * inv_s8, hv[3] * inv_s8);
+            }
           }
         }
       }
+      ss += __shfl_xor(ss, 32, 64);
+      amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+      if (mv && lane < 32 && nw0 < N) {
+        const size_t tt = (size_t)(nw0 / kRmsTileWidth);
+        psum[tt * M + m] = ss;
+        if (pamax) pamax[tt * M + m] = amax;
+      }
     }
-    ss += __shfl_xor(ss, 32, 64);
-    amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
-    if (mv && lane < 32 && nw0 < N) {
-      const size_t t = (size_t)(nw0 / kRmsTileWidth);
-      psum[t * M + m] = ss;
-      if (pamax) pamax[t * M + m] = amax;
-    }
+    prefetched = has_next;
   }
 }
 
@@ -85,45 +94,69 @@ __global__ __launch_bounds__(kThreads, 1) void k_residual_partialrms_fp8(
 // GEMM2 (fp8 operands): g = r * acc_g * sx * sg, u = r * acc_u * sx * su,
 // out = silu(g) * u (stored bf16).  Output tile 256 tokens x 128 features.
 // ---------------------------------------------------------------------------
+constexpr int kSwigluStores8 = 32;  // 8-byte stores per lane per tile
+
 __global__ __launch_bounds__(kThreads, 1) void k_rowscale_swiglu_fp8(
     const uint8_t* __restrict__ X, const float* __restrict__ x_scale,
     const uint8_t* __restrict__ Wg, const uint8_t* __restrict__ Wu,
     const float* __restrict__ wg_scale, const float* __restrict__ wu_scale,
     const float* __restrict__ r, uint16_t* __restrict__ out, int M, int N, int K, int gm, int gn) {
   __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
-  const TileCoord tc = map_tile(blockIdx.x, gm, gn, 8);
-  const int m0 = tc.tm * kBM, n0 = tc.tn * (kBN / 2);
-  MainloopSrc src{X, Wg, Wu, M, N, K, m0, n0};
-  Acc8 acc;
-  mainloop_fp8<true>(acc, smem, src);
-
   const float sg = x_scale[0] * wg_scale[0];
-  const float su = x_scale[0] * wu_scale[0];
+  const float sgu = sg * (x_scale[0] * wu_scale[0]);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int nw0 = n0 + wn * 64;
   const int g4 = (lane >> 5) * 4;
+  const int nt = gm * gn;
+  bool prefetched = false;
+  for (int t = blockIdx.x; t < nt; t += gridDim.x) {
+    const TileCoord tc = map_tile(t, gm, gn, 8);
+    const int m0 = tc.tm * kBM, n0 = tc.tn * (kBN / 2);
+    TileChain ch;
+    ch.prefetched = prefetched;
+    const bool has_next = t + (int)gridDim.x < nt;
+    const TileCoord nc = has_next ? map_tile(t + gridDim.x, gm, gn, 8) : tc;
+    ch.next = MainloopSrc{X, Wg, Wu, M, N, K, nc.tm * kBM, nc.tn * (kBN / 2)};
+    float rr[4];
+    auto pre = [&]() {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = m0 + wm * 128 + i * 32 + (lane & 31);
-    const bool mv = m < M;
-    const float rr = r[min(m, M - 1)];
-    const size_t row = (size_t)min(m, M - 1) * (size_t)N;
+      for (int i = 0; i < 4; ++i) rr[i] = r[min(m0 + wm * 128 + i * 32 + (lane & 31), M - 1)];
+    };
+    Acc8 acc;
+    mainloop_fp8<true, kSwigluStores8>(acc, smem, MainloopSrc{X, Wg, Wu, M, N, K, m0, n0}, ch,
+                                       pre, [] {});
+
+    // same store scheme as the bf16 kernel: 32 stores per lane, masked
+    // lanes at an out-of-range offset of a buffer starting at row m0
+    const __amdgpu_buffer_rsrc_t orsrc =
+        make_rsrc(out + (size_t)m0 * N, (uint32_t)min(kBM, M - m0) * (uint32_t)N * 2u);
+    const int nw0 = n0 + wn * 64;
+    const float kNegLog2e = -1.4426950408889634f;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int i = 0; i < 4; ++i) {
+      const int ml = wm * 128 + i * 32 + (lane & 31);
+      const bool mv = m0 + ml < M;
+      // silu(g) u = (a b sx^2 sg su r^2) / (1 + 2^(-log2e sx sg r a))
+      const float c1 = kNegLog2e * sg * rr[i], k = sgu * rr[i] * rr[i];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = nw0 + j * 32 + g * 8 + g4;
-        float o[4];
+      for (int j = 0; j < 2; ++j) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float gv = acc.v[j][i][g * 4 + v] * sg * rr;
-          const float uv = acc.v[j + 2][i][g * 4 + v] * su * rr;
-          o[v] = silu_f32(gv) * uv;
+        for (int g = 0; g < 4; ++g) {
+          const int n = nw0 + j * 32 + g * 8 + g4;
+          float o[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const float a = acc.v[j][i][g * 4 + v], b = acc.v[j + 2][i][g * 4 + v];
+            const float e = __builtin_amdgcn_exp2f(a * c1);
+            o[v] = (a * k) * b * __builtin_amdgcn_rcpf(1.0f + e);
+          }
+          const uint32_t off = (mv && n < N) ? ((uint32_t)ml * (uint32_t)N + (uint32_t)n) * 2u
+                                             : kOobOffset;
+          store8(orsrc, pack_bf16x4(o[0], o[1], o[2], o[3]), off);
         }
-        if (mv && n < N) *(u32x2_t*)(out + row + n) = pack_bf16x4(o[0], o[1], o[2], o[3]);
       }
     }
+    prefetched = has_next;
   }
 }
 
@@ -134,7 +167,8 @@ hipError_t launch_residual_partialrms_fp8(const uint8_t* A, const uint8_t* W, co
                                           float* psum, const float* h8_scale, uint8_t* h8,
                                           float* pamax, int M, int N, int K, hipStream_t stream) {
   const int gm = cdiv(M, kBM), gn = cdiv(N, kBN);
-  hipLaunchKernelGGL(k_residual_partialrms_fp8, dim3(gm * gn), dim3(kThreads), 0, stream, A, W,
+  hipLaunchKernelGGL(k_residual_partialrms_fp8, dim3(min(gm * gn, cu_count())), dim3(kThreads), 0,
+                     stream, A, W,
                      a_scale, w_scale, res, h, psum, h8_scale, h8, pamax, M, N, K, gm, gn);
   return hipGetLastError();
 }
@@ -144,7 +178,8 @@ hipError_t launch_rowscale_swiglu_fp8(const uint8_t* X, const float* x_scale, co
                                       const float* wu_scale, const float* r, uint16_t* out, int M,
                                       int N, int K, hipStream_t stream) {
   const int gm = cdiv(M, kBM), gn = cdiv(N, kBN / 2);
-  hipLaunchKernelGGL(k_rowscale_swiglu_fp8, dim3(gm * gn), dim3(kThreads), 0, stream, X, x_scale,
+  hipLaunchKernelGGL(k_rowscale_swiglu_fp8, dim3(min(gm * gn, cu_count())), dim3(kThreads), 0,
+                     stream, X, x_scale,
                      Wg, Wu, wg_scale, wu_scale, r, out, M, N, K, gm, gn);
   return hipGetLastError();
 }

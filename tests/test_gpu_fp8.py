@@ -58,13 +58,18 @@ def oracle_rows(w, rows=None, eps=EPS, s_h=None):
                                 w.arrays["wu"], w.scales["wu"], eps, h_scale=s_h)
 
 
-def test_fp8_gemm1_integer_exact():
+@pytest.mark.parametrize("M,N,K", [
+    (300, 272, 256),     # ragged M and N
+    (8192, 4096, 128),   # 512 tiles: every workgroup chains, one stage per tile
+    (4096, 8192, 256),   # 512 tiles, two stages
+    (4096, 8192, 384),   # 512 tiles, three stages
+])
+def test_fp8_gemm1_integer_exact(M, N, K):
     """e4m3 codes of -1, 0, 1 with unit scales: h is an exact integer in fp32,
     so h (bf16, rounded once), the partial sums of squares, the partial amax
     and the e4m3 codes of h (scale 1, with some |h| > 448 to hit saturation)
-    must all match the oracle bit for bit.  M and N ragged."""
-    M, N, K = 300, 272, 256
-    rng = np.random.default_rng(1)
+    must all match the oracle bit for bit."""
+    rng = np.random.default_rng(M + N + K)
     a = rng.integers(-1, 2, size=(M, K)).astype(np.float64)
     wt = rng.integers(-1, 2, size=(N, K)).astype(np.float64)
     res = rng.integers(-8, 9, size=(M, N)).astype(np.float64)
@@ -90,6 +95,29 @@ def test_fp8_gemm1_integer_exact():
     ref_am = np.stack([np.max(np.abs(ref_h[:, t * w_:(t + 1) * w_]), axis=1) for t in range(T)])
     assert np.array_equal(f32_host(PA), ref_am)
     assert np.array_equal(h8.cpu().numpy(), codecs.e4m3_encode_fast(ref_h))
+
+
+@pytest.mark.parametrize("M,N,K", [(8192, 2048, 128), (4096, 4096, 256), (300, 48, 384)])
+def test_fp8_swiglu_chained(M, N, K):
+    """fp8 GEMM2 with more tiles than compute units (or a ragged single
+    tile): e4m3 codes of -1, 0, 1 make the pre-activations exact integers;
+    the scales and r are applied in the epilogue."""
+    rng = np.random.default_rng(3 + K)
+    x = rng.integers(-1, 2, size=(M, K)).astype(np.float64)
+    wg = rng.integers(-1, 2, size=(N, K)).astype(np.float64)
+    wu = rng.integers(-1, 2, size=(N, K)).astype(np.float64)
+    r = rng.uniform(0.5, 1.5, size=M)
+    sx, sg, su = 0.5, 0.125, 0.25
+    say(f"fp8 swiglu chained M={M} N={N} K={K}")
+    enc = codecs.e4m3_encode_fast
+    out = torch.empty(M, N, dtype=torch.bfloat16, device=DEV)
+    ops.gemm_rowscale_swiglu(u8_dev(enc(x)), u8_dev(enc(wg)), u8_dev(enc(wu)),
+                             torch.from_numpy(r.astype(np.float32)).to(DEV), out,
+                             x_scale=scalar(sx), wg_scale=scalar(sg), wu_scale=scalar(su))
+    torch.cuda.synchronize()
+    rr = r.astype(np.float32).astype(np.float64)[:, None]
+    ref = oracle.swiglu(rr * sx * sg * oracle.gemm_nt(x, wg), rr * sx * su * oracle.gemm_nt(x, wu))
+    assert norm_err(bf16_host(out), ref) <= TOL_BF16
 
 
 def test_fp8_block_ragged():
