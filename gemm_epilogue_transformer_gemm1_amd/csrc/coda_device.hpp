@@ -41,6 +41,13 @@ __device__ __forceinline__ void load16_to_lds(__amdgpu_buffer_rsrc_t rsrc, void*
 // instructions as the others.
 constexpr uint32_t kOobOffset = 0x80000000u;
 
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16 bytes per lane to rsrc + voffset (dropped if out of range).
+__device__ __forceinline__ void store16(__amdgpu_buffer_rsrc_t rsrc, u32x4_t v, uint32_t voffset) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, rsrc, voffset, 0, 0);
+}
+
 // 8 bytes per lane to rsrc + voffset (dropped if voffset + 8 > the range).
 __device__ __forceinline__ void store8(__amdgpu_buffer_rsrc_t rsrc, u32x2_t v, uint32_t voffset) {
   __builtin_amdgcn_raw_buffer_store_b64(v, rsrc, voffset, 0, 0);

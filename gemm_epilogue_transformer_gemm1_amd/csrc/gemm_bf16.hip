@@ -85,6 +85,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_residual_partialrms_bf16(
     }
     prefetched = has_next;
   }
+  wait_vm0();  // the last tile's unused prefetch into LDS lands before the block ends
 }
 
 // ---------------------------------------------------------------------------
@@ -153,6 +154,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_rowscale_swiglu_bf16(
     }
     prefetched = has_next;
   }
+  wait_vm0();  // the last tile's unused prefetch into LDS lands before the block ends
 }
 
 // ---------------------------------------------------------------------------
@@ -237,6 +239,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_rope_bf16(
     }
     prefetched = has_next;
   }
+  wait_vm0();  // the last tile's unused prefetch into LDS lands before the block ends
 }
 
 // ---------------------------------------------------------------------------
@@ -320,6 +323,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_block_lse_bf16(
     }
     prefetched = has_next;
   }
+  wait_vm0();  // the last tile's unused prefetch into LDS lands before the block ends
 }
 
 // ---------------------------------------------------------------------------
@@ -362,6 +366,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_plain_bf16(const uint16_t*
     }
     prefetched = has_next;
   }
+  wait_vm0();  // the last tile's unused prefetch into LDS lands before the block ends
 }
 
 // ---------------------------------------------------------------------------

@@ -99,11 +99,12 @@ struct MainloopSrc {
 // harmless re-reads that nobody consumes, and the MFMA code has no branch
 // (a branch there makes the register allocator copy accumulators).
 //
-// The next tile's stage-0 loads are issued first, then its stage-1 loads, then
-// the epilogue's own vector memory operations.  Those retire in issue order,
-// so an epilogue that issues exactly E of them per wave (kEpiVmem = E) lets
-// the next tile wait for stage 0 alone with vmcnt(16 + E) instead of draining
-// its stores first; kEpiVmem < 0 means "not a fixed count" and waits for all.
+// The next tile's stage-0 loads are issued first, then its stage-1 loads,
+// then the epilogue's own vector memory operations.  Those retire in issue
+// order, so if the epilogue issues at least E of them per wave
+// (kEpiVmem = E), the next tile waits for its stage 0 alone with
+// vmcnt(min(16 + E, 63)) instead of draining the stores too; kEpiVmem < 0
+// means no such bound and waits for everything.
 struct TileChain {
   bool prefetched;   // stages 0 and 1 of this tile are already in flight
   MainloopSrc next;  // the workgroup's next tile, or this tile if none
@@ -233,11 +234,12 @@ __device__ __forceinline__ void read_frag(Frags& f, int q, const char* stage, ui
     f.b[q - 8] = *(const bf16x8_t*)(stage + wo + wrow_of_subtile<kGated>(q - 8) * kRowBytes);
 }
 
-// `pre` runs once, in the second-to-last stage (the last one if there is only
-// one), and `pre_last` in the last stage, both before the next tile's loads
-// are issued: epilogue operands loaded there arrive during the last stages
-// and are not queued behind those loads (vector memory operations complete in
-// order).
+// `pre` runs once, in the second-to-last stage after its end-of-stage wait
+// (in the last stage if there is only one), and `pre_last` in the last stage,
+// both before the next tile's loads are issued: epilogue operands loaded
+// there arrive during the last stages and are not queued behind those loads
+// (vector memory operations complete in order), and no stage wait includes
+// them.
 template <bool kGated, int kEpiVmem = -1, class Pre, class PreLast>
 __device__ __forceinline__ void mainloop_bf16(Acc& acc, char* smem, const MainloopSrc& s,
                                               const TileChain& chain, Pre&& pre,
@@ -275,9 +277,9 @@ __device__ __forceinline__ void mainloop_bf16(Acc& acc, char* smem, const Mainlo
     prologue(lp, nk);
   } else {
     // stage 0, issued during the previous tile before stage 1 and that
-    // tile's epilogue stores
-    if constexpr (kEpiVmem >= 0 && kEpiVmem + 16 < 64)
-      wait_vm<kEpiVmem + 16>();
+    // tile's epilogue operations
+    if constexpr (kEpiVmem >= 0)
+      wait_vm<(kEpiVmem + 16 < 63 ? kEpiVmem + 16 : 63)>();
     else
       wait_vm0();
     __syncthreads();
@@ -369,10 +371,6 @@ __device__ __forceinline__ void mainloop_bf16(Acc& acc, char* smem, const Mainlo
       pre_last();
       __builtin_amdgcn_sched_barrier(0);
       r2(std::true_type{});
-    } else if constexpr (!load2) {  // stage nk-2: no stage loads of its own
-      pre();
-      __builtin_amdgcn_sched_barrier(0);
-      r2(std::false_type{});
     } else {
       r2(std::false_type{});
     }
@@ -383,6 +381,9 @@ __device__ __forceinline__ void mainloop_bf16(Acc& acc, char* smem, const Mainlo
         wait_vm0();
       bare_barrier();
     }
+    // stage nk-2 (no stage loads of its own): the epilogue operand loads go
+    // out after B2's wait, so that wait does not include them
+    if constexpr (!load2 && next) pre();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int q = 0; q < 16; ++q) {  // R3
@@ -466,8 +467,8 @@ __device__ __forceinline__ void mainloop_fp8(Acc8& acc, char* smem, const Mainlo
   if (!chain.prefetched) {
     prologue(lp, nk);
   } else {
-    if constexpr (kEpiVmem >= 0 && kEpiVmem + 16 < 64)
-      wait_vm<kEpiVmem + 16>();
+    if constexpr (kEpiVmem >= 0)  // as in mainloop_bf16
+      wait_vm<(kEpiVmem + 16 < 63 ? kEpiVmem + 16 : 63)>();
     else
       wait_vm0();
     __syncthreads();
@@ -532,10 +533,6 @@ __device__ __forceinline__ void mainloop_fp8(Acc8& acc, char* smem, const Mainlo
       pre_last();
       __builtin_amdgcn_sched_barrier(0);
       r2(std::true_type{});
-    } else if constexpr (!load2) {
-      pre();
-      __builtin_amdgcn_sched_barrier(0);
-      r2(std::false_type{});
     } else {
       r2(std::false_type{});
     }
@@ -546,6 +543,7 @@ __device__ __forceinline__ void mainloop_fp8(Acc8& acc, char* smem, const Mainlo
         wait_vm0();
       bare_barrier();
     }
+    if constexpr (!load2 && next) pre();  // as in mainloop_bf16
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int q = 0; q < 8; ++q) {  // R3

@@ -24,6 +24,12 @@ namespace coda {
 // h8 = E4M3(h / s_h) for the fp8 second GEMM (delayed scaling: s_h is a
 // device scalar written by the previous reduction).
 // ---------------------------------------------------------------------------
+// At least this many vector memory operations per lane follow a tile's
+// prefetch of the next tile (the 16-byte h stores; the residual loads, h8
+// and partial stores come on top), so the next tile waits for its stage 0
+// without draining them.
+constexpr int kGemm1Stores8 = 32;
+
 __global__ __launch_bounds__(kThreads, 1) void k_residual_partialrms_fp8(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ W, const float* __restrict__ a_scale,
     const float* __restrict__ w_scale, const uint16_t* __restrict__ res, uint16_t* __restrict__ h,
@@ -45,56 +51,104 @@ __global__ __launch_bounds__(kThreads, 1) void k_residual_partialrms_fp8(
     const bool has_next = t + (int)gridDim.x < nt;
     const TileCoord nc = has_next ? map_tile(t + gridDim.x, gm, gn, 8) : tc;
     ch.next = MainloopSrc{A, W, nullptr, M, N, K, nc.tm * kBM, nc.tn * kBN};
-    Acc8 acc;
-    mainloop_fp8<false>(acc, smem, MainloopSrc{A, W, nullptr, M, N, K, m0, n0}, ch, [] {}, [] {});
-
     const int nw0 = n0 + wn * 128;
+    // the residual tile (16 runs of 4 features x 4 token subtiles per lane)
+    // is loaded at the start of the epilogue into the registers the fragments
+    // used (loaded during the last stages it would make their waits longer
+    // and push the mainloop into spills)
+    u32x2_t rq[4][16];
+    auto load_res = [&](int i0) {
+#pragma unroll
+      for (int i = i0; i < i0 + 2; ++i) {
+        const size_t row = (size_t)min(m0 + wm * 128 + i * 32 + (lane & 31), M - 1) * (size_t)N;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int n = min(nw0 + (q >> 2) * 32 + (q & 3) * 8 + g4, N - 4);
+          rq[i][q] = *(const u32x2_t*)(res + row + n);
+        }
+      }
+    };
+    Acc8 acc;
+    mainloop_fp8<false, kGemm1Stores8>(acc, smem, MainloopSrc{A, W, nullptr, M, N, K, m0, n0},
+                                       ch, [] {}, [] {});
+    load_res(0);
+    load_res(2);
+
+    // Lanes L and L + 32 hold the runs 8g + 0..3 and 8g + 4..7 (g = 0..3) of
+    // the same row in each 32-feature block j.  Exchanges between them give
+    // every lane contiguous output: for h, one whole 8-feature run per pair
+    // of runs (two 16-byte stores per block); for h8, features 0..15 (lane L)
+    // or 16..31 (lane L + 32) of the block (one 16-byte store).  Each store
+    // then covers 32 rows with 32 contiguous bytes a row, instead of 8 or 4
+    // bytes from each of two lanes: the store path pays per row touched.
+    // Buffers start at the tile's first row; masked lanes store out of range.
+    const uint32_t rows_here = (uint32_t)min(kBM, M - m0);
+    const __amdgpu_buffer_rsrc_t hrsrc = make_rsrc(h + (size_t)m0 * N, rows_here * (uint32_t)N * 2u);
+    const __amdgpu_buffer_rsrc_t qrsrc =
+        make_rsrc(h8 ? h8 + (size_t)m0 * N : nullptr, h8 ? rows_here * (uint32_t)N : 0u);
+    const bool hi = lane >= 32;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int m = m0 + wm * 128 + i * 32 + (lane & 31);
-      const bool mv = m < M;
-      const size_t row = (size_t)min(m, M - 1) * (size_t)N;
+      const int ml = wm * 128 + i * 32 + (lane & 31);  // row within the tile
+      const bool mv = m0 + ml < M;
+      const uint32_t erow = (uint32_t)ml * (uint32_t)N;
       float ss = 0.f, amax = 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
+        u32x2_t hb[4];
+        uint32_t qb[4];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int n = nw0 + j * 32 + g * 8 + g4;
-          if (n < N) {
-            float rv[4], hv[4];
-            unpack_bf16x4(*(const u32x2_t*)(res + row + n), rv);
+          const bool nv = nw0 + j * 32 + g * 8 + g4 < N;
+          float rv[4], hv[4];
+          unpack_bf16x4(rq[i][j * 4 + g], rv);
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              hv[v] = rv[v] + acc.v[j][i][g * 4 + v] * scale;
-              ss += hv[v] * hv[v];
-              amax = fmaxf(amax, fabsf(hv[v]));
-            }
-            if (mv) {
-              *(u32x2_t*)(h + row + n) = pack_bf16x4(hv[0], hv[1], hv[2], hv[3]);
-              if (h8)
-                *(uint32_t*)(h8 + row + n) = pack_e4m3x4_sat(hv[0] * inv_s8, hv[1] * inv_s8,
-                                                             hv[2] * inv_s8, hv[3] * inv_s8);
-            }
+          for (int v = 0; v < 4; ++v) {
+            hv[v] = rv[v] + acc.v[j][i][g * 4 + v] * scale;
+            ss += nv ? hv[v] * hv[v] : 0.f;
+            amax = nv ? fmaxf(amax, fabsf(hv[v])) : amax;
           }
+          hb[g] = pack_bf16x4(hv[0], hv[1], hv[2], hv[3]);
+          qb[g] = pack_e4m3x4_sat(hv[0] * inv_s8, hv[1] * inv_s8, hv[2] * inv_s8, hv[3] * inv_s8);
+        }
+#pragma unroll
+        for (int gp = 0; gp < 4; gp += 2) {  // h: runs gp (lane L) and gp + 1 (lane L + 32)
+          const int n = nw0 + j * 32 + (gp + (hi ? 1 : 0)) * 8;
+          const u32x2_t hs = hi ? hb[gp] : hb[gp + 1];
+          const u32x2_t hr = {(unsigned)__shfl_xor((int)hs.x, 32, 64),
+                              (unsigned)__shfl_xor((int)hs.y, 32, 64)};
+          store16(hrsrc,
+                  hi ? u32x4_t{hr.x, hr.y, hb[gp + 1].x, hb[gp + 1].y}
+                     : u32x4_t{hb[gp].x, hb[gp].y, hr.x, hr.y},
+                  (mv && n < N) ? (erow + (uint32_t)n) * 2u : kOobOffset);
+        }
+        if (h8) {  // lane L: features 0..15 of the block, lane L + 32: 16..31
+          const int n = nw0 + j * 32 + (hi ? 16 : 0);
+          const uint32_t q0 = hi ? qb[0] : qb[2], q1 = hi ? qb[1] : qb[3];
+          const uint32_t r0 = (unsigned)__shfl_xor((int)q0, 32, 64);
+          const uint32_t r1 = (unsigned)__shfl_xor((int)q1, 32, 64);
+          store16(qrsrc, hi ? u32x4_t{r0, qb[2], r1, qb[3]} : u32x4_t{qb[0], r0, qb[1], r1},
+                  (mv && n < N) ? erow + (uint32_t)n : kOobOffset);
         }
       }
       ss += __shfl_xor(ss, 32, 64);
       amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
       if (mv && lane < 32 && nw0 < N) {
         const size_t tt = (size_t)(nw0 / kRmsTileWidth);
-        psum[tt * M + m] = ss;
-        if (pamax) pamax[tt * M + m] = amax;
+        psum[tt * M + m0 + ml] = ss;
+        if (pamax) pamax[tt * M + m0 + ml] = amax;
       }
     }
     prefetched = has_next;
   }
+  wait_vm0();  // the last tile's unused prefetch into LDS lands before the block ends
 }
 
 // ---------------------------------------------------------------------------
 // GEMM2 (fp8 operands): g = r * acc_g * sx * sg, u = r * acc_u * sx * su,
 // out = silu(g) * u (stored bf16).  Output tile 256 tokens x 128 features.
 // ---------------------------------------------------------------------------
-constexpr int kSwigluStores8 = 32;  // 8-byte stores per lane per tile
+constexpr int kSwigluStores8 = 16;  // 16-byte stores per lane per tile
 
 __global__ __launch_bounds__(kThreads, 1) void k_rowscale_swiglu_fp8(
     const uint8_t* __restrict__ X, const float* __restrict__ x_scale,
@@ -106,7 +160,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_rowscale_swiglu_fp8(
   const float sgu = sg * (x_scale[0] * wu_scale[0]);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int g4 = (lane >> 5) * 4;
   const int nt = gm * gn;
   bool prefetched = false;
   for (int t = blockIdx.x; t < nt; t += gridDim.x) {
@@ -126,11 +179,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_rowscale_swiglu_fp8(
     mainloop_fp8<true, kSwigluStores8>(acc, smem, MainloopSrc{X, Wg, Wu, M, N, K, m0, n0}, ch,
                                        pre, [] {});
 
-    // same store scheme as the bf16 kernel: 32 stores per lane, masked
-    // lanes at an out-of-range offset of a buffer starting at row m0
+    // 16 stores per lane (masked ones at an out-of-range offset of a buffer
+    // starting at row m0); lanes L and L + 32 exchange halves of their 4-run
+    // pairs so that each stores a whole 8-feature run (see GEMM1 above).
     const __amdgpu_buffer_rsrc_t orsrc =
         make_rsrc(out + (size_t)m0 * N, (uint32_t)min(kBM, M - m0) * (uint32_t)N * 2u);
     const int nw0 = n0 + wn * 64;
+    const bool hi = lane >= 32;
     const float kNegLog2e = -1.4426950408889634f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -141,23 +196,34 @@ __global__ __launch_bounds__(kThreads, 1) void k_rowscale_swiglu_fp8(
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int n = nw0 + j * 32 + g * 8 + g4;
-          float o[4];
+        for (int gp = 0; gp < 4; gp += 2) {
+          u32x2_t ob[2];
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const float a = acc.v[j][i][g * 4 + v], b = acc.v[j + 2][i][g * 4 + v];
-            const float e = __builtin_amdgcn_exp2f(a * c1);
-            o[v] = (a * k) * b * __builtin_amdgcn_rcpf(1.0f + e);
+          for (int u = 0; u < 2; ++u) {
+            const int g = gp + u;
+            float o[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const float a = acc.v[j][i][g * 4 + v], b = acc.v[j + 2][i][g * 4 + v];
+              const float e = __builtin_amdgcn_exp2f(a * c1);
+              o[v] = (a * k) * b * __builtin_amdgcn_rcpf(1.0f + e);
+            }
+            ob[u] = pack_bf16x4(o[0], o[1], o[2], o[3]);
           }
+          const int n = nw0 + j * 32 + (gp + (hi ? 1 : 0)) * 8;
+          const u32x2_t os = hi ? ob[0] : ob[1];
+          const u32x2_t orx = {(unsigned)__shfl_xor((int)os.x, 32, 64),
+                               (unsigned)__shfl_xor((int)os.y, 32, 64)};
           const uint32_t off = (mv && n < N) ? ((uint32_t)ml * (uint32_t)N + (uint32_t)n) * 2u
                                              : kOobOffset;
-          store8(orsrc, pack_bf16x4(o[0], o[1], o[2], o[3]), off);
+          store16(orsrc, hi ? u32x4_t{orx.x, orx.y, ob[1].x, ob[1].y}
+                            : u32x4_t{ob[0].x, ob[0].y, orx.x, orx.y}, off);
         }
       }
     }
     prefetched = has_next;
   }
+  wait_vm0();  // the last tile's unused prefetch into LDS lands before the block ends
 }
 
 static inline int cdiv(int a, int b) { return (a + b - 1) / b; }

@@ -40,6 +40,14 @@ def u8_dev(a):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).to(DEV)
 
 
+def bf16_encode_few(x):
+    """The oracle's bf16 encoder applied to each distinct value of `x` and
+    mapped back: the same bits, fast for large arrays of few values (the
+    integer-exact tests)."""
+    vals, inv = np.unique(np.asarray(x, dtype=np.float64), return_inverse=True)
+    return codecs.bf16_encode(vals)[inv].reshape(np.shape(x))
+
+
 def bf16_host(t):
     """torch.bfloat16 device tensor -> float64 numpy (via the oracle's decoder)."""
     bits = t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
