@@ -94,7 +94,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_residual_partialrms_bf16(
 // is re-parameterised the same way).  Output tile 256 tokens x 128 features:
 // the block's LDS weight tile holds 128 gate rows and the same 128 up rows.
 // ---------------------------------------------------------------------------
-constexpr int kSwigluStores = 32;  // 8-byte stores per lane per tile
+constexpr int kSwigluStores = 16;  // 16-byte stores per lane per tile
 
 __global__ __launch_bounds__(kThreads, 1) void k_rowscale_swiglu_bf16(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wg,
@@ -103,7 +103,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_rowscale_swiglu_bf16(
   __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int g4 = (lane >> 4) * 4;
   const int nt = gm * gn;
   bool prefetched = false;
   for (int t = blockIdx.x; t < nt; t += gridDim.x) {
@@ -123,12 +122,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_rowscale_swiglu_bf16(
     mainloop_bf16<true, kSwigluStores>(acc, smem, MainloopSrc{X, Wg, Wu, M, N, K, m0, n0}, ch,
                                        pre, [] {});
 
-    // Every lane issues the same 32 stores (masked ones at an out-of-range
+    // Lane L = 16 g + r holds the run of 4 features 16 j + 4 g of token r
+    // for each subtile j.  For a pair of subtiles (j0, j0 + 1), lanes g and
+    // g ^ 1 exchange one run, so that every lane holds 8 contiguous features
+    // and one 16-byte store writes 64 contiguous bytes of each of 16 rows
+    // (instead of 4 runs of 8 bytes): the store path pays per row touched.
+    // Every lane issues the same 16 stores (masked ones at an out-of-range
     // offset), which the next tile's first wait counts on.  The buffer starts
     // at the tile's first row, so offsets stay below 256 * N * 2 bytes.
     const __amdgpu_buffer_rsrc_t orsrc =
         make_rsrc(out + (size_t)m0 * N, (uint32_t)min(kBM, M - m0) * (uint32_t)N * 2u);
     const int nw0 = n0 + wn * 64;
+    const int g = lane >> 4;
+    const bool godd = (g & 1) != 0;
     const float kNegLog2e = -1.4426950408889634f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -138,18 +144,29 @@ __global__ __launch_bounds__(kThreads, 1) void k_rowscale_swiglu_bf16(
       // the denominator one fma with 1/r^2 = mean(h^2) + eps (finite)
       const float s2 = __builtin_amdgcn_rcpf(rr[i] * rr[i]), c1 = rr[i] * kNegLog2e;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int n = nw0 + j * 16 + g4;
-        float o[4];
+      for (int j0 = 0; j0 < 4; j0 += 2) {
+        u32x2_t pk[2];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float a = acc.v[j][i][v], b = acc.v[j + 4][i][v];
-          const float e = __builtin_amdgcn_exp2f(a * c1);
-          o[v] = (a * b) * __builtin_amdgcn_rcpf(__builtin_fmaf(e, s2, s2));
+        for (int u = 0; u < 2; ++u) {
+          const int j = j0 + u;
+          float o[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const float a = acc.v[j][i][v], b = acc.v[j + 4][i][v];
+            const float e = __builtin_amdgcn_exp2f(a * c1);
+            o[v] = (a * b) * __builtin_amdgcn_rcpf(__builtin_fmaf(e, s2, s2));
+          }
+          pk[u] = pack_bf16x4(o[0], o[1], o[2], o[3]);
         }
+        const u32x2_t sd = godd ? pk[0] : pk[1];
+        const u32x2_t rv = {(unsigned)__shfl_xor((int)sd.x, 16, 64),
+                            (unsigned)__shfl_xor((int)sd.y, 16, 64)};
+        // even g: features 16 j0 + 8 (g/2) + 0..7; odd g: the same in j0 + 1
+        const int n = nw0 + 16 * (j0 + (godd ? 1 : 0)) + 8 * (g >> 1);
         const uint32_t off = (mv && n < N) ? ((uint32_t)ml * (uint32_t)N + (uint32_t)n) * 2u
                                            : kOobOffset;
-        store8(orsrc, pack_bf16x4(o[0], o[1], o[2], o[3]), off);
+        store16(orsrc, godd ? u32x4_t{rv.x, rv.y, pk[1].x, pk[1].y}
+                            : u32x4_t{pk[0].x, pk[0].y, rv.x, rv.y}, off);
       }
     }
     prefetched = has_next;
