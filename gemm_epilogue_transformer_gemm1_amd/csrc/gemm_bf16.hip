@@ -301,37 +301,56 @@ __global__ __launch_bounds__(kThreads, 1) void k_block_lse_bf16(
     mainloop_bf16<false>(acc, smem, MainloopSrc{X, W, nullptr, M, V, K, m0, n0}, ch, pre, [] {});
 
     const int nw0 = n0 + wn * kLseTileWidth;
+    // Per token row i (the lane's 32 logits of it): the max is taken on the
+    // raw accumulators and scaled once (r > 0 and rounding r z is monotonic
+    // in z, so max(r z) = r max(z) exactly).  Entries past V need no mask in
+    // the max: their weight rows are clamped copies of row V - 1, so their
+    // logits repeat a valid one; only the sum of a ragged last tile masks
+    // them.  The label logit lies in this wave's 128 entries for about one
+    // tile in a thousand, so one wave-wide vote decides whether to look.
+    const bool full = nw0 + kLseTileWidth <= V;
+    const int lim = V - nw0 - g4;  // entry 16 j + v of this lane exists iff 16 j + v < lim
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int m = m0 + wm * 128 + i * 16 + (lane & 15);
       const bool mv = m < M;
-      const float rr2 = rr[i] * kLog2e;
-      float mx = -INFINITY;
+      float mxr = acc.v[0][i][0];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int n = nw0 + j * 16 + g4;
+      for (int j = 0; j < 8; ++j)
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-          if (n + v < V) mx = fmaxf(mx, acc.v[j][i][v] * rr[i]);
-      }
-      mx = max_over_lane_groups(mx);
-      const float mx2 = mx * kLog2e;
-      float se = 0.f, zl = 0.f;
-      bool has = false;
+        for (int v = 0; v < 4; ++v) mxr = fmaxf(mxr, acc.v[j][i][v]);
+      const float mx = max_over_lane_groups(mxr) * rr[i];
+      const float rr2 = rr[i] * kLog2e, mx2 = mx * kLog2e;
+      float se = 0.f;
+      if (full) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int n = nw0 + j * 16 + g4;
+        for (int j = 0; j < 8; ++j)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          if (n + v < V) se += __builtin_amdgcn_exp2f(acc.v[j][i][v] * rr2 - mx2);
-          if (n + v == lab[i]) {
-            zl = acc.v[j][i][v] * rr[i];
-            has = true;
+          for (int v = 0; v < 4; ++v) se += __builtin_amdgcn_exp2f(acc.v[j][i][v] * rr2 - mx2);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const float e = __builtin_amdgcn_exp2f(acc.v[j][i][v] * rr2 - mx2);
+            se += (j * 16 + v < lim) ? e : 0.f;
           }
-        }
       }
       se = sum_over_lane_groups(se);
-      if (mv && has) label_logit[m] = zl;
+      const int loff = lab[i] - nw0;  // label's entry within this wave's window
+      if (__any((unsigned)loff < (unsigned)kLseTileWidth)) {
+        float zl = 0.f;
+        bool has = false;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const bool hit = loff == j * 16 + g4 + v;
+            zl = hit ? acc.v[j][i][v] : zl;
+            has = has || hit;
+          }
+        if (mv && has) label_logit[m] = zl * rr[i];
+      }
       if (mv && lane < 16 && nw0 < V) {
         const size_t tt = (size_t)(nw0 / kLseTileWidth);
         tmax[tt * M + m] = mx;

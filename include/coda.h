@@ -162,7 +162,8 @@ int coda_gemm_rope(const void* h, const void* Wqkv, const float* r, const float*
  * section "CODA: the secret in the epilogue": cross-entropy re-parameterised;
  * section "Five building blocks and a LEGO language": block log-sum-exp
  * reduction and the running max / sum-exp statistics).
- *   z[m,v] = r[m] * (X[m,:] . W[v,:])   (r == NULL means r = 1); z never stored
+ *   z[m,v] = r[m] * (X[m,:] . W[v,:])   (r == NULL means r = 1; r > 0, as an
+ *            RMS scale is: the tile max is taken before scaling); z never stored
  *   per tile t of w = coda_lse_tile_width() vocabulary entries:
  *     tile_max[t*M+m]    = max over v in tile of z[m,v]
  *     tile_sumexp[t*M+m] = sum over v in tile of exp(z[m,v] - tile_max)
