@@ -21,68 +21,114 @@ namespace coda {
 // Output tile 256 tokens x 256 features; each wave's 128 features form one
 // partial tile, so T = ceil(N / 128).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads, 1) void k_residual_partialrms_bf16(
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
-    const uint16_t* __restrict__ res, uint16_t* __restrict__ h, float* __restrict__ psum, int M,
-    int N, int K, int gm, int gn) {
-  __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// The thread index as an opaque value: lane/wave arithmetic derived from it
+// is recomputed in each tile body instead of being kept live (or spilled)
+// across the phases of a kernel that runs several kinds of tiles.
+__device__ __forceinline__ int tile_tid() {
+  int t = (int)threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
+struct Gemm1Args {
+  const uint16_t* A;    // [M, K]
+  const uint16_t* W;    // [N, K]
+  const uint16_t* res;  // [M, N]
+  uint16_t* h;          // [M, N]
+  float* psum;          // [T, M]
+  int M, N, K;
+};
+
+__device__ __forceinline__ void gemm1_tile(const Gemm1Args& g, char* smem, int m0, int n0,
+                                           const TileChain& ch) {
+  const int tid = tile_tid();
+  const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int g4 = (lane >> 4) * 4;
+  const int gq = lane >> 4;
+  const int M = g.M, N = g.N;
+  const int nw0 = n0 + wn * 128;  // first feature of this wave = partial tile start
+  // Residual and h go through buffers that start at the tile's first row
+  // (offsets below 256 * N * 2 bytes; out-of-range loads return zero and
+  // out-of-range stores are dropped).  Lane L = 16 gq + r, run j: features
+  // nw0 + 16 j + 4 gq + 0..3 of row r.
+  const uint32_t rows_here = (uint32_t)min(kBM, M - m0);
+  const __amdgpu_buffer_rsrc_t rrsrc = make_rsrc(g.res + (size_t)m0 * N, rows_here * (uint32_t)N * 2u);
+  const __amdgpu_buffer_rsrc_t hrsrc = make_rsrc(g.h + (size_t)m0 * N, rows_here * (uint32_t)N * 2u);
+  auto row_off = [&](int i) {  // byte offset of this lane's row i at feature nw0 + 4 gq
+    const int ml = wm * 128 + i * 16 + (lane & 15);
+    return ((uint32_t)ml * (uint32_t)N + (uint32_t)(nw0 + 4 * gq)) * 2u;
+  };
+  // the residual tile (4 features x 8 x 8 token subtiles per lane) is
+  // loaded during the last two stages, ahead of the next tile's loads:
+  // token subtiles 0, 1 in stage nk-2 (both fragment sets still live), 2..7
+  // in the last stage
+  u32x2_t rv[8][8];
+  auto load_res = [&](int i0, int i1) {
+#pragma unroll
+    for (int i = i0; i < i1; ++i) {
+      const uint32_t o = row_off(i);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        rv[i][j] = __builtin_amdgcn_raw_buffer_load_b64(rrsrc, o + (uint32_t)j * 32u, 0, 0);
+    }
+  };
+  Acc acc;
+  mainloop_bf16<false>(acc, smem, MainloopSrc{g.A, g.W, nullptr, M, N, g.K, m0, n0}, ch,
+                       [&] { load_res(0, 2); }, [&] { load_res(2, 8); });
+
+  // h stores: lanes gq and gq ^ 1 exchange one run per pair of subtiles (as in
+  // GEMM2), so each 16-byte store writes 64 contiguous bytes of 16 rows.
+  const bool godd = (gq & 1) != 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int m = m0 + wm * 128 + i * 16 + (lane & 15);
+    const bool mv = m < M;
+    const int ml = m - m0;
+    float ss = 0.f;
+#pragma unroll
+    for (int j0 = 0; j0 < 8; j0 += 2) {
+      u32x2_t pk[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int j = j0 + u;
+        const bool nv = nw0 + j * 16 + 4 * gq < N;
+        float r4[4];
+        unpack_bf16x4(rv[i][j], r4);
+        float hv[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          hv[v] = acc.v[j][i][v] + r4[v];
+          ss += nv ? hv[v] * hv[v] : 0.f;
+        }
+        pk[u] = pack_bf16x4(hv[0], hv[1], hv[2], hv[3]);
+      }
+      const u32x2_t sd = godd ? pk[0] : pk[1];
+      const u32x2_t rx = {(unsigned)__shfl_xor((int)sd.x, 16, 64),
+                          (unsigned)__shfl_xor((int)sd.y, 16, 64)};
+      const int n = nw0 + 16 * (j0 + (godd ? 1 : 0)) + 8 * (gq >> 1);
+      const uint32_t off = (mv && n < N) ? ((uint32_t)ml * (uint32_t)N + (uint32_t)n) * 2u
+                                         : kOobOffset;
+      store16(hrsrc, godd ? u32x4_t{rx.x, rx.y, pk[1].x, pk[1].y}
+                          : u32x4_t{pk[0].x, pk[0].y, rx.x, rx.y}, off);
+    }
+    ss = sum_over_lane_groups(ss);
+    if (mv && lane < 16 && nw0 < N) g.psum[(size_t)(nw0 / kRmsTileWidth) * M + m] = ss;
+  }
+}
+
+__global__ __launch_bounds__(kThreads, 1) void k_residual_partialrms_bf16(Gemm1Args g, int gm,
+                                                                          int gn) {
+  __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
   const int nt = gm * gn;
   bool prefetched = false;
   for (int t = blockIdx.x; t < nt; t += gridDim.x) {
     const TileCoord tc = map_tile(t, gm, gn, 8);
-    const int m0 = tc.tm * kBM, n0 = tc.tn * kBN;
     TileChain ch;
     ch.prefetched = prefetched;
     const bool has_next = t + (int)gridDim.x < nt;
     const TileCoord nc = has_next ? map_tile(t + gridDim.x, gm, gn, 8) : tc;
-    ch.next = MainloopSrc{A, W, nullptr, M, N, K, nc.tm * kBM, nc.tn * kBN};
-    const int nw0 = n0 + wn * 128;  // first feature of this wave = partial tile start
-    // the residual tile (4 features x 8 x 8 token subtiles per lane) is
-    // loaded during the last two stages, ahead of the next tile's loads:
-    // token subtiles 0..3 in stage nk-2, 4..7 in the last stage
-    u32x2_t rv[8][8];
-    auto load_res = [&](int i0) {
-#pragma unroll
-      for (int i = i0; i < i0 + 4; ++i) {
-        const size_t row = (size_t)min(m0 + wm * 128 + i * 16 + (lane & 15), M - 1) * (size_t)N;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int n = min(nw0 + j * 16 + g4, N - 4);
-          rv[i][j] = *(const u32x2_t*)(res + row + n);
-        }
-      }
-    };
-    Acc acc;
-    mainloop_bf16<false>(acc, smem, MainloopSrc{A, W, nullptr, M, N, K, m0, n0}, ch,
-                         [&] { load_res(0); }, [&] { load_res(4); });
-
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int m = m0 + wm * 128 + i * 16 + (lane & 15);
-      const bool mv = m < M;
-      const size_t row = (size_t)min(m, M - 1) * (size_t)N;
-      float ss = 0.f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int n = nw0 + j * 16 + g4;
-        if (n < N) {
-          float r4[4];
-          unpack_bf16x4(rv[i][j], r4);
-          float hv[4];
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            hv[v] = acc.v[j][i][v] + r4[v];
-            ss += hv[v] * hv[v];
-          }
-          if (mv) *(u32x2_t*)(h + row + n) = pack_bf16x4(hv[0], hv[1], hv[2], hv[3]);
-        }
-      }
-      ss = sum_over_lane_groups(ss);
-      if (mv && lane < 16 && nw0 < N) psum[(size_t)(nw0 / kRmsTileWidth) * M + m] = ss;
-    }
+    ch.next = MainloopSrc{g.A, g.W, nullptr, g.M, g.N, g.K, nc.tm * kBM, nc.tn * kBN};
+    gemm1_tile(g, smem, tc.tm * kBM, tc.tn * kBN, ch);
     prefetched = has_next;
   }
   wait_vm0();  // the last tile's unused prefetch into LDS lands before the block ends
@@ -96,79 +142,95 @@ __global__ __launch_bounds__(kThreads, 1) void k_residual_partialrms_bf16(
 // ---------------------------------------------------------------------------
 constexpr int kSwigluStores = 16;  // 16-byte stores per lane per tile
 
-__global__ __launch_bounds__(kThreads, 1) void k_rowscale_swiglu_bf16(
-    const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wg,
-    const uint16_t* __restrict__ Wu, const float* __restrict__ r, uint16_t* __restrict__ out,
-    int M, int N, int K, int gm, int gn) {
-  __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+struct Gemm2Args {
+  const uint16_t* X;   // [M, K]
+  const uint16_t* Wg;  // [N, K]
+  const uint16_t* Wu;  // [N, K]
+  const float* r;      // [M]
+  uint16_t* out;       // [M, N]
+  int M, N, K;
+};
+
+__device__ __forceinline__ MainloopSrc gemm2_src(const Gemm2Args& g, TileCoord c) {
+  return MainloopSrc{g.X, g.Wg, g.Wu, g.M, g.N, g.K, c.tm * kBM, c.tn * (kBN / 2)};
+}
+
+__device__ __forceinline__ void gemm2_tile(const Gemm2Args& g, char* smem, int m0, int n0,
+                                           const TileChain& ch) {
+  const int tid = tile_tid();
+  const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
+  const int M = g.M, N = g.N;
+  float rr[8];
+  auto pre = [&]() {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) rr[i] = g.r[min(m0 + wm * 128 + i * 16 + (lane & 15), M - 1)];
+  };
+  Acc acc;
+  mainloop_bf16<true, kSwigluStores>(acc, smem, MainloopSrc{g.X, g.Wg, g.Wu, M, N, g.K, m0, n0},
+                                     ch, pre, [] {});
+
+  // Lane L = 16 g + r holds the run of 4 features 16 j + 4 g of token r
+  // for each subtile j.  For a pair of subtiles (j0, j0 + 1), lanes g and
+  // g ^ 1 exchange one run, so that every lane holds 8 contiguous features
+  // and one 16-byte store writes 64 contiguous bytes of each of 16 rows
+  // (instead of 4 runs of 8 bytes): the store path pays per row touched.
+  // Every lane issues the same 16 stores (masked ones at an out-of-range
+  // offset), which the next tile's first wait counts on.  The buffer starts
+  // at the tile's first row, so offsets stay below 256 * N * 2 bytes.
+  const __amdgpu_buffer_rsrc_t orsrc =
+      make_rsrc(g.out + (size_t)m0 * N, (uint32_t)min(kBM, M - m0) * (uint32_t)N * 2u);
+  const int nw0 = n0 + wn * 64;
+  const int gq = lane >> 4;
+  const bool godd = (gq & 1) != 0;
+  const float kNegLog2e = -1.4426950408889634f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int ml = wm * 128 + i * 16 + (lane & 15);  // row within the tile
+    const bool mv = m0 + ml < M;
+    // silu(g) u with g = r a, u = r b:  a b / ((1 + 2^(-log2e r a)) / r^2),
+    // the denominator one fma with 1/r^2 = mean(h^2) + eps (finite)
+    const float s2 = __builtin_amdgcn_rcpf(rr[i] * rr[i]), c1 = rr[i] * kNegLog2e;
+#pragma unroll
+    for (int j0 = 0; j0 < 4; j0 += 2) {
+      u32x2_t pk[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int j = j0 + u;
+        float o[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float a = acc.v[j][i][v], b = acc.v[j + 4][i][v];
+          const float e = __builtin_amdgcn_exp2f(a * c1);
+          o[v] = (a * b) * __builtin_amdgcn_rcpf(__builtin_fmaf(e, s2, s2));
+        }
+        pk[u] = pack_bf16x4(o[0], o[1], o[2], o[3]);
+      }
+      const u32x2_t sd = godd ? pk[0] : pk[1];
+      const u32x2_t rv = {(unsigned)__shfl_xor((int)sd.x, 16, 64),
+                          (unsigned)__shfl_xor((int)sd.y, 16, 64)};
+      // even g: features 16 j0 + 8 (g/2) + 0..7; odd g: the same in j0 + 1
+      const int n = nw0 + 16 * (j0 + (godd ? 1 : 0)) + 8 * (gq >> 1);
+      const uint32_t off = (mv && n < N) ? ((uint32_t)ml * (uint32_t)N + (uint32_t)n) * 2u
+                                         : kOobOffset;
+      store16(orsrc, godd ? u32x4_t{rv.x, rv.y, pk[1].x, pk[1].y}
+                          : u32x4_t{pk[0].x, pk[0].y, rv.x, rv.y}, off);
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads, 1) void k_rowscale_swiglu_bf16(Gemm2Args g, int gm,
+                                                                      int gn) {
+  __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
   const int nt = gm * gn;
   bool prefetched = false;
   for (int t = blockIdx.x; t < nt; t += gridDim.x) {
     const TileCoord tc = map_tile(t, gm, gn, 8);
-    const int m0 = tc.tm * kBM, n0 = tc.tn * (kBN / 2);
     TileChain ch;
     ch.prefetched = prefetched;
     const bool has_next = t + (int)gridDim.x < nt;
-    const TileCoord nc = has_next ? map_tile(t + gridDim.x, gm, gn, 8) : tc;
-    ch.next = MainloopSrc{X, Wg, Wu, M, N, K, nc.tm * kBM, nc.tn * (kBN / 2)};
-    float rr[8];
-    auto pre = [&]() {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) rr[i] = r[min(m0 + wm * 128 + i * 16 + (lane & 15), M - 1)];
-    };
-    Acc acc;
-    mainloop_bf16<true, kSwigluStores>(acc, smem, MainloopSrc{X, Wg, Wu, M, N, K, m0, n0}, ch,
-                                       pre, [] {});
-
-    // Lane L = 16 g + r holds the run of 4 features 16 j + 4 g of token r
-    // for each subtile j.  For a pair of subtiles (j0, j0 + 1), lanes g and
-    // g ^ 1 exchange one run, so that every lane holds 8 contiguous features
-    // and one 16-byte store writes 64 contiguous bytes of each of 16 rows
-    // (instead of 4 runs of 8 bytes): the store path pays per row touched.
-    // Every lane issues the same 16 stores (masked ones at an out-of-range
-    // offset), which the next tile's first wait counts on.  The buffer starts
-    // at the tile's first row, so offsets stay below 256 * N * 2 bytes.
-    const __amdgpu_buffer_rsrc_t orsrc =
-        make_rsrc(out + (size_t)m0 * N, (uint32_t)min(kBM, M - m0) * (uint32_t)N * 2u);
-    const int nw0 = n0 + wn * 64;
-    const int g = lane >> 4;
-    const bool godd = (g & 1) != 0;
-    const float kNegLog2e = -1.4426950408889634f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int ml = wm * 128 + i * 16 + (lane & 15);  // row within the tile
-      const bool mv = m0 + ml < M;
-      // silu(g) u with g = r a, u = r b:  a b / ((1 + 2^(-log2e r a)) / r^2),
-      // the denominator one fma with 1/r^2 = mean(h^2) + eps (finite)
-      const float s2 = __builtin_amdgcn_rcpf(rr[i] * rr[i]), c1 = rr[i] * kNegLog2e;
-#pragma unroll
-      for (int j0 = 0; j0 < 4; j0 += 2) {
-        u32x2_t pk[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int j = j0 + u;
-          float o[4];
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const float a = acc.v[j][i][v], b = acc.v[j + 4][i][v];
-            const float e = __builtin_amdgcn_exp2f(a * c1);
-            o[v] = (a * b) * __builtin_amdgcn_rcpf(__builtin_fmaf(e, s2, s2));
-          }
-          pk[u] = pack_bf16x4(o[0], o[1], o[2], o[3]);
-        }
-        const u32x2_t sd = godd ? pk[0] : pk[1];
-        const u32x2_t rv = {(unsigned)__shfl_xor((int)sd.x, 16, 64),
-                            (unsigned)__shfl_xor((int)sd.y, 16, 64)};
-        // even g: features 16 j0 + 8 (g/2) + 0..7; odd g: the same in j0 + 1
-        const int n = nw0 + 16 * (j0 + (godd ? 1 : 0)) + 8 * (g >> 1);
-        const uint32_t off = (mv && n < N) ? ((uint32_t)ml * (uint32_t)N + (uint32_t)n) * 2u
-                                           : kOobOffset;
-        store16(orsrc, godd ? u32x4_t{rv.x, rv.y, pk[1].x, pk[1].y}
-                            : u32x4_t{pk[0].x, pk[0].y, rv.x, rv.y}, off);
-      }
-    }
+    ch.next = gemm2_src(g, has_next ? map_tile(t + gridDim.x, gm, gn, 8) : tc);
+    gemm2_tile(g, smem, tc.tm * kBM, tc.tn * (kBN / 2), ch);
     prefetched = has_next;
   }
   wait_vm0();  // the last tile's unused prefetch into LDS lands before the block ends
@@ -414,8 +476,8 @@ hipError_t launch_residual_partialrms_bf16(const uint16_t* A, const uint16_t* W,
                                            const uint16_t* res, uint16_t* h, float* psum, int M,
                                            int N, int K, hipStream_t stream) {
   const int gm = cdiv(M, kBM), gn = cdiv(N, kBN);
-  hipLaunchKernelGGL(k_residual_partialrms_bf16, dim3(min(gm * gn, cu_count())), dim3(kThreads), 0, stream, A, W,
-                     res, h, psum, M, N, K, gm, gn);
+  hipLaunchKernelGGL(k_residual_partialrms_bf16, dim3(min(gm * gn, cu_count())), dim3(kThreads), 0,
+                     stream, Gemm1Args{A, W, res, h, psum, M, N, K}, gm, gn);
   return hipGetLastError();
 }
 
@@ -423,10 +485,11 @@ hipError_t launch_rowscale_swiglu_bf16(const uint16_t* X, const uint16_t* Wg, co
                                        const float* r, uint16_t* out, int M, int N, int K,
                                        hipStream_t stream) {
   const int gm = cdiv(M, kBM), gn = cdiv(N, kBN / 2);
-  hipLaunchKernelGGL(k_rowscale_swiglu_bf16, dim3(min(gm * gn, cu_count())), dim3(kThreads), 0, stream, X, Wg, Wu,
-                     r, out, M, N, K, gm, gn);
+  hipLaunchKernelGGL(k_rowscale_swiglu_bf16, dim3(min(gm * gn, cu_count())), dim3(kThreads), 0,
+                     stream, Gemm2Args{X, Wg, Wu, r, out, M, N, K}, gm, gn);
   return hipGetLastError();
 }
+
 
 hipError_t launch_rope_bf16(const uint16_t* X, const uint16_t* W, const float* r,
                             const float* rcos, const float* rsin, const int* pos, int max_pos,
