@@ -253,7 +253,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_rope_bf16(
   __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int g4 = (lane >> 4) * 4;
+  const int gq = lane >> 4;
   const int nt = gm * gn;
   bool prefetched = false;
   for (int t = blockIdx.x; t < nt; t += gridDim.x) {
@@ -278,29 +278,40 @@ __global__ __launch_bounds__(kThreads, 1) void k_rope_bf16(
     mainloop_bf16<false>(acc, smem, MainloopSrc{X, W, nullptr, M, N, K, m0, n0}, ch, pre, [] {});
 
     const int nw0 = n0 + wn * 128;  // multiple of 128: two whole heads of 64
+    // cos/sin of the 8 token subtiles, all loaded before the first use (one
+    // latency instead of eight); the fragment registers are free by now.
+    // Positions outside the table are clamped into it (memory safety).
+    // Angle index of subtile jj (0, 1) of a head: 16 jj + 4 gq + v.
+    f32x4_t ct[8][2], st[8][2];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int m = m0 + wm * 128 + i * 16 + (lane & 15);
-      const bool mv = m < M;
-      const int mc = min(m, M - 1);
+      const size_t p = (size_t)min(max(pp[i], 0), max_pos - 1) * 32 + 4 * gq;
+      ct[i][0] = *(const f32x4_t*)(rcos + p);
+      ct[i][1] = *(const f32x4_t*)(rcos + p + 16);
+      st[i][0] = *(const f32x4_t*)(rsin + p);
+      st[i][1] = *(const f32x4_t*)(rsin + p + 16);
+    }
+    // Stores as in GEMM2: lanes gq and gq ^ 1 exchange one run of each pair of
+    // subtiles (jj = 0, 1 of a half-head), so each 16-byte store writes 64
+    // contiguous bytes of 16 rows; masked lanes store out of range of a
+    // buffer that starts at the tile's first row.
+    const __amdgpu_buffer_rsrc_t orsrc =
+        make_rsrc(out + (size_t)m0 * N, (uint32_t)min(kBM, M - m0) * (uint32_t)N * 2u);
+    const bool godd = (gq & 1) != 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int ml = wm * 128 + i * 16 + (lane & 15);  // row within the tile
+      const bool mv = m0 + ml < M;
       const float rr_i = rr[i];
-      // positions outside the table are clamped into it (memory safety)
-      const int p = min(max(pp[i], 0), max_pos - 1);
-      // angle index of subtile jj (0, 1) of a head: 16*jj + g4 + v
-      const f32x4_t c0 = *(const f32x4_t*)(rcos + (size_t)p * 32 + g4);
-      const f32x4_t c1 = *(const f32x4_t*)(rcos + (size_t)p * 32 + 16 + g4);
-      const f32x4_t s0 = *(const f32x4_t*)(rsin + (size_t)p * 32 + g4);
-      const f32x4_t s1 = *(const f32x4_t*)(rsin + (size_t)p * 32 + 16 + g4);
-      const size_t row = (size_t)mc * (size_t)N;
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const int hbase = nw0 + hh * 64;
-        if (hbase >= N) continue;
         const bool rot = hbase < rot_features;
+        u32x2_t plo[2], phi[2];
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
           const int ja = hh * 4 + jj, jb = ja + 2;
-          const f32x4_t cs = jj ? c1 : c0, sn = jj ? s1 : s0;
+          const f32x4_t cs = ct[i][jj], sn = st[i][jj];
           float lo[4], hi[4];
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
@@ -308,11 +319,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_rope_bf16(
             lo[v] = rot ? a * cs[v] - b * sn[v] : a;
             hi[v] = rot ? b * cs[v] + a * sn[v] : b;
           }
-          if (mv) {
-            const int na = hbase + jj * 16 + g4;
-            *(u32x2_t*)(out + row + na) = pack_bf16x4(lo[0], lo[1], lo[2], lo[3]);
-            *(u32x2_t*)(out + row + na + 32) = pack_bf16x4(hi[0], hi[1], hi[2], hi[3]);
-          }
+          plo[jj] = pack_bf16x4(lo[0], lo[1], lo[2], lo[3]);
+          phi[jj] = pack_bf16x4(hi[0], hi[1], hi[2], hi[3]);
+        }
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {  // features [0,32) and [32,64) of the head
+          const u32x2_t* pk = half ? phi : plo;
+          const u32x2_t sd = godd ? pk[0] : pk[1];
+          const u32x2_t rx = {(unsigned)__shfl_xor((int)sd.x, 16, 64),
+                              (unsigned)__shfl_xor((int)sd.y, 16, 64)};
+          const int n = hbase + 32 * half + 16 * (godd ? 1 : 0) + 8 * (gq >> 1);
+          const uint32_t off = (mv && n < N) ? ((uint32_t)ml * (uint32_t)N + (uint32_t)n) * 2u
+                                             : kOobOffset;
+          store16(orsrc, godd ? u32x4_t{rx.x, rx.y, pk[1].x, pk[1].y}
+                              : u32x4_t{pk[0].x, pk[0].y, rx.x, rx.y}, off);
         }
       }
     }
