@@ -100,12 +100,16 @@ def main():
         if ev is not None:
             ev[3].record(stream)
 
-    def unfused_step():
+    def unfused_step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
         ops.gemm_bf16(x, w1, y_u)
         ops.residual_add(y_u, res, h_u)
         ops.rmsnorm(h_u, gamma, eps, n_u)
         ops.gemm_bf16(n_u, wgu, gu_u)
         ops.swiglu(gu_u, out_u)
+        if ev is not None:
+            ev[3].record(stream)
 
     def timed(step_fn, steps, per_kernel=False):
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
@@ -147,6 +151,9 @@ def main():
     _, _, per = timed(fused_step, args.steps, per_kernel=True)
     print(f"[bench] timing {args.steps} unfused steps", file=sys.stderr, flush=True)
     unfused_ms, _, _ = timed(unfused_step, args.steps)
+    # per-step distribution (events before and after every step)
+    fused_steps = np.array([per[k].sum() for k in range(args.steps)])
+    unf_steps = step_times(torch, stream, unfused_step, args.steps)
 
     ms_step = fused_ms / args.steps
     tflops = flops / (ms_step * 1e-3) / 1e12
@@ -182,8 +189,10 @@ def main():
                                "gate/up with SwiGLU, eps=1e-5",
                    "M": M, "d": d, "K1": K1, "ffn": ffn, "parallelism": "none (1 GPU)"},
         "pct_of_mfma_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "step_ms": pctl(fused_steps),
         "unfused": {"ms_per_step": round(unf_ms_step, 4), "tflops": round(unf_tflops, 2),
-                    "speedup_fused_vs_unfused": round(unf_ms_step / ms_step, 3)},
+                    "speedup_fused_vs_unfused": round(unf_ms_step / ms_step, 3),
+                    "step_ms": pctl(unf_steps)},
         "kernels_ms": {"gemm_residual_partialrms": round(g1_ms, 4),
                        "rms_reduce": round(red_ms, 4),
                        "gemm_rowscale_swiglu": round(g2_ms, 4)},
@@ -200,6 +209,27 @@ def main():
 
 
 PEAK_FP8_TFLOPS = 5033.2  # MI355X dense OCP fp8 MFMA, 2.4 GHz
+
+
+def pctl(ms):
+    """Median, 10th and 90th percentile of per-step times (ms)."""
+    ms = np.asarray(ms, dtype=np.float64)
+    return {"median": round(float(np.median(ms)), 4), "p10": round(float(np.percentile(ms, 10)), 4),
+            "p90": round(float(np.percentile(ms, 90)), 4)}
+
+
+def step_times(torch, stream, fn, steps):
+    """Per-step times (ms) from events recorded before and after every step
+    (no synchronisation between steps)."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    for e0, e1 in evs:
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return [e0.elapsed_time(e1) for e0, e1 in evs]
 
 
 def _events_time(torch, stream, fn, steps, warmup):
@@ -249,12 +279,26 @@ def time_other_rows(torch, ops, inputs, stream, steps, warmup):
         ops.rms_reduce(P, d, eps, r)
         ops.gemm_rope(h, wqkv_f, r, cos, sin, pos, qkv, nq, nkv, hd)
     ms = _events_time(torch, stream, attn_step, steps, warmup)
+    # unfused: plain GEMM -> add -> RMSNorm -> plain QKV GEMM -> RoPE in place
+    y_u, h_u, n_u = (torch.empty(M, d, dtype=torch.bfloat16, device=dev) for _ in range(3))
+    qkv_u = torch.empty_like(qkv)
+
+    def attn_unfused():
+        ops.gemm_bf16(x, w1, y_u)
+        ops.residual_add(y_u, res, h_u)
+        ops.rmsnorm(h_u, gamma, eps, n_u)
+        ops.gemm_bf16(n_u, wqkv, qkv_u)
+        ops.rope_apply(qkv_u, cos, sin, pos, nq, nkv, hd)
+    ms_u = _events_time(torch, stream, attn_unfused, steps, warmup)
     fl = 2.0 * M * d * K1 + 2.0 * M * (nq + 2 * nkv) * hd * d
     out["attn_rope"] = {"workload": "M=8192, d=2048, GEMM1 K=8192, 32 q / 8 kv heads of 64, "
                                     "RoPE theta=5e5", "ms_per_step": round(ms, 4),
                         "tflops": round(fl / ms / 1e9, 1),
-                        "pct_of_bf16_peak": round(100 * fl / ms / 1e9 / PEAK_BF16_TFLOPS, 2)}
-    del x, res, w1, wqkv, wqkv_f, h, P, r, qkv, w
+                        "pct_of_bf16_peak": round(100 * fl / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
+                        "unfused": {"ms_per_step": round(ms_u, 4),
+                                    "tflops": round(fl / ms_u / 1e9, 1),
+                                    "speedup_fused_vs_unfused": round(ms_u / ms, 3)}}
+    del x, res, w1, wqkv, wqkv_f, h, P, r, qkv, w, y_u, h_u, n_u, qkv_u
 
     # LM head: block log-sum-exp GEMM + merge
     print("[bench] lm_head", file=sys.stderr, flush=True)
@@ -268,11 +312,24 @@ def time_other_rows(torch, ops, inputs, stream, steps, warmup):
     zl, loss = (torch.empty(M, dtype=torch.float32, device=dev) for _ in range(2))
     ms = _events_time(torch, stream, lambda: ops.gemm_block_lse(x, wl, lab, tmax, tsum, zl, loss),
                       steps, warmup)
+    # unfused: plain GEMM -> bf16 logits in HBM (2.1 GB) -> row cross entropy
+    logits = torch.empty(M, V, dtype=torch.bfloat16, device=dev)
+    lse_u, loss_u = (torch.empty(M, dtype=torch.float32, device=dev) for _ in range(2))
+
+    def lm_unfused():
+        ops.gemm_bf16(x, wl, logits)
+        ops.cross_entropy_rows(logits, lab, lse_u, loss_u)
+    ms_u = _events_time(torch, stream, lm_unfused, steps, warmup)
     fl = 2.0 * M * V * d
     out["lm_head"] = {"workload": "M=8192, d=2048, V=128256, per-row CE via block LSE",
                       "ms_per_step": round(ms, 4), "tflops": round(fl / ms / 1e9, 1),
-                      "pct_of_bf16_peak": round(100 * fl / ms / 1e9 / PEAK_BF16_TFLOPS, 2)}
-    del x, wl, tmax, tsum, w
+                      "pct_of_bf16_peak": round(100 * fl / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
+                      "unfused": {"ms_per_step": round(ms_u, 4),
+                                  "tflops": round(fl / ms_u / 1e9, 1),
+                                  "speedup_fused_vs_unfused": round(ms_u / ms, 3),
+                                  "max_loss_diff_vs_fused":
+                                      round(float((loss_u - loss).abs().max().item()), 6)}}
+    del x, wl, tmax, tsum, w, logits, lse_u, loss_u
 
     # fp8 8B-shaped MLP block (delayed scaling: the previous step's scale)
     print("[bench] mlp_8b_fp8", file=sys.stderr, flush=True)
@@ -309,24 +366,32 @@ def time_other_rows(torch, ops, inputs, stream, steps, warmup):
     return out
 
 
+# the sources the bf16 GEMM kernels are compiled from
+KERNEL_SOURCES = ("coda_device.hpp", "gemm_core.hpp", "gemm_bf16.hip")
+
+
+def kernel_sources_sha256():
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        h.update(name.encode())
+        with open(os.path.join(root, "gemm_epilogue_transformer_gemm1_amd", "csrc", name),
+                  "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def measured_traffic(kernel):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary, or None when the kernel sources changed since it was taken."""
-    import glob
-    import hashlib
+    summary, or None when the kernel's sources changed since it was taken."""
     root = os.path.dirname(os.path.abspath(__file__))
     try:
         with open(os.path.join(root, "profiles", "traffic.json")) as f:
             rec = json.load(f)[kernel]
     except (OSError, KeyError, ValueError):
         return None
-    h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(root, "gemm_epilogue_transformer_gemm1_amd", "csrc",
-                                           "*"))):
-        h.update(os.path.basename(p).encode())
-        with open(p, "rb") as f:
-            h.update(f.read())
-    if h.hexdigest() != rec.get("csrc_sha256"):
+    if kernel_sources_sha256() != rec.get("sources_sha256"):
         return None
     return int(rec["fetch_bytes"] + rec["write_bytes"])
 
@@ -363,8 +428,22 @@ def cpu_baseline(w, eps, budget_s):
         if elapsed >= budget_s:
             break
     flops = 2.0 * done * (d * K1 + 2 * ffn * d)
+    cpu_model, blas = None, None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")),
+                             None)
+    except OSError:
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        b = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if b:
+            blas = f"{b[0].get('internal_api')} {b[0].get('version')}"
+    except Exception:  # pragma: no cover
+        pass
     return {"value": round(flops / elapsed / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model, "blas": blas,
             "sample": f"{done} token rows of mlp_1b ({done / M:.2f} passes over its {M} rows, "
                       f"chunks of 512; fp64 numpy, unfused) in {elapsed:.1f} s; "
                       f"host cores visible {len(os.sched_getaffinity(0))}"}

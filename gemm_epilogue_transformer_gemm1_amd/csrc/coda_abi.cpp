@@ -310,4 +310,37 @@ int coda_swiglu(const void* gu, void* out, int M, int N, void* stream) {
   }
 }
 
+int coda_rope_apply(void* qkv, const float* rope_cos, const float* rope_sin, const int32_t* pos,
+                    int max_pos, int M, int n_q_heads, int n_kv_heads, int head_dim, void* stream) {
+  try {
+    if (!qkv || !rope_cos || !rope_sin || !pos) return CODA_ERR_NULL;
+    if (head_dim != 64 || n_q_heads < 1 || n_kv_heads < 1 || max_pos < 1 || M < 1)
+      return CODA_ERR_SHAPE;
+    const int64_t N = (int64_t)(n_q_heads + 2 * n_kv_heads) * head_dim;
+    if (N > (int64_t(1) << 24) || !small_enough(M, N)) return CODA_ERR_SHAPE;
+    if (!aligned(qkv, 16) || !aligned(rope_cos, 16) || !aligned(rope_sin, 16) || !aligned(pos, 4))
+      return CODA_ERR_ALIGN;
+    if (int st = check_device()) return st;
+    return launched(coda::launch_rope_apply(static_cast<uint16_t*>(qkv), rope_cos, rope_sin, pos,
+                                            max_pos, M, n_q_heads, n_kv_heads, as_stream(stream)));
+  } catch (...) {
+    return CODA_ERR_LAUNCH;
+  }
+}
+
+int coda_cross_entropy_rows(const void* logits, const int32_t* labels, float* lse, float* loss,
+                            int M, int V, void* stream) {
+  try {
+    if (!logits || !labels || !lse || !loss) return CODA_ERR_NULL;
+    if (M < 1 || V < 8 || V % 8 != 0 || !small_enough(M, V)) return CODA_ERR_SHAPE;
+    if (!aligned(logits, 16) || !aligned(labels, 4) || !aligned(lse, 4) || !aligned(loss, 4))
+      return CODA_ERR_ALIGN;
+    if (int st = check_device()) return st;
+    return launched(coda::launch_ce_rows(static_cast<const uint16_t*>(logits), labels, lse, loss,
+                                         M, V, as_stream(stream)));
+  } catch (...) {
+    return CODA_ERR_LAUNCH;
+  }
+}
+
 }  // extern "C"

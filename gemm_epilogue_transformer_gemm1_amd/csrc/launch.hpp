@@ -52,5 +52,9 @@ hipError_t launch_residual_add(const uint16_t* y, const uint16_t* res, uint16_t*
 hipError_t launch_rmsnorm(const uint16_t* h, const float* gamma, float eps, uint16_t* out, int M,
                           int N, hipStream_t stream);
 hipError_t launch_swiglu(const uint16_t* gu, uint16_t* out, int M, int N, hipStream_t stream);
+hipError_t launch_rope_apply(uint16_t* qkv, const float* rcos, const float* rsin, const int* pos,
+                             int max_pos, int M, int n_q, int n_kv, hipStream_t stream);
+hipError_t launch_ce_rows(const uint16_t* z, const int* labels, float* lse, float* loss, int M,
+                          int V, hipStream_t stream);
 
 }  // namespace coda

@@ -292,4 +292,94 @@ hipError_t launch_swiglu(const uint16_t* gu, uint16_t* out, int M, int N, hipStr
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Unfused baseline pieces for the attention-input and LM-head workloads (the
+// sequences the fused epilogues replace; not on the hot path).
+// ---------------------------------------------------------------------------
+
+// In-place rotate-half RoPE on the first n_rot heads (q, then k) of a stored
+// qkv tensor [M, N], heads of 64: one thread per (row, head, 4 pairs).
+// Positions outside the table are clamped into it, as in the fused kernel.
+__global__ __launch_bounds__(256) void k_rope_apply(uint16_t* __restrict__ qkv,
+                                                    const float* __restrict__ rcos,
+                                                    const float* __restrict__ rsin,
+                                                    const int* __restrict__ pos, int max_pos,
+                                                    int M, int N, int n_rot) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t per_row = (int64_t)n_rot * 8;
+  if (idx >= (int64_t)M * per_row) return;
+  const int64_t m = idx / per_row;
+  const int rem = (int)(idx - m * per_row);
+  const int q4 = (rem & 7) * 4;
+  uint16_t* base = qkv + m * N + (rem >> 3) * 64;
+  const size_t p = (size_t)min(max(pos[m], 0), max_pos - 1) * 32 + q4;
+  const f32x4_t c = *(const f32x4_t*)(rcos + p), sn = *(const f32x4_t*)(rsin + p);
+  float a[4], b[4], ra[4], rb[4];
+  unpack_bf16x4(*(const u32x2_t*)(base + q4), a);
+  unpack_bf16x4(*(const u32x2_t*)(base + 32 + q4), b);
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    ra[v] = a[v] * c[v] - b[v] * sn[v];
+    rb[v] = b[v] * c[v] + a[v] * sn[v];
+  }
+  *(u32x2_t*)(base + q4) = pack_bf16x4(ra[0], ra[1], ra[2], ra[3]);
+  *(u32x2_t*)(base + 32 + q4) = pack_bf16x4(rb[0], rb[1], rb[2], rb[3]);
+}
+
+hipError_t launch_rope_apply(uint16_t* qkv, const float* rcos, const float* rsin, const int* pos,
+                             int max_pos, int M, int n_q, int n_kv, hipStream_t stream) {
+  const int N = (n_q + 2 * n_kv) * 64, n_rot = n_q + n_kv;
+  hipLaunchKernelGGL(k_rope_apply, dim3(cdiv((int64_t)M * n_rot * 8, 256)), dim3(256), 0, stream,
+                     qkv, rcos, rsin, pos, max_pos, M, N, n_rot);
+  return hipGetLastError();
+}
+
+// loss[m] = logsumexp_n z[m, n] - z[m, label[m]] over stored bf16 logits
+// [M, V]: one block per row; each thread keeps a running (max, sum exp) over
+// its chunks of 8 logits, then the 256 pairs are merged.
+__global__ __launch_bounds__(256) void k_ce_rows(const uint16_t* __restrict__ z,
+                                                 const int* __restrict__ labels,
+                                                 float* __restrict__ lse, float* __restrict__ loss,
+                                                 int V) {
+  __shared__ float pm[4], ps[4];
+  const int m = blockIdx.x;
+  const uint16_t* row = z + (size_t)m * V;
+  float mx = -INFINITY, se = 0.f;
+  for (int c = threadIdx.x * 8; c < V; c += 256 * 8) {
+    float f[8];
+    load8(row + c, f);
+    float cm = f[0];
+#pragma unroll
+    for (int q = 1; q < 8; ++q) cm = fmaxf(cm, f[q]);
+    if (cm > mx) {
+      se = mx == -INFINITY ? 0.f : se * __expf(mx - cm);
+      mx = cm;
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) se += __expf(f[q] - mx);
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    const float m2 = __shfl_xor(mx, o, 64), s2 = __shfl_xor(se, o, 64);
+    lse_combine(mx, se, m2, s2);
+  }
+  if ((threadIdx.x & 63) == 0) {
+    pm[threadIdx.x >> 6] = mx;
+    ps[threadIdx.x >> 6] = se;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 4; ++w) lse_combine(mx, se, pm[w], ps[w]);
+    const float l = mx + logf(se);
+    const int lab = min(max(labels[m], 0), V - 1);
+    lse[m] = l;
+    loss[m] = l - bf16_to_f32(row[lab]);
+  }
+}
+
+hipError_t launch_ce_rows(const uint16_t* z, const int* labels, float* lse, float* loss, int M,
+                          int V, hipStream_t stream) {
+  hipLaunchKernelGGL(k_ce_rows, dim3(M), dim3(256), 0, stream, z, labels, lse, loss, V);
+  return hipGetLastError();
+}
+
 }  // namespace coda

@@ -48,6 +48,8 @@ _SIGNATURES = {
     "coda_residual_add": ([_p, _p, _p, _i64, _p], _c_int),
     "coda_rmsnorm": ([_p, _p, _c_float, _p, _c_int, _c_int, _p], _c_int),
     "coda_swiglu": ([_p, _p, _c_int, _c_int, _p], _c_int),
+    "coda_rope_apply": ([_p, _p, _p, _p, _c_int, _c_int, _c_int, _c_int, _c_int, _p], _c_int),
+    "coda_cross_entropy_rows": ([_p, _p, _p, _p, _c_int, _c_int, _p], _c_int),
 }
 
 
@@ -218,3 +220,18 @@ def swiglu(gu, out, stream=None):
     M, N2 = gu.shape
     _call("coda_swiglu", _ptr(gu, _BF16, "gu"), _ptr(out, _BF16, "out"), M, N2 // 2,
           _stream(stream))
+
+
+def rope_apply(qkv, rope_cos, rope_sin, pos, n_q_heads, n_kv_heads, head_dim, stream=None):
+    """In-place RoPE on the q and k heads of a stored qkv (unfused baseline)."""
+    M = qkv.shape[0]
+    _call("coda_rope_apply", _ptr(qkv, _BF16, "qkv"), _ptr(rope_cos, _F32, "rope_cos"),
+          _ptr(rope_sin, _F32, "rope_sin"), _ptr(pos, _I32, "pos"), rope_cos.shape[0], M,
+          n_q_heads, n_kv_heads, head_dim, _stream(stream))
+
+
+def cross_entropy_rows(logits, labels, lse, loss, stream=None):
+    """Per-row cross entropy of stored bf16 logits (unfused baseline)."""
+    M, V = logits.shape
+    _call("coda_cross_entropy_rows", _ptr(logits, _BF16, "logits"), _ptr(labels, _I32, "labels"),
+          _ptr(lse, _F32, "lse"), _ptr(loss, _F32, "loss"), M, V, _stream(stream))

@@ -204,6 +204,16 @@ int coda_rmsnorm(const void* h, const float* gamma, float eps, void* out, int M,
                  void* stream);
 /* out[m,n] = bf16( silu(gu[m,n]) * gu[m,N+n] ); gu [M,2N], out [M,N] bf16; N % 8 == 0. */
 int coda_swiglu(const void* gu, void* out, int M, int N, void* stream);
+/* In place on a stored qkv [M, (nq+2nkv)*hd] bf16 (as a plain GEMM writes it): the
+ * rotate-half RoPE of coda_gemm_rope on the q and k heads, each pair rounded to bf16
+ * again.  Tables, positions and sizes as coda_gemm_rope (head_dim 64). */
+int coda_rope_apply(void* qkv, const float* rope_cos, const float* rope_sin, const int32_t* pos,
+                    int max_pos, int M, int n_q_heads, int n_kv_heads, int head_dim, void* stream);
+/* Cross entropy of stored bf16 logits z [M,V] (as a plain GEMM writes them):
+ *   lse[m] = ln sum_v exp z[m,v],  loss[m] = lse[m] - z[m, labels[m]]
+ * labels [M] int32 in [0,V) (clamped, not checked); lse, loss [M] fp32; V % 8 == 0. */
+int coda_cross_entropy_rows(const void* logits, const int32_t* labels, float* lse, float* loss,
+                            int M, int V, void* stream);
 
 #ifdef __cplusplus
 }
