@@ -162,6 +162,7 @@ def main():
     g1_ms, red_ms, g2_ms = (float(np.mean(per[:, i])) for i in range(3))
     g2_tflops = flops_g2 / (g2_ms * 1e-3) / 1e12
 
+    clock = measured_clock_ghz("gemm_rowscale_swiglu")
     rows = {}
     if not args.no_rows:
         rows = time_other_rows(torch, ops, inputs, stream, min(args.steps, 10), 3)
@@ -201,7 +202,10 @@ def main():
                      "unit": "TFLOP/s", "frac": round(g2_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic("gemm_rowscale_swiglu"),
                      "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE, "
-                                     "copy-calibrated)"},
+                                     "copy-calibrated)",
+                     "clock_ghz_measured": clock,
+                     "frac_at_measured_clock":
+                         None if clock is None else round(g2_tflops / (PEAK_BF16_TFLOPS * clock / 2.4), 4)},
         "cpu_baseline": cpu,
         "other_rows": rows,
     }
@@ -380,6 +384,20 @@ def kernel_sources_sha256():
                   "rb") as f:
             h.update(f.read())
     return h.hexdigest()
+
+
+def measured_clock_ghz(kernel):
+    """Average shader clock during `kernel` from the committed rocprofv3 counter
+    summary, or None when the kernel's sources changed since it was taken."""
+    root = os.path.dirname(os.path.abspath(__file__))
+    try:
+        with open(os.path.join(root, "profiles", "clock.json")) as f:
+            rec = json.load(f)[kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    if kernel_sources_sha256() != rec.get("sources_sha256"):
+        return None
+    return float(rec["clock_ghz"])
 
 
 def measured_traffic(kernel):
