@@ -310,6 +310,41 @@ int coda_swiglu(const void* gu, void* out, int M, int N, void* stream) {
   }
 }
 
+int coda_gemm_fp8(const void* A, const void* W, const float* a_scale, const float* w_scale,
+                  void* C, int ldc, int M, int N, int K, void* stream) {
+  try {
+    if (!A || !W || !a_scale || !w_scale || !C) return CODA_ERR_NULL;
+    if (int st = check_gemm_shape(M, N, K, 128)) return st;
+    if (ldc < N || ldc % 8 != 0 || !small_enough(M, ldc)) return CODA_ERR_SHAPE;
+    if (!aligned(A, 16) || !aligned(W, 16) || !aligned(C, 16) || !aligned(a_scale, 4) ||
+        !aligned(w_scale, 4))
+      return CODA_ERR_ALIGN;
+    if (int st = check_device()) return st;
+    return launched(coda::launch_gemm_plain_fp8(
+        static_cast<const uint8_t*>(A), static_cast<const uint8_t*>(W), a_scale, w_scale,
+        static_cast<uint16_t*>(C), M, N, K, ldc, as_stream(stream)));
+  } catch (...) {
+    return CODA_ERR_LAUNCH;
+  }
+}
+
+int coda_quantize_e4m3(const void* x, int64_t count, const float* s_in, void* out, float* amax,
+                       float* s_out, void* stream) {
+  try {
+    if (!x || !s_in || !out || !amax || !s_out) return CODA_ERR_NULL;
+    if (count < 8 || count % 8 != 0 || count >= (int64_t(1) << 34)) return CODA_ERR_SHAPE;
+    if (!aligned(x, 16) || !aligned(out, 8) || !aligned(s_in, 4) || !aligned(amax, 4) ||
+        !aligned(s_out, 4))
+      return CODA_ERR_ALIGN;
+    if (int st = check_device()) return st;
+    return launched(coda::launch_quantize_e4m3(static_cast<const uint16_t*>(x), s_in,
+                                               static_cast<uint8_t*>(out), count, amax, s_out,
+                                               as_stream(stream)));
+  } catch (...) {
+    return CODA_ERR_LAUNCH;
+  }
+}
+
 int coda_rope_apply(void* qkv, const float* rope_cos, const float* rope_sin, const int32_t* pos,
                     int max_pos, int M, int n_q_heads, int n_kv_heads, int head_dim, void* stream) {
   try {

@@ -226,7 +226,77 @@ __global__ __launch_bounds__(kThreads, 1) void k_rowscale_swiglu_fp8(
   wait_vm0();  // the last tile's unused prefetch into LDS lands before the block ends
 }
 
+// ---------------------------------------------------------------------------
+// Plain fp8 GEMM for the unfused baseline: C[m, n] = bf16(A[m,:] . W[n,:] *
+// sa * sw), C with row stride ldc (so two GEMMs with different weight scales
+// can fill the two halves of one [M, 2N] buffer).  Stores as in GEMM1: lanes
+// L and L + 32 exchange halves of their run pairs, 16 bytes per store.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads, 1) void k_gemm_plain_fp8(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ W, const float* __restrict__ a_scale,
+    const float* __restrict__ w_scale, uint16_t* __restrict__ C, int M, int N, int K, int ldc,
+    int gm, int gn) {
+  __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
+  const float scale = a_scale[0] * w_scale[0];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int nt = gm * gn;
+  const bool hi = lane >= 32;
+  bool prefetched = false;
+  for (int t = blockIdx.x; t < nt; t += gridDim.x) {
+    const TileCoord tc = map_tile(t, gm, gn, 8);
+    const int m0 = tc.tm * kBM, n0 = tc.tn * kBN;
+    TileChain ch;
+    ch.prefetched = prefetched;
+    const bool has_next = t + (int)gridDim.x < nt;
+    const TileCoord nc = has_next ? map_tile(t + gridDim.x, gm, gn, 8) : tc;
+    ch.next = MainloopSrc{A, W, nullptr, M, N, K, nc.tm * kBM, nc.tn * kBN};
+    Acc8 acc;
+    mainloop_fp8<false>(acc, smem, MainloopSrc{A, W, nullptr, M, N, K, m0, n0}, ch, [] {}, [] {});
+    const __amdgpu_buffer_rsrc_t crsrc =
+        make_rsrc(C + (size_t)m0 * ldc, (uint32_t)min(kBM, M - m0) * (uint32_t)ldc * 2u);
+    const int nw0 = n0 + wn * 128;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ml = wm * 128 + i * 32 + (lane & 31);
+      const bool mv = m0 + ml < M;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u32x2_t pk[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x16_t& a = acc.v[j][i];
+          pk[g] = pack_bf16x4(a[g * 4] * scale, a[g * 4 + 1] * scale, a[g * 4 + 2] * scale,
+                              a[g * 4 + 3] * scale);
+        }
+#pragma unroll
+        for (int gp = 0; gp < 4; gp += 2) {
+          const int n = nw0 + j * 32 + (gp + (hi ? 1 : 0)) * 8;
+          const u32x2_t sd = hi ? pk[gp] : pk[gp + 1];
+          const u32x2_t rx = {(unsigned)__shfl_xor((int)sd.x, 32, 64),
+                              (unsigned)__shfl_xor((int)sd.y, 32, 64)};
+          store16(crsrc,
+                  hi ? u32x4_t{rx.x, rx.y, pk[gp + 1].x, pk[gp + 1].y}
+                     : u32x4_t{pk[gp].x, pk[gp].y, rx.x, rx.y},
+                  (mv && n < N) ? ((uint32_t)ml * (uint32_t)ldc + (uint32_t)n) * 2u : kOobOffset);
+        }
+      }
+    }
+    prefetched = has_next;
+  }
+  wait_vm0();  // the last tile's unused prefetch into LDS lands before the block ends
+}
+
 static inline int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+hipError_t launch_gemm_plain_fp8(const uint8_t* A, const uint8_t* W, const float* a_scale,
+                                 const float* w_scale, uint16_t* C, int M, int N, int K, int ldc,
+                                 hipStream_t stream) {
+  const int gm = cdiv(M, kBM), gn = cdiv(N, kBN);
+  hipLaunchKernelGGL(k_gemm_plain_fp8, dim3(min(gm * gn, cu_count())), dim3(kThreads), 0, stream,
+                     A, W, a_scale, w_scale, C, M, N, K, ldc, gm, gn);
+  return hipGetLastError();
+}
 
 hipError_t launch_residual_partialrms_fp8(const uint8_t* A, const uint8_t* W, const float* a_scale,
                                           const float* w_scale, const uint16_t* res, uint16_t* h,

@@ -54,6 +54,11 @@ hipError_t launch_rmsnorm(const uint16_t* h, const float* gamma, float eps, uint
 hipError_t launch_swiglu(const uint16_t* gu, uint16_t* out, int M, int N, hipStream_t stream);
 hipError_t launch_rope_apply(uint16_t* qkv, const float* rcos, const float* rsin, const int* pos,
                              int max_pos, int M, int n_q, int n_kv, hipStream_t stream);
+hipError_t launch_gemm_plain_fp8(const uint8_t* A, const uint8_t* W, const float* a_scale,
+                                 const float* w_scale, uint16_t* C, int M, int N, int K, int ldc,
+                                 hipStream_t stream);
+hipError_t launch_quantize_e4m3(const uint16_t* x, const float* s_in, uint8_t* out, int64_t count,
+                                float* amax, float* s_out, hipStream_t stream);
 hipError_t launch_ce_rows(const uint16_t* z, const int* labels, float* lse, float* loss, int M,
                           int V, hipStream_t stream);
 

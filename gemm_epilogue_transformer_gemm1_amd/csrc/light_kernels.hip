@@ -376,6 +376,44 @@ __global__ __launch_bounds__(256) void k_ce_rows(const uint16_t* __restrict__ z,
   }
 }
 
+// e4m3 quantisation for the unfused fp8 baseline (delayed scaling):
+// out = E4M3_sat(x / s_in) with s_in the previous scale, and the amax of |x|
+// for the next one (one atomicMax per block on the non-negative float's bits).
+__global__ __launch_bounds__(256) void k_quantize_e4m3(const uint16_t* __restrict__ x,
+                                                       const float* __restrict__ s_in,
+                                                       uint8_t* __restrict__ out, int64_t total8,
+                                                       unsigned int* __restrict__ amax_bits) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  float mx = 0.f;
+  if (idx < total8) {
+    const float inv = 1.0f / s_in[0];
+    float f[8];
+    load8(x + idx * 8, f);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) mx = fmaxf(mx, fabsf(f[q]));
+    const uint32_t lo = pack_e4m3x4_sat(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv);
+    const uint32_t hi = pack_e4m3x4_sat(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv);
+    *(u32x2_t*)(out + idx * 8) = u32x2_t{lo, hi};
+  }
+  __shared__ float red[4];
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    atomicMax(amax_bits, __float_as_uint(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]))));
+}
+
+hipError_t launch_quantize_e4m3(const uint16_t* x, const float* s_in, uint8_t* out, int64_t count,
+                                float* amax, float* s_out, hipStream_t stream) {
+  unsigned int* bits = reinterpret_cast<unsigned int*>(amax);
+  const int64_t total8 = count / 8;
+  hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(1), 0, stream, bits);
+  hipLaunchKernelGGL(k_quantize_e4m3, dim3(cdiv(total8, 256)), dim3(256), 0, stream, x, s_in, out,
+                     total8, bits);
+  hipLaunchKernelGGL(k_amax_to_scale, dim3(1), dim3(1), 0, stream, bits, amax, s_out);
+  return hipGetLastError();
+}
+
 hipError_t launch_ce_rows(const uint16_t* z, const int* labels, float* lse, float* loss, int M,
                           int V, hipStream_t stream) {
   hipLaunchKernelGGL(k_ce_rows, dim3(M), dim3(256), 0, stream, z, labels, lse, loss, V);

@@ -48,6 +48,8 @@ _SIGNATURES = {
     "coda_residual_add": ([_p, _p, _p, _i64, _p], _c_int),
     "coda_rmsnorm": ([_p, _p, _c_float, _p, _c_int, _c_int, _p], _c_int),
     "coda_swiglu": ([_p, _p, _c_int, _c_int, _p], _c_int),
+    "coda_gemm_fp8": ([_p, _p, _p, _p, _p, _c_int, _c_int, _c_int, _c_int, _p], _c_int),
+    "coda_quantize_e4m3": ([_p, _i64, _p, _p, _p, _p, _p], _c_int),
     "coda_rope_apply": ([_p, _p, _p, _p, _c_int, _c_int, _c_int, _c_int, _c_int, _p], _c_int),
     "coda_cross_entropy_rows": ([_p, _p, _p, _p, _c_int, _c_int, _p], _c_int),
 }
@@ -235,3 +237,23 @@ def cross_entropy_rows(logits, labels, lse, loss, stream=None):
     M, V = logits.shape
     _call("coda_cross_entropy_rows", _ptr(logits, _BF16, "logits"), _ptr(labels, _I32, "labels"),
           _ptr(lse, _F32, "lse"), _ptr(loss, _F32, "loss"), M, V, _stream(stream))
+
+
+def gemm_fp8(A, W, a_scale, w_scale, C, stream=None):
+    """C = bf16(A W^T * a_scale * w_scale), e4m3 operands (unfused baseline).
+    C may be a column slice of a wider row-major buffer (its row stride is used)."""
+    M, K = A.shape
+    N = W.shape[0]
+    if C.stride(1) != 1 or C.shape != (M, N):
+        raise ValueError("C must be [M, N] with unit column stride")
+    if not C.is_cuda or C.dtype != _BF16:
+        raise TypeError("C must be a bf16 device tensor")
+    _call("coda_gemm_fp8", _ptr(A, _E4M3, "A"), _ptr(W, _E4M3, "W"), _ptr(a_scale, _F32, "a_scale"),
+          _ptr(w_scale, _F32, "w_scale"), C.data_ptr(), C.stride(0), M, N, K, _stream(stream))
+
+
+def quantize_e4m3(x, s_in, out, amax, s_out, stream=None):
+    """out = e4m3(x / s_in), amax = max|x|, s_out = amax / 448 (unfused baseline)."""
+    _call("coda_quantize_e4m3", _ptr(x, _BF16, "x"), x.numel(), _ptr(s_in, _F32, "s_in"),
+          _ptr(out, _E4M3, "out"), _ptr(amax, _F32, "amax"), _ptr(s_out, _F32, "s_out"),
+          _stream(stream))

@@ -204,6 +204,15 @@ int coda_rmsnorm(const void* h, const float* gamma, float eps, void* out, int M,
                  void* stream);
 /* out[m,n] = bf16( silu(gu[m,n]) * gu[m,N+n] ); gu [M,2N], out [M,N] bf16; N % 8 == 0. */
 int coda_swiglu(const void* gu, void* out, int M, int N, void* stream);
+/* C[m, n] = bf16( A[m,:] . W[n,:] * a_scale * w_scale ), e4m3 operands A [M,K], W [N,K],
+ * device fp32 scalars a_scale, w_scale; C rows ldc elements apart (ldc >= N, ldc % 8 == 0).
+ * Sizes as coda_gemm_residual_partialrms (fp8: K % 128). */
+int coda_gemm_fp8(const void* A, const void* W, const float* a_scale, const float* w_scale,
+                  void* C, int ldc, int M, int N, int K, void* stream);
+/* out[i] = E4M3_sat( x[i] / *s_in ) (x bf16, out e4m3 bytes, count elements, count % 8 == 0);
+ * *amax = max |x|, *s_out = *amax / 448 (1 if amax is 0): delayed scaling, the next call's s_in. */
+int coda_quantize_e4m3(const void* x, int64_t count, const float* s_in, void* out, float* amax,
+                       float* s_out, void* stream);
 /* In place on a stored qkv [M, (nq+2nkv)*hd] bf16 (as a plain GEMM writes it): the
  * rotate-half RoPE of coda_gemm_rope on the q and k heads, each pair rounded to bf16
  * again.  Tables, positions and sizes as coda_gemm_rope (head_dim 64). */

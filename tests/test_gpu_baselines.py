@@ -50,3 +50,48 @@ def test_cross_entropy_rows_vs_oracle(M, V):
     ref_loss = ref_lse - zd[np.arange(M), labels]
     assert row_rel_err(f32_host(lse), ref_lse) <= TOL_ROW
     assert np.max(np.abs(f32_host(loss) - ref_loss)) <= TOL_ROW * np.max(np.abs(ref_lse))
+
+
+def test_gemm_fp8_plain_exact_and_strided():
+    """e4m3 codes of -2..2 and power-of-two scales: every product sum is exact
+    in fp32 and in bf16, so C matches the oracle bit for bit; the two halves of
+    a [M, 2N] buffer are written through the row stride."""
+    from oracle import codecs
+    M, N, K = 300, 272, 256
+    rng = np.random.default_rng(9)
+    a = rng.integers(-2, 3, size=(M, K)).astype(np.float64)
+    w1 = rng.integers(-1, 2, size=(N, K)).astype(np.float64)
+    w2 = rng.integers(-1, 2, size=(N, K)).astype(np.float64)
+    enc = codecs.e4m3_encode_fast
+    say(f"gemm_fp8 M={M} N={N} K={K}")
+    u8 = lambda v: torch.from_numpy(np.ascontiguousarray(v)).to(DEV)
+    sc = lambda v: torch.tensor([v], dtype=torch.float32, device=DEV)
+    C = torch.full((M, 2 * N), float("nan"), dtype=torch.bfloat16, device=DEV)
+    ops.gemm_fp8(u8(enc(a)), u8(enc(w1)), sc(0.5), sc(0.25), C[:, :N])
+    ops.gemm_fp8(u8(enc(a)), u8(enc(w2)), sc(0.5), sc(2.0), C[:, N:])
+    torch.cuda.synchronize()
+    got = bf16_host(C)
+    assert np.array_equal(got[:, :N], oracle.gemm_nt(a, w1) * 0.125)
+    assert np.array_equal(got[:, N:], oracle.gemm_nt(a, w2) * 1.0)
+
+
+def test_quantize_e4m3_vs_oracle():
+    """Power-of-two scale: x / s is exact, so the codes are the oracle's
+    round-to-nearest-even saturating codes bit for bit (values beyond 448 s
+    saturate); amax exact; the next scale amax / 448 to fp32 rounding."""
+    from oracle import codecs
+    n = 4096 * 24
+    rng = np.random.default_rng(2)
+    x = (rng.standard_normal(n) * 60).astype(np.float32)
+    bits = inputs.to_bf16_bits(x)
+    xd = dec_bf16(bits)
+    say(f"quantize_e4m3 n={n}")
+    s_in = torch.tensor([0.25], dtype=torch.float32, device=DEV)
+    out = torch.empty(n, dtype=torch.uint8, device=DEV)
+    amax = torch.empty(1, dtype=torch.float32, device=DEV)
+    s_out = torch.empty(1, dtype=torch.float32, device=DEV)
+    ops.quantize_e4m3(bf16_dev(bits), s_in, out, amax, s_out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), codecs.e4m3_encode_fast(xd / 0.25))
+    assert float(amax.item()) == float(np.max(np.abs(xd)))
+    assert abs(float(s_out.item()) - np.max(np.abs(xd)) / 448) <= 1e-6 * np.max(np.abs(xd)) / 448
