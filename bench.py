@@ -236,7 +236,21 @@ def step_times(torch, stream, fn, steps):
     return [e0.elapsed_time(e1) for e0, e1 in evs]
 
 
-def _events_time(torch, stream, fn, steps, warmup):
+def _events_time(torch, stream, fn, steps, warmup, min_ms=40.0):
+    """Mean step time (ms) over back-to-back steps.  Warmup and timed region
+    each cover at least `min_ms` of GPU work (the shader clock settles over
+    tens of milliseconds under sustained MFMA load), so short steps are
+    repeated more often than `steps`/`warmup`."""
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    est = max(e0.elapsed_time(e1), 1e-3)
+    reps = int(min(2000, max(1, np.ceil(min_ms / est))))
+    steps, warmup = max(steps, reps), max(warmup, reps)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -247,6 +261,22 @@ def _events_time(torch, stream, fn, steps, warmup):
     e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps
+
+
+def _kernel_times(torch, stream, fns, steps):
+    """Mean duration (ms) of each launch in `fns`, from events recorded on the
+    launch stream between consecutive launches over `steps` passes."""
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    for e in evs:
+        e[0].record(stream)
+        for i, f in enumerate(fns):
+            f()
+            e[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(len(fns))] for e in evs])
+    return [round(float(v), 4) for v in per.mean(axis=0)]
 
 
 def time_other_rows(torch, ops, inputs, stream, steps, warmup):
@@ -335,6 +365,10 @@ def time_other_rows(torch, ops, inputs, stream, steps, warmup):
                                       round(float((loss_u - loss).abs().max().item()), 6)}}
     del x, wl, tmax, tsum, w, logits, lse_u, loss_u
 
+    # the bf16 MLP block at the 7B and 70B hidden sizes
+    for name in ("mlp_7b", "mlp_70b"):
+        out[name] = _mlp_row(torch, ops, inputs, stream, name, steps, warmup, bf)
+
     # fp8 8B-shaped MLP block (delayed scaling: the previous step's scale)
     print("[bench] mlp_8b_fp8", file=sys.stderr, flush=True)
     w = inputs.make_workload("mlp_8b_fp8")
@@ -393,6 +427,64 @@ def time_other_rows(torch, ops, inputs, stream, steps, warmup):
                                      "tflops": round(fl / ms_u / 1e9, 1),
                                      "speedup_fused_vs_unfused": round(ms_u / ms, 3)}}
     return out
+
+
+def _mlp_row(torch, ops, inputs, stream, name, steps, warmup, bf, **sizes):
+    """Fused and unfused step time of a bf16 MLP workload (same kernels and
+    timing policy as the headline line, inputs resident in HBM)."""
+    dev = "cuda:0"
+    eps = 1e-5
+    print(f"[bench] {name}", file=sys.stderr, flush=True)
+    w = inputs.make_workload(name, **sizes)
+    M, d, K1, ffn = (w.sizes[k] for k in ("M", "d", "K1", "ffn"))
+    x, res, w1, wg, wu = (bf(w.arrays[k]) for k in ("x", "res", "w1", "wg", "wu"))
+    gamma = torch.from_numpy(w.arrays["gamma"]).to(dev)
+    del w
+    wg_f, wu_f = torch.empty_like(wg), torch.empty_like(wu)
+    ops.fold_gamma(wg, gamma, wg_f)
+    ops.fold_gamma(wu, gamma, wu_f)
+    h = torch.empty(M, d, dtype=torch.bfloat16, device=dev)
+    P = torch.empty(ops.rms_tiles(d), M, dtype=torch.float32, device=dev)
+    r = torch.empty(M, dtype=torch.float32, device=dev)
+    o = torch.empty(M, ffn, dtype=torch.bfloat16, device=dev)
+
+    fused_k = [lambda: ops.gemm_residual_partialrms(x, w1, res, h, P),
+               lambda: ops.rms_reduce(P, d, eps, r),
+               lambda: ops.gemm_rowscale_swiglu(h, wg_f, wu_f, r, o)]
+
+    def fused():
+        for f in fused_k:
+            f()
+    ms = _events_time(torch, stream, fused, steps, warmup)
+    k_ms = _kernel_times(torch, stream, fused_k, steps)
+    del wg_f, wu_f
+    wgu = torch.cat([wg, wu], 0).contiguous()
+    del wg, wu
+    y_u, h_u, n_u = (torch.empty(M, d, dtype=torch.bfloat16, device=dev) for _ in range(3))
+    gu = torch.empty(M, 2 * ffn, dtype=torch.bfloat16, device=dev)
+    o_u = torch.empty(M, ffn, dtype=torch.bfloat16, device=dev)
+
+    unfused_k = [lambda: ops.gemm_bf16(x, w1, y_u),
+                 lambda: ops.residual_add(y_u, res, h_u),
+                 lambda: ops.rmsnorm(h_u, gamma, eps, n_u),
+                 lambda: ops.gemm_bf16(n_u, wgu, gu),
+                 lambda: ops.swiglu(gu, o_u)]
+
+    def unfused():
+        for f in unfused_k:
+            f()
+    ms_u = _events_time(torch, stream, unfused, steps, warmup)
+    ku_ms = _kernel_times(torch, stream, unfused_k, steps)
+    fl = 2.0 * M * d * K1 + 2.0 * M * 2 * ffn * d
+    return {"workload": f"M={M}, d={d}, K1={K1}, ffn={ffn}, gate/up with SwiGLU, eps=1e-5",
+            "ms_per_step": round(ms, 4), "tflops": round(fl / ms / 1e9, 1),
+            "pct_of_bf16_peak": round(100 * fl / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
+            "kernels_ms": dict(zip(("gemm_residual_partialrms", "rms_reduce",
+                                    "gemm_rowscale_swiglu"), k_ms)),
+            "unfused": {"ms_per_step": round(ms_u, 4), "tflops": round(fl / ms_u / 1e9, 1),
+                        "speedup_fused_vs_unfused": round(ms_u / ms, 3),
+                        "kernels_ms": dict(zip(("gemm_bf16", "residual_add", "rmsnorm",
+                                                "gemm_bf16_gate_up", "swiglu"), ku_ms))}}
 
 
 # the sources the bf16 GEMM kernels are compiled from

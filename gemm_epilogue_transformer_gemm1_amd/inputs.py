@@ -19,6 +19,8 @@ The shapes and distributions follow the LLaMA-3-shaped workloads:
   attn_rope  M=8192,  d=2048, K1=8192, 32 q / 8 kv heads of 64, theta 5e5
   lm_head    M=8192,  d=2048, V=128256
   mlp_8b_fp8 M=16384, d=4096, K1=4096, ffn=14336 (e4m3)
+  mlp_7b     M=8192,  d=4096, K1=4096, ffn=11008 (bf16)
+  mlp_70b    M=8192,  d=8192, K1=8192, ffn=28672 (bf16)
 Activations and residuals ~ N(0, 1); weights ~ N(0, 1/fan_in of the layer
 they feed, i.e. 1/d for the d-wide layers); gamma = 1 + 0.1 N(0, 1).
 """
@@ -38,6 +40,10 @@ WORKLOADS = {
                                   theta=500000.0, seq_len=2048)),
     "lm_head": (3, "lm", dict(M=8192, d=2048, V=128256)),
     "mlp_8b_fp8": (4, "mlp_fp8", dict(M=16384, d=4096, K1=4096, ffn=14336)),
+    # the same MLP block at the 7B and 70B hidden sizes (LLaMA-2-7B: d=4096,
+    # ffn=11008; LLaMA-2/3-70B: d=8192, ffn=28672), M=8192 tokens as for 1B
+    "mlp_7b": (5, "mlp", dict(M=8192, d=4096, K1=4096, ffn=11008)),
+    "mlp_70b": (6, "mlp", dict(M=8192, d=8192, K1=8192, ffn=28672)),
 }
 
 _TENSOR_IDS = {"x": 0, "res": 1, "w1": 2, "wg": 3, "wu": 4, "gamma": 5, "wqkv": 6,

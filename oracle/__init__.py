@@ -26,6 +26,9 @@ tests/test_oracle_*.py.  Parity status per function:
   lm_head_ce, lse_*         pinned (brute force with math.fsum, torch
                             cross_entropy, W=0 closed form, merge order)
   partial_sumsq, tile_lse   pinned (sum identities with the row results)
+  swiglu_grad, rmsnorm_bwd, pinned (central finite differences in numpy,
+  mlp_layer_bwd             torch float64 autograd, scale invariance of
+                            RMSNorm: dh . h = 0 when eps = 0 and dy = 0)
 The page's own numbers: the page prints none for this path, so nothing is
 pinned to page values (parity unpinned against the page itself).
 """
@@ -39,6 +42,9 @@ from .reference import (  # noqa: F401
     silu,
     swiglu,
     mlp_block,
+    swiglu_grad,
+    rmsnorm_bwd,
+    mlp_layer_bwd,
     fp8_mlp_block,
     fp8_h_amax,
     rope_tables,

@@ -87,6 +87,67 @@ def mlp_block(x, res, wo, wg, wu, gamma, eps):
     return {"h": h, "r": r, "g": g, "u": u, "out": swiglu(g, u)}
 
 
+# ---------------------------------------------------------------------------
+# Backward of the MLP sub-layer.  Section "CODA: the secret in the epilogue"
+# states that when the tail of the forward pass is block-local the backward
+# pass inherits the same structure, and section "Results" reports backward
+# kernels for GEMM-Residual-PartialRMS-GEMM and for SwiGLU.  The page prints
+# no formulas: what follows is the chain rule applied to the forward
+# definitions above, in the order the forward computes.
+# ---------------------------------------------------------------------------
+
+def swiglu_grad(dout, g, u):
+    """Gradients of out = silu(g) * u given dout = dL/dout:
+    du = dout * silu(g) and dg = dout * u * silu'(g), where, with
+    s = 1 / (1 + exp(-g)), silu'(g) = s + g s (1 - s)."""
+    dout = np.asarray(dout, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    u = np.asarray(u, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        s = 1.0 / (1.0 + np.exp(-g))
+    dsilu = s + g * s * (1.0 - s)
+    return dout * u * dsilu, dout * (g * s)
+
+
+def rmsnorm_bwd(dn, h, gamma, eps):
+    """Gradient w.r.t. h of n = r h gamma, r = (mean_j h_j^2 + eps)^(-1/2),
+    given dn = dL/dn.  Per row, d r / d h_j = -r^3 h_j / d, so
+        dh_j = r gamma_j dn_j - (r^3 / d) h_j sum_k gamma_k dn_k h_k.
+    Returns (dh, coefficient r^3/d sum_k gamma_k dn_k h_k per row)."""
+    h = np.asarray(h, dtype=np.float64)
+    dng = np.asarray(dn, dtype=np.float64) * np.asarray(gamma, dtype=np.float64)[None, :]
+    r = rms_scale(h, eps)
+    d = h.shape[1]
+    coef = r ** 3 / d * np.sum(dng * h, axis=1)
+    return r[:, None] * dng - coef[:, None] * h, coef
+
+
+def mlp_layer_bwd(x, res, wo, wg, wu, gamma, eps, wd, dy):
+    """Backward of the MLP sub-layer of a pre-norm block,
+        h = res + x wo^T,  out = mlp_block(...)["out"],  next = h + out wd^T,
+    given dy = dL/dnext [M,d] (wd [d,ffn] is the down projection).
+
+    Returns the forward values of mlp_block plus
+      dout [M,ffn] = dy wd                    (through the down projection)
+      dg, du       = swiglu_grad(dout, g, u)
+      dn   [M,d]   = dg wg + du wu            (gradient w.r.t. n = r h gamma)
+      dh   [M,d]   = rmsnorm_bwd(dn, h) + dy  (the skip connection adds dy)
+      coef [M]     = the per-row coefficient of rmsnorm_bwd
+      dres = dh,  dx [M,K1] = dh wo           (h = res + x wo^T)
+    """
+    f = mlp_block(x, res, wo, wg, wu, gamma, eps)
+    dy = np.asarray(dy, dtype=np.float64)
+    dout = dy @ np.asarray(wd, dtype=np.float64)
+    dg, du = swiglu_grad(dout, f["g"], f["u"])
+    dn = dg @ np.asarray(wg, dtype=np.float64) + du @ np.asarray(wu, dtype=np.float64)
+    dh_norm, coef = rmsnorm_bwd(dn, f["h"], gamma, eps)
+    dh = dh_norm + dy
+    dx = dh @ np.asarray(wo, dtype=np.float64)
+    f.update({"dout": dout, "dg": dg, "du": du, "dn": dn, "coef": coef, "dh": dh,
+              "dres": dh, "dx": dx})
+    return f
+
+
 def fp8_mlp_block(xq, sx, res, woq, swo, wgq, swg, wuq, swu, eps, h_scale=None):
     """The same block with e4m3 operands (section "The cost of laziness in
     large-model training" names FP8 as the regime where data movement

@@ -372,11 +372,142 @@ def pin_fp8_block(seed=13):
                    abs(am - am_ref) / am_ref), 1e-12, "fp8 block brute force")
 
 
+# ---------------------------------------------------------------------------
+# backward of the MLP sub-layer
+# ---------------------------------------------------------------------------
+
+def _bf_layer_loss(x, res, wo, wg, wu, gamma, eps, wd, dy):
+    """sum(next * dy) of the sub-layer next = h + swiglu(...) wd^T, in pure
+    Python (the function whose derivative the backward oracle claims to be)."""
+    M, d, ffn = len(x), len(wo), len(wg)
+    y = _bf_gemm_nt(x, wo)
+    h = [[res[m][n] + y[m][n] for n in range(d)] for m in range(M)]
+    tot = []
+    for m in range(M):
+        r = 1.0 / math.sqrt(math.fsum(v * v for v in h[m]) / d + eps)
+        nrm = [r * h[m][n] * gamma[n] for n in range(d)]
+        g = [math.fsum(nrm[k] * wg[j][k] for k in range(d)) for j in range(ffn)]
+        u = [math.fsum(nrm[k] * wu[j][k] for k in range(d)) for j in range(ffn)]
+        out = [_bf_silu(g[j]) * u[j] for j in range(ffn)]
+        for n in range(d):
+            nxt = h[m][n] + math.fsum(out[j] * wd[n][j] for j in range(ffn))
+            tot.append(nxt * dy[m][n])
+    return math.fsum(tot)
+
+
+def _layer_inputs(seed, M=3, K1=5, d=4, ffn=6):
+    rng = random.Random(seed)
+    return dict(x=_rand(rng, M, K1), res=_rand(rng, M, d), wo=_rand(rng, d, K1, 0.5),
+                wg=_rand(rng, ffn, d, 0.5), wu=_rand(rng, ffn, d, 0.5),
+                gamma=[1.0 + 0.1 * rng.gauss(0, 1) for _ in range(d)], eps=1e-3,
+                wd=_rand(rng, d, ffn, 0.5), dy=_rand(rng, M, d))
+
+
+def _oracle_bwd(p):
+    a = lambda k: np.array(p[k], dtype=np.float64)
+    return oracle.mlp_layer_bwd(a("x"), a("res"), a("wo"), a("wg"), a("wu"), a("gamma"),
+                                p["eps"], a("wd"), a("dy"))
+
+
+def pin_swiglu_grad(seed=14):
+    """Central differences of silu(g) u, torch float64 autograd, and the
+    closed form at g = 0 (silu'(0) = 1/2, silu(0) = 0)."""
+    rng = np.random.default_rng(seed)
+    g, u, dout = (rng.standard_normal((3, 5)) * 3 for _ in range(3))
+    dg, du = R.swiglu_grad(dout, g, u)
+    step = 1e-6
+    fd_g = np.array([[(_bf_silu(g[i, j] + step) - _bf_silu(g[i, j] - step)) / (2 * step)
+                      * u[i, j] * dout[i, j] for j in range(5)] for i in range(3)])
+    fd_u = np.array([[_bf_silu(g[i, j]) * dout[i, j] for j in range(5)] for i in range(3)])
+    e1 = max(_rel(dg, fd_g), _rel(du, fd_u))
+    tg = torch.from_numpy(g).requires_grad_(True)
+    tu = torch.from_numpy(u).requires_grad_(True)
+    (torch.nn.functional.silu(tg) * tu * torch.from_numpy(dout)).sum().backward()
+    e2 = max(_rel(dg, tg.grad.numpy()), _rel(du, tu.grad.numpy()))
+    z = np.zeros((1, 4))
+    dg0, du0 = R.swiglu_grad(np.full((1, 4), 3.0), z, np.arange(4.0)[None, :])
+    e3 = float(np.max(np.abs(dg0 - 1.5 * np.arange(4.0)))) + float(np.max(np.abs(du0)))
+    return _ok(max(e1 / 1e3, e2, e3), 1e-12, "swiglu grad (fd/1e3, torch, g=0)")
+
+
+def pin_layer_bwd_finite_differences(seed=15):
+    """Every entry of dx and dres against central differences of the
+    pure-Python sub-layer loss sum(next * dy) (step 1e-6: error ~1e-9)."""
+    p = _layer_inputs(seed)
+    o = _oracle_bwd(p)
+    step = 1e-6
+    errs = []
+    for key, grad in (("x", o["dx"]), ("res", o["dres"])):
+        fd = np.zeros_like(grad)
+        for i in range(grad.shape[0]):
+            for j in range(grad.shape[1]):
+                hi = {**p, key: [row[:] for row in p[key]]}
+                lo = {**p, key: [row[:] for row in p[key]]}
+                hi[key][i][j] += step
+                lo[key][i][j] -= step
+                fd[i, j] = (_bf_layer_loss(**hi) - _bf_layer_loss(**lo)) / (2 * step)
+        errs.append(_rel(grad, fd))
+    return _ok(max(errs), 1e-7, "layer backward vs finite differences")
+
+
+def pin_layer_bwd_torch(seed=16):
+    """dout, dg, du, dn, dh and dx against torch float64 autograd of the same
+    sub-layer built from library routines (torch rms_norm and silu)."""
+    rng = np.random.default_rng(seed)
+    M, K1, d, ffn, eps = 5, 12, 8, 10, 1e-5
+    t = lambda *s, sc=1.0: torch.from_numpy(rng.standard_normal(s) * sc).requires_grad_(True)
+    x, res = t(M, K1), t(M, d)
+    wo, wg, wu, wd = t(d, K1, sc=0.3), t(ffn, d, sc=0.3), t(ffn, d, sc=0.3), t(d, ffn, sc=0.3)
+    gamma = torch.from_numpy(1 + 0.1 * rng.standard_normal(d))
+    dy = torch.from_numpy(rng.standard_normal((M, d)))
+    h = res + x @ wo.T
+    xh = torch.nn.functional.rms_norm(h, (d,), eps=eps)
+    n = xh * gamma
+    g, u = n @ wg.T, n @ wu.T
+    out = torch.nn.functional.silu(g) * u
+    for v in (n, g, u, out, h):
+        v.retain_grad()
+    ((h + out @ wd.T) * dy).sum().backward()
+    num = lambda v: v.detach().numpy()
+    o = oracle.mlp_layer_bwd(num(x), num(res), num(wo), num(wg), num(wu), gamma.numpy(), eps,
+                             num(wd), dy.numpy())
+    errs = [_rel(o["dout"], out.grad.numpy()), _rel(o["dg"], g.grad.numpy()),
+            _rel(o["du"], u.grad.numpy()), _rel(o["dn"], n.grad.numpy()),
+            _rel(o["dh"], res.grad.numpy()), _rel(o["dx"], x.grad.numpy())]
+    return _ok(max(errs), 1e-12, "layer backward vs torch autograd")
+
+
+def pin_rmsnorm_bwd_scale_invariance(seed=17):
+    """With eps = 0, RMSNorm is invariant to scaling h, so its gradient is
+    orthogonal to h: sum_j dh_j h_j = 0 on every row."""
+    rng = np.random.default_rng(seed)
+    h = rng.standard_normal((6, 20)) * rng.uniform(0.2, 5, size=(6, 1))
+    dn = rng.standard_normal((6, 20))
+    gamma = 1 + 0.1 * rng.standard_normal(20)
+    dh, _ = R.rmsnorm_bwd(dn, h, gamma, 0.0)
+    dots = np.abs(np.sum(dh * h, axis=1)) / (np.linalg.norm(dh, axis=1) * np.linalg.norm(h, axis=1))
+    return _ok(float(np.max(dots)), 1e-13, "rmsnorm backward orthogonal to h")
+
+
+def pin_bwd_row_coefficient(seed=18):
+    """The row coefficient of the RMSNorm backward equals r^2/d times the
+    row sum of dz * z over the gate and up pre-activations (z = r h W'^T with
+    gamma folded into W', so sum_j h_j G_j = sum_n dz_n z_n / r), the form in
+    which a SwiGLU-backward GEMM epilogue can emit it as a partial sum."""
+    p = _layer_inputs(seed, M=4, K1=6, d=5, ffn=7)
+    o = _oracle_bwd(p)
+    d = len(p["wo"])
+    alt = o["r"] ** 2 / d * np.sum(o["dg"] * o["g"] + o["du"] * o["u"], axis=1)
+    return _ok(_rel(o["coef"], alt), 1e-12, "row coefficient from dz . z")
+
+
 ALL_PINS = [
     pin_mlp_bruteforce, pin_mlp_exact_example, pin_rmsnorm_torch, pin_rms_closed_forms,
     pin_unit_rms, pin_rowscale_commutes, pin_swiglu, pin_rope_closed_forms,
     pin_rope_torch_complex, pin_rope_relative, pin_attn_bruteforce, pin_ce_bruteforce,
     pin_ce_torch, pin_ce_zero_weights, pin_lse_merge, pin_partial_sumsq, pin_fp8_block,
+    pin_swiglu_grad, pin_layer_bwd_finite_differences, pin_layer_bwd_torch,
+    pin_rmsnorm_bwd_scale_invariance, pin_bwd_row_coefficient,
 ]
 
 

@@ -111,11 +111,13 @@ def test_mlp_tiny_config():
     assert norm_err(bf16_host(got["out"]), ref["out"]) <= TOL_BF16
 
 
-def test_mlp_1b_sampled_rows():
-    """Full LLaMA-3-1B MLP shape in the launch configuration the benchmark
-    times; the oracle checks sampled rows (the block is row-independent)."""
-    w = inputs.make_workload("mlp_1b")
-    say("mlp_1b full size, sampled rows")
+@pytest.mark.parametrize("name", ["mlp_1b", "mlp_7b", "mlp_70b"])
+def test_mlp_full_size_sampled_rows(name):
+    """Full MLP shapes at the 1B, 7B and 70B hidden sizes in the launch
+    configuration the benchmark times; the oracle checks sampled rows (the
+    block is row-independent)."""
+    w = inputs.make_workload(name)
+    say(f"{name} full size {w.sizes}, sampled rows")
     got = run_fused(w)
     rows = sample_rows(w.sizes["M"])
     ref = oracle_rows(w, rows)

@@ -61,6 +61,36 @@ def _lm_head_label_shift(x, wlm, labels, r=None, chunk=256):
     return _ORIG_LM(x, wlm, (np.asarray(labels) + 1) % V, r=r, chunk=chunk)
 
 
+_ORIG_LAYER_BWD = R.mlp_layer_bwd
+
+
+def _swiglu_grad_no_curvature(dout, g, u):
+    g, u, dout = (np.asarray(v, dtype=np.float64) for v in (g, u, dout))
+    s = 1.0 / (1.0 + np.exp(-g))
+    return dout * u * s, dout * g * s
+
+
+def _rmsnorm_bwd_variant(sign=-1.0, power=3, use_gamma=True):
+    def f(dn, h, gamma, eps):
+        h = np.asarray(h, dtype=np.float64)
+        gm = np.asarray(gamma, dtype=np.float64) if use_gamma else np.ones(h.shape[1])
+        dng = np.asarray(dn, dtype=np.float64) * gm[None, :]
+        r = R.rms_scale(h, eps)
+        coef = r ** power / h.shape[1] * np.sum(dng * h, axis=1)
+        return r[:, None] * dng + sign * coef[:, None] * h, coef
+    return f
+
+
+def _layer_bwd_no_skip(x, res, wo, wg, wu, gamma, eps, wd, dy):
+    o = _ORIG_LAYER_BWD(x, res, wo, wg, wu, gamma, eps, wd, dy)
+    o["dh"] = o["dres"] = o["dh"] - np.asarray(dy)
+    o["dx"] = o["dh"] @ np.asarray(wo)
+    return o
+
+
+def _layer_bwd_up_gate_swapped(x, res, wo, wg, wu, gamma, eps, wd, dy):
+    return _ORIG_LAYER_BWD(x, res, wo, wu, wg, gamma, eps, wd, dy)
+
 
 MUTANTS = {
     "eps outside sqrt": ("rms_scale", lambda h, eps: 1.0 / np.sqrt(np.mean(np.asarray(h) ** 2, axis=1)) + eps),
@@ -77,6 +107,13 @@ MUTANTS = {
     "lse without max": ("logsumexp_rows", lambda z: np.log(np.sum(np.exp(np.asarray(z)), axis=1)) + 1e-3),
     "merge without rescale": ("lse_merge", _lse_merge_no_rescale),
     "label off by one": ("lm_head_ce", _lm_head_label_shift),
+    "swiglu grad without the s(1-s) term": ("swiglu_grad", _swiglu_grad_no_curvature),
+    "rmsnorm bwd correction dropped": ("rmsnorm_bwd", _rmsnorm_bwd_variant(sign=0.0)),
+    "rmsnorm bwd correction sign": ("rmsnorm_bwd", _rmsnorm_bwd_variant(sign=1.0)),
+    "rmsnorm bwd r^2 for r^3": ("rmsnorm_bwd", _rmsnorm_bwd_variant(power=2)),
+    "rmsnorm bwd gamma dropped": ("rmsnorm_bwd", _rmsnorm_bwd_variant(use_gamma=False)),
+    "skip-connection gradient dropped": ("mlp_layer_bwd", _layer_bwd_no_skip),
+    "gate and up swapped in backward": ("mlp_layer_bwd", _layer_bwd_up_gate_swapped),
     "abs instead of square": ("partial_sumsq", lambda h, w: np.stack([np.sum(np.abs(np.asarray(h)[:, t * w:(t + 1) * w]), axis=1) for t in range((np.asarray(h).shape[1] + w - 1) // w)])),
 }
 
