@@ -263,6 +263,113 @@ def _events_time(torch, stream, fn, steps, warmup, min_ms=40.0):
     return e0.elapsed_time(e1) / steps
 
 
+def _mlp_bwd_row(torch, ops, inputs, stream, steps, warmup, bf, name="mlp_1b_bwd", **sizes):
+    """Backward of the MLP sub-layer given dY: fused (SwiGLU-backward GEMM ->
+    row-coefficient reduce -> RMSNorm-backward GEMM -> dx GEMM) against the
+    unfused sequence (plain GEMMs with a SwiGLU-backward pass and an
+    RMSNorm-backward pass between them), and the forward that saves z plus
+    the backward against the unfused forward plus backward."""
+    dev = "cuda:0"
+    eps = 1e-5
+    print(f"[bench] {name}", file=sys.stderr, flush=True)
+    w = inputs.make_workload(name, **sizes)
+    M, d, K1, ffn = (w.sizes[k] for k in ("M", "d", "K1", "ffn"))
+    x, res, wo, wg, wu, wd, dy = (bf(w.arrays[k]) for k in
+                                  ("x", "res", "w1", "wg", "wu", "wd", "dy"))
+    gamma = torch.from_numpy(w.arrays["gamma"]).to(dev)
+    del w
+    bf16 = dict(dtype=torch.bfloat16, device=dev)
+    # weight preparation (untimed): gamma folded, transposed copies
+    wg_f, wu_f = torch.empty_like(wg), torch.empty_like(wu)
+    ops.fold_gamma(wg, gamma, wg_f)
+    ops.fold_gamma(wu, gamma, wu_f)
+    WdT = torch.empty(ffn, d, **bf16)
+    ops.transpose(wd, WdT)
+    W2T = torch.empty(d, 2 * ffn, **bf16)
+    ops.transpose(wg_f, W2T[:, :ffn])
+    ops.transpose(wu_f, W2T[:, ffn:])
+    WoT = torch.empty(K1, d, **bf16)
+    ops.transpose(wo, WoT)
+    wgu = torch.cat([wg, wu], 0).contiguous()
+    del wd, wg, wu
+    h = torch.empty(M, d, **bf16)
+    P = torch.empty(ops.rms_tiles(d), M, dtype=torch.float32, device=dev)
+    r = torch.empty(M, dtype=torch.float32, device=dev)
+    o = torch.empty(M, ffn, **bf16)
+    gu = torch.empty(M, 2 * ffn, **bf16)
+    dz = torch.empty(M, 2 * ffn, **bf16)
+    pdot = torch.empty(ops.rms_tiles(ffn), M, dtype=torch.float32, device=dev)
+    c = torch.empty(M, dtype=torch.float32, device=dev)
+    dh = torch.empty(M, d, **bf16)
+    dx = torch.empty(M, K1, **bf16)
+
+    def fwd_save():
+        ops.gemm_residual_partialrms(x, wo, res, h, P)
+        ops.rms_reduce(P, d, eps, r)
+        ops.gemm_rowscale_swiglu_save(h, wg_f, wu_f, r, o, gu)
+    bwd_k = [lambda: ops.gemm_swiglu_bwd(dy, WdT, gu, dz, pdot),
+             lambda: ops.rms_bwd_reduce(pdot, d, r, c),
+             lambda: ops.gemm_rmsnorm_bwd(dz, W2T, h, dy, r, c, dh),
+             lambda: ops.gemm_bf16(dh, WoT, dx)]
+
+    def bwd():
+        for f in bwd_k:
+            f()
+
+    def train():
+        fwd_save()
+        bwd()
+    fwd_save()
+    ms_b = _events_time(torch, stream, bwd, steps, warmup)
+    kb = _kernel_times(torch, stream, bwd_k, steps)
+    ms_t = _events_time(torch, stream, train, steps, warmup)
+    # unfused: forward stores g|u from one plain GEMM (the backward reads it)
+    y_u, h_u, n_u, G_u, dh_u = (torch.empty(M, d, **bf16) for _ in range(5))
+    gu_u, dz_u = torch.empty(M, 2 * ffn, **bf16), torch.empty(M, 2 * ffn, **bf16)
+    o_u, dout_u = torch.empty(M, ffn, **bf16), torch.empty(M, ffn, **bf16)
+    dx_u = torch.empty(M, K1, **bf16)
+
+    def fwd_u():
+        ops.gemm_bf16(x, wo, y_u)
+        ops.residual_add(y_u, res, h_u)
+        ops.rmsnorm(h_u, gamma, eps, n_u)
+        ops.gemm_bf16(n_u, wgu, gu_u)
+        ops.swiglu(gu_u, o_u)
+    bwd_uk = [lambda: ops.gemm_bf16(dy, WdT, dout_u),
+              lambda: ops.swiglu_bwd(dout_u, gu_u, dz_u),
+              lambda: ops.gemm_bf16(dz_u, W2T, G_u),
+              lambda: ops.rmsnorm_bwd(G_u, h_u, dy, eps, dh_u),
+              lambda: ops.gemm_bf16(dh_u, WoT, dx_u)]
+
+    def bwd_u():
+        for f in bwd_uk:
+            f()
+
+    def train_u():
+        fwd_u()
+        bwd_u()
+    fwd_u()
+    ms_bu = _events_time(torch, stream, bwd_u, steps, warmup)
+    kbu = _kernel_times(torch, stream, bwd_uk, steps)
+    ms_tu = _events_time(torch, stream, train_u, steps, warmup)
+    fl_b = 2.0 * M * ffn * d + 2.0 * M * d * 2 * ffn + 2.0 * M * K1 * d
+    fl_t = fl_b + 2.0 * M * d * K1 + 2.0 * M * 2 * ffn * d
+    return {"workload": f"M={M}, d={d}, K1={K1}, ffn={ffn}: backward of the MLP sub-layer "
+                        "given dY (dx and dres), and forward (saving g|u) + backward",
+            "bwd_ms": round(ms_b, 4), "bwd_tflops": round(fl_b / ms_b / 1e9, 1),
+            "bwd_pct_of_bf16_peak": round(100 * fl_b / ms_b / 1e9 / PEAK_BF16_TFLOPS, 2),
+            "bwd_kernels_ms": dict(zip(("gemm_swiglu_bwd", "rms_bwd_reduce", "gemm_rmsnorm_bwd",
+                                        "gemm_bf16_dx"), kb)),
+            "fwd_bwd_ms": round(ms_t, 4), "fwd_bwd_tflops": round(fl_t / ms_t / 1e9, 1),
+            "unfused": {"bwd_ms": round(ms_bu, 4), "bwd_tflops": round(fl_b / ms_bu / 1e9, 1),
+                        "bwd_speedup_fused_vs_unfused": round(ms_bu / ms_b, 3),
+                        "bwd_kernels_ms": dict(zip(("gemm_bf16_dout", "swiglu_bwd",
+                                                    "gemm_bf16_G", "rmsnorm_bwd",
+                                                    "gemm_bf16_dx"), kbu)),
+                        "fwd_bwd_ms": round(ms_tu, 4),
+                        "fwd_bwd_speedup_fused_vs_unfused": round(ms_tu / ms_t, 3)}}
+
+
 def _kernel_times(torch, stream, fns, steps):
     """Mean duration (ms) of each launch in `fns`, from events recorded on the
     launch stream between consecutive launches over `steps` passes."""
@@ -368,6 +475,9 @@ def time_other_rows(torch, ops, inputs, stream, steps, warmup):
     # the bf16 MLP block at the 7B and 70B hidden sizes
     for name in ("mlp_7b", "mlp_70b"):
         out[name] = _mlp_row(torch, ops, inputs, stream, name, steps, warmup, bf)
+
+    # backward of the 1B-shaped MLP sub-layer (and forward + backward)
+    out["mlp_1b_bwd"] = _mlp_bwd_row(torch, ops, inputs, stream, steps, warmup, bf)
 
     # fp8 8B-shaped MLP block (delayed scaling: the previous step's scale)
     print("[bench] mlp_8b_fp8", file=sys.stderr, flush=True)

@@ -176,6 +176,93 @@ int coda_gemm_rowscale_swiglu(int dtype, const void* X, const float* x_scale, co
   }
 }
 
+int coda_gemm_rowscale_swiglu_save(const void* X, const void* Wg, const void* Wu, const float* r,
+                                   void* out, void* gu, int M, int N, int K, void* stream) {
+  try {
+    if (!X || !Wg || !Wu || !r || !out || !gu) return CODA_ERR_NULL;
+    if (int st = check_gemm_shape(M, N, K, 64)) return st;
+    if (!small_enough(M, 2 * (int64_t)N)) return CODA_ERR_SHAPE;
+    if (!aligned(X, 16) || !aligned(Wg, 16) || !aligned(Wu, 16) || !aligned(out, 16) ||
+        !aligned(gu, 16) || !aligned(r, 4))
+      return CODA_ERR_ALIGN;
+    if (int st = check_device()) return st;
+    return launched(coda::launch_rowscale_swiglu_save_bf16(
+        static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(Wg),
+        static_cast<const uint16_t*>(Wu), r, static_cast<uint16_t*>(out),
+        static_cast<uint16_t*>(gu), M, N, K, as_stream(stream)));
+  } catch (...) {
+    return CODA_ERR_LAUNCH;
+  }
+}
+
+int coda_gemm_swiglu_bwd(const void* dY, const void* WdT, const void* gu, void* dz,
+                         float* partial_dot, int M, int N, int K, void* stream) {
+  try {
+    if (!dY || !WdT || !gu || !dz || !partial_dot) return CODA_ERR_NULL;
+    if (int st = check_gemm_shape(M, N, K, 64)) return st;
+    if (!small_enough(M, 2 * (int64_t)N)) return CODA_ERR_SHAPE;
+    if (!aligned(dY, 16) || !aligned(WdT, 16) || !aligned(gu, 16) || !aligned(dz, 16) ||
+        !aligned(partial_dot, 4))
+      return CODA_ERR_ALIGN;
+    if (int st = check_device()) return st;
+    return launched(coda::launch_swiglu_bwd_bf16(
+        static_cast<const uint16_t*>(dY), static_cast<const uint16_t*>(WdT),
+        static_cast<const uint16_t*>(gu), static_cast<uint16_t*>(dz), partial_dot, M, N, K,
+        as_stream(stream)));
+  } catch (...) {
+    return CODA_ERR_LAUNCH;
+  }
+}
+
+int coda_rms_bwd_reduce(const float* partial_dot, int T, int M, const float* r, int N, float* c,
+                        void* stream) {
+  try {
+    if (!partial_dot || !r || !c) return CODA_ERR_NULL;
+    if (T < 1 || M < 1 || N < 1 || !small_enough(T, M)) return CODA_ERR_SHAPE;
+    if (!aligned(partial_dot, 4) || !aligned(r, 4) || !aligned(c, 4)) return CODA_ERR_ALIGN;
+    if (int st = check_device()) return st;
+    return launched(coda::launch_rms_bwd_reduce(partial_dot, T, M, r, N, c, as_stream(stream)));
+  } catch (...) {
+    return CODA_ERR_LAUNCH;
+  }
+}
+
+int coda_gemm_rmsnorm_bwd(const void* dz, const void* W2T, const void* h, const void* dY,
+                          const float* r, const float* c, void* dh, int M, int N, int K,
+                          void* stream) {
+  try {
+    if (!dz || !W2T || !h || !dY || !r || !c || !dh) return CODA_ERR_NULL;
+    if (int st = check_gemm_shape(M, N, K, 64)) return st;
+    if (!aligned(dz, 16) || !aligned(W2T, 16) || !aligned(h, 16) || !aligned(dY, 16) ||
+        !aligned(dh, 16) || !aligned(r, 4) || !aligned(c, 4))
+      return CODA_ERR_ALIGN;
+    if (int st = check_device()) return st;
+    return launched(coda::launch_rmsnorm_bwd_bf16(
+        static_cast<const uint16_t*>(dz), static_cast<const uint16_t*>(W2T),
+        static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(dY), r, c,
+        static_cast<uint16_t*>(dh), M, N, K, as_stream(stream)));
+  } catch (...) {
+    return CODA_ERR_LAUNCH;
+  }
+}
+
+int coda_transpose_bf16(const void* src, int rows, int cols, void* dst, int ld_dst,
+                        void* stream) {
+  try {
+    if (!src || !dst) return CODA_ERR_NULL;
+    if (rows < 1 || cols < 1 || ld_dst < rows || (int64_t)rows * cols >= (int64_t(1) << 31) ||
+        (int64_t)cols * ld_dst >= (int64_t(1) << 31) || cols > 65535 * 64 || rows > 65535 * 64)
+      return CODA_ERR_SHAPE;
+    if (!aligned(src, 2) || !aligned(dst, 2)) return CODA_ERR_ALIGN;
+    if (int st = check_device()) return st;
+    return launched(coda::launch_transpose_bf16(static_cast<const uint16_t*>(src), rows, cols,
+                                                static_cast<uint16_t*>(dst), ld_dst,
+                                                as_stream(stream)));
+  } catch (...) {
+    return CODA_ERR_LAUNCH;
+  }
+}
+
 int coda_gemm_rope(const void* h, const void* Wqkv, const float* r, const float* rope_cos,
                    const float* rope_sin, const int32_t* pos, int max_pos, void* qkv, int M, int K,
                    int n_q_heads, int n_kv_heads, int head_dim, void* stream) {
@@ -305,6 +392,38 @@ int coda_swiglu(const void* gu, void* out, int M, int N, void* stream) {
     if (int st = check_device()) return st;
     return launched(coda::launch_swiglu(static_cast<const uint16_t*>(gu),
                                         static_cast<uint16_t*>(out), M, N, as_stream(stream)));
+  } catch (...) {
+    return CODA_ERR_LAUNCH;
+  }
+}
+
+int coda_swiglu_bwd(const void* dout, const void* gu, void* dz, int M, int N, void* stream) {
+  try {
+    if (!dout || !gu || !dz) return CODA_ERR_NULL;
+    if (M < 1 || N < 8 || N % 8 != 0 || !small_enough(M, 2 * (int64_t)N)) return CODA_ERR_SHAPE;
+    if (!aligned(dout, 16) || !aligned(gu, 16) || !aligned(dz, 16)) return CODA_ERR_ALIGN;
+    if (int st = check_device()) return st;
+    return launched(coda::launch_swiglu_bwd(static_cast<const uint16_t*>(dout),
+                                            static_cast<const uint16_t*>(gu),
+                                            static_cast<uint16_t*>(dz), M, N, as_stream(stream)));
+  } catch (...) {
+    return CODA_ERR_LAUNCH;
+  }
+}
+
+int coda_rmsnorm_bwd(const void* G, const void* h, const void* dY, float eps, void* dh, int M,
+                     int N, void* stream) {
+  try {
+    if (!G || !h || !dY || !dh) return CODA_ERR_NULL;
+    if (M < 1 || N < 8 || N % 8 != 0 || N > 16384 || !(eps >= 0.f) || !small_enough(M, N))
+      return CODA_ERR_SHAPE;
+    if (!aligned(G, 16) || !aligned(h, 16) || !aligned(dY, 16) || !aligned(dh, 16))
+      return CODA_ERR_ALIGN;
+    if (int st = check_device()) return st;
+    return launched(coda::launch_rmsnorm_bwd(
+        static_cast<const uint16_t*>(G), static_cast<const uint16_t*>(h),
+        static_cast<const uint16_t*>(dY), eps, static_cast<uint16_t*>(dh), M, N,
+        as_stream(stream)));
   } catch (...) {
     return CODA_ERR_LAUNCH;
   }

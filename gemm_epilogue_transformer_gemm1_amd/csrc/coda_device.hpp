@@ -48,6 +48,21 @@ __device__ __forceinline__ void store16(__amdgpu_buffer_rsrc_t rsrc, u32x4_t v, 
   __builtin_amdgcn_raw_buffer_store_b128(v, rsrc, voffset, 0, 0);
 }
 
+// A lane of 16-lane group g holds, for one token row, the runs of 4 features
+// 16 j0 + 4 g + 0..3 (pk[0]) and 16 (j0 + 1) + 4 g + 0..3 (pk[1]).  Groups g
+// and g ^ 1 swap one run, so each lane stores 8 contiguous features with one
+// 16-byte store: features 16 j0 + 8 (g / 2) + 0..7 for even g, the same in
+// subtile j0 + 1 for odd g.  `voffset` is the byte offset of that run (or
+// kOobOffset).  All 64 lanes must take part (the swap is a lane shuffle).
+__device__ __forceinline__ void store16_exchanged(__amdgpu_buffer_rsrc_t rsrc, const u32x2_t (&pk)[2],
+                                                  bool godd, uint32_t voffset) {
+  const u32x2_t sd = godd ? pk[0] : pk[1];
+  const u32x2_t rx = {(unsigned)__shfl_xor((int)sd.x, 16, 64),
+                      (unsigned)__shfl_xor((int)sd.y, 16, 64)};
+  store16(rsrc, godd ? u32x4_t{rx.x, rx.y, pk[1].x, pk[1].y} : u32x4_t{pk[0].x, pk[0].y, rx.x, rx.y},
+          voffset);
+}
+
 // 8 bytes per lane to rsrc + voffset (dropped if voffset + 8 > the range).
 __device__ __forceinline__ void store8(__amdgpu_buffer_rsrc_t rsrc, u32x2_t v, uint32_t voffset) {
   __builtin_amdgcn_raw_buffer_store_b64(v, rsrc, voffset, 0, 0);

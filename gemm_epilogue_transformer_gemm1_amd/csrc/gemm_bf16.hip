@@ -141,6 +141,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_residual_partialrms_bf16(Gemm1A
 // the block's LDS weight tile holds 128 gate rows and the same 128 up rows.
 // ---------------------------------------------------------------------------
 constexpr int kSwigluStores = 16;  // 16-byte stores per lane per tile
+// ... when the pre-activations are saved too (out, g and u)
+constexpr int kSwigluSaveStores = 48;
 
 struct Gemm2Args {
   const uint16_t* X;   // [M, K]
@@ -148,6 +150,7 @@ struct Gemm2Args {
   const uint16_t* Wu;  // [N, K]
   const float* r;      // [M]
   uint16_t* out;       // [M, N]
+  uint16_t* gu;        // [M, 2N] g | u for the backward pass, or unused
   int M, N, K;
 };
 
@@ -155,6 +158,11 @@ __device__ __forceinline__ MainloopSrc gemm2_src(const Gemm2Args& g, TileCoord c
   return MainloopSrc{g.X, g.Wg, g.Wu, g.M, g.N, g.K, c.tm * kBM, c.tn * (kBN / 2)};
 }
 
+// kSave: also store the pre-activations g = r a and u = r b (bf16) into
+// gu[m, n] and gu[m, N + n] (section "Five building blocks and a LEGO
+// language": tile stores that keep intermediate activations for the backward
+// pass).
+template <bool kSave>
 __device__ __forceinline__ void gemm2_tile(const Gemm2Args& g, char* smem, int m0, int n0,
                                            const TileChain& ch) {
   const int tid = tile_tid();
@@ -167,8 +175,8 @@ __device__ __forceinline__ void gemm2_tile(const Gemm2Args& g, char* smem, int m
     for (int i = 0; i < 8; ++i) rr[i] = g.r[min(m0 + wm * 128 + i * 16 + (lane & 15), M - 1)];
   };
   Acc acc;
-  mainloop_bf16<true, kSwigluStores>(acc, smem, MainloopSrc{g.X, g.Wg, g.Wu, M, N, g.K, m0, n0},
-                                     ch, pre, [] {});
+  mainloop_bf16<true, kSave ? kSwigluSaveStores : kSwigluStores>(
+      acc, smem, MainloopSrc{g.X, g.Wg, g.Wu, M, N, g.K, m0, n0}, ch, pre, [] {});
 
   // Lane L = 16 g + r holds the run of 4 features 16 j + 4 g of token r
   // for each subtile j.  For a pair of subtiles (j0, j0 + 1), lanes g and
@@ -180,6 +188,9 @@ __device__ __forceinline__ void gemm2_tile(const Gemm2Args& g, char* smem, int m
   // at the tile's first row, so offsets stay below 256 * N * 2 bytes.
   const __amdgpu_buffer_rsrc_t orsrc =
       make_rsrc(g.out + (size_t)m0 * N, (uint32_t)min(kBM, M - m0) * (uint32_t)N * 2u);
+  __amdgpu_buffer_rsrc_t zrsrc;
+  if constexpr (kSave)
+    zrsrc = make_rsrc(g.gu + (size_t)m0 * 2 * N, (uint32_t)min(kBM, M - m0) * (uint32_t)N * 4u);
   const int nw0 = n0 + wn * 64;
   const int gq = lane >> 4;
   const bool godd = (gq & 1) != 0;
@@ -193,7 +204,7 @@ __device__ __forceinline__ void gemm2_tile(const Gemm2Args& g, char* smem, int m
     const float s2 = __builtin_amdgcn_rcpf(rr[i] * rr[i]), c1 = rr[i] * kNegLog2e;
 #pragma unroll
     for (int j0 = 0; j0 < 4; j0 += 2) {
-      u32x2_t pk[2];
+      u32x2_t pk[2], pg[2], pu[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int j = j0 + u;
@@ -205,6 +216,13 @@ __device__ __forceinline__ void gemm2_tile(const Gemm2Args& g, char* smem, int m
           o[v] = (a * b) * __builtin_amdgcn_rcpf(__builtin_fmaf(e, s2, s2));
         }
         pk[u] = pack_bf16x4(o[0], o[1], o[2], o[3]);
+        if constexpr (kSave) {
+          const f32x4_t& a = acc.v[j][i];
+          const f32x4_t& b = acc.v[j + 4][i];
+          const float q = rr[i];
+          pg[u] = pack_bf16x4(a[0] * q, a[1] * q, a[2] * q, a[3] * q);
+          pu[u] = pack_bf16x4(b[0] * q, b[1] * q, b[2] * q, b[3] * q);
+        }
       }
       const u32x2_t sd = godd ? pk[0] : pk[1];
       const u32x2_t rv = {(unsigned)__shfl_xor((int)sd.x, 16, 64),
@@ -215,10 +233,18 @@ __device__ __forceinline__ void gemm2_tile(const Gemm2Args& g, char* smem, int m
                                          : kOobOffset;
       store16(orsrc, godd ? u32x4_t{rv.x, rv.y, pk[1].x, pk[1].y}
                           : u32x4_t{pk[0].x, pk[0].y, rv.x, rv.y}, off);
+      if constexpr (kSave) {
+        const bool ok = mv && n < N;
+        const uint32_t og = ok ? ((uint32_t)ml * (uint32_t)(2 * N) + (uint32_t)n) * 2u : kOobOffset;
+        const uint32_t ou = ok ? og + (uint32_t)N * 2u : kOobOffset;
+        store16_exchanged(zrsrc, pg, godd, og);
+        store16_exchanged(zrsrc, pu, godd, ou);
+      }
     }
   }
 }
 
+template <bool kSave>
 __global__ __launch_bounds__(kThreads, 1) void k_rowscale_swiglu_bf16(Gemm2Args g, int gm,
                                                                       int gn) {
   __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
@@ -230,7 +256,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_rowscale_swiglu_bf16(Gemm2Args 
     ch.prefetched = prefetched;
     const bool has_next = t + (int)gridDim.x < nt;
     ch.next = gemm2_src(g, has_next ? map_tile(t + gridDim.x, gm, gn, 8) : tc);
-    gemm2_tile(g, smem, tc.tm * kBM, tc.tn * (kBN / 2), ch);
+    gemm2_tile<kSave>(g, smem, tc.tm * kBM, tc.tn * (kBN / 2), ch);
     prefetched = has_next;
   }
   wait_vm0();  // the last tile's unused prefetch into LDS lands before the block ends
@@ -447,6 +473,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_block_lse_bf16(
 // ---------------------------------------------------------------------------
 // Plain GEMM (unfused baseline): the same mainloop, epilogue = convert + store.
 // ---------------------------------------------------------------------------
+constexpr int kPlainStores = 32;  // 16-byte stores per lane per tile
+
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_plain_bf16(const uint16_t* __restrict__ A,
                                                                  const uint16_t* __restrict__ W,
                                                                  uint16_t* __restrict__ C, int M,
@@ -454,7 +482,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_plain_bf16(const uint16_t*
   __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int g4 = (lane >> 4) * 4;
+  const int gq = lane >> 4;
+  const bool godd = (gq & 1) != 0;
   const int nt = gm * gn;
   bool prefetched = false;
   for (int t = blockIdx.x; t < nt; t += gridDim.x) {
@@ -466,20 +495,29 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_plain_bf16(const uint16_t*
     const TileCoord nc = has_next ? map_tile(t + gridDim.x, gm, gn, 8) : tc;
     ch.next = MainloopSrc{A, W, nullptr, M, N, K, nc.tm * kBM, nc.tn * kBN};
     Acc acc;
-    mainloop_bf16<false>(acc, smem, MainloopSrc{A, W, nullptr, M, N, K, m0, n0}, ch, [] {}, [] {});
+    mainloop_bf16<false, kPlainStores>(acc, smem, MainloopSrc{A, W, nullptr, M, N, K, m0, n0},
+                                       ch, [] {}, [] {});
 
+    // 16-byte stores of exchanged runs, as in the fused epilogues
     const int nw0 = n0 + wn * 128;
+    const __amdgpu_buffer_rsrc_t crsrc =
+        make_rsrc(C + (size_t)m0 * N, (uint32_t)min(kBM, M - m0) * (uint32_t)N * 2u);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int m = m0 + wm * 128 + i * 16 + (lane & 15);
-      if (m >= M) continue;
-      const size_t row = (size_t)m * (size_t)N;
+      const int ml = wm * 128 + i * 16 + (lane & 15);
+      const bool mv = m0 + ml < M;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int n = nw0 + j * 16 + g4;
-        if (n < N)
-          *(u32x2_t*)(C + row + n) =
-              pack_bf16x4(acc.v[j][i][0], acc.v[j][i][1], acc.v[j][i][2], acc.v[j][i][3]);
+      for (int j0 = 0; j0 < 8; j0 += 2) {
+        u32x2_t pk[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const f32x4_t& a = acc.v[j0 + u][i];
+          pk[u] = pack_bf16x4(a[0], a[1], a[2], a[3]);
+        }
+        const int n = nw0 + 16 * (j0 + (godd ? 1 : 0)) + 8 * (gq >> 1);
+        store16_exchanged(crsrc, pk, godd,
+                          (mv && n < N) ? ((uint32_t)ml * (uint32_t)N + (uint32_t)n) * 2u
+                                        : kOobOffset);
       }
     }
     prefetched = has_next;
@@ -505,8 +543,20 @@ hipError_t launch_rowscale_swiglu_bf16(const uint16_t* X, const uint16_t* Wg, co
                                        const float* r, uint16_t* out, int M, int N, int K,
                                        hipStream_t stream) {
   const int gm = cdiv(M, kBM), gn = cdiv(N, kBN / 2);
-  hipLaunchKernelGGL(k_rowscale_swiglu_bf16, dim3(min(gm * gn, cu_count())), dim3(kThreads), 0,
-                     stream, Gemm2Args{X, Wg, Wu, r, out, M, N, K}, gm, gn);
+  hipLaunchKernelGGL(k_rowscale_swiglu_bf16<false>, dim3(min(gm * gn, cu_count())),
+                     dim3(kThreads), 0, stream, Gemm2Args{X, Wg, Wu, r, out, nullptr, M, N, K},
+                     gm, gn);
+  return hipGetLastError();
+}
+
+hipError_t launch_rowscale_swiglu_save_bf16(const uint16_t* X, const uint16_t* Wg,
+                                            const uint16_t* Wu, const float* r, uint16_t* out,
+                                            uint16_t* gu, int M, int N, int K,
+                                            hipStream_t stream) {
+  const int gm = cdiv(M, kBM), gn = cdiv(N, kBN / 2);
+  hipLaunchKernelGGL(k_rowscale_swiglu_bf16<true>, dim3(min(gm * gn, cu_count())),
+                     dim3(kThreads), 0, stream, Gemm2Args{X, Wg, Wu, r, out, gu, M, N, K}, gm,
+                     gn);
   return hipGetLastError();
 }
 

@@ -1,0 +1,297 @@
+// bf16 backward GEMMs of the MLP sub-layer with epilogue programs, on the
+// mainloop of gemm_core.hpp.
+//
+// Citations name sections of the news page "CODA: New Research Optimizes
+// Transformer Training with GEMM-Epilogue Programming" (KuCoin news flash).
+// Section "CODA: the secret in the epilogue" states that a block-local forward
+// tail gives a backward pass of the same structure; section "Results" reports
+// backward kernels for SwiGLU and for GEMM-Residual-PartialRMS-GEMM.  The page
+// prints no formulas; the ones below are the chain rule of the forward
+//   h = res + x Wo^T,  z = [g | u] = r h W'^T (W' = [Wg; Wu] diag(gamma)),
+//   out = silu(g) u,   next = h + out Wd^T,
+// given dY = dL/dnext.  With dz = [dg | du] and G = dz W':
+//   dh = r G - c h + dY,  c = (r^3 / d) sum_j h_j G_j = (r^2 / d) sum_n dz_n z_n
+// (sum_j h_j G_j = sum_n dz_n (h W'^T)_n = sum_n dz_n z_n / r).  The second
+// form of c needs only values the SwiGLU-backward epilogue already holds, so
+// that epilogue emits it as per-(row, tile) partial sums -- the same partial
+// reduction the forward GEMM1 epilogue does for the RMS -- and the GEMM that
+// forms G applies the whole RMSNorm backward and the skip connection at its
+// end.
+//
+// Accumulator layout: lane L, register v of the 16x16 tile (j, i) holds
+// output feature nbase + 16 j + 4 (L / 16) + v of token mbase + 16 i + L % 16.
+
+#include "gemm_core.hpp"
+#include "launch.hpp"
+
+namespace coda {
+
+// The thread index as an opaque value (lane/wave arithmetic is recomputed in
+// each tile body instead of being kept live across phases).
+__device__ __forceinline__ int bwd_tile_tid() {
+  int t = (int)threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
+// Vector memory operations each epilogue below issues per lane after the next
+// tile's loads (operand loads of token subtiles 3..7 plus the stores) is well
+// above 47, so the next tile's first wait is vmcnt(63).
+constexpr int kBwdEpiVmem = 47;
+
+// Two bf16 operand tiles of the epilogue, [M, ld] each at column offsets
+// col_a and col_b, loaded per token subtile i as 8 runs of 4 features per
+// lane (8 bytes).  Subtiles 0..2 are loaded during the last two stages of the
+// mainloop, subtile i + 3 while subtile i is processed.  Feature runs past N
+// read at an out-of-range offset (zeros); rows past M lie beyond the buffer,
+// which starts at the tile's first row.
+struct EpiPair {
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t ld, col_a, col_b;
+  int nw0, N, wm, lane;
+  u32x2_t a[8][8], b[8][8];
+
+  __device__ __forceinline__ uint32_t off(int i, int j, uint32_t col) const {
+    const int n = nw0 + 16 * j;
+    if (n >= N) return kOobOffset;  // wave-uniform
+    const uint32_t ml = (uint32_t)(wm * 128 + i * 16 + (lane & 15));
+    return (ml * ld + col + (uint32_t)(n + 4 * (lane >> 4))) * 2u;
+  }
+  __device__ __forceinline__ void load(int i) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      a[i][j] = __builtin_amdgcn_raw_buffer_load_b64(rs, off(i, j, col_a), 0, 0);
+      b[i][j] = __builtin_amdgcn_raw_buffer_load_b64(rs, off(i, j, col_b), 0, 0);
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// SwiGLU backward: dout = dY Wd (weight passed as WdT = Wd^T, [N = ffn, K = d]);
+// epilogue with the saved pre-activations g = gu[:, :N], u = gu[:, N:]:
+//   s = sigmoid(g), du = dout silu(g), dg = dout u (s + silu(g) (1 - s)),
+// stores dz = [dg | du] and the partial sums  sum (dg g + du u)  over each
+// wave's 128 features (T = ceil(N / 128) tiles, [T, M]).
+// ---------------------------------------------------------------------------
+struct SwigluBwdArgs {
+  const uint16_t* dY;   // [M, K]
+  const uint16_t* WdT;  // [N, K]
+  const uint16_t* gu;   // [M, 2N]
+  uint16_t* dz;         // [M, 2N]
+  float* pdot;          // [T, M]
+  int M, N, K;
+};
+
+__device__ __forceinline__ void swiglu_bwd_tile(const SwigluBwdArgs& g, char* smem, int m0, int n0,
+                                                const TileChain& ch) {
+  const int tid = bwd_tile_tid();
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int gq = lane >> 4;
+  const int M = g.M, N = g.N;
+  const uint32_t ld = 2u * (uint32_t)N;
+  const int nw0 = n0 + wn * 128;
+  const uint32_t rows_here = (uint32_t)min(kBM, M - m0);
+  EpiPair z;
+  z.rs = make_rsrc(g.gu + (size_t)m0 * ld, rows_here * ld * 2u);
+  z.ld = ld;
+  z.col_a = 0;
+  z.col_b = (uint32_t)N;
+  z.nw0 = nw0;
+  z.N = N;
+  z.wm = wm;
+  z.lane = lane;
+  const __amdgpu_buffer_rsrc_t drsrc = make_rsrc(g.dz + (size_t)m0 * ld, rows_here * ld * 2u);
+  Acc acc;
+  mainloop_bf16<false, kBwdEpiVmem>(acc, smem, MainloopSrc{g.dY, g.WdT, nullptr, M, N, g.K, m0, n0},
+                                    ch, [&] { z.load(0); }, [&] { z.load(1); z.load(2); });
+
+  const bool godd = (gq & 1) != 0;
+  const float kNegLog2e = -1.4426950408889634f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (i + 3 < 8) z.load(i + 3);
+    const int ml = wm * 128 + i * 16 + (lane & 15);
+    const bool mv = m0 + ml < M;
+    float ps = 0.f;
+#pragma unroll
+    for (int j0 = 0; j0 < 8; j0 += 2) {
+      u32x2_t pg[2], pu[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int j = j0 + u;
+        float gv[4], uv[4], dg[4], du[4];
+        unpack_bf16x4(z.a[i][j], gv);
+        unpack_bf16x4(z.b[i][j], uv);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float d = acc.v[j][i][v];
+          // s = 1 / (1 + 2^(-log2e g)): 0 for very negative g (2^x = inf)
+          const float s = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(gv[v] * kNegLog2e));
+          const float sl = gv[v] * s;
+          du[v] = d * sl;
+          dg[v] = (d * uv[v]) * __builtin_fmaf(sl, 1.0f - s, s);
+          ps += dg[v] * gv[v] + du[v] * uv[v];
+        }
+        pg[u] = pack_bf16x4(dg[0], dg[1], dg[2], dg[3]);
+        pu[u] = pack_bf16x4(du[0], du[1], du[2], du[3]);
+      }
+      const int n = nw0 + 16 * (j0 + (godd ? 1 : 0)) + 8 * (gq >> 1);
+      const bool ok = mv && n < N;
+      const uint32_t og = ok ? ((uint32_t)ml * ld + (uint32_t)n) * 2u : kOobOffset;
+      const uint32_t ou = ok ? og + (uint32_t)N * 2u : kOobOffset;
+      store16_exchanged(drsrc, pg, godd, og);
+      store16_exchanged(drsrc, pu, godd, ou);
+    }
+    ps = sum_over_lane_groups(ps);
+    if (mv && lane < 16 && nw0 < N) g.pdot[(size_t)(nw0 / kRmsTileWidth) * M + m0 + ml] = ps;
+  }
+}
+
+__global__ __launch_bounds__(kThreads, 1) void k_swiglu_bwd_bf16(SwigluBwdArgs g, int gm, int gn) {
+  __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
+  const int nt = gm * gn;
+  bool prefetched = false;
+  for (int t = blockIdx.x; t < nt; t += gridDim.x) {
+    const TileCoord tc = map_tile(t, gm, gn, 8);
+    TileChain ch;
+    ch.prefetched = prefetched;
+    const bool has_next = t + (int)gridDim.x < nt;
+    const TileCoord nc = has_next ? map_tile(t + gridDim.x, gm, gn, 8) : tc;
+    ch.next = MainloopSrc{g.dY, g.WdT, nullptr, g.M, g.N, g.K, nc.tm * kBM, nc.tn * kBN};
+    swiglu_bwd_tile(g, smem, tc.tm * kBM, tc.tn * kBN, ch);
+    prefetched = has_next;
+  }
+  wait_vm0();  // the last tile's unused prefetch into LDS lands before the block ends
+}
+
+// ---------------------------------------------------------------------------
+// RMSNorm backward through GEMM2: G = dz W' (weight passed as W2T = W'^T,
+// [N = d, K = 2 ffn], gamma folded in), epilogue
+//   dh = r G - c h + dY
+// with the forward row scale r, the row coefficient c, the forward h and the
+// gradient dY arriving through the skip connection.
+// ---------------------------------------------------------------------------
+struct RmsBwdArgs {
+  const uint16_t* dz;   // [M, K]
+  const uint16_t* W2T;  // [N, K]
+  const uint16_t* h;    // [M, N]
+  const uint16_t* dY;   // [M, N]
+  const float* r;       // [M]
+  const float* c;       // [M]
+  uint16_t* dh;         // [M, N]
+  int M, N, K;
+};
+
+__device__ __forceinline__ void rmsnorm_bwd_tile(const RmsBwdArgs& g, char* smem, int m0, int n0,
+                                                 const TileChain& ch) {
+  const int tid = bwd_tile_tid();
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int gq = lane >> 4;
+  const int M = g.M, N = g.N;
+  const int nw0 = n0 + wn * 128;
+  const uint32_t rows_here = (uint32_t)min(kBM, M - m0);
+  // h and dY are separate [M, N] matrices: one pair, two buffers
+  EpiPair hy;
+  hy.rs = make_rsrc(g.h + (size_t)m0 * N, rows_here * (uint32_t)N * 2u);
+  hy.ld = (uint32_t)N;
+  hy.col_a = 0;
+  hy.col_b = 0;
+  hy.nw0 = nw0;
+  hy.N = N;
+  hy.wm = wm;
+  hy.lane = lane;
+  const __amdgpu_buffer_rsrc_t yrsrc = make_rsrc(g.dY + (size_t)m0 * N, rows_here * (uint32_t)N * 2u);
+  auto load = [&](int i) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t o = hy.off(i, j, 0);
+      hy.a[i][j] = __builtin_amdgcn_raw_buffer_load_b64(hy.rs, o, 0, 0);
+      hy.b[i][j] = __builtin_amdgcn_raw_buffer_load_b64(yrsrc, o, 0, 0);
+    }
+  };
+  float rr[8], cc[8];
+  auto pre = [&] {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int mc = min(m0 + wm * 128 + i * 16 + (lane & 15), M - 1);
+      rr[i] = g.r[mc];
+      cc[i] = g.c[mc];
+    }
+    load(0);
+  };
+  const __amdgpu_buffer_rsrc_t orsrc = make_rsrc(g.dh + (size_t)m0 * N, rows_here * (uint32_t)N * 2u);
+  Acc acc;
+  mainloop_bf16<false, kBwdEpiVmem>(acc, smem, MainloopSrc{g.dz, g.W2T, nullptr, M, N, g.K, m0, n0},
+                                    ch, pre, [&] { load(1); load(2); });
+
+  const bool godd = (gq & 1) != 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (i + 3 < 8) load(i + 3);
+    const int ml = wm * 128 + i * 16 + (lane & 15);
+    const bool mv = m0 + ml < M;
+#pragma unroll
+    for (int j0 = 0; j0 < 8; j0 += 2) {
+      u32x2_t pk[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int j = j0 + u;
+        float hv[4], yv[4], o[4];
+        unpack_bf16x4(hy.a[i][j], hv);
+        unpack_bf16x4(hy.b[i][j], yv);
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          o[v] = __builtin_fmaf(rr[i], acc.v[j][i][v], __builtin_fmaf(-cc[i], hv[v], yv[v]));
+        pk[u] = pack_bf16x4(o[0], o[1], o[2], o[3]);
+      }
+      const int n = nw0 + 16 * (j0 + (godd ? 1 : 0)) + 8 * (gq >> 1);
+      store16_exchanged(orsrc, pk, godd,
+                        (mv && n < N) ? ((uint32_t)ml * (uint32_t)N + (uint32_t)n) * 2u
+                                      : kOobOffset);
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads, 1) void k_rmsnorm_bwd_bf16(RmsBwdArgs g, int gm, int gn) {
+  __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
+  const int nt = gm * gn;
+  bool prefetched = false;
+  for (int t = blockIdx.x; t < nt; t += gridDim.x) {
+    const TileCoord tc = map_tile(t, gm, gn, 8);
+    TileChain ch;
+    ch.prefetched = prefetched;
+    const bool has_next = t + (int)gridDim.x < nt;
+    const TileCoord nc = has_next ? map_tile(t + gridDim.x, gm, gn, 8) : tc;
+    ch.next = MainloopSrc{g.dz, g.W2T, nullptr, g.M, g.N, g.K, nc.tm * kBM, nc.tn * kBN};
+    rmsnorm_bwd_tile(g, smem, tc.tm * kBM, tc.tn * kBN, ch);
+    prefetched = has_next;
+  }
+  wait_vm0();  // the last tile's unused prefetch into LDS lands before the block ends
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+static inline int cdiv_b(int a, int b) { return (a + b - 1) / b; }
+
+hipError_t launch_swiglu_bwd_bf16(const uint16_t* dY, const uint16_t* WdT, const uint16_t* gu,
+                                  uint16_t* dz, float* pdot, int M, int N, int K,
+                                  hipStream_t stream) {
+  const int gm = cdiv_b(M, kBM), gn = cdiv_b(N, kBN);
+  hipLaunchKernelGGL(k_swiglu_bwd_bf16, dim3(min(gm * gn, cu_count())), dim3(kThreads), 0, stream,
+                     SwigluBwdArgs{dY, WdT, gu, dz, pdot, M, N, K}, gm, gn);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_bwd_bf16(const uint16_t* dz, const uint16_t* W2T, const uint16_t* h,
+                                   const uint16_t* dY, const float* r, const float* c,
+                                   uint16_t* dh, int M, int N, int K, hipStream_t stream) {
+  const int gm = cdiv_b(M, kBM), gn = cdiv_b(N, kBN);
+  hipLaunchKernelGGL(k_rmsnorm_bwd_bf16, dim3(min(gm * gn, cu_count())), dim3(kThreads), 0, stream,
+                     RmsBwdArgs{dz, W2T, h, dY, r, c, dh, M, N, K}, gm, gn);
+  return hipGetLastError();
+}
+
+}  // namespace coda

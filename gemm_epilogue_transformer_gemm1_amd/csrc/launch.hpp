@@ -21,6 +21,21 @@ hipError_t launch_residual_partialrms_bf16(const uint16_t* A, const uint16_t* W,
 hipError_t launch_rowscale_swiglu_bf16(const uint16_t* X, const uint16_t* Wg, const uint16_t* Wu,
                                        const float* r, uint16_t* out, int M, int N, int K,
                                        hipStream_t stream);
+hipError_t launch_rowscale_swiglu_save_bf16(const uint16_t* X, const uint16_t* Wg,
+                                            const uint16_t* Wu, const float* r, uint16_t* out,
+                                            uint16_t* gu, int M, int N, int K, hipStream_t stream);
+hipError_t launch_swiglu_bwd_bf16(const uint16_t* dY, const uint16_t* WdT, const uint16_t* gu,
+                                  uint16_t* dz, float* pdot, int M, int N, int K,
+                                  hipStream_t stream);
+hipError_t launch_rmsnorm_bwd_bf16(const uint16_t* dz, const uint16_t* W2T, const uint16_t* h,
+                                   const uint16_t* dY, const float* r, const float* c,
+                                   uint16_t* dh, int M, int N, int K, hipStream_t stream);
+hipError_t launch_rms_bwd_reduce(const float* pdot, int T, int M, const float* r, int N, float* c,
+                                 hipStream_t stream);
+hipError_t launch_swiglu_bwd(const uint16_t* dout, const uint16_t* gu, uint16_t* dz, int M, int N,
+                             hipStream_t stream);
+hipError_t launch_rmsnorm_bwd(const uint16_t* G, const uint16_t* h, const uint16_t* dY, float eps,
+                              uint16_t* dh, int M, int N, hipStream_t stream);
 hipError_t launch_rope_bf16(const uint16_t* X, const uint16_t* W, const float* r,
                             const float* rcos, const float* rsin, const int* pos, int max_pos,
                             uint16_t* out, int M, int K, int n_q, int n_kv, hipStream_t stream);
@@ -45,6 +60,8 @@ hipError_t launch_rowscale_swiglu_fp8(const uint8_t* X, const float* x_scale, co
 
 hipError_t launch_rms_reduce(const float* psum, const float* pamax, int T, int M, int N, float eps,
                              float* r, float* h_amax, float* h8_scale_out, hipStream_t stream);
+hipError_t launch_transpose_bf16(const uint16_t* src, int rows, int cols, uint16_t* dst,
+                                 int ld_dst, hipStream_t stream);
 hipError_t launch_fold_gamma(const uint16_t* W, const float* gamma, uint16_t* W_out, int N, int K,
                              hipStream_t stream);
 hipError_t launch_residual_add(const uint16_t* y, const uint16_t* res, uint16_t* h, int64_t count,

@@ -59,6 +59,43 @@ __global__ __launch_bounds__(256) void k_rms_reduce(const float* __restrict__ ps
   }
 }
 
+// Backward row coefficient: the SwiGLU-backward GEMM's epilogue leaves partial
+// sums of dz * z per (row, 128-feature tile), combined here into
+//   c[m] = r[m]^2 / N * sum_t pdot[t, m]
+// (N = the normalised width d), the coefficient of h in the RMSNorm backward
+// dh = r G - c h + dY.  Same 4-lanes-per-row split as k_rms_reduce.
+__global__ __launch_bounds__(256) void k_rms_bwd_reduce(const float* __restrict__ pdot, int T,
+                                                        int M, const float* __restrict__ r,
+                                                        float inv_n, float* __restrict__ c) {
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4;
+  const int m = blockIdx.x * kReduceRowsPerBlock + (threadIdx.x >> 6) * 16 + (lane & 15);
+  const bool row_ok = m < M;
+  float s = 0.f;
+  if (row_ok) {
+    int t = g;
+    for (; t + 12 < T; t += 16) {
+      const float a0 = pdot[(size_t)t * M + m], a1 = pdot[(size_t)(t + 4) * M + m];
+      const float a2 = pdot[(size_t)(t + 8) * M + m], a3 = pdot[(size_t)(t + 12) * M + m];
+      s += (a0 + a1) + (a2 + a3);
+    }
+    for (; t < T; t += 4) s += pdot[(size_t)t * M + m];
+  }
+  s += __shfl_xor(s, 16, 64);
+  s += __shfl_xor(s, 32, 64);
+  if (row_ok && g == 0) {
+    const float rm = r[m];
+    c[m] = (rm * rm) * (s * inv_n);
+  }
+}
+
+hipError_t launch_rms_bwd_reduce(const float* pdot, int T, int M, const float* r, int N, float* c,
+                                 hipStream_t stream) {
+  hipLaunchKernelGGL(k_rms_bwd_reduce, dim3(cdiv(M, kReduceRowsPerBlock)), dim3(256), 0, stream,
+                     pdot, T, M, r, 1.0f / (float)N, c);
+  return hipGetLastError();
+}
+
 __global__ void k_zero_u32(unsigned int* p) { *p = 0u; }
 
 __global__ void k_amax_to_scale(const unsigned int* amax_bits, float* h_amax, float* scale_out) {
@@ -100,6 +137,36 @@ __global__ __launch_bounds__(256) void k_fold_gamma(const uint16_t* __restrict__
   const u32x2_t plo = pack_bf16x4(f[0], f[1], f[2], f[3]);
   const u32x2_t phi = pack_bf16x4(f[4], f[5], f[6], f[7]);
   *(i32x4_t*)(out + e) = i32x4_t{(int)plo.x, (int)plo.y, (int)phi.x, (int)phi.y};
+}
+
+// Weight preparation for the backward GEMMs, which read weights with the
+// forward's output features along K:  dst[c * ld_dst + r] = src[r * cols + c].
+// 64 x 64 tiles through LDS (one padding column against bank conflicts), so
+// both the reads and the writes are row-contiguous.
+__global__ __launch_bounds__(256) void k_transpose_bf16(const uint16_t* __restrict__ src, int rows,
+                                                        int cols, uint16_t* __restrict__ dst,
+                                                        int ld_dst) {
+  __shared__ uint16_t tile[64][65];
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int r = r0 + ty * 16 + k, c = c0 + tx;
+    if (r < rows && c < cols) tile[ty * 16 + k][tx] = src[(size_t)r * cols + c];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int c = c0 + ty * 16 + k, r = r0 + tx;
+    if (r < rows && c < cols) dst[(size_t)c * ld_dst + r] = tile[tx][ty * 16 + k];
+  }
+}
+
+hipError_t launch_transpose_bf16(const uint16_t* src, int rows, int cols, uint16_t* dst,
+                                 int ld_dst, hipStream_t stream) {
+  hipLaunchKernelGGL(k_transpose_bf16, dim3(cdiv(cols, 64), cdiv(rows, 64)), dim3(256), 0, stream,
+                     src, rows, cols, dst, ld_dst);
+  return hipGetLastError();
 }
 
 hipError_t launch_fold_gamma(const uint16_t* W, const float* gamma, uint16_t* W_out, int N, int K,
@@ -289,6 +356,95 @@ __global__ __launch_bounds__(256) void k_swiglu(const uint16_t* __restrict__ gu,
 hipError_t launch_swiglu(const uint16_t* gu, uint16_t* out, int M, int N, hipStream_t stream) {
   hipLaunchKernelGGL(k_swiglu, dim3(cdiv((int64_t)M * (N / 8), 256)), dim3(256), 0, stream, gu,
                      out, M, N);
+  return hipGetLastError();
+}
+
+// Unfused backward pieces (the passes the fused backward epilogues replace).
+// SwiGLU backward from a stored dout [M, N] and the saved gu = [g | u]:
+// dz = [dg | du], 8 features per thread.
+__global__ __launch_bounds__(256) void k_swiglu_bwd(const uint16_t* __restrict__ dout,
+                                                    const uint16_t* __restrict__ gu,
+                                                    uint16_t* __restrict__ dz, int M, int N) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int n8 = N / 8;
+  if (idx >= (int64_t)M * n8) return;
+  const int64_t m = idx / n8;
+  const int n = (int)(idx - m * n8) * 8;
+  float d[8], g[8], u[8], dg[8], du[8];
+  load8(dout + (size_t)m * N + n, d);
+  load8(gu + (size_t)m * 2 * N + n, g);
+  load8(gu + (size_t)m * 2 * N + N + n, u);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const float sg = 1.0f / (1.0f + __expf(-g[q]));
+    const float sl = g[q] * sg;
+    du[q] = d[q] * sl;
+    dg[q] = d[q] * u[q] * (sg + sl * (1.0f - sg));
+  }
+  store8(dz + (size_t)m * 2 * N + n, dg);
+  store8(dz + (size_t)m * 2 * N + N + n, du);
+}
+
+hipError_t launch_swiglu_bwd(const uint16_t* dout, const uint16_t* gu, uint16_t* dz, int M, int N,
+                             hipStream_t stream) {
+  hipLaunchKernelGGL(k_swiglu_bwd, dim3(cdiv((int64_t)M * (N / 8), 256)), dim3(256), 0, stream,
+                     dout, gu, dz, M, N);
+  return hipGetLastError();
+}
+
+// RMSNorm backward from a stored G = dz W' [M, N] (gamma folded into W'),
+// one block per row; the row scale is recomputed from h in the same pass:
+//   r = 1 / sqrt(mean h^2 + eps),  dh = r G - (r^3 / N) (sum_j h_j G_j) h + dY.
+__global__ __launch_bounds__(256) void k_rmsnorm_bwd(const uint16_t* __restrict__ G,
+                                                     const uint16_t* __restrict__ h,
+                                                     const uint16_t* __restrict__ dY, float eps,
+                                                     uint16_t* __restrict__ dh, int N) {
+  const int m = blockIdx.x;
+  const size_t row = (size_t)m * N;
+  float gv[kNormMaxGroups][8], hv[kNormMaxGroups][8];
+  float dot = 0.f, ss = 0.f;
+#pragma unroll
+  for (int g = 0; g < kNormMaxGroups; ++g) {
+    const int n = (g * 256 + threadIdx.x) * 8;
+    if (n < N) {
+      load8(G + row + n, gv[g]);
+      load8(h + row + n, hv[g]);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        dot += gv[g][q] * hv[g][q];
+        ss += hv[g][q] * hv[g][q];
+      }
+    }
+  }
+  __shared__ float red[2][4];
+  for (int o = 32; o > 0; o >>= 1) {
+    dot += __shfl_xor(dot, o, 64);
+    ss += __shfl_xor(ss, o, 64);
+  }
+  if ((threadIdx.x & 63) == 0) {
+    red[0][threadIdx.x >> 6] = dot;
+    red[1][threadIdx.x >> 6] = ss;
+  }
+  __syncthreads();
+  const float inv_n = 1.0f / (float)N;
+  const float rr = 1.0f / sqrtf((red[1][0] + red[1][1] + red[1][2] + red[1][3]) * inv_n + eps);
+  const float cm = rr * rr * rr * ((red[0][0] + red[0][1] + red[0][2] + red[0][3]) * inv_n);
+#pragma unroll
+  for (int g = 0; g < kNormMaxGroups; ++g) {
+    const int n = (g * 256 + threadIdx.x) * 8;
+    if (n < N) {
+      float y[8], o[8];
+      load8(dY + row + n, y);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) o[q] = rr * gv[g][q] - cm * hv[g][q] + y[q];
+      store8(dh + row + n, o);
+    }
+  }
+}
+
+hipError_t launch_rmsnorm_bwd(const uint16_t* G, const uint16_t* h, const uint16_t* dY, float eps,
+                              uint16_t* dh, int M, int N, hipStream_t stream) {
+  hipLaunchKernelGGL(k_rmsnorm_bwd, dim3(M), dim3(256), 0, stream, G, h, dY, eps, dh, N);
   return hipGetLastError();
 }
 

@@ -21,6 +21,7 @@ The shapes and distributions follow the LLaMA-3-shaped workloads:
   mlp_8b_fp8 M=16384, d=4096, K1=4096, ffn=14336 (e4m3)
   mlp_7b     M=8192,  d=4096, K1=4096, ffn=11008 (bf16)
   mlp_70b    M=8192,  d=8192, K1=8192, ffn=28672 (bf16)
+  mlp_1b_bwd as mlp_1b, plus down projection wd and output gradient dy
 Activations and residuals ~ N(0, 1); weights ~ N(0, 1/fan_in of the layer
 they feed, i.e. 1/d for the d-wide layers); gamma = 1 + 0.1 N(0, 1).
 """
@@ -44,10 +45,13 @@ WORKLOADS = {
     # ffn=11008; LLaMA-2/3-70B: d=8192, ffn=28672), M=8192 tokens as for 1B
     "mlp_7b": (5, "mlp", dict(M=8192, d=4096, K1=4096, ffn=11008)),
     "mlp_70b": (6, "mlp", dict(M=8192, d=8192, K1=8192, ffn=28672)),
+    # forward + backward of the 1B-shaped MLP sub-layer (adds the down
+    # projection and the gradient arriving at the sub-layer's output)
+    "mlp_1b_bwd": (7, "mlp_bwd", dict(M=8192, d=2048, K1=2048, ffn=8192)),
 }
 
 _TENSOR_IDS = {"x": 0, "res": 1, "w1": 2, "wg": 3, "wu": 4, "gamma": 5, "wqkv": 6,
-               "wlm": 7, "labels": 8}
+               "wlm": 7, "labels": 8, "wd": 9, "dy": 10}
 
 
 def _rng(seed, workload_id, tensor):
@@ -110,6 +114,17 @@ def make_mlp(seed=0, M=64, d=256, K1=256, ffn=512, workload_id=0, name="mlp"):
     return w
 
 
+def make_mlp_bwd(seed=0, M=64, d=256, K1=256, ffn=512, workload_id=7, name="mlp_bwd"):
+    """MLP sub-layer inputs for the backward pass: those of make_mlp plus the
+    down projection wd [d,ffn] ~ N(0, 1/ffn) and the gradient dy [M,d] ~ N(0,1)
+    of the sub-layer output."""
+    w = make_mlp(seed, M, d, K1, ffn, workload_id, name)
+    w.kind = "mlp_bwd"
+    w.arrays["wd"] = to_bf16_bits(normal_f32(seed, workload_id, "wd", (d, ffn), ffn ** -0.5))
+    w.arrays["dy"] = to_bf16_bits(normal_f32(seed, workload_id, "dy", (M, d), 1.0))
+    return w
+
+
 def make_attn(seed=0, M=64, d=256, K1=256, n_q=4, n_kv=2, head_dim=64, theta=500000.0,
               seq_len=2048, workload_id=2, name="attn"):
     """Attention-input block inputs: a [M,K1], res [M,d], w1 [d,K1],
@@ -162,6 +177,8 @@ def make_workload(name, seed=0, **overrides):
         return make_attn(seed, workload_id=wid, name=name, **sizes)
     if kind == "lm":
         return make_lm(seed, workload_id=wid, name=name, **sizes)
+    if kind == "mlp_bwd":
+        return make_mlp_bwd(seed, workload_id=wid, name=name, **sizes)
     if kind == "mlp_fp8":
         return make_mlp_fp8(seed, workload_id=wid, name=name, **sizes)
     raise KeyError(name)

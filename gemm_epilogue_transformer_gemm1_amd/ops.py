@@ -52,6 +52,14 @@ _SIGNATURES = {
     "coda_quantize_e4m3": ([_p, _i64, _p, _p, _p, _p, _p], _c_int),
     "coda_rope_apply": ([_p, _p, _p, _p, _c_int, _c_int, _c_int, _c_int, _c_int, _p], _c_int),
     "coda_cross_entropy_rows": ([_p, _p, _p, _p, _c_int, _c_int, _p], _c_int),
+    "coda_gemm_rowscale_swiglu_save": ([_p, _p, _p, _p, _p, _p, _c_int, _c_int, _c_int, _p],
+                                       _c_int),
+    "coda_gemm_swiglu_bwd": ([_p, _p, _p, _p, _p, _c_int, _c_int, _c_int, _p], _c_int),
+    "coda_rms_bwd_reduce": ([_p, _c_int, _c_int, _p, _c_int, _p, _p], _c_int),
+    "coda_gemm_rmsnorm_bwd": ([_p, _p, _p, _p, _p, _p, _p, _c_int, _c_int, _c_int, _p], _c_int),
+    "coda_swiglu_bwd": ([_p, _p, _p, _c_int, _c_int, _p], _c_int),
+    "coda_transpose_bf16": ([_p, _c_int, _c_int, _p, _c_int, _p], _c_int),
+    "coda_rmsnorm_bwd": ([_p, _p, _p, _c_float, _p, _c_int, _c_int, _p], _c_int),
 }
 
 
@@ -166,6 +174,92 @@ def gemm_rowscale_swiglu(X, Wg, Wu, r, out, x_scale=None, wg_scale=None, wu_scal
           _ptr(Wg, wt, "Wg"), _ptr(Wu, wt, "Wu"), _ptr(wg_scale, _F32, "wg_scale"),
           _ptr(wu_scale, _F32, "wu_scale"), _ptr(r, _F32, "r"), _ptr(out, _BF16, "out"),
           M, N, K, _stream(stream))
+
+
+def _shape(t, shape, what):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def gemm_rowscale_swiglu_save(X, Wg, Wu, r, out, gu, stream=None):
+    """out = silu(g) * u with g = r * X Wg^T, u = r * X Wu^T, and gu = [g | u]
+    kept for the backward pass (bf16)."""
+    M, K = X.shape
+    N = Wg.shape[0]
+    for t, shp, what in ((Wg, (N, K), "Wg"), (Wu, (N, K), "Wu"), (r, (M,), "r"),
+                         (out, (M, N), "out"), (gu, (M, 2 * N), "gu")):
+        _shape(t, shp, what)
+    _call("coda_gemm_rowscale_swiglu_save", _ptr(X, _BF16, "X"), _ptr(Wg, _BF16, "Wg"),
+          _ptr(Wu, _BF16, "Wu"), _ptr(r, _F32, "r"), _ptr(out, _BF16, "out"),
+          _ptr(gu, _BF16, "gu"), M, N, K, _stream(stream))
+
+
+def gemm_swiglu_bwd(dY, WdT, gu, dz, partial_dot, stream=None):
+    """dz = [dg | du] of SwiGLU given dout = dY WdT^T (never stored) and the
+    saved gu = [g | u]; partial_dot[t, m] = sum over tile t of dg g + du u."""
+    M, K = dY.shape
+    N = WdT.shape[0]
+    for t, shp, what in ((WdT, (N, K), "WdT"), (gu, (M, 2 * N), "gu"), (dz, (M, 2 * N), "dz"),
+                         (partial_dot, (rms_tiles(N), M), "partial_dot")):
+        _shape(t, shp, what)
+    _call("coda_gemm_swiglu_bwd", _ptr(dY, _BF16, "dY"), _ptr(WdT, _BF16, "WdT"),
+          _ptr(gu, _BF16, "gu"), _ptr(dz, _BF16, "dz"), _ptr(partial_dot, _F32, "partial_dot"),
+          M, N, K, _stream(stream))
+
+
+def rms_bwd_reduce(partial_dot, N, r, c, stream=None):
+    """c[m] = r[m]^2 / N * sum_t partial_dot[t, m] (N = the normalised width)."""
+    T, M = partial_dot.shape
+    _shape(r, (M,), "r")
+    _shape(c, (M,), "c")
+    _call("coda_rms_bwd_reduce", _ptr(partial_dot, _F32, "partial_dot"), T, M, _ptr(r, _F32, "r"),
+          int(N), _ptr(c, _F32, "c"), _stream(stream))
+
+
+def gemm_rmsnorm_bwd(dz, W2T, h, dY, r, c, dh, stream=None):
+    """dh = r * (dz W2T^T) - c * h + dY."""
+    M, K = dz.shape
+    N = W2T.shape[0]
+    for t, shp, what in ((W2T, (N, K), "W2T"), (h, (M, N), "h"), (dY, (M, N), "dY"),
+                         (r, (M,), "r"), (c, (M,), "c"), (dh, (M, N), "dh")):
+        _shape(t, shp, what)
+    _call("coda_gemm_rmsnorm_bwd", _ptr(dz, _BF16, "dz"), _ptr(W2T, _BF16, "W2T"),
+          _ptr(h, _BF16, "h"), _ptr(dY, _BF16, "dY"), _ptr(r, _F32, "r"), _ptr(c, _F32, "c"),
+          _ptr(dh, _BF16, "dh"), M, N, K, _stream(stream))
+
+
+def transpose(src, dst, stream=None):
+    """dst[:, :rows] = src^T for src [rows, cols] (bf16); dst [cols, ld] may be
+    a column slice of a wider row-major matrix (its row stride is ld)."""
+    rows, cols = src.shape
+    if dst.dim() != 2 or dst.shape[0] != cols or dst.shape[1] < rows or dst.stride(1) != 1:
+        raise ValueError(f"dst {tuple(dst.shape)} cannot hold the transpose of {tuple(src.shape)}")
+    if dst.dtype != _BF16 or not dst.is_cuda:
+        raise TypeError("dst must be a bf16 device tensor")
+    ld = dst.stride(0)
+    if ld < rows or dst.storage_offset() + (cols - 1) * ld + rows > dst.untyped_storage().nbytes() // 2:
+        raise ValueError("dst's storage is too small for the transpose")
+    _call("coda_transpose_bf16", _ptr(src, _BF16, "src"), rows, cols, dst.data_ptr(), ld,
+          _stream(stream))
+
+
+def swiglu_bwd(dout, gu, dz, stream=None):
+    """Unfused SwiGLU backward from a stored dout [M, N]."""
+    M, N = dout.shape
+    _shape(gu, (M, 2 * N), "gu")
+    _shape(dz, (M, 2 * N), "dz")
+    _call("coda_swiglu_bwd", _ptr(dout, _BF16, "dout"), _ptr(gu, _BF16, "gu"),
+          _ptr(dz, _BF16, "dz"), M, N, _stream(stream))
+
+
+def rmsnorm_bwd(G, h, dY, eps, dh, stream=None):
+    """Unfused RMSNorm backward from a stored G = dz W' [M, N] (the row scale
+    is recomputed from h)."""
+    M, N = G.shape
+    for t, shp, what in ((h, (M, N), "h"), (dY, (M, N), "dY"), (dh, (M, N), "dh")):
+        _shape(t, shp, what)
+    _call("coda_rmsnorm_bwd", _ptr(G, _BF16, "G"), _ptr(h, _BF16, "h"), _ptr(dY, _BF16, "dY"),
+          float(eps), _ptr(dh, _BF16, "dh"), M, N, _stream(stream))
 
 
 def gemm_rope(h, Wqkv, r, rope_cos, rope_sin, pos, qkv, n_q_heads, n_kv_heads, head_dim,

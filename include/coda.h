@@ -179,12 +179,77 @@ int coda_gemm_block_lse(const void* X, const void* W, const float* r, const int3
                         float* tile_max, float* tile_sumexp, float* label_logit, float* lse,
                         float* loss, int M, int V, int K, void* stream);
 
+/* ---- backward of the MLP sub-layer ----
+ *
+ * Page section "CODA: the secret in the epilogue": when the forward tail is
+ * block-local the backward pass inherits the same structure; section
+ * "Results": backward kernels of SwiGLU and of GEMM-Residual-PartialRMS-GEMM.
+ * The page prints no formulas; these calls compute the chain rule of
+ *   h = res + x Wo^T,  z = [g | u] = r h W'^T,  W' = [Wg; Wu] diag(gamma),
+ *   out = silu(g) u,   next = h + out Wd^T
+ * given dY = dL/dnext [M, d] (bf16).  Weights enter transposed copies (the
+ * GEMMs read K-contiguous rows): WdT = Wd^T [ffn, d], W2T = W'^T [d, 2 ffn].
+ * The sequence is
+ *   coda_gemm_rowscale_swiglu_save  (forward, keeps z)
+ *   coda_gemm_swiglu_bwd -> coda_rms_bwd_reduce -> coda_gemm_rmsnorm_bwd
+ * and then dx = dh Wo is a plain GEMM with Wo^T (coda_gemm_bf16).  Weight
+ * gradients (reductions over tokens) are plain GEMMs with no epilogue and are
+ * not part of this library.
+ */
+
+/* coda_gemm_rowscale_swiglu (bf16) that also stores the pre-activations for
+ * the backward pass (section "Five building blocks and a LEGO language": tile
+ * stores that keep intermediate activations):
+ *   gu[m, n] = bf16(g[m,n]),  gu[m, N + n] = bf16(u[m,n])
+ * X [M,K], Wg, Wu [N,K] bf16 (gamma folded), r [M] fp32, out [M,N] bf16,
+ * gu [M, 2N] bf16.  Sizes as coda_gemm_rowscale_swiglu (bf16). */
+int coda_gemm_rowscale_swiglu_save(const void* X, const void* Wg, const void* Wu, const float* r,
+                                   void* out, void* gu, int M, int N, int K, void* stream);
+
+/* SwiGLU backward as the epilogue of the GEMM that forms dout = dY Wd:
+ *   dout[m,n] = dY[m,:] . WdT[n,:]                    (fp32, never stored)
+ *   s = 1/(1+e^-g),  du = dout silu(g),  dg = dout u (s + silu(g)(1 - s))
+ *   dz[m, n] = bf16(dg),  dz[m, N + n] = bf16(du)     (g, u read from gu)
+ *   partial_dot[t*M + m] = sum over n in tile t of (dg g + du u)   (fp32)
+ * with tiles of coda_rms_tile_width() features, T = coda_rms_tiles(N).
+ * dY [M,K] bf16 (K = d), WdT [N,K] bf16 (N = ffn), gu [M,2N] bf16 (from
+ * coda_gemm_rowscale_swiglu_save), dz [M,2N] bf16, partial_dot [T,M] fp32.
+ * Sizes: M >= 1; N >= 16, N % 16 == 0; K >= 64, K % 64 == 0. */
+int coda_gemm_swiglu_bwd(const void* dY, const void* WdT, const void* gu, void* dz,
+                         float* partial_dot, int M, int N, int K, void* stream);
+
+/* Row coefficient of the RMSNorm backward, the light reduction of the
+ * SwiGLU-backward partial sums:
+ *   c[m] = r[m]^2 / N * sum_{t < T} partial_dot[t*M + m]
+ * which equals (r^3 / N) sum_j h_j G_j with G = dz W' (sum_j h_j G_j =
+ * sum_n dz_n z_n / r).  N = d, the normalised width; r [M] the forward row
+ * scale; partial_dot [T,M], c [M] fp32.  Sizes: T, M, N >= 1. */
+int coda_rms_bwd_reduce(const float* partial_dot, int T, int M, const float* r, int N, float* c,
+                        void* stream);
+
+/* RMSNorm backward and skip connection as the epilogue of the GEMM that forms
+ * G = dz W':
+ *   dh[m,n] = bf16( r[m] (dz[m,:] . W2T[n,:]) - c[m] h[m,n] + dY[m,n] )
+ * dh is also dres, and dy for the GEMM before (dx = dh Wo).
+ * dz [M,K] bf16 (K = 2 ffn), W2T [N,K] bf16 (N = d, gamma folded), h [M,N]
+ * bf16 (the forward h), dY [M,N] bf16, r, c [M] fp32, dh [M,N] bf16.
+ * Sizes: M >= 1; N >= 16, N % 16 == 0; K >= 64, K % 64 == 0. */
+int coda_gemm_rmsnorm_bwd(const void* dz, const void* W2T, const void* h, const void* dY,
+                          const float* r, const float* c, void* dh, int M, int N, int K,
+                          void* stream);
+
 /* ---- weight preparation (run once per weight update, not per token) ---- */
 
 /* W_out[n,k] = bf16( W[n,k] * gamma[k] ): folds the RMSNorm gain, which lies
  * along GEMM2's K axis, into the weight columns.  W, W_out [N,K] bf16,
  * gamma [K] fp32.  Sizes: N, K >= 1, K % 8 == 0. */
 int coda_fold_gamma(const void* W, const float* gamma, void* W_out, int N, int K, void* stream);
+
+/* dst[c * ld_dst + r] = src[r * cols + c]: bf16 transpose of src [rows, cols]
+ * into the first `rows` columns of dst [cols, ld_dst] (ld_dst >= rows), for
+ * the transposed weight copies the backward GEMMs read (Wd^T, W'^T, Wo^T).
+ * Sizes: rows, cols >= 1; rows * cols and cols * ld_dst below 2^31. */
+int coda_transpose_bf16(const void* src, int rows, int cols, void* dst, int ld_dst, void* stream);
 
 /* rope_cos/rope_sin[p*(hd/2)+i] = cos/sin(p * theta^(-2i/hd)), angles and
  * trigonometry in fp64, stored fp32.  Sizes: max_pos >= 1, head_dim even. */
@@ -204,6 +269,15 @@ int coda_rmsnorm(const void* h, const float* gamma, float eps, void* out, int M,
                  void* stream);
 /* out[m,n] = bf16( silu(gu[m,n]) * gu[m,N+n] ); gu [M,2N], out [M,N] bf16; N % 8 == 0. */
 int coda_swiglu(const void* gu, void* out, int M, int N, void* stream);
+/* SwiGLU backward from a stored dout [M,N] bf16 and gu [M,2N]: dz [M,2N] as
+ * coda_gemm_swiglu_bwd writes it (no partial sums).  N % 8 == 0. */
+int coda_swiglu_bwd(const void* dout, const void* gu, void* dz, int M, int N, void* stream);
+/* RMSNorm backward from a stored G = dz W' [M,N] bf16, one pass per row that
+ * also recomputes the row scale from h:  r = 1/sqrt(mean_n h^2 + eps),
+ *   dh = bf16( r G - (r^3 / N) (sum_j h_j G_j) h + dY )
+ * G, h, dY, dh [M,N] bf16.  N % 8 == 0, N <= 16384. */
+int coda_rmsnorm_bwd(const void* G, const void* h, const void* dY, float eps, void* dh, int M,
+                     int N, void* stream);
 /* C[m, n] = bf16( A[m,:] . W[n,:] * a_scale * w_scale ), e4m3 operands A [M,K], W [N,K],
  * device fp32 scalars a_scale, w_scale; C rows ldc elements apart (ldc >= N, ldc % 8 == 0).
  * Sizes as coda_gemm_residual_partialrms (fp8: K % 128). */
