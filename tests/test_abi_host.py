@@ -97,3 +97,53 @@ def test_valid_arguments_without_gpu_report_device_error(L):
     # fails cleanly on a machine without a gfx950 GPU.
     st = L.coda_gemm_bf16(A16, A16, A16, 64, 64, 64, None)
     assert st == ERR_DEVICE
+
+
+def test_backward_validation(L):
+    # coda_gemm_rowscale_swiglu_save(X, Wg, Wu, r, out, gu, M, N, K, stream)
+    s = L.coda_gemm_rowscale_swiglu_save
+    assert s(A16, A16, A16, A16, A16, None, 64, 256, 256, None) == ERR_NULL
+    assert s(A16, A16, A16, A16, A16, A16, 64, 264, 256, None) == ERR_SHAPE
+    assert s(A16, A16, A16, A16, A16, A16 + 8, 64, 256, 256, None) == ERR_ALIGN
+    assert s(A16, A16, A16, A16, A16, A16, 1 << 16, 1 << 14, 64, None) == ERR_SHAPE  # M x 2N
+    # coda_gemm_swiglu_bwd(dY, WdT, gu, dz, partial_dot, M, N, K, stream)
+    b = L.coda_gemm_swiglu_bwd
+    assert b(A16, A16, A16, A16, None, 64, 256, 256, None) == ERR_NULL
+    assert b(A16, A16, A16, A16, A16, 64, 256, 96, None) == ERR_SHAPE   # K % 64
+    assert b(A16, A16, A16, A16, A16, 64, 8, 256, None) == ERR_SHAPE    # N >= 16
+    assert b(A16, A16, A16 + 4, A16, A16, 64, 256, 256, None) == ERR_ALIGN
+    assert b(A16, A16, A16, A16, A16 + 2, 64, 256, 256, None) == ERR_ALIGN
+    # coda_rms_bwd_reduce(partial_dot, T, M, r, N, c, stream)
+    c = L.coda_rms_bwd_reduce
+    assert c(A16, 2, 8, None, 8, A16, None) == ERR_NULL
+    assert c(A16, 0, 8, A16, 8, A16, None) == ERR_SHAPE
+    assert c(A16, 2, 8, A16, 0, A16, None) == ERR_SHAPE
+    assert c(A16, 2, 8, A16, 8, A16 + 2, None) == ERR_ALIGN
+    # coda_gemm_rmsnorm_bwd(dz, W2T, h, dY, r, c, dh, M, N, K, stream)
+    g = L.coda_gemm_rmsnorm_bwd
+    assert g(A16, A16, A16, A16, A16, None, A16, 64, 256, 512, None) == ERR_NULL
+    assert g(A16, A16, A16, A16, A16, A16, A16, 0, 256, 512, None) == ERR_SHAPE
+    assert g(A16, A16, A16, A16, A16, A16, A16, 64, 256, 544, None) == ERR_SHAPE  # K % 64
+    assert g(A16, A16, A16 + 8, A16, A16, A16, A16, 64, 256, 512, None) == ERR_ALIGN
+    # unfused pieces and the transpose
+    assert L.coda_swiglu_bwd(A16, None, A16, 64, 256, None) == ERR_NULL
+    assert L.coda_swiglu_bwd(A16, A16, A16, 64, 12, None) == ERR_SHAPE
+    assert L.coda_rmsnorm_bwd(A16, A16, A16, 1e-5, A16, 64, 32768, None) == ERR_SHAPE
+    assert L.coda_rmsnorm_bwd(A16, A16, A16, -1.0, A16, 64, 256, None) == ERR_SHAPE
+    assert L.coda_transpose_bf16(A16, 4, 8, None, 4, None) == ERR_NULL
+    assert L.coda_transpose_bf16(A16, 4, 8, A16, 3, None) == ERR_SHAPE    # ld_dst < rows
+    assert L.coda_transpose_bf16(A16 + 1, 4, 8, A16, 4, None) == ERR_ALIGN
+
+
+def test_binding_checks_backward_shapes():
+    """The Python binding refuses output tensors of the wrong shape before any
+    call (CPU tensors are rejected for not being on the device, which needs
+    no GPU to check)."""
+    x = torch.zeros(4, 8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        ops.gemm_swiglu_bwd(x, torch.zeros(16, 8, dtype=torch.bfloat16),
+                            torch.zeros(4, 16, dtype=torch.bfloat16),
+                            torch.zeros(4, 32, dtype=torch.bfloat16),
+                            torch.zeros(1, 4, dtype=torch.float32))
+    with pytest.raises(ValueError):
+        ops.transpose(x, torch.zeros(8, 3, dtype=torch.bfloat16))
