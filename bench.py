@@ -40,11 +40,22 @@ def parse():
                         "copy kernel of known size, to scale HBM byte counters)")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="approximate CPU time budget of the oracle baseline")
+    p.add_argument("--row-min-ms", type=float, default=40.0,
+                   help="minimum GPU time of the warm-up and of the timed steps of each "
+                        "other_rows workload (0: exactly --steps / 3 warm-up steps)")
+    p.add_argument("--no-cold", action="store_true",
+                   help="skip the pass that overwrites 1 GiB between steps (operands evicted "
+                        "from the 256 MB memory-side cache)")
     return p.parse_args()
 
 
+_ROW_MIN_MS = 40.0
+
+
 def main():
+    global _ROW_MIN_MS
     args = parse()
+    _ROW_MIN_MS = args.row_min_ms
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
@@ -155,6 +166,20 @@ def main():
     fused_steps = np.array([per[k].sum() for k in range(args.steps)])
     unf_steps = step_times(torch, stream, unfused_step, args.steps)
 
+    cold = None
+    if not args.no_cold:
+        print("[bench] cold pass (1 GiB overwritten before every step)", file=sys.stderr,
+              flush=True)
+        scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        cold = {"fused_step_ms": pctl(step_times_cold(torch, stream, fused_step, args.steps,
+                                                      scratch)),
+                "unfused_step_ms": pctl(step_times_cold(torch, stream, unfused_step,
+                                                        args.steps, scratch)),
+                "note": "events around each step only; before each step a 1 GiB buffer is "
+                        "overwritten so the step's operands are not resident in the "
+                        "256 MB memory-side cache"}
+        del scratch
+
     ms_step = fused_ms / args.steps
     tflops = flops / (ms_step * 1e-3) / 1e12
     unf_ms_step = unfused_ms / args.steps
@@ -191,6 +216,7 @@ def main():
                    "M": M, "d": d, "K1": K1, "ffn": ffn, "parallelism": "none (1 GPU)"},
         "pct_of_mfma_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "step_ms": pctl(fused_steps),
+        "cold_cache": cold,
         "unfused": {"ms_per_step": round(unf_ms_step, 4), "tflops": round(unf_tflops, 2),
                     "speedup_fused_vs_unfused": round(unf_ms_step / ms_step, 3),
                     "step_ms": pctl(unf_steps)},
@@ -236,11 +262,28 @@ def step_times(torch, stream, fn, steps):
     return [e0.elapsed_time(e1) for e0, e1 in evs]
 
 
-def _events_time(torch, stream, fn, steps, warmup, min_ms=40.0):
+def step_times_cold(torch, stream, fn, steps, scratch):
+    """Per-step times (ms) with `scratch` overwritten before every step (not
+    timed), so the step starts with its operands evicted from the caches."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    for k, (e0, e1) in enumerate(evs):
+        scratch.fill_(float(k))
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return [e0.elapsed_time(e1) for e0, e1 in evs]
+
+
+def _events_time(torch, stream, fn, steps, warmup, min_ms=None):
     """Mean step time (ms) over back-to-back steps.  Warmup and timed region
     each cover at least `min_ms` of GPU work (the shader clock settles over
     tens of milliseconds under sustained MFMA load), so short steps are
     repeated more often than `steps`/`warmup`."""
+    if min_ms is None:
+        min_ms = _ROW_MIN_MS
     fn()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
