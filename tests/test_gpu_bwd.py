@@ -140,6 +140,7 @@ def test_forward_save_matches_forward():
     (8192, 2048, 4096),  # 512 SwiGLU-backward tiles: every workgroup chains
     (4096, 4096, 32),    # RMSNorm backward: one K stage per tile, 256 tiles
     (16384, 4096, 64),   # RMSNorm backward: two stages per tile, 1024 tiles
+    (1, 64, 32),         # one token row, the smallest widths (one stage, one partial tile)
 ])
 def test_bwd_epilogues_exact(M, d, ffn):
     """Values chosen so that every step is exact in fp32 (the bf16 stores
