@@ -4,7 +4,7 @@
 // Citations name sections of the news page "CODA: New Research Optimizes
 // Transformer Training with GEMM-Epilogue Programming" (KuCoin news flash).
 // Section "CODA: the secret in the epilogue" states that a block-local forward
-// tail gives a backward pass of the same structure; section "Results" reports
+// tail gives a backward pass of the same structure; section "Experimental results" reports
 // backward kernels for SwiGLU and for GEMM-Residual-PartialRMS-GEMM.  The page
 // prints no formulas; the ones below are the chain rule of the forward
 //   h = res + x Wo^T,  z = [g | u] = r h W'^T (W' = [Wg; Wu] diag(gamma)),

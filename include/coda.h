@@ -183,7 +183,7 @@ int coda_gemm_block_lse(const void* X, const void* W, const float* r, const int3
  *
  * Page section "CODA: the secret in the epilogue": when the forward tail is
  * block-local the backward pass inherits the same structure; section
- * "Results": backward kernels of SwiGLU and of GEMM-Residual-PartialRMS-GEMM.
+ * "Experimental results": backward kernels of SwiGLU and of GEMM-Residual-PartialRMS-GEMM.
  * The page prints no formulas; these calls compute the chain rule of
  *   h = res + x Wo^T,  z = [g | u] = r h W'^T,  W' = [Wg; Wu] diag(gamma),
  *   out = silu(g) u,   next = h + out Wd^T

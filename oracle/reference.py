@@ -90,7 +90,7 @@ def mlp_block(x, res, wo, wg, wu, gamma, eps):
 # ---------------------------------------------------------------------------
 # Backward of the MLP sub-layer.  Section "CODA: the secret in the epilogue"
 # states that when the tail of the forward pass is block-local the backward
-# pass inherits the same structure, and section "Results" reports backward
+# pass inherits the same structure, and section "Experimental results" reports backward
 # kernels for GEMM-Residual-PartialRMS-GEMM and for SwiGLU.  The page prints
 # no formulas: what follows is the chain rule applied to the forward
 # definitions above, in the order the forward computes.
