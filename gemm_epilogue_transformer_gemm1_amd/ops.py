@@ -109,6 +109,23 @@ def _ptr(t, dtype=None, what="tensor"):
     return t.data_ptr()
 
 
+def _shape(t, shape, what):
+    """Host-side size check: the kernels index the buffers by the sizes passed
+    through the C ABI, which cannot see a buffer's extent."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _want(t, shape, what):
+    if t is not None:
+        _shape(t, shape, what)
+
+
+def _scalar(t, what):
+    if t is not None and t.numel() < 1:
+        raise ValueError(f"{what} must hold one value (shape {tuple(t.shape)})")
+
+
 def _stream(stream=None):
     s = stream if stream is not None else torch.cuda.current_stream()
     return s.cuda_stream
@@ -143,6 +160,13 @@ def gemm_residual_partialrms(A, W, residual, h, partial_sumsq, a_scale=None, w_s
     dt = CODA_FP8_E4M3 if fp8 else CODA_BF16
     M, K = A.shape
     N = W.shape[0]
+    T = rms_tiles(N)
+    for t, shp, what in ((W, (N, K), "W"), (residual, (M, N), "residual"), (h, (M, N), "h"),
+                         (partial_sumsq, (T, M), "partial_sumsq"), (h8, (M, N), "h8"),
+                         (partial_amax, (T, M), "partial_amax")):
+        _want(t, shp, what)
+    for t, what in ((a_scale, "a_scale"), (w_scale, "w_scale"), (h8_scale, "h8_scale")):
+        _scalar(t, what)
     _call("coda_gemm_residual_partialrms", dt,
           _ptr(A, _E4M3 if fp8 else _BF16, "A"), _ptr(W, _E4M3 if fp8 else _BF16, "W"),
           _ptr(a_scale, _F32, "a_scale"), _ptr(w_scale, _F32, "w_scale"),
@@ -156,6 +180,10 @@ def rms_reduce(partial_sumsq, N, eps, r, partial_amax=None, h_amax=None, h8_scal
                stream=None):
     """r = 1/sqrt(sum_t partial / N + eps) per row (plus the fp8 amax)."""
     T, M = partial_sumsq.shape
+    _shape(r, (M,), "r")
+    _want(partial_amax, (T, M), "partial_amax")
+    _scalar(h_amax, "h_amax")
+    _scalar(h8_scale_out, "h8_scale_out")
     _call("coda_rms_reduce", _ptr(partial_sumsq, _F32, "partial_sumsq"),
           _ptr(partial_amax, _F32, "partial_amax"), T, M, N, float(eps), _ptr(r, _F32, "r"),
           _ptr(h_amax, _F32, "h_amax"), _ptr(h8_scale_out, _F32, "h8_scale_out"),
@@ -170,15 +198,15 @@ def gemm_rowscale_swiglu(X, Wg, Wu, r, out, x_scale=None, wg_scale=None, wu_scal
     M, K = X.shape
     N = Wg.shape[0]
     wt = _E4M3 if fp8 else _BF16
+    for t, shp, what in ((Wg, (N, K), "Wg"), (Wu, (N, K), "Wu"), (r, (M,), "r"),
+                         (out, (M, N), "out")):
+        _shape(t, shp, what)
+    for t, what in ((x_scale, "x_scale"), (wg_scale, "wg_scale"), (wu_scale, "wu_scale")):
+        _scalar(t, what)
     _call("coda_gemm_rowscale_swiglu", dt, _ptr(X, wt, "X"), _ptr(x_scale, _F32, "x_scale"),
           _ptr(Wg, wt, "Wg"), _ptr(Wu, wt, "Wu"), _ptr(wg_scale, _F32, "wg_scale"),
           _ptr(wu_scale, _F32, "wu_scale"), _ptr(r, _F32, "r"), _ptr(out, _BF16, "out"),
           M, N, K, _stream(stream))
-
-
-def _shape(t, shape, what):
-    if tuple(t.shape) != tuple(shape):
-        raise ValueError(f"{what} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
 def gemm_rowscale_swiglu_save(X, Wg, Wu, r, out, gu, stream=None):
@@ -266,6 +294,11 @@ def gemm_rope(h, Wqkv, r, rope_cos, rope_sin, pos, qkv, n_q_heads, n_kv_heads, h
               stream=None):
     """qkv = RoPE(r * h Wqkv^T) on the q and k heads."""
     M, K = h.shape
+    Nq = (n_q_heads + 2 * n_kv_heads) * head_dim
+    _check_rope(rope_cos, rope_sin, head_dim)
+    for t, shp, what in ((Wqkv, (Nq, K), "Wqkv"), (r, (M,), "r"), (pos, (M,), "pos"),
+                         (qkv, (M, Nq), "qkv")):
+        _shape(t, shp, what)
     _call("coda_gemm_rope", _ptr(h, _BF16, "h"), _ptr(Wqkv, _BF16, "Wqkv"), _ptr(r, _F32, "r"),
           _ptr(rope_cos, _F32, "rope_cos"), _ptr(rope_sin, _F32, "rope_sin"),
           _ptr(pos, _I32, "pos"), rope_cos.shape[0], _ptr(qkv, _BF16, "qkv"), M, K,
@@ -277,6 +310,11 @@ def gemm_block_lse(X, W, labels, tile_max, tile_sumexp, label_logit, loss, lse=N
     """Per-row cross entropy of z = (r *) X W^T without storing z."""
     M, K = X.shape
     V = W.shape[0]
+    T = lse_tiles(V)
+    for t, shp, what in ((W, (V, K), "W"), (labels, (M,), "labels"), (tile_max, (T, M), "tile_max"),
+                         (tile_sumexp, (T, M), "tile_sumexp"), (label_logit, (M,), "label_logit"),
+                         (loss, (M,), "loss"), (lse, (M,), "lse"), (r, (M,), "r")):
+        _want(t, shp, what)
     _call("coda_gemm_block_lse", _ptr(X, _BF16, "X"), _ptr(W, _BF16, "W"), _ptr(r, _F32, "r"),
           _ptr(labels, _I32, "labels"), _ptr(tile_max, _F32, "tile_max"),
           _ptr(tile_sumexp, _F32, "tile_sumexp"), _ptr(label_logit, _F32, "label_logit"),
@@ -285,11 +323,21 @@ def gemm_block_lse(X, W, labels, tile_max, tile_sumexp, label_logit, loss, lse=N
 
 def fold_gamma(W, gamma, W_out, stream=None):
     N, K = W.shape
+    _shape(gamma, (K,), "gamma")
+    _shape(W_out, (N, K), "W_out")
     _call("coda_fold_gamma", _ptr(W, _BF16, "W"), _ptr(gamma, _F32, "gamma"),
           _ptr(W_out, _BF16, "W_out"), N, K, _stream(stream))
 
 
+def _check_rope(rope_cos, rope_sin, head_dim):
+    if rope_cos.dim() != 2 or rope_cos.shape[1] != head_dim // 2:
+        raise ValueError(f"rope_cos has shape {tuple(rope_cos.shape)}, expected [max_pos, {head_dim // 2}]")
+    _shape(rope_sin, rope_cos.shape, "rope_sin")
+
+
 def rope_tables(theta, max_pos, head_dim, rope_cos, rope_sin, stream=None):
+    _shape(rope_cos, (max_pos, head_dim // 2), "rope_cos")
+    _shape(rope_sin, (max_pos, head_dim // 2), "rope_sin")
     _call("coda_rope_tables", float(theta), max_pos, head_dim, _ptr(rope_cos, _F32, "rope_cos"),
           _ptr(rope_sin, _F32, "rope_sin"), _stream(stream))
 
@@ -297,23 +345,32 @@ def rope_tables(theta, max_pos, head_dim, rope_cos, rope_sin, stream=None):
 def gemm_bf16(A, W, C, stream=None):
     M, K = A.shape
     N = W.shape[0]
+    _shape(W, (N, K), "W")
+    _shape(C, (M, N), "C")
     _call("coda_gemm_bf16", _ptr(A, _BF16, "A"), _ptr(W, _BF16, "W"), _ptr(C, _BF16, "C"),
           M, N, K, _stream(stream))
 
 
 def residual_add(y, res, h, stream=None):
+    _shape(res, y.shape, "res")
+    _shape(h, y.shape, "h")
     _call("coda_residual_add", _ptr(y, _BF16, "y"), _ptr(res, _BF16, "res"), _ptr(h, _BF16, "h"),
           y.numel(), _stream(stream))
 
 
 def rmsnorm(h, gamma, eps, out, stream=None):
     M, N = h.shape
+    _shape(gamma, (N,), "gamma")
+    _shape(out, (M, N), "out")
     _call("coda_rmsnorm", _ptr(h, _BF16, "h"), _ptr(gamma, _F32, "gamma"), float(eps),
           _ptr(out, _BF16, "out"), M, N, _stream(stream))
 
 
 def swiglu(gu, out, stream=None):
     M, N2 = gu.shape
+    if N2 % 2:
+        raise ValueError(f"gu has an odd width {N2}")
+    _shape(out, (M, N2 // 2), "out")
     _call("coda_swiglu", _ptr(gu, _BF16, "gu"), _ptr(out, _BF16, "out"), M, N2 // 2,
           _stream(stream))
 
@@ -321,6 +378,9 @@ def swiglu(gu, out, stream=None):
 def rope_apply(qkv, rope_cos, rope_sin, pos, n_q_heads, n_kv_heads, head_dim, stream=None):
     """In-place RoPE on the q and k heads of a stored qkv (unfused baseline)."""
     M = qkv.shape[0]
+    _check_rope(rope_cos, rope_sin, head_dim)
+    _shape(qkv, (M, (n_q_heads + 2 * n_kv_heads) * head_dim), "qkv")
+    _shape(pos, (M,), "pos")
     _call("coda_rope_apply", _ptr(qkv, _BF16, "qkv"), _ptr(rope_cos, _F32, "rope_cos"),
           _ptr(rope_sin, _F32, "rope_sin"), _ptr(pos, _I32, "pos"), rope_cos.shape[0], M,
           n_q_heads, n_kv_heads, head_dim, _stream(stream))
@@ -329,6 +389,8 @@ def rope_apply(qkv, rope_cos, rope_sin, pos, n_q_heads, n_kv_heads, head_dim, st
 def cross_entropy_rows(logits, labels, lse, loss, stream=None):
     """Per-row cross entropy of stored bf16 logits (unfused baseline)."""
     M, V = logits.shape
+    for t, shp, what in ((labels, (M,), "labels"), (lse, (M,), "lse"), (loss, (M,), "loss")):
+        _shape(t, shp, what)
     _call("coda_cross_entropy_rows", _ptr(logits, _BF16, "logits"), _ptr(labels, _I32, "labels"),
           _ptr(lse, _F32, "lse"), _ptr(loss, _F32, "loss"), M, V, _stream(stream))
 
@@ -338,6 +400,9 @@ def gemm_fp8(A, W, a_scale, w_scale, C, stream=None):
     C may be a column slice of a wider row-major buffer (its row stride is used)."""
     M, K = A.shape
     N = W.shape[0]
+    _shape(W, (N, K), "W")
+    _scalar(a_scale, "a_scale")
+    _scalar(w_scale, "w_scale")
     if C.stride(1) != 1 or C.shape != (M, N):
         raise ValueError("C must be [M, N] with unit column stride")
     if not C.is_cuda or C.dtype != _BF16:
@@ -348,6 +413,10 @@ def gemm_fp8(A, W, a_scale, w_scale, C, stream=None):
 
 def quantize_e4m3(x, s_in, out, amax, s_out, stream=None):
     """out = e4m3(x / s_in), amax = max|x|, s_out = amax / 448 (unfused baseline)."""
+    if out.numel() != x.numel():
+        raise ValueError(f"out holds {out.numel()} values, x {x.numel()}")
+    for t, what in ((s_in, "s_in"), (amax, "amax"), (s_out, "s_out")):
+        _scalar(t, what)
     _call("coda_quantize_e4m3", _ptr(x, _BF16, "x"), x.numel(), _ptr(s_in, _F32, "s_in"),
           _ptr(out, _E4M3, "out"), _ptr(amax, _F32, "amax"), _ptr(s_out, _F32, "s_out"),
           _stream(stream))

@@ -147,3 +147,38 @@ def test_binding_checks_backward_shapes():
                             torch.zeros(1, 4, dtype=torch.float32))
     with pytest.raises(ValueError):
         ops.transpose(x, torch.zeros(8, 3, dtype=torch.bfloat16))
+
+
+def test_binding_checks_forward_shapes(L):
+    """Wrong-sized outputs or operands are refused on the host, before the
+    kernels could index past a buffer (shape errors are raised before the
+    device check, so CPU tensors suffice)."""
+    bf, f32 = torch.bfloat16, torch.float32
+    A, W = torch.zeros(64, 256, dtype=bf), torch.zeros(256, 256, dtype=bf)
+    res, h = torch.zeros(64, 256, dtype=bf), torch.zeros(64, 256, dtype=bf)
+    T = ops.rms_tiles(256)
+    with pytest.raises(ValueError, match="shape"):   # partial sums too small
+        ops.gemm_residual_partialrms(A, W, res, h, torch.zeros(T - 1, 64, dtype=f32))
+    with pytest.raises(ValueError, match="shape"):   # h of another width
+        ops.gemm_residual_partialrms(A, W, res, torch.zeros(64, 128, dtype=bf),
+                                     torch.zeros(T, 64, dtype=f32))
+    with pytest.raises(ValueError, match="shape"):   # r too short
+        ops.rms_reduce(torch.zeros(T, 64, dtype=f32), 256, 1e-5, torch.zeros(32, dtype=f32))
+    with pytest.raises(ValueError, match="shape"):   # out of the wrong width
+        ops.gemm_rowscale_swiglu(A, W, W, torch.zeros(64, dtype=f32),
+                                 torch.zeros(64, 512, dtype=bf))
+    with pytest.raises(ValueError, match="shape"):
+        ops.gemm_bf16(A, W, torch.zeros(64, 255, dtype=bf))
+    with pytest.raises(ValueError, match="shape"):   # LSE workspace for fewer tiles
+        ops.gemm_block_lse(A, W, torch.zeros(64, dtype=torch.int32),
+                           torch.zeros(1, 64, dtype=f32), torch.zeros(1, 64, dtype=f32),
+                           torch.zeros(64, dtype=f32), torch.zeros(64, dtype=f32))
+    with pytest.raises(ValueError, match="shape"):   # RoPE tables of another head size
+        ops.gemm_rope(A, torch.zeros(6 * 64, 256, dtype=bf), torch.zeros(64, dtype=f32),
+                      torch.zeros(16, 16, dtype=f32), torch.zeros(16, 16, dtype=f32),
+                      torch.zeros(64, dtype=torch.int32), torch.zeros(64, 6 * 64, dtype=bf),
+                      4, 1, 64)
+    with pytest.raises(ValueError, match="shape"):
+        ops.rmsnorm(h, torch.zeros(255, dtype=f32), 1e-5, h)
+    with pytest.raises(ValueError, match="shape"):
+        ops.swiglu(torch.zeros(64, 512, dtype=bf), torch.zeros(64, 512, dtype=bf))
