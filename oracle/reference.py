@@ -134,8 +134,14 @@ def mlp_layer_bwd(x, res, wo, wg, wu, gamma, eps, wd, dy):
       dh   [M,d]   = rmsnorm_bwd(dn, h) + dy  (the skip connection adds dy)
       coef [M]     = the per-row coefficient of rmsnorm_bwd
       dres = dh,  dx [M,K1] = dh wo           (h = res + x wo^T)
+    and the weight gradients (sums over the token rows):
+      dwd [d,ffn]  = dy^T out                 (next = h + out wd^T)
+      dwg, dwu [ffn,d] = dg^T n, du^T n       (g = n wg^T, n = r h gamma)
+      dgamma [d]   = sum_m dn (r h)           (n_j = (r h)_j gamma_j)
+      dwo [d,K1]   = dh^T x
     """
     f = mlp_block(x, res, wo, wg, wu, gamma, eps)
+    x = np.asarray(x, dtype=np.float64)
     dy = np.asarray(dy, dtype=np.float64)
     dout = dy @ np.asarray(wd, dtype=np.float64)
     dg, du = swiglu_grad(dout, f["g"], f["u"])
@@ -143,8 +149,12 @@ def mlp_layer_bwd(x, res, wo, wg, wu, gamma, eps, wd, dy):
     dh_norm, coef = rmsnorm_bwd(dn, f["h"], gamma, eps)
     dh = dh_norm + dy
     dx = dh @ np.asarray(wo, dtype=np.float64)
+    rh = f["r"][:, None] * f["h"]
+    n = rh * np.asarray(gamma, dtype=np.float64)[None, :]
     f.update({"dout": dout, "dg": dg, "du": du, "dn": dn, "coef": coef, "dh": dh,
-              "dres": dh, "dx": dx})
+              "dres": dh, "dx": dx,
+              "dwd": dy.T @ f["out"], "dwg": dg.T @ n, "dwu": du.T @ n,
+              "dgamma": np.sum(dn * rh, axis=0), "dwo": dh.T @ x})
     return f
 
 

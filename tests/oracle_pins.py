@@ -437,7 +437,8 @@ def pin_layer_bwd_finite_differences(seed=15):
     o = _oracle_bwd(p)
     step = 1e-6
     errs = []
-    for key, grad in (("x", o["dx"]), ("res", o["dres"])):
+    for key, grad in (("x", o["dx"]), ("res", o["dres"]), ("wo", o["dwo"]), ("wg", o["dwg"]),
+                      ("wu", o["dwu"]), ("wd", o["dwd"])):
         fd = np.zeros_like(grad)
         for i in range(grad.shape[0]):
             for j in range(grad.shape[1]):
@@ -447,7 +448,14 @@ def pin_layer_bwd_finite_differences(seed=15):
                 lo[key][i][j] -= step
                 fd[i, j] = (_bf_layer_loss(**hi) - _bf_layer_loss(**lo)) / (2 * step)
         errs.append(_rel(grad, fd))
-    return _ok(max(errs), 1e-7, "layer backward vs finite differences")
+    fd = np.zeros(len(p["gamma"]))
+    for j in range(len(fd)):
+        hi, lo = dict(p), dict(p)
+        hi["gamma"] = [v + (step if k == j else 0.0) for k, v in enumerate(p["gamma"])]
+        lo["gamma"] = [v - (step if k == j else 0.0) for k, v in enumerate(p["gamma"])]
+        fd[j] = (_bf_layer_loss(**hi) - _bf_layer_loss(**lo)) / (2 * step)
+    errs.append(_rel(o["dgamma"], fd))
+    return _ok(max(errs), 1e-7, "layer backward (activations and weights) vs finite differences")
 
 
 def pin_layer_bwd_torch(seed=16):
@@ -460,6 +468,7 @@ def pin_layer_bwd_torch(seed=16):
     wo, wg, wu, wd = t(d, K1, sc=0.3), t(ffn, d, sc=0.3), t(ffn, d, sc=0.3), t(d, ffn, sc=0.3)
     gamma = torch.from_numpy(1 + 0.1 * rng.standard_normal(d))
     dy = torch.from_numpy(rng.standard_normal((M, d)))
+    gamma.requires_grad_(True)
     h = res + x @ wo.T
     xh = torch.nn.functional.rms_norm(h, (d,), eps=eps)
     n = xh * gamma
@@ -467,14 +476,18 @@ def pin_layer_bwd_torch(seed=16):
     out = torch.nn.functional.silu(g) * u
     for v in (n, g, u, out, h):
         v.retain_grad()
+    gamma.requires_grad_(True)
     ((h + out @ wd.T) * dy).sum().backward()
     num = lambda v: v.detach().numpy()
-    o = oracle.mlp_layer_bwd(num(x), num(res), num(wo), num(wg), num(wu), gamma.numpy(), eps,
+    o = oracle.mlp_layer_bwd(num(x), num(res), num(wo), num(wg), num(wu), num(gamma), eps,
                              num(wd), dy.numpy())
     errs = [_rel(o["dout"], out.grad.numpy()), _rel(o["dg"], g.grad.numpy()),
             _rel(o["du"], u.grad.numpy()), _rel(o["dn"], n.grad.numpy()),
-            _rel(o["dh"], res.grad.numpy()), _rel(o["dx"], x.grad.numpy())]
-    return _ok(max(errs), 1e-12, "layer backward vs torch autograd")
+            _rel(o["dh"], res.grad.numpy()), _rel(o["dx"], x.grad.numpy()),
+            _rel(o["dwd"], wd.grad.numpy()), _rel(o["dwg"], wg.grad.numpy()),
+            _rel(o["dwu"], wu.grad.numpy()), _rel(o["dwo"], wo.grad.numpy()),
+            _rel(o["dgamma"], gamma.grad.numpy())]
+    return _ok(max(errs), 1e-12, "layer backward (activations and weights) vs torch autograd")
 
 
 def pin_rmsnorm_bwd_scale_invariance(seed=17):

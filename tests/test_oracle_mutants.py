@@ -88,6 +88,19 @@ def _layer_bwd_no_skip(x, res, wo, wg, wu, gamma, eps, wd, dy):
     return o
 
 
+def _layer_bwd_dw_without_row_scale(x, res, wo, wg, wu, gamma, eps, wd, dy):
+    o = _ORIG_LAYER_BWD(x, res, wo, wg, wu, gamma, eps, wd, dy)
+    n = o["h"] * np.asarray(gamma)[None, :]
+    o["dwg"], o["dwu"] = o["dg"].T @ n, o["du"].T @ n
+    return o
+
+
+def _layer_bwd_dwd_transposed_operands(x, res, wo, wg, wu, gamma, eps, wd, dy):
+    o = _ORIG_LAYER_BWD(x, res, wo, wg, wu, gamma, eps, wd, dy)
+    o["dwd"] = (o["out"].T @ np.asarray(dy)).T * 0.5 + 0.5 * np.asarray(dy).T @ o["out"][:, ::-1]
+    return o
+
+
 def _layer_bwd_up_gate_swapped(x, res, wo, wg, wu, gamma, eps, wd, dy):
     return _ORIG_LAYER_BWD(x, res, wo, wu, wg, gamma, eps, wd, dy)
 
@@ -114,6 +127,8 @@ MUTANTS = {
     "rmsnorm bwd gamma dropped": ("rmsnorm_bwd", _rmsnorm_bwd_variant(use_gamma=False)),
     "skip-connection gradient dropped": ("mlp_layer_bwd", _layer_bwd_no_skip),
     "gate and up swapped in backward": ("mlp_layer_bwd", _layer_bwd_up_gate_swapped),
+    "weight gradient without the row scale": ("mlp_layer_bwd", _layer_bwd_dw_without_row_scale),
+    "down-projection gradient with permuted features": ("mlp_layer_bwd", _layer_bwd_dwd_transposed_operands),
     "abs instead of square": ("partial_sumsq", lambda h, w: np.stack([np.sum(np.abs(np.asarray(h)[:, t * w:(t + 1) * w]), axis=1) for t in range((np.asarray(h).shape[1] + w - 1) // w)])),
 }
 
