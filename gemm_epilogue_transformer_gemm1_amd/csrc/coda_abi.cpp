@@ -246,17 +246,18 @@ int coda_gemm_rmsnorm_bwd(const void* dz, const void* W2T, const void* h, const 
   }
 }
 
-int coda_transpose_bf16(const void* src, int rows, int cols, void* dst, int ld_dst,
-                        void* stream) {
+int coda_transpose_bf16(const void* src, const float* row_scale, int rows, int cols, void* dst,
+                        int ld_dst, void* stream) {
   try {
     if (!src || !dst) return CODA_ERR_NULL;
     if (rows < 1 || cols < 1 || ld_dst < rows || (int64_t)rows * cols >= (int64_t(1) << 31) ||
         (int64_t)cols * ld_dst >= (int64_t(1) << 31) || cols > 65535 * 64 || rows > 65535 * 64)
       return CODA_ERR_SHAPE;
-    if (!aligned(src, 2) || !aligned(dst, 2)) return CODA_ERR_ALIGN;
+    if (!aligned(src, 2) || !aligned(dst, 2) || (row_scale && !aligned(row_scale, 4)))
+      return CODA_ERR_ALIGN;
     if (int st = check_device()) return st;
-    return launched(coda::launch_transpose_bf16(static_cast<const uint16_t*>(src), rows, cols,
-                                                static_cast<uint16_t*>(dst), ld_dst,
+    return launched(coda::launch_transpose_bf16(static_cast<const uint16_t*>(src), row_scale,
+                                                rows, cols, static_cast<uint16_t*>(dst), ld_dst,
                                                 as_stream(stream)));
   } catch (...) {
     return CODA_ERR_LAUNCH;

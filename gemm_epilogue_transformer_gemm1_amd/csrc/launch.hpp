@@ -60,8 +60,8 @@ hipError_t launch_rowscale_swiglu_fp8(const uint8_t* X, const float* x_scale, co
 
 hipError_t launch_rms_reduce(const float* psum, const float* pamax, int T, int M, int N, float eps,
                              float* r, float* h_amax, float* h8_scale_out, hipStream_t stream);
-hipError_t launch_transpose_bf16(const uint16_t* src, int rows, int cols, uint16_t* dst,
-                                 int ld_dst, hipStream_t stream);
+hipError_t launch_transpose_bf16(const uint16_t* src, const float* row_scale, int rows, int cols,
+                                 uint16_t* dst, int ld_dst, hipStream_t stream);
 hipError_t launch_fold_gamma(const uint16_t* W, const float* gamma, uint16_t* W_out, int N, int K,
                              hipStream_t stream);
 hipError_t launch_residual_add(const uint16_t* y, const uint16_t* res, uint16_t* h, int64_t count,

@@ -139,20 +139,30 @@ __global__ __launch_bounds__(256) void k_fold_gamma(const uint16_t* __restrict__
   *(i32x4_t*)(out + e) = i32x4_t{(int)plo.x, (int)plo.y, (int)phi.x, (int)phi.y};
 }
 
-// Weight preparation for the backward GEMMs, which read weights with the
-// forward's output features along K:  dst[c * ld_dst + r] = src[r * cols + c].
+// Transposed copies for the backward GEMMs, which reduce along what the
+// forward keeps in rows (weights with the output features along K; token-major
+// activations for the weight gradients):
+//   dst[c * ld_dst + r] = src[r * cols + c]                       (row_scale NULL)
+//   dst[c * ld_dst + r] = bf16(src[r * cols + c] * row_scale[r])  (one rounding)
+// The second form carries the RMS row scale into the gradient of the folded
+// GEMM2 weight, dW' = dz^T (r h), whose reduction runs over the token rows.
 // 64 x 64 tiles through LDS (one padding column against bank conflicts), so
 // both the reads and the writes are row-contiguous.
-__global__ __launch_bounds__(256) void k_transpose_bf16(const uint16_t* __restrict__ src, int rows,
-                                                        int cols, uint16_t* __restrict__ dst,
-                                                        int ld_dst) {
+__global__ __launch_bounds__(256) void k_transpose_bf16(const uint16_t* __restrict__ src,
+                                                        const float* __restrict__ row_scale,
+                                                        int rows, int cols,
+                                                        uint16_t* __restrict__ dst, int ld_dst) {
   __shared__ uint16_t tile[64][65];
   const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
     const int r = r0 + ty * 16 + k, c = c0 + tx;
-    if (r < rows && c < cols) tile[ty * 16 + k][tx] = src[(size_t)r * cols + c];
+    if (r < rows && c < cols) {
+      uint16_t v = src[(size_t)r * cols + c];
+      if (row_scale) v = __builtin_bit_cast(uint16_t, (__bf16)(bf16_to_f32(v) * row_scale[r]));
+      tile[ty * 16 + k][tx] = v;
+    }
   }
   __syncthreads();
 #pragma unroll
@@ -162,10 +172,10 @@ __global__ __launch_bounds__(256) void k_transpose_bf16(const uint16_t* __restri
   }
 }
 
-hipError_t launch_transpose_bf16(const uint16_t* src, int rows, int cols, uint16_t* dst,
-                                 int ld_dst, hipStream_t stream) {
+hipError_t launch_transpose_bf16(const uint16_t* src, const float* row_scale, int rows, int cols,
+                                 uint16_t* dst, int ld_dst, hipStream_t stream) {
   hipLaunchKernelGGL(k_transpose_bf16, dim3(cdiv(cols, 64), cdiv(rows, 64)), dim3(256), 0, stream,
-                     src, rows, cols, dst, ld_dst);
+                     src, row_scale, rows, cols, dst, ld_dst);
   return hipGetLastError();
 }
 

@@ -58,7 +58,7 @@ _SIGNATURES = {
     "coda_rms_bwd_reduce": ([_p, _c_int, _c_int, _p, _c_int, _p, _p], _c_int),
     "coda_gemm_rmsnorm_bwd": ([_p, _p, _p, _p, _p, _p, _p, _c_int, _c_int, _c_int, _p], _c_int),
     "coda_swiglu_bwd": ([_p, _p, _p, _c_int, _c_int, _p], _c_int),
-    "coda_transpose_bf16": ([_p, _c_int, _c_int, _p, _c_int, _p], _c_int),
+    "coda_transpose_bf16": ([_p, _p, _c_int, _c_int, _p, _c_int, _p], _c_int),
     "coda_rmsnorm_bwd": ([_p, _p, _p, _c_float, _p, _c_int, _c_int, _p], _c_int),
 }
 
@@ -256,10 +256,12 @@ def gemm_rmsnorm_bwd(dz, W2T, h, dY, r, c, dh, stream=None):
           _ptr(dh, _BF16, "dh"), M, N, K, _stream(stream))
 
 
-def transpose(src, dst, stream=None):
-    """dst[:, :rows] = src^T for src [rows, cols] (bf16); dst [cols, ld] may be
-    a column slice of a wider row-major matrix (its row stride is ld)."""
+def transpose(src, dst, row_scale=None, stream=None):
+    """dst[:, :rows] = src^T for src [rows, cols] (bf16), each source row
+    scaled by row_scale[row] first if given; dst [cols, ld] may be a column
+    slice of a wider row-major matrix (its row stride is ld)."""
     rows, cols = src.shape
+    _want(row_scale, (rows,), "row_scale")
     if dst.dim() != 2 or dst.shape[0] != cols or dst.shape[1] < rows or dst.stride(1) != 1:
         raise ValueError(f"dst {tuple(dst.shape)} cannot hold the transpose of {tuple(src.shape)}")
     if dst.dtype != _BF16 or not dst.is_cuda:
@@ -267,8 +269,8 @@ def transpose(src, dst, stream=None):
     ld = dst.stride(0)
     if ld < rows or dst.storage_offset() + (cols - 1) * ld + rows > dst.untyped_storage().nbytes() // 2:
         raise ValueError("dst's storage is too small for the transpose")
-    _call("coda_transpose_bf16", _ptr(src, _BF16, "src"), rows, cols, dst.data_ptr(), ld,
-          _stream(stream))
+    _call("coda_transpose_bf16", _ptr(src, _BF16, "src"), _ptr(row_scale, _F32, "row_scale"),
+          rows, cols, dst.data_ptr(), ld, _stream(stream))
 
 
 def swiglu_bwd(dout, gu, dz, stream=None):

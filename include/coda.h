@@ -246,10 +246,17 @@ int coda_gemm_rmsnorm_bwd(const void* dz, const void* W2T, const void* h, const 
 int coda_fold_gamma(const void* W, const float* gamma, void* W_out, int N, int K, void* stream);
 
 /* dst[c * ld_dst + r] = src[r * cols + c]: bf16 transpose of src [rows, cols]
- * into the first `rows` columns of dst [cols, ld_dst] (ld_dst >= rows), for
- * the transposed weight copies the backward GEMMs read (Wd^T, W'^T, Wo^T).
+ * into the first `rows` columns of dst [cols, ld_dst] (ld_dst >= rows).  With
+ * row_scale [rows] fp32 (else NULL) each row is scaled first and rounded once:
+ * dst[c * ld_dst + r] = bf16(src[r * cols + c] * row_scale[r]).
+ * Used for the transposed weight copies the backward GEMMs read (Wd^T, W'^T,
+ * Wo^T) and for the token-major operands of the weight gradients, which are
+ * plain GEMMs reducing over the tokens (coda_gemm_bf16):
+ *   dWd = dY^T out,  dW' = dz^T (r h) (row_scale = r: the RMS row scale moves
+ *   onto the reduction axis),  dWo = dh^T x.
  * Sizes: rows, cols >= 1; rows * cols and cols * ld_dst below 2^31. */
-int coda_transpose_bf16(const void* src, int rows, int cols, void* dst, int ld_dst, void* stream);
+int coda_transpose_bf16(const void* src, const float* row_scale, int rows, int cols, void* dst,
+                        int ld_dst, void* stream);
 
 /* rope_cos/rope_sin[p*(hd/2)+i] = cos/sin(p * theta^(-2i/hd)), angles and
  * trigonometry in fp64, stored fp32.  Sizes: max_pos >= 1, head_dim even. */

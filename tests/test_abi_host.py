@@ -130,9 +130,10 @@ def test_backward_validation(L):
     assert L.coda_swiglu_bwd(A16, A16, A16, 64, 12, None) == ERR_SHAPE
     assert L.coda_rmsnorm_bwd(A16, A16, A16, 1e-5, A16, 64, 32768, None) == ERR_SHAPE
     assert L.coda_rmsnorm_bwd(A16, A16, A16, -1.0, A16, 64, 256, None) == ERR_SHAPE
-    assert L.coda_transpose_bf16(A16, 4, 8, None, 4, None) == ERR_NULL
-    assert L.coda_transpose_bf16(A16, 4, 8, A16, 3, None) == ERR_SHAPE    # ld_dst < rows
-    assert L.coda_transpose_bf16(A16 + 1, 4, 8, A16, 4, None) == ERR_ALIGN
+    assert L.coda_transpose_bf16(A16, None, 4, 8, None, 4, None) == ERR_NULL
+    assert L.coda_transpose_bf16(A16, None, 4, 8, A16, 3, None) == ERR_SHAPE    # ld_dst < rows
+    assert L.coda_transpose_bf16(A16 + 1, None, 4, 8, A16, 4, None) == ERR_ALIGN
+    assert L.coda_transpose_bf16(A16, A16 + 2, 4, 8, A16, 4, None) == ERR_ALIGN
 
 
 def test_binding_checks_backward_shapes():

@@ -223,3 +223,77 @@ def test_mlp_1b_bwd_sampled_rows():
     check_against_oracle(got, ref, rows)
     for k in ("dz", "dh", "dx"):
         assert bool(torch.isfinite(got[k].float()).all()), k
+
+
+def run_weight_grads(w, fz):
+    """Weight gradients from the fused pass's tensors: token-major copies by
+    the transpose kernel (the RMS row scale applied while copying h), then
+    plain GEMMs reducing over the token rows."""
+    M, d, K1, ffn = (w.sizes[k] for k in ("M", "d", "K1", "ffn"))
+    bf = dict(dtype=torch.bfloat16, device=DEV)
+    x, dy = bf16_dev(w.arrays["x"]), bf16_dev(w.arrays["dy"])
+    hT, dzT = torch.empty(d, M, **bf), torch.empty(2 * ffn, M, **bf)
+    dyT, outT = torch.empty(d, M, **bf), torch.empty(ffn, M, **bf)
+    dhT, xT = torch.empty(d, M, **bf), torch.empty(K1, M, **bf)
+    ops.transpose(fz["h"], hT, row_scale=fz["r"])
+    ops.transpose(fz["dz"], dzT)
+    ops.transpose(dy, dyT)
+    ops.transpose(fz["out"], outT)
+    ops.transpose(fz["dh"], dhT)
+    ops.transpose(x, xT)
+    dW2, dWd, dWo = (torch.empty(2 * ffn, d, **bf), torch.empty(d, ffn, **bf),
+                     torch.empty(d, K1, **bf))
+    ops.gemm_bf16(dzT, hT, dW2)   # gradient of the folded [Wg'; Wu']
+    ops.gemm_bf16(dyT, outT, dWd)
+    ops.gemm_bf16(dhT, xT, dWo)
+    torch.cuda.synchronize()
+    return dict(dW2=dW2, dWd=dWd, dWo=dWo)
+
+
+def check_weight_grads(w, wg_, ref):
+    ffn = w.sizes["ffn"]
+    gamma = w.arrays["gamma"].astype(np.float64)[None, :]
+    dW2 = bf16_host(wg_["dW2"])
+    # the oracle differentiates the unfolded weights: dL/dW = dL/dW' diag(gamma)
+    errs = {"dwg": norm_err(dW2[:ffn] * gamma, ref["dwg"]),
+            "dwu": norm_err(dW2[ffn:] * gamma, ref["dwu"]),
+            "dwd": norm_err(bf16_host(wg_["dWd"]), ref["dwd"]),
+            "dwo": norm_err(bf16_host(wg_["dWo"]), ref["dwo"])}
+    say(f"weight gradient errors {errs}")
+    for k, e in errs.items():
+        assert e <= TOL_BF16, (k, e)
+
+
+def test_weight_grads_ragged_features():
+    """Weight gradients at M = 576 (the token count is the GEMM reduction, a
+    multiple of 64) with ragged feature counts, against the fp64 oracle."""
+    w = inputs.make_mlp_bwd(seed=6, M=576, d=448, K1=320, ffn=1056)
+    say("weight gradients M=576 d=448 K1=320 ffn=1056")
+    fz = run_fused(w)
+    check_weight_grads(w, run_weight_grads(w, fz), oracle_rows(w))
+
+
+def test_transpose_row_scale_exact():
+    """The scaled transpose rounds src * scale once (RNE) per element."""
+    rng = np.random.default_rng(7)
+    a = rng.standard_normal((130, 70)).astype(np.float32)
+    s = rng.uniform(0.5, 2.0, size=130).astype(np.float32)
+    bits = inputs.to_bf16_bits(a)
+    say("scaled transpose 130x70")
+    dst = torch.empty(70, 130, dtype=torch.bfloat16, device=DEV)
+    ops.transpose(bf16_dev(bits), dst, row_scale=f32_dev(s))
+    torch.cuda.synchronize()
+    # the product of a bf16 value and an fp32 scale, rounded to fp32 (as the
+    # kernel computes it), then to bf16
+    prod = (dec_bf16(bits) * s.astype(np.float64)[:, None]).astype(np.float32).astype(np.float64)
+    assert np.array_equal(bf16_host(dst), dec_bf16(bf16_encode_few(prod)).T)
+
+
+def test_mlp_1b_weight_grads_full():
+    """Weight gradients at the full 1B shape (sums over all 8192 tokens), against
+    the fp64 oracle of the whole sub-layer."""
+    w = inputs.make_workload("mlp_1b_bwd")
+    say("mlp_1b_bwd weight gradients, full size")
+    fz = run_fused(w)
+    wg_ = run_weight_grads(w, fz)
+    check_weight_grads(w, wg_, oracle_rows(w))
