@@ -359,12 +359,32 @@ def _mlp_bwd_row(torch, ops, inputs, stream, steps, warmup, bf, name="mlp_1b_bwd
         for f in bwd_k:
             f()
 
+    # weight gradients: token-major copies (the row scale r applied while
+    # copying h), then plain GEMMs reducing over the tokens
+    x_T, h_T, dy_T, dh_T = (torch.empty(n, M, **bf16) for n in (K1, d, d, d))
+    dz_T, o_T = torch.empty(2 * ffn, M, **bf16), torch.empty(ffn, M, **bf16)
+    dW2, dWd, dWo = (torch.empty(2 * ffn, d, **bf16), torch.empty(d, ffn, **bf16),
+                     torch.empty(d, K1, **bf16))
+
+    def dw():
+        ops.transpose(h, h_T, row_scale=r)
+        ops.transpose(dz, dz_T)
+        ops.transpose(dy, dy_T)
+        ops.transpose(o, o_T)
+        ops.transpose(dh, dh_T)
+        ops.transpose(x, x_T)
+        ops.gemm_bf16(dz_T, h_T, dW2)
+        ops.gemm_bf16(dy_T, o_T, dWd)
+        ops.gemm_bf16(dh_T, x_T, dWo)
+
     def train():
         fwd_save()
         bwd()
+        dw()
     fwd_save()
     ms_b = _events_time(torch, stream, bwd, steps, warmup)
     kb = _kernel_times(torch, stream, bwd_k, steps)
+    ms_w = _events_time(torch, stream, dw, steps, warmup)
     ms_t = _events_time(torch, stream, train, steps, warmup)
     # unfused: forward stores g|u from one plain GEMM (the backward reads it)
     y_u, h_u, n_u, G_u, dh_u = (torch.empty(M, d, **bf16) for _ in range(5))
@@ -388,29 +408,46 @@ def _mlp_bwd_row(torch, ops, inputs, stream, steps, warmup, bf, name="mlp_1b_bwd
         for f in bwd_uk:
             f()
 
+    n_T = torch.empty(d, M, **bf16)
+
+    def dw_u():  # the same GEMMs; the normalised n (with gamma) is stored here
+        ops.transpose(n_u, n_T)
+        ops.transpose(dz_u, dz_T)
+        ops.transpose(dy, dy_T)
+        ops.transpose(o_u, o_T)
+        ops.transpose(dh_u, dh_T)
+        ops.transpose(x, x_T)
+        ops.gemm_bf16(dz_T, n_T, dW2)
+        ops.gemm_bf16(dy_T, o_T, dWd)
+        ops.gemm_bf16(dh_T, x_T, dWo)
+
     def train_u():
         fwd_u()
         bwd_u()
+        dw_u()
     fwd_u()
     ms_bu = _events_time(torch, stream, bwd_u, steps, warmup)
     kbu = _kernel_times(torch, stream, bwd_uk, steps)
     ms_tu = _events_time(torch, stream, train_u, steps, warmup)
     fl_b = 2.0 * M * ffn * d + 2.0 * M * d * 2 * ffn + 2.0 * M * K1 * d
-    fl_t = fl_b + 2.0 * M * d * K1 + 2.0 * M * 2 * ffn * d
+    fl_w = 2.0 * M * 2 * ffn * d + 2.0 * M * d * ffn + 2.0 * M * d * K1
+    fl_t = fl_b + fl_w + 2.0 * M * d * K1 + 2.0 * M * 2 * ffn * d
     return {"workload": f"M={M}, d={d}, K1={K1}, ffn={ffn}: backward of the MLP sub-layer "
-                        "given dY (dx and dres), and forward (saving g|u) + backward",
+                        "given dY (dx and dres), its weight gradients, and the training step "
+                        "forward (saving g|u) + backward + weight gradients",
             "bwd_ms": round(ms_b, 4), "bwd_tflops": round(fl_b / ms_b / 1e9, 1),
             "bwd_pct_of_bf16_peak": round(100 * fl_b / ms_b / 1e9 / PEAK_BF16_TFLOPS, 2),
             "bwd_kernels_ms": dict(zip(("gemm_swiglu_bwd", "rms_bwd_reduce", "gemm_rmsnorm_bwd",
                                         "gemm_bf16_dx"), kb)),
-            "fwd_bwd_ms": round(ms_t, 4), "fwd_bwd_tflops": round(fl_t / ms_t / 1e9, 1),
+            "dw_ms": round(ms_w, 4), "dw_tflops": round(fl_w / ms_w / 1e9, 1),
+            "train_step_ms": round(ms_t, 4), "train_step_tflops": round(fl_t / ms_t / 1e9, 1),
             "unfused": {"bwd_ms": round(ms_bu, 4), "bwd_tflops": round(fl_b / ms_bu / 1e9, 1),
                         "bwd_speedup_fused_vs_unfused": round(ms_bu / ms_b, 3),
                         "bwd_kernels_ms": dict(zip(("gemm_bf16_dout", "swiglu_bwd",
                                                     "gemm_bf16_G", "rmsnorm_bwd",
                                                     "gemm_bf16_dx"), kbu)),
-                        "fwd_bwd_ms": round(ms_tu, 4),
-                        "fwd_bwd_speedup_fused_vs_unfused": round(ms_tu / ms_t, 3)}}
+                        "train_step_ms": round(ms_tu, 4),
+                        "train_step_speedup_fused_vs_unfused": round(ms_tu / ms_t, 3)}}
 
 
 def _kernel_times(torch, stream, fns, steps):

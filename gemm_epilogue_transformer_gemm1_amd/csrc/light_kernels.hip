@@ -172,10 +172,64 @@ __global__ __launch_bounds__(256) void k_transpose_bf16(const uint16_t* __restri
   }
 }
 
+// The same with 16-byte accesses on both sides, for rows % 8 == cols % 8 ==
+// ld_dst % 8 == 0 and 16-byte aligned pointers: a thread loads 8 consecutive
+// elements of a source row, and stores 8 consecutive elements of a
+// destination row gathered from a column of the LDS tile.
+__global__ __launch_bounds__(256) void k_transpose_bf16_v8(const uint16_t* __restrict__ src,
+                                                           const float* __restrict__ row_scale,
+                                                           int rows, int cols,
+                                                           uint16_t* __restrict__ dst,
+                                                           int ld_dst) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];  // 144-byte rows
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int q = (int)threadIdx.x + k * 256;  // 64 rows x 8 chunks of 8
+    const int rr = q >> 3, cc = (q & 7) * 8;
+    const int r = r0 + rr, c = c0 + cc;
+    i32x4_t v = {0, 0, 0, 0};
+    if (r < rows && c < cols) {
+      v = *(const i32x4_t*)(src + (size_t)r * cols + c);
+      if (row_scale) {
+        const float sc = row_scale[r];
+        float f[8];
+        unpack_bf16x4(u32x2_t{(unsigned)v.x, (unsigned)v.y}, f);
+        unpack_bf16x4(u32x2_t{(unsigned)v.z, (unsigned)v.w}, f + 4);
+        const u32x2_t lo = pack_bf16x4(f[0] * sc, f[1] * sc, f[2] * sc, f[3] * sc);
+        const u32x2_t hi = pack_bf16x4(f[4] * sc, f[5] * sc, f[6] * sc, f[7] * sc);
+        v = i32x4_t{(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
+      }
+    }
+    *(i32x4_t*)&tile[rr][cc] = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int q = (int)threadIdx.x + k * 256;  // 64 destination rows x 8 chunks of 8
+    const int oc = q >> 3, orr = (q & 7) * 8;
+    const int c = c0 + oc, r = r0 + orr;
+    if (c < cols && r < rows) {
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        w[e] = (uint32_t)tile[orr + 2 * e][oc] | ((uint32_t)tile[orr + 2 * e + 1][oc] << 16);
+      *(i32x4_t*)(dst + (size_t)c * ld_dst + r) = i32x4_t{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+    }
+  }
+}
+
 hipError_t launch_transpose_bf16(const uint16_t* src, const float* row_scale, int rows, int cols,
                                  uint16_t* dst, int ld_dst, hipStream_t stream) {
-  hipLaunchKernelGGL(k_transpose_bf16, dim3(cdiv(cols, 64), cdiv(rows, 64)), dim3(256), 0, stream,
-                     src, row_scale, rows, cols, dst, ld_dst);
+  const bool v8 = rows % 8 == 0 && cols % 8 == 0 && ld_dst % 8 == 0 &&
+                  (reinterpret_cast<uintptr_t>(src) & 15) == 0 &&
+                  (reinterpret_cast<uintptr_t>(dst) & 15) == 0;
+  if (v8)
+    hipLaunchKernelGGL(k_transpose_bf16_v8, dim3(cdiv(cols, 64), cdiv(rows, 64)), dim3(256), 0,
+                       stream, src, row_scale, rows, cols, dst, ld_dst);
+  else
+    hipLaunchKernelGGL(k_transpose_bf16, dim3(cdiv(cols, 64), cdiv(rows, 64)), dim3(256), 0,
+                       stream, src, row_scale, rows, cols, dst, ld_dst);
   return hipGetLastError();
 }
 

@@ -109,7 +109,7 @@ def check_against_oracle(got, ref, rows=None, w=None):
 
 def test_transpose_exact():
     rng = np.random.default_rng(0)
-    for rows, cols in ((1, 1), (70, 130), (257, 64), (64, 1000)):
+    for rows, cols in ((1, 1), (70, 130), (257, 64), (64, 1000), (136, 200), (8, 8)):
         say(f"transpose {rows}x{cols}")
         a = bf16_dev(inputs.to_bf16_bits(rng.standard_normal((rows, cols)).astype(np.float32)))
         dst = torch.zeros(cols, rows + 24, dtype=torch.bfloat16, device=DEV)
@@ -273,14 +273,16 @@ def test_weight_grads_ragged_features():
     check_weight_grads(w, run_weight_grads(w, fz), oracle_rows(w))
 
 
-def test_transpose_row_scale_exact():
-    """The scaled transpose rounds src * scale once (RNE) per element."""
+@pytest.mark.parametrize("rows,cols", [(130, 70), (128, 72), (8, 1024)])
+def test_transpose_row_scale_exact(rows, cols):
+    """The scaled transpose rounds src * scale once (RNE) per element (ragged
+    sizes take the element-wise kernel, multiples of 8 the 16-byte one)."""
     rng = np.random.default_rng(7)
-    a = rng.standard_normal((130, 70)).astype(np.float32)
-    s = rng.uniform(0.5, 2.0, size=130).astype(np.float32)
+    a = rng.standard_normal((rows, cols)).astype(np.float32)
+    s = rng.uniform(0.5, 2.0, size=rows).astype(np.float32)
     bits = inputs.to_bf16_bits(a)
-    say("scaled transpose 130x70")
-    dst = torch.empty(70, 130, dtype=torch.bfloat16, device=DEV)
+    say(f"scaled transpose {rows}x{cols}")
+    dst = torch.empty(cols, rows, dtype=torch.bfloat16, device=DEV)
     ops.transpose(bf16_dev(bits), dst, row_scale=f32_dev(s))
     torch.cuda.synchronize()
     # the product of a bf16 value and an fp32 scale, rounded to fp32 (as the
