@@ -192,9 +192,10 @@ int coda_gemm_block_lse(const void* X, const void* W, const float* r, const int3
  * The sequence is
  *   coda_gemm_rowscale_swiglu_save  (forward, keeps z)
  *   coda_gemm_swiglu_bwd -> coda_rms_bwd_reduce -> coda_gemm_rmsnorm_bwd
- * and then dx = dh Wo is a plain GEMM with Wo^T (coda_gemm_bf16).  Weight
- * gradients (reductions over tokens) are plain GEMMs with no epilogue and are
- * not part of this library.
+ * and then dx = dh Wo is a plain GEMM with Wo^T (coda_gemm_bf16).  The weight
+ * gradients reduce over the tokens and have no epilogue: token-major copies
+ * (coda_transpose_bf16; the row scale r is applied while copying h) and plain
+ * GEMMs (coda_gemm_bf16) give dWd = dY^T out, dW' = dz^T (r h) and dWo = dh^T x.
  */
 
 /* coda_gemm_rowscale_swiglu (bf16) that also stores the pre-activations for
