@@ -317,24 +317,30 @@ def _mlp_bwd_row(torch, ops, inputs, stream, steps, warmup, bf, name="mlp_1b_bwd
     print(f"[bench] {name}", file=sys.stderr, flush=True)
     w = inputs.make_workload(name, **sizes)
     M, d, K1, ffn = (w.sizes[k] for k in ("M", "d", "K1", "ffn"))
-    x, res, wo, wg, wu, wd, dy = (bf(w.arrays[k]) for k in
-                                  ("x", "res", "w1", "wg", "wu", "wd", "dy"))
+    x, res, wo, wd, dy = (bf(w.arrays[k]) for k in ("x", "res", "w1", "wd", "dy"))
+    # gate and up weights live in one [2 ffn, d] buffer (the unfused gate|up GEMM
+    # reads it whole, the fused path its two halves)
+    wgu = torch.cat([bf(w.arrays["wg"]), bf(w.arrays["wu"])], 0).contiguous()
+    wg, wu = wgu[:ffn], wgu[ffn:]
     gamma = torch.from_numpy(w.arrays["gamma"]).to(dev)
     del w
     bf16 = dict(dtype=torch.bfloat16, device=dev)
-    # weight preparation (untimed): gamma folded, transposed copies
+    # weight preparation: gamma folded, transposed copies for the backward
+    # GEMMs.  Weights change every training step, so the training-step timings
+    # below include it (both sequences need the same copies); the backward and
+    # weight-gradient timings alone do not.
     wg_f, wu_f = torch.empty_like(wg), torch.empty_like(wu)
-    ops.fold_gamma(wg, gamma, wg_f)
-    ops.fold_gamma(wu, gamma, wu_f)
-    WdT = torch.empty(ffn, d, **bf16)
-    ops.transpose(wd, WdT)
-    W2T = torch.empty(d, 2 * ffn, **bf16)
-    ops.transpose(wg_f, W2T[:, :ffn])
-    ops.transpose(wu_f, W2T[:, ffn:])
-    WoT = torch.empty(K1, d, **bf16)
-    ops.transpose(wo, WoT)
-    wgu = torch.cat([wg, wu], 0).contiguous()
-    del wd, wg, wu
+    WdT, W2T, WoT = (torch.empty(ffn, d, **bf16), torch.empty(d, 2 * ffn, **bf16),
+                     torch.empty(K1, d, **bf16))
+
+    def prep():
+        ops.fold_gamma(wg, gamma, wg_f)
+        ops.fold_gamma(wu, gamma, wu_f)
+        ops.transpose(wd, WdT)
+        ops.transpose(wg_f, W2T[:, :ffn])
+        ops.transpose(wu_f, W2T[:, ffn:])
+        ops.transpose(wo, WoT)
+    prep()
     h = torch.empty(M, d, **bf16)
     P = torch.empty(ops.rms_tiles(d), M, dtype=torch.float32, device=dev)
     r = torch.empty(M, dtype=torch.float32, device=dev)
@@ -378,6 +384,7 @@ def _mlp_bwd_row(torch, ops, inputs, stream, steps, warmup, bf, name="mlp_1b_bwd
         ops.gemm_bf16(dh_T, x_T, dWo)
 
     def train():
+        prep()
         fwd_save()
         bwd()
         dw()
@@ -385,6 +392,7 @@ def _mlp_bwd_row(torch, ops, inputs, stream, steps, warmup, bf, name="mlp_1b_bwd
     ms_b = _events_time(torch, stream, bwd, steps, warmup)
     kb = _kernel_times(torch, stream, bwd_k, steps)
     ms_w = _events_time(torch, stream, dw, steps, warmup)
+    ms_p = _events_time(torch, stream, prep, steps, warmup)
     ms_t = _events_time(torch, stream, train, steps, warmup)
     # unfused: forward stores g|u from one plain GEMM (the backward reads it)
     y_u, h_u, n_u, G_u, dh_u = (torch.empty(M, d, **bf16) for _ in range(5))
@@ -422,6 +430,7 @@ def _mlp_bwd_row(torch, ops, inputs, stream, steps, warmup, bf, name="mlp_1b_bwd
         ops.gemm_bf16(dh_T, x_T, dWo)
 
     def train_u():
+        prep()
         fwd_u()
         bwd_u()
         dw_u()
@@ -434,12 +443,13 @@ def _mlp_bwd_row(torch, ops, inputs, stream, steps, warmup, bf, name="mlp_1b_bwd
     fl_t = fl_b + fl_w + 2.0 * M * d * K1 + 2.0 * M * 2 * ffn * d
     return {"workload": f"M={M}, d={d}, K1={K1}, ffn={ffn}: backward of the MLP sub-layer "
                         "given dY (dx and dres), its weight gradients, and the training step "
-                        "forward (saving g|u) + backward + weight gradients",
+                        "(weight preparation, forward saving g|u, backward, weight gradients)",
             "bwd_ms": round(ms_b, 4), "bwd_tflops": round(fl_b / ms_b / 1e9, 1),
             "bwd_pct_of_bf16_peak": round(100 * fl_b / ms_b / 1e9 / PEAK_BF16_TFLOPS, 2),
             "bwd_kernels_ms": dict(zip(("gemm_swiglu_bwd", "rms_bwd_reduce", "gemm_rmsnorm_bwd",
                                         "gemm_bf16_dx"), kb)),
             "dw_ms": round(ms_w, 4), "dw_tflops": round(fl_w / ms_w / 1e9, 1),
+            "weight_prep_ms": round(ms_p, 4),
             "train_step_ms": round(ms_t, 4), "train_step_tflops": round(fl_t / ms_t / 1e9, 1),
             "unfused": {"bwd_ms": round(ms_bu, 4), "bwd_tflops": round(fl_b / ms_bu / 1e9, 1),
                         "bwd_speedup_fused_vs_unfused": round(ms_bu / ms_b, 3),
