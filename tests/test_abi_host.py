@@ -183,3 +183,14 @@ def test_binding_checks_forward_shapes(L):
         ops.rmsnorm(h, torch.zeros(255, dtype=f32), 1e-5, h)
     with pytest.raises(ValueError, match="shape"):
         ops.swiglu(torch.zeros(64, 512, dtype=bf), torch.zeros(64, 512, dtype=bf))
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU; asked for more it exits with a message
+    (before touching torch or a device)."""
+    import subprocess
+    import sys
+    p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=60)
+    assert p.returncode == 2
+    assert "one GPU" in p.stderr
