@@ -1,0 +1,36 @@
+"""Host-side pieces of bench.py (no GPU): step-time percentiles, and the
+committed rocprofv3 records (HBM traffic, shader clock) that the bench line
+reports only while the GEMM kernel sources are the ones they were measured
+on."""
+import importlib.util
+import os
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def bench():
+    spec = importlib.util.spec_from_file_location("bench", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_percentiles(bench):
+    p = bench.pctl([1.0, 2.0, 3.0, 4.0, 5.0])
+    assert p == {"median": 3.0, "p10": 1.4, "p90": 4.6}
+
+
+def test_records_follow_the_kernel_sources(bench, monkeypatch):
+    traffic = bench.measured_traffic("gemm_rowscale_swiglu")
+    clock = bench.measured_clock_ghz("gemm_rowscale_swiglu")
+    # the committed records were taken on the committed sources
+    assert isinstance(traffic, int) and traffic > 0
+    assert clock is not None and 1.0 < clock < 2.5
+    # any change to the sources voids them
+    monkeypatch.setattr(bench, "kernel_sources_sha256", lambda: "0" * 64)
+    assert bench.measured_traffic("gemm_rowscale_swiglu") is None
+    assert bench.measured_clock_ghz("gemm_rowscale_swiglu") is None
+    assert bench.measured_traffic("no_such_kernel") is None
