@@ -175,7 +175,9 @@ __global__ __launch_bounds__(256) void k_transpose_bf16(const uint16_t* __restri
 // The same with 16-byte accesses on both sides, for rows % 8 == cols % 8 ==
 // ld_dst % 8 == 0 and 16-byte aligned pointers: a thread loads 8 consecutive
 // elements of a source row, and stores 8 consecutive elements of a
-// destination row gathered from a column of the LDS tile.
+// destination row gathered from a column of the LDS tile.  The 16-byte
+// chunks of tile row rr are rotated by rr / 8: the lanes gathering one column
+// read rows 8 apart, which would otherwise all fall in the same bank.
 __global__ __launch_bounds__(256) void k_transpose_bf16_v8(const uint16_t* __restrict__ src,
                                                            const float* __restrict__ row_scale,
                                                            int rows, int cols,
@@ -201,7 +203,7 @@ __global__ __launch_bounds__(256) void k_transpose_bf16_v8(const uint16_t* __res
         v = i32x4_t{(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
       }
     }
-    *(i32x4_t*)&tile[rr][cc] = v;
+    *(i32x4_t*)&tile[rr][(((cc >> 3) + (rr >> 3)) & 7) * 8] = v;
   }
   __syncthreads();
 #pragma unroll
@@ -210,10 +212,11 @@ __global__ __launch_bounds__(256) void k_transpose_bf16_v8(const uint16_t* __res
     const int oc = q >> 3, orr = (q & 7) * 8;
     const int c = c0 + oc, r = r0 + orr;
     if (c < cols && r < rows) {
+      const int pos = ((((oc >> 3) + (orr >> 3)) & 7) * 8) + (oc & 7);  // rows orr..orr+7
       uint32_t w[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        w[e] = (uint32_t)tile[orr + 2 * e][oc] | ((uint32_t)tile[orr + 2 * e + 1][oc] << 16);
+        w[e] = (uint32_t)tile[orr + 2 * e][pos] | ((uint32_t)tile[orr + 2 * e + 1][pos] << 16);
       *(i32x4_t*)(dst + (size_t)c * ld_dst + r) = i32x4_t{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
     }
   }
