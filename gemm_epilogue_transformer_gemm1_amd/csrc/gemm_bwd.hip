@@ -39,29 +39,75 @@ __device__ __forceinline__ int bwd_tile_tid() {
 // above 47, so the next tile's first wait is vmcnt(63).
 constexpr int kBwdEpiVmem = 47;
 
-// Two bf16 operand tiles of the epilogue, [M, ld] each at column offsets
-// col_a and col_b, loaded per token subtile i as 8 runs of 4 features per
-// lane (8 bytes).  Subtiles 0..2 are loaded during the last two stages of the
-// mainloop, subtile i + 3 while subtile i is processed.  Feature runs past N
-// read at an out-of-range offset (zeros); rows past M lie beyond the buffer,
-// which starts at the tile's first row.
+// Two bf16 operand tiles of the epilogue, [M, ld] each (buffers rs_a / rs_b
+// at column offsets col_a / col_b), loaded per token subtile i.  The
+// accumulator layout wants 4-feature runs (8 bytes) per lane; instead each
+// lane loads 16 bytes, 8 features of one row: for the feature subtile pair
+// (2 jp, 2 jp + 1), lanes of even 16-lane groups g read subtile 2 jp at
+// features 8 (g / 2) .. + 7 (their own run and that of group g + 1), lanes of
+// odd groups subtile 2 jp + 1 (the run of group g - 1 and their own), and
+// `runs` swaps the foreign halves between lanes 16 apart.  That halves the
+// vector memory instructions per subtile (8 instead of 16), so the operands
+// of three subtiles ahead and the stores between them stay within the 63
+// operations the wait counter can track and a wait for a subtile's operands
+// does not also wait for older stores.  Subtiles 0..2 are loaded during the
+// last two stages of the mainloop, subtile i + 3 while subtile i is processed.
+// Feature runs at or past N read at an out-of-range offset (zeros); rows past
+// M lie beyond the buffers, which start at the tile's first row.
 struct EpiPair {
-  __amdgpu_buffer_rsrc_t rs;
+  __amdgpu_buffer_rsrc_t rs_a, rs_b;
   uint32_t ld, col_a, col_b;
+  int nw0, N, wm, lane;
+  u32x4_t a[8][4], b[8][4];
+
+  __device__ __forceinline__ uint32_t off(int i, int jp, uint32_t col) const {
+    const int gq = lane >> 4;
+    const int n = nw0 + 16 * (2 * jp + (gq & 1));
+    const uint32_t ml = (uint32_t)(wm * 128 + i * 16 + (lane & 15));
+    return n < N ? (ml * ld + col + (uint32_t)(n + 8 * (gq >> 1))) * 2u : kOobOffset;
+  }
+  __device__ __forceinline__ void load(int i) {
+#pragma unroll
+    for (int jp = 0; jp < 4; ++jp) {
+      a[i][jp] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_a, off(i, jp, col_a), 0, 0));
+      b[i][jp] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_b, off(i, jp, col_b), 0, 0));
+    }
+  }
+  // This lane's runs of subtiles 2 jp (out[0]) and 2 jp + 1 (out[1]) from the
+  // 16 bytes it loaded; all 64 lanes must take part (lane shuffle).
+  __device__ __forceinline__ static void runs(const u32x4_t& v, bool godd, u32x2_t (&out)[2]) {
+    const u32x2_t lo = {v.x, v.y}, hi = {v.z, v.w};
+    const u32x2_t sd = godd ? lo : hi;
+    const u32x2_t rx = {(unsigned)__shfl_xor((int)sd.x, 16, 64),
+                        (unsigned)__shfl_xor((int)sd.y, 16, 64)};
+    out[0] = godd ? rx : lo;
+    out[1] = godd ? hi : rx;
+  }
+};
+
+// The RMSNorm-backward epilogue keeps 8-byte operand loads (one 4-feature run
+// per lane, the accumulator layout itself): with the 16-byte form its extra
+// exchange temporaries push the kernel past the register file.  Its epilogue
+// is small next to its mainloop (K = 2 ffn).  Same subtile schedule as
+// EpiPair; rows past M lie beyond the buffers.
+struct EpiPairNarrow {
+  __amdgpu_buffer_rsrc_t rs_a, rs_b;
+  uint32_t ld;
   int nw0, N, wm, lane;
   u32x2_t a[8][8], b[8][8];
 
-  __device__ __forceinline__ uint32_t off(int i, int j, uint32_t col) const {
+  __device__ __forceinline__ uint32_t off(int i, int j) const {
     const int n = nw0 + 16 * j;
     if (n >= N) return kOobOffset;  // wave-uniform
     const uint32_t ml = (uint32_t)(wm * 128 + i * 16 + (lane & 15));
-    return (ml * ld + col + (uint32_t)(n + 4 * (lane >> 4))) * 2u;
+    return (ml * ld + (uint32_t)(n + 4 * (lane >> 4))) * 2u;
   }
   __device__ __forceinline__ void load(int i) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      a[i][j] = __builtin_amdgcn_raw_buffer_load_b64(rs, off(i, j, col_a), 0, 0);
-      b[i][j] = __builtin_amdgcn_raw_buffer_load_b64(rs, off(i, j, col_b), 0, 0);
+      const uint32_t o = off(i, j);
+      a[i][j] = __builtin_amdgcn_raw_buffer_load_b64(rs_a, o, 0, 0);
+      b[i][j] = __builtin_amdgcn_raw_buffer_load_b64(rs_b, o, 0, 0);
     }
   }
 };
@@ -93,7 +139,8 @@ __device__ __forceinline__ void swiglu_bwd_tile(const SwigluBwdArgs& g, char* sm
   const int nw0 = n0 + wn * 128;
   const uint32_t rows_here = (uint32_t)min(kBM, M - m0);
   EpiPair z;
-  z.rs = make_rsrc(g.gu + (size_t)m0 * ld, rows_here * ld * 2u);
+  z.rs_a = make_rsrc(g.gu + (size_t)m0 * ld, rows_here * ld * 2u);
+  z.rs_b = z.rs_a;
   z.ld = ld;
   z.col_a = 0;
   z.col_b = (uint32_t)N;
@@ -116,13 +163,15 @@ __device__ __forceinline__ void swiglu_bwd_tile(const SwigluBwdArgs& g, char* sm
     float ps = 0.f;
 #pragma unroll
     for (int j0 = 0; j0 < 8; j0 += 2) {
-      u32x2_t pg[2], pu[2];
+      u32x2_t pg[2], pu[2], ga[2], ub[2];
+      EpiPair::runs(z.a[i][j0 / 2], godd, ga);
+      EpiPair::runs(z.b[i][j0 / 2], godd, ub);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int j = j0 + u;
         float gv[4], uv[4], dg[4], du[4];
-        unpack_bf16x4(z.a[i][j], gv);
-        unpack_bf16x4(z.b[i][j], uv);
+        unpack_bf16x4(ga[u], gv);
+        unpack_bf16x4(ub[u], uv);
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const float d = acc.v[j][i][v];
@@ -193,24 +242,15 @@ __device__ __forceinline__ void rmsnorm_bwd_tile(const RmsBwdArgs& g, char* smem
   const int nw0 = n0 + wn * 128;
   const uint32_t rows_here = (uint32_t)min(kBM, M - m0);
   // h and dY are separate [M, N] matrices: one pair, two buffers
-  EpiPair hy;
-  hy.rs = make_rsrc(g.h + (size_t)m0 * N, rows_here * (uint32_t)N * 2u);
+  EpiPairNarrow hy;
+  hy.rs_a = make_rsrc(g.h + (size_t)m0 * N, rows_here * (uint32_t)N * 2u);
+  hy.rs_b = make_rsrc(g.dY + (size_t)m0 * N, rows_here * (uint32_t)N * 2u);
   hy.ld = (uint32_t)N;
-  hy.col_a = 0;
-  hy.col_b = 0;
   hy.nw0 = nw0;
   hy.N = N;
   hy.wm = wm;
   hy.lane = lane;
-  const __amdgpu_buffer_rsrc_t yrsrc = make_rsrc(g.dY + (size_t)m0 * N, rows_here * (uint32_t)N * 2u);
-  auto load = [&](int i) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t o = hy.off(i, j, 0);
-      hy.a[i][j] = __builtin_amdgcn_raw_buffer_load_b64(hy.rs, o, 0, 0);
-      hy.b[i][j] = __builtin_amdgcn_raw_buffer_load_b64(yrsrc, o, 0, 0);
-    }
-  };
+  auto load = [&](int i) { hy.load(i); };
   float rr[8], cc[8];
   auto pre = [&] {
 #pragma unroll
