@@ -183,6 +183,36 @@ def test_bwd_epilogues_exact(M, d, ffn):
     assert np.array_equal(bf16_host(dh), dec_bf16(bf16_encode_few(ref)))
 
 
+@pytest.mark.parametrize("M,d,ffn", [
+    (200, 128, 1040),  # last tile: subtile 0 of a feature pair in range, subtile 1 past N
+    (200, 128, 1072),  # last tile: subtiles 0..2 in range, 3 past N
+    (70, 64, 16),      # a single 16-feature subtile
+])
+def test_swiglu_bwd_exact_partial_pairs(M, d, ffn):
+    """SwiGLU-backward epilogue where a feature width that is a multiple of 16
+    but not of 32 leaves one subtile of the epilogue's 32-feature load pairs
+    past N: exact values as in test_bwd_epilogues_exact; dz and the partial
+    sums bit for bit."""
+    rng = np.random.default_rng(7 * M + ffn)
+    dy, wdT = _ints(rng, (M, d), -1, 1), _ints(rng, (ffn, d), -1, 1)
+    g = 64.0 * rng.integers(0, 2, size=(M, ffn)).astype(np.float32)
+    u = _ints(rng, (M, ffn), -1, 2)
+    say(f"exact SwiGLU backward, partial feature pairs M={M} d={d} ffn={ffn}")
+    gu_np = np.concatenate([g, u], axis=1)
+    dY, WdT, GU = (bf16_dev(inputs.to_bf16_bits(v)) for v in (dy, wdT, gu_np))
+    dz = torch.empty(M, 2 * ffn, dtype=torch.bfloat16, device=DEV)
+    pdot = torch.empty(ops.rms_tiles(ffn), M, dtype=torch.float32, device=DEV)
+    ops.gemm_swiglu_bwd(dY, WdT, GU, dz, pdot)
+    torch.cuda.synchronize()
+    dout = dy.astype(np.float64) @ wdT.astype(np.float64).T
+    dg, du = oracle.swiglu_grad(dout, g, u)
+    assert np.array_equal(bf16_host(dz), dec_bf16(bf16_encode_few(np.concatenate([dg, du], axis=1))))
+    width = ops.rms_tile_width()
+    ref_p = np.stack([np.sum((dg * g + du * u)[:, t * width:(t + 1) * width], axis=1)
+                      for t in range(ops.rms_tiles(ffn))])
+    assert np.array_equal(f32_host(pdot), ref_p)
+
+
 def test_bwd_chain_ragged():
     """Forward (saving z) and the whole backward chain on a ragged shape with
     several tiles in every dimension, against the fp64 oracle."""
