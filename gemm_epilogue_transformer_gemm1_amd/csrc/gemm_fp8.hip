@@ -52,21 +52,37 @@ __global__ __launch_bounds__(kThreads, 1) void k_residual_partialrms_fp8(
     const TileCoord nc = has_next ? map_tile(t + gridDim.x, gm, gn, 8) : tc;
     ch.next = MainloopSrc{A, W, nullptr, M, N, K, nc.tm * kBM, nc.tn * kBN};
     const int nw0 = n0 + wn * 128;
-    // the residual tile (16 runs of 4 features x 4 token subtiles per lane)
-    // is loaded at the start of the epilogue into the registers the fragments
-    // used (loaded during the last stages it would make their waits longer
-    // and push the mainloop into spills)
-    u32x2_t rq[4][16];
+    // The residual tile is loaded at the start of the epilogue into the
+    // registers the fragments used (loaded during the last stages it would
+    // make their waits longer and push the mainloop into spills).  Lanes L
+    // and L + 32 hold the runs 8g + 0..3 and 8g + 4..7 of one row in each
+    // 32-feature block; for a pair of runs (gp, gp + 1) lane L loads the 16
+    // bytes of run gp (its own half and lane L + 32's) and lane L + 32 those
+    // of run gp + 1, and `res_runs` swaps the foreign halves: 32 loads of 16
+    // bytes per lane instead of 64 of 8.  Column starts are clamped to N - 8
+    // and rows to M - 1 (those values are never used).
+    u32x4_t rq[4][8];
+    const bool hi = lane >= 32;
     auto load_res = [&](int i0) {
 #pragma unroll
       for (int i = i0; i < i0 + 2; ++i) {
         const size_t row = (size_t)min(m0 + wm * 128 + i * 32 + (lane & 31), M - 1) * (size_t)N;
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int n = min(nw0 + (q >> 2) * 32 + (q & 3) * 8 + g4, N - 4);
-          rq[i][q] = *(const u32x2_t*)(res + row + n);
+        for (int q = 0; q < 8; ++q) {  // q = 2 j + gp / 2
+          const int n = min(nw0 + (q >> 1) * 32 + ((q & 1) * 2 + (hi ? 1 : 0)) * 8, N - 8);
+          rq[i][q] = *(const u32x4_t*)(res + row + n);
         }
       }
+    };
+    // this lane's runs gp (out[0]) and gp + 1 (out[1]) from its 16 bytes;
+    // all 64 lanes take part (lane shuffle)
+    auto res_runs = [&](const u32x4_t& v, u32x2_t (&out)[2]) {
+      const u32x2_t lo2 = {v.x, v.y}, hi2 = {v.z, v.w};
+      const u32x2_t sd = hi ? lo2 : hi2;
+      const u32x2_t rx = {(unsigned)__shfl_xor((int)sd.x, 32, 64),
+                          (unsigned)__shfl_xor((int)sd.y, 32, 64)};
+      out[0] = hi ? rx : lo2;
+      out[1] = hi ? hi2 : rx;
     };
     Acc8 acc;
     mainloop_fp8<false, kGemm1Stores8>(acc, smem, MainloopSrc{A, W, nullptr, M, N, K, m0, n0},
@@ -86,57 +102,66 @@ __global__ __launch_bounds__(kThreads, 1) void k_residual_partialrms_fp8(
     const __amdgpu_buffer_rsrc_t hrsrc = make_rsrc(h + (size_t)m0 * N, rows_here * (uint32_t)N * 2u);
     const __amdgpu_buffer_rsrc_t qrsrc =
         make_rsrc(h8 ? h8 + (size_t)m0 * N : nullptr, h8 ? rows_here * (uint32_t)N : 0u);
-    const bool hi = lane >= 32;
+    // Partial statistics leave out features at or past N (one select per
+    // value; a branch to a mask-free copy of this code for full-width waves
+    // makes the register allocator copy the accumulators).
+    {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ml = wm * 128 + i * 32 + (lane & 31);  // row within the tile
-      const bool mv = m0 + ml < M;
-      const uint32_t erow = (uint32_t)ml * (uint32_t)N;
-      float ss = 0.f, amax = 0.f;
+      for (int i = 0; i < 4; ++i) {
+        const int ml = wm * 128 + i * 32 + (lane & 31);  // row within the tile
+        const bool mv = m0 + ml < M;
+        const uint32_t erow = (uint32_t)ml * (uint32_t)N;
+        float ss = 0.f, amax = 0.f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        u32x2_t hb[4];
-        uint32_t qb[4];
+        for (int j = 0; j < 4; ++j) {
+          u32x2_t hb[4], rr[2][2];  // rr[gp / 2][g - gp]: residual run g
+          uint32_t qb[4];
+          res_runs(rq[i][2 * j], rr[0]);
+          res_runs(rq[i][2 * j + 1], rr[1]);
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const bool nv = nw0 + j * 32 + g * 8 + g4 < N;
-          float rv[4], hv[4];
-          unpack_bf16x4(rq[i][j * 4 + g], rv);
+          for (int g = 0; g < 4; ++g) {
+            const bool nv = nw0 + j * 32 + g * 8 + g4 < N;
+            float rv[4], hv[4];
+            unpack_bf16x4(rr[g >> 1][g & 1], rv);
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            hv[v] = rv[v] + acc.v[j][i][g * 4 + v] * scale;
-            ss += nv ? hv[v] * hv[v] : 0.f;
-            amax = nv ? fmaxf(amax, fabsf(hv[v])) : amax;
+            for (int v = 0; v < 4; ++v) {
+              hv[v] = rv[v] + acc.v[j][i][g * 4 + v] * scale;
+              const float hm = nv ? hv[v] : 0.f;
+              ss = __builtin_fmaf(hm, hm, ss);
+              // max(amax, |hm|) in one instruction (fmaxf would first
+              // canonicalise both operands)
+              asm("v_max_f32_e64 %0, %1, |%2|" : "=v"(amax) : "v"(amax), "v"(hm));
+            }
+            hb[g] = pack_bf16x4(hv[0], hv[1], hv[2], hv[3]);
+            qb[g] = pack_e4m3x4_sat(hv[0] * inv_s8, hv[1] * inv_s8, hv[2] * inv_s8, hv[3] * inv_s8);
           }
-          hb[g] = pack_bf16x4(hv[0], hv[1], hv[2], hv[3]);
-          qb[g] = pack_e4m3x4_sat(hv[0] * inv_s8, hv[1] * inv_s8, hv[2] * inv_s8, hv[3] * inv_s8);
-        }
 #pragma unroll
-        for (int gp = 0; gp < 4; gp += 2) {  // h: runs gp (lane L) and gp + 1 (lane L + 32)
-          const int n = nw0 + j * 32 + (gp + (hi ? 1 : 0)) * 8;
-          const u32x2_t hs = hi ? hb[gp] : hb[gp + 1];
-          const u32x2_t hr = {(unsigned)__shfl_xor((int)hs.x, 32, 64),
-                              (unsigned)__shfl_xor((int)hs.y, 32, 64)};
-          store16(hrsrc,
-                  hi ? u32x4_t{hr.x, hr.y, hb[gp + 1].x, hb[gp + 1].y}
-                     : u32x4_t{hb[gp].x, hb[gp].y, hr.x, hr.y},
-                  (mv && n < N) ? (erow + (uint32_t)n) * 2u : kOobOffset);
+          for (int gp = 0; gp < 4; gp += 2) {  // h: runs gp (lane L) and gp + 1 (lane L + 32)
+            const int n = nw0 + j * 32 + (gp + (hi ? 1 : 0)) * 8;
+            const u32x2_t hs = hi ? hb[gp] : hb[gp + 1];
+            const u32x2_t hr = {(unsigned)__shfl_xor((int)hs.x, 32, 64),
+                                (unsigned)__shfl_xor((int)hs.y, 32, 64)};
+            store16(hrsrc,
+                    hi ? u32x4_t{hr.x, hr.y, hb[gp + 1].x, hb[gp + 1].y}
+                       : u32x4_t{hb[gp].x, hb[gp].y, hr.x, hr.y},
+                    (mv && n < N) ? (erow + (uint32_t)n) * 2u : kOobOffset);
+          }
+          if (h8) {  // lane L: features 0..15 of the block, lane L + 32: 16..31
+            const int n = nw0 + j * 32 + (hi ? 16 : 0);
+            const uint32_t q0 = hi ? qb[0] : qb[2], q1 = hi ? qb[1] : qb[3];
+            const uint32_t r0 = (unsigned)__shfl_xor((int)q0, 32, 64);
+            const uint32_t r1 = (unsigned)__shfl_xor((int)q1, 32, 64);
+            store16(qrsrc, hi ? u32x4_t{r0, qb[2], r1, qb[3]} : u32x4_t{qb[0], r0, qb[1], r1},
+                    (mv && n < N) ? erow + (uint32_t)n : kOobOffset);
+          }
         }
-        if (h8) {  // lane L: features 0..15 of the block, lane L + 32: 16..31
-          const int n = nw0 + j * 32 + (hi ? 16 : 0);
-          const uint32_t q0 = hi ? qb[0] : qb[2], q1 = hi ? qb[1] : qb[3];
-          const uint32_t r0 = (unsigned)__shfl_xor((int)q0, 32, 64);
-          const uint32_t r1 = (unsigned)__shfl_xor((int)q1, 32, 64);
-          store16(qrsrc, hi ? u32x4_t{r0, qb[2], r1, qb[3]} : u32x4_t{qb[0], r0, qb[1], r1},
-                  (mv && n < N) ? erow + (uint32_t)n : kOobOffset);
+        ss += __shfl_xor(ss, 32, 64);
+        amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+        if (mv && lane < 32 && nw0 < N) {
+          const size_t tt = (size_t)(nw0 / kRmsTileWidth);
+          psum[tt * M + m0 + ml] = ss;
+          if (pamax) pamax[tt * M + m0 + ml] = amax;
         }
-      }
-      ss += __shfl_xor(ss, 32, 64);
-      amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
-      if (mv && lane < 32 && nw0 < N) {
-        const size_t tt = (size_t)(nw0 / kRmsTileWidth);
-        psum[tt * M + m0 + ml] = ss;
-        if (pamax) pamax[tt * M + m0 + ml] = amax;
       }
     }
     prefetched = has_next;
