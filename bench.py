@@ -31,7 +31,10 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=100,
+                   help="untimed steps (fused and unfused sequence each) before timing; the "
+                        "shader clock settles over the first ~35 ms of sustained load, so the "
+                        "default covers about 100 ms")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-rows", action="store_true",
                    help="skip timing the attention-input, LM-head and fp8 workloads")
@@ -40,7 +43,7 @@ def parse():
                         "copy kernel of known size, to scale HBM byte counters)")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="approximate CPU time budget of the oracle baseline")
-    p.add_argument("--row-min-ms", type=float, default=40.0,
+    p.add_argument("--row-min-ms", type=float, default=60.0,
                    help="minimum GPU time of the warm-up and of the timed steps of each "
                         "other_rows workload (0: exactly --steps / 3 warm-up steps)")
     p.add_argument("--no-cold", action="store_true",
@@ -49,7 +52,7 @@ def parse():
     return p.parse_args()
 
 
-_ROW_MIN_MS = 40.0
+_ROW_MIN_MS = 60.0
 
 
 def main():
