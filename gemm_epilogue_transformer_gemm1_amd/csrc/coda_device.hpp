@@ -12,7 +12,6 @@ namespace coda {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
@@ -80,11 +79,11 @@ __device__ __forceinline__ void mfma16x16x32_acc(f32x4_t& c, const bf16x8_t& a,
   asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
 }
 
-// Same for the e4m3 MFMA: 32x32 output tile, 64-deep reduction, both
-// operands OCP E4M3FN (32 bytes per lane each).
-__device__ __forceinline__ void mfma32x32x64_f8_acc(f32x16_t& c, const i32x8_t& a,
-                                                   const i32x8_t& b) {
-  asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+// e4m3 MFMA with a 16x16 output tile and a 128-deep reduction (32 bytes of
+// each operand per lane); same output layout as the 16x16 bf16 form.
+__device__ __forceinline__ void mfma16x16x128_f8_acc(f32x4_t& c, const i32x8_t& a,
+                                                    const i32x8_t& b) {
+  asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
 }
 
 // Round-to-nearest-even float -> bf16 bits for four values, packed in 8 bytes.

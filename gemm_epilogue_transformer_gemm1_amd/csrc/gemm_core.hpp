@@ -17,12 +17,14 @@
 //     partials, log-sum-exp) are mostly lane-local;
 //   * each wave owns a 128-token x 128-weight-row quarter, 256 fp32
 //     accumulators per lane, pinned to AGPRs;
-//   * bf16: v_mfma_f32_16x16x32_bf16, 8x8 tiles of 16x16 per wave;
-//     e4m3: v_mfma_f32_32x32x64_f8f6f4, 4x4 tiles of 32x32 per wave;
-//   * pipeline: the reduction of a stage is two MFMA steps with fragment sets
-//     fa / fb; a stage's LDS slot is refilled as soon as every wave holds its
-//     second step's fragments, so each stage's loads are issued about one and
-//     a half stages of MFMA work before they are needed.
+//   * bf16: v_mfma_f32_16x16x32_bf16, e4m3: v_mfma_f32_16x16x128_f8f6f4;
+//     8x8 tiles of 16x16 per wave in both;
+//   * pipeline (bf16): the reduction of a stage is two MFMA steps with
+//     fragment sets fa / fb; a stage's LDS slot is refilled as soon as every
+//     wave holds its second step's fragments, so each stage's loads are
+//     issued about one and a half stages of MFMA work before they are needed.
+//     The e4m3 loop (one 128-deep step per stage) is described at
+//     mainloop_fp8.
 #pragma once
 
 #include <type_traits>
@@ -45,13 +47,6 @@ constexpr int kSmemBytes = 2 * kStageBytes;   // 128 KiB
 // of token 16i + L%16 (relative to the wave's corner).
 struct Acc {
   f32x4_t v[8][8];
-};
-
-// e4m3 accumulators: v[j][i] is the 32x32 tile of weight subtile j and token
-// subtile i.  Lane L, register r holds feature 32j + 8(r/4) + 4(L/32) + r%4
-// of token 32i + L%32.
-struct Acc8 {
-  f32x16_t v[4][4];
 };
 
 struct TileCoord {
@@ -401,87 +396,77 @@ __device__ __forceinline__ void mainloop_bf16(Acc& acc, char* smem, const Mainlo
 }
 
 // ===========================================================================
-// e4m3 mainloop: v_mfma_f32_32x32x64_f8f6f4 (OCP E4M3FN operands, fp32
-// accumulate), two k64 steps per stage.  A fragment is 32 reduction bytes of
-// one row: two 16 B chunks.
+// e4m3 mainloop on v_mfma_f32_16x16x128_f8f6f4: one 128-deep reduction step
+// per stage, accumulators in the bf16 layout (struct Acc).  Under the power
+// limit this MFMA form keeps a higher clock than the 32x32x64 one.  A
+// fragment is 32 bytes of one row (two 16-byte chunks): lane L reads row
+// base + L % 16, logical chunks 2 (L / 16) and 2 (L / 16) + 1; both operands
+// use the same lane -> chunk map, so every product pairs equal k.
+//
+// Registers: token fragments A[0..7] and weight fragments B[0..7] of one
+// stage (128 VGPRs).  Per stage kt (slot kt & 1), with A[0..3] and B of kt
+// already loaded:
+//   P1a: token subtile 0 (8 MFMAs) with the reads of A[4..7] of kt
+//   B1:  slot kt & 1 read by every wave (only when stage kt+2 exists)
+//   P1b: token subtiles 1..3 (24 MFMAs) with the 16 loads of stage kt+2
+//   B2:  this wave's stage kt+1 loads landed, barrier
+//   P2:  token subtiles 4..7 weight-subtile-major: 8 groups of 4 MFMAs on
+//        B[j]; after group j the next stage's B[j-1] is read into the
+//        registers group j-1 used (one group of distance), and in groups
+//        0..3 the next stage's A[j] (free since P1b)
+// Tile chaining, the epilogue operand hooks and the vector memory accounting
+// are as in mainloop_bf16: `pre` after B2 of stage nk-2 (in the last stage
+// if there is only one), `pre_last` in the last stage before the next
+// tile's loads, which start after a barrier at the head of P1b there.
 // ===========================================================================
-struct Frags8 {
-  i32x8_t a[4];  // token subtiles i = 0..3 (32 rows each)
-  i32x8_t b[4];  // weight subtiles j = 0..3
-};
-
-template <bool kGated>
-__device__ __forceinline__ constexpr int wrow_of_subtile8(int j) {
-  return kGated ? (j < 2 ? j * 32 : 128 + (j - 2) * 32) : j * 32;
-}
-
-// fragment q (0..3 token, 4..7 weight) of one step: two 16 B chunk reads
-template <bool kGated>
-__device__ __forceinline__ void read_frag8(Frags8& f, int q, const char* stage, uint32_t xo0,
-                                           uint32_t xo1, uint32_t wo0, uint32_t wo1) {
-  i32x4_t lo, hi;
-  if (q < 4) {
-    lo = *(const i32x4_t*)(stage + xo0 + q * 32 * kRowBytes);
-    hi = *(const i32x4_t*)(stage + xo1 + q * 32 * kRowBytes);
-    f.a[q] = i32x8_t{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-  } else {
-    const int off = wrow_of_subtile8<kGated>(q - 4) * kRowBytes;
-    lo = *(const i32x4_t*)(stage + wo0 + off);
-    hi = *(const i32x4_t*)(stage + wo1 + off);
-    f.b[q - 4] = i32x8_t{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-  }
-}
-
 template <bool kGated, int kEpiVmem = -1, class Pre, class PreLast>
-__device__ __forceinline__ void mainloop_fp8(Acc8& acc, char* smem, const MainloopSrc& s,
-                                             const TileChain& chain, Pre&& pre,
-                                             PreLast&& pre_last) {
+__device__ __forceinline__ void mainloop_fp8(Acc& acc, char* smem, const MainloopSrc& s,
+                                                const TileChain& chain, Pre&& pre,
+                                                PreLast&& pre_last) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const LoadPlan<kGated> lp(s, smem, wave, lane, 1);
 
-  // Lane reads row (base + lane%32), logical chunks 4*step + 2*(lane/32) + {0,1};
-  // row & 7 == lane & 7 because every fragment base is a multiple of 32.
-  const int r32 = lane & 31;
-  uint32_t xo[2][2], wo[2][2];
+  // row base + lane % 16 has row & 7 == lane & 7 (every subtile base is a
+  // multiple of 16)
+  uint32_t xo[2], wo[2];
 #pragma unroll
-  for (int st = 0; st < 2; ++st)
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint32_t slot = (uint32_t)((st * 4 + 2 * (lane >> 5) + h) ^ (lane & 7)) * 16u;
-      xo[st][h] = (uint32_t)(wm * 128 + r32) * kRowBytes + slot;
-      wo[st][h] =
-          (uint32_t)kXBytes + (uint32_t)(wave_wrow_base<kGated>(wn) + r32) * kRowBytes + slot;
-    }
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t slot = (uint32_t)((2 * (lane >> 4) + h) ^ (lane & 7)) * 16u;
+    xo[h] = (uint32_t)(wm * 128 + (lane & 15)) * kRowBytes + slot;
+    wo[h] = (uint32_t)kXBytes + (uint32_t)(wave_wrow_base<kGated>(wn) + (lane & 15)) * kRowBytes + slot;
+  }
+  auto rd = [&](const char* stage, const uint32_t (&o)[2], int rowoff) {
+    const i32x4_t lo = *(const i32x4_t*)(stage + o[0] + rowoff);
+    const i32x4_t hi = *(const i32x4_t*)(stage + o[1] + rowoff);
+    return i32x8_t{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  };
+  auto rd_a = [&](const char* stage, int i) { return rd(stage, xo, i * 16 * kRowBytes); };
+  auto rd_b = [&](const char* stage, int j) {
+    return rd(stage, wo, wrow_of_subtile<kGated>(j) * kRowBytes);
+  };
 
-  // Same schedule as the bf16 loop, with 16 MFMAs (of 4x the work) per step:
-  //   R1: 8 x {two fb chunk reads, 2 MFMAs on fa}
-  //   B1; R2: 8 x {two stage kt+2 loads, 1 MFMA on fb (weight subtiles 0,1)}
-  //   B2; R3: 8 x {two fa chunk reads, 1 MFMA on fb (weight subtiles 2,3)}
-  // In a tile's last stage R2 starts with a barrier and carries the next
-  // tile's 32 loads (stage 0 in its first four groups, stage 1 in the rest).
   const int nk = s.K / 128;
-  Frags8 fa, fb;
+  i32x8_t A[8], B[8];
   if (!chain.prefetched) {
     prologue(lp, nk);
   } else {
-    if constexpr (kEpiVmem >= 0)  // as in mainloop_bf16
+    if constexpr (kEpiVmem >= 0)
       wait_vm<(kEpiVmem + 16 < 63 ? kEpiVmem + 16 : 63)>();
     else
       wait_vm0();
     __syncthreads();
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int j = 0; j < 8; ++j)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i) acc.v[j][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc.v[j][i][e] = 0.f;
+  for (int i = 0; i < 4; ++i) A[i] = rd_a(smem, i);
 #pragma unroll
-  for (int q = 0; q < 8; ++q)
-    read_frag8<kGated>(fa, q, smem, xo[0][0], xo[0][1], wo[0][0], wo[0][1]);
+  for (int j = 0; j < 8; ++j) B[j] = rd_b(smem, j);
 
   auto stage = [&](int kt, auto load_tag, auto next_tag) {
     constexpr bool load2 = decltype(load_tag)::value;
@@ -491,12 +476,12 @@ __device__ __forceinline__ void mainloop_fp8(Acc8& acc, char* smem, const Mainlo
     const char* base = smem + cur * kStageBytes;
     const char* nbase = smem + (cur ^ 1) * kStageBytes;
     __builtin_amdgcn_sched_barrier(0);
+    // P1a: token subtile 0 with the reads of A[4..7]
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {  // R1
-      read_frag8<kGated>(fb, q, base, xo[1][0], xo[1][1], wo[1][0], wo[1][1]);
-      const int j = q >> 1, i0 = (q & 1) * 2;
-#pragma unroll
-      for (int i = i0; i < i0 + 2; ++i) mfma32x32x64_f8_acc(acc.v[j][i], fa.b[j], fa.a[i]);
+    for (int q = 0; q < 4; ++q) {
+      A[4 + q] = rd_a(base, 4 + q);
+      mfma16x16x128_f8_acc(acc.v[2 * q][0], B[2 * q], A[0]);
+      mfma16x16x128_f8_acc(acc.v[2 * q + 1][0], B[2 * q + 1], A[0]);
       __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (load2) {  // B1
@@ -504,37 +489,32 @@ __device__ __forceinline__ void mainloop_fp8(Acc8& acc, char* smem, const Mainlo
       bare_barrier();
       __builtin_amdgcn_sched_barrier(0);
     }
-    auto r2 = [&](auto chain_tag) {
-      constexpr bool chained = decltype(chain_tag)::value;
-      if constexpr (chained) {
-        wait_lgkm0();
-        bare_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      const LoadPlan<kGated> nlp(chain.next, smem, wave, lane, 1);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        if constexpr (load2) {
-          lp.issue(cur, kt + 2, 2 * q);
-          lp.issue(cur, kt + 2, 2 * q + 1);
-        }
-        if constexpr (chained) {  // see mainloop_bf16: stage 1 is always loaded
-          const int st = q >> 2, q0 = (q & 3) * 4;
-#pragma unroll
-          for (int u = 0; u < 4; ++u) nlp.issue(st, st, q0 + u);
-        }
-        const int j = q >> 2, i = q & 3;
-        mfma32x32x64_f8_acc(acc.v[j][i], fb.b[j], fb.a[i]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    };
+    const LoadPlan<kGated> nlp(chain.next, smem, wave, lane, 1);
     if constexpr (last) {
       if (nk == 1) pre();
       pre_last();
+      // every wave holds all fragments of both slots: both are free for the
+      // next tile's stages 0 and 1 (stage 1 is loaded even when K has one
+      // stage, as in mainloop_bf16)
+      wait_lgkm0();
+      bare_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      r2(std::true_type{});
-    } else {
-      r2(std::false_type{});
+    }
+    // P1b: token subtiles 1..3 with the stage loads
+#pragma unroll
+    for (int q = 0; q < 24; ++q) {
+      if constexpr (load2) {
+        if (q < 16) lp.issue(cur, kt + 2, q);
+      }
+      if constexpr (last) {  // next tile: all of stage 0 (slot 0), then stage 1 (slot 1)
+        if (q < 16) {
+          nlp.issue(q >> 3, q >> 3, 2 * (q & 7));
+          nlp.issue(q >> 3, q >> 3, 2 * (q & 7) + 1);
+        }
+      }
+      const int i = 1 + q / 8, j = q % 8;
+      mfma16x16x128_f8_acc(acc.v[j][i], B[j], A[i]);
+      __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (next) {  // B2
       if constexpr (load2)
@@ -543,21 +523,25 @@ __device__ __forceinline__ void mainloop_fp8(Acc8& acc, char* smem, const Mainlo
         wait_vm0();
       bare_barrier();
     }
-    if constexpr (!load2 && next) pre();  // as in mainloop_bf16
+    if constexpr (!load2 && next) pre();  // stage nk-2, as in mainloop_bf16
     __builtin_amdgcn_sched_barrier(0);
+    // P2: token subtiles 4..7, weight-subtile-major, refilling the fragments
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {  // R3
-      if constexpr (next)
-        read_frag8<kGated>(fa, q, nbase, xo[0][0], xo[0][1], wo[0][0], wo[0][1]);
-      const int j = 2 + (q >> 2), i = q & 3;
-      mfma32x32x64_f8_acc(acc.v[j][i], fb.b[j], fb.a[i]);
+    for (int j = 0; j < 8; ++j) {
+#pragma unroll
+      for (int i = 4; i < 8; ++i) mfma16x16x128_f8_acc(acc.v[j][i], B[j], A[i]);
+      if constexpr (next) {
+        if (j >= 1) B[j - 1] = rd_b(nbase, j - 1);
+        if (j < 4) A[j] = rd_a(nbase, j);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (next) B[7] = rd_b(nbase, 7);
   };
   for (int kt = 0; kt < nk - 2; ++kt) stage(kt, std::true_type{}, std::true_type{});
   if (nk >= 2) stage(nk - 2, std::false_type{}, std::true_type{});
   stage(nk - 1, std::false_type{}, std::false_type{});
-  settle_accumulators<Acc8, 4, 4>(acc);
+  settle_accumulators<Acc, 8, 8>(acc);
 }
 
 }  // namespace coda

@@ -7,11 +7,12 @@
 // the matrix products faster while the data movement around them does not
 // shrink, which is what fusing the epilogues removes.
 //
-// Accumulator layout (32x32 tiles): lane L, register r of tile (j, i) holds
-// feature nbase + 32j + 8(r/4) + 4(L/32) + r%4 of token mbase + 32i + L%32.
-// Each group g = r/4 is a run of 4 consecutive features (8 bytes of bf16, 4
-// bytes of e4m3), and a per-token sum over the wave's features is a
-// lane-local sum plus one exchange between lanes L and L^32.
+// The mainloop is gemm_core.hpp's mainloop_fp8 (v_mfma_f32_16x16x128_f8f6f4),
+// whose accumulators have the bf16 kernels' layout: lane L = 16 gq + r,
+// register v of the 16x16 tile (j, i) holds feature nbase + 16 j + 4 gq + v
+// of token mbase + 16 i + r.  A run of 4 consecutive features is 8 bytes of
+// bf16 or 4 bytes of e4m3, and a per-token sum over the wave's features is a
+// lane-local sum plus exchanges between lanes 16 and 32 apart.
 
 #include "gemm_core.hpp"
 #include "launch.hpp"
@@ -20,12 +21,21 @@ namespace coda {
 
 // ---------------------------------------------------------------------------
 // GEMM1 (fp8 operands): h = residual + acc * sa * sw, stored bf16; partial
-// sums of squares and partial amax of the unrounded h; optionally
-// h8 = E4M3(h / s_h) for the fp8 second GEMM (delayed scaling: s_h is a
-// device scalar written by the previous reduction).
+// sums of squares and partial amax of the unrounded h (features at or past N
+// left out); optionally h8 = E4M3(h / s_h) for the fp8 second GEMM (delayed
+// scaling: s_h is a device scalar written by the previous reduction).
+//   residual: 16 bytes per lane at the start of the epilogue; for a pair of
+//     subtiles (2 p, 2 p + 1), lanes of even gq load subtile 2 p at features
+//     8 (gq / 2) + 0..7 and lanes of odd gq subtile 2 p + 1, then lanes 16
+//     apart swap one run (32 loads per lane);
+//   h: lanes 16 apart exchange one run per pair of subtiles, one 16-byte
+//     store of 8 features (as the bf16 GEMM1);
+//   h8: the 4-byte e4m3 runs of four subtiles go through two exchanges
+//     (lanes 16 apart, then 32 apart) so that each lane stores one whole
+//     16-feature subtile row, 16 bytes.
 // ---------------------------------------------------------------------------
 // At least this many vector memory operations per lane follow a tile's
-// prefetch of the next tile (the 16-byte h stores; the residual loads, h8
+// prefetch of the next tile (the residual loads and the 16-byte h stores; h8
 // and partial stores come on top), so the next tile waits for its stage 0
 // without draining them.
 constexpr int kGemm1Stores8 = 32;
@@ -40,7 +50,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_residual_partialrms_fp8(
   const float inv_s8 = h8 ? 1.0f / h8_scale[0] : 1.0f;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int g4 = (lane >> 5) * 4;
+  const int gq = lane >> 4;
+  const bool godd = (gq & 1) != 0, ghi = gq >= 2;
   const int nt = gm * gn;
   bool prefetched = false;
   for (int t = blockIdx.x; t < nt; t += gridDim.x) {
@@ -52,116 +63,100 @@ __global__ __launch_bounds__(kThreads, 1) void k_residual_partialrms_fp8(
     const TileCoord nc = has_next ? map_tile(t + gridDim.x, gm, gn, 8) : tc;
     ch.next = MainloopSrc{A, W, nullptr, M, N, K, nc.tm * kBM, nc.tn * kBN};
     const int nw0 = n0 + wn * 128;
-    // The residual tile is loaded at the start of the epilogue into the
-    // registers the fragments used (loaded during the last stages it would
-    // make their waits longer and push the mainloop into spills).  Lanes L
-    // and L + 32 hold the runs 8g + 0..3 and 8g + 4..7 of one row in each
-    // 32-feature block; for a pair of runs (gp, gp + 1) lane L loads the 16
-    // bytes of run gp (its own half and lane L + 32's) and lane L + 32 those
-    // of run gp + 1, and `res_runs` swaps the foreign halves: 32 loads of 16
-    // bytes per lane instead of 64 of 8.  Column starts are clamped to N - 8
-    // and rows to M - 1 (those values are never used).
-    u32x4_t rq[4][8];
-    const bool hi = lane >= 32;
-    auto load_res = [&](int i0) {
-#pragma unroll
-      for (int i = i0; i < i0 + 2; ++i) {
-        const size_t row = (size_t)min(m0 + wm * 128 + i * 32 + (lane & 31), M - 1) * (size_t)N;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {  // q = 2 j + gp / 2
-          const int n = min(nw0 + (q >> 1) * 32 + ((q & 1) * 2 + (hi ? 1 : 0)) * 8, N - 8);
-          rq[i][q] = *(const u32x4_t*)(res + row + n);
-        }
-      }
-    };
-    // this lane's runs gp (out[0]) and gp + 1 (out[1]) from its 16 bytes;
-    // all 64 lanes take part (lane shuffle)
-    auto res_runs = [&](const u32x4_t& v, u32x2_t (&out)[2]) {
-      const u32x2_t lo2 = {v.x, v.y}, hi2 = {v.z, v.w};
-      const u32x2_t sd = hi ? lo2 : hi2;
-      const u32x2_t rx = {(unsigned)__shfl_xor((int)sd.x, 32, 64),
-                          (unsigned)__shfl_xor((int)sd.y, 32, 64)};
-      out[0] = hi ? rx : lo2;
-      out[1] = hi ? hi2 : rx;
-    };
-    Acc8 acc;
-    mainloop_fp8<false, kGemm1Stores8>(acc, smem, MainloopSrc{A, W, nullptr, M, N, K, m0, n0},
-                                       ch, [] {}, [] {});
-    load_res(0);
-    load_res(2);
-
-    // Lanes L and L + 32 hold the runs 8g + 0..3 and 8g + 4..7 (g = 0..3) of
-    // the same row in each 32-feature block j.  Exchanges between them give
-    // every lane contiguous output: for h, one whole 8-feature run per pair
-    // of runs (two 16-byte stores per block); for h8, features 0..15 (lane L)
-    // or 16..31 (lane L + 32) of the block (one 16-byte store).  Each store
-    // then covers 32 rows with 32 contiguous bytes a row, instead of 8 or 4
-    // bytes from each of two lanes: the store path pays per row touched.
-    // Buffers start at the tile's first row; masked lanes store out of range.
     const uint32_t rows_here = (uint32_t)min(kBM, M - m0);
+    const __amdgpu_buffer_rsrc_t rrsrc = make_rsrc(res + (size_t)m0 * N, rows_here * (uint32_t)N * 2u);
     const __amdgpu_buffer_rsrc_t hrsrc = make_rsrc(h + (size_t)m0 * N, rows_here * (uint32_t)N * 2u);
     const __amdgpu_buffer_rsrc_t qrsrc =
         make_rsrc(h8 ? h8 + (size_t)m0 * N : nullptr, h8 ? rows_here * (uint32_t)N : 0u);
-    // Partial statistics leave out features at or past N (one select per
-    // value; a branch to a mask-free copy of this code for full-width waves
-    // makes the register allocator copy the accumulators).
-    {
+    Acc acc;
+    mainloop_fp8<false, kGemm1Stores8>(acc, smem, MainloopSrc{A, W, nullptr, M, N, K, m0, n0},
+                                          ch, [] {}, [] {});
+    u32x4_t rq[8][4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int ml = wm * 128 + i * 32 + (lane & 31);  // row within the tile
-        const bool mv = m0 + ml < M;
-        const uint32_t erow = (uint32_t)ml * (uint32_t)N;
-        float ss = 0.f, amax = 0.f;
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t ml = (uint32_t)(wm * 128 + i * 16 + (lane & 15));
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          u32x2_t hb[4], rr[2][2];  // rr[gp / 2][g - gp]: residual run g
-          uint32_t qb[4];
-          res_runs(rq[i][2 * j], rr[0]);
-          res_runs(rq[i][2 * j + 1], rr[1]);
+      for (int p = 0; p < 4; ++p) {
+        const int n = nw0 + 16 * (2 * p + (godd ? 1 : 0));
+        const uint32_t off = n < N ? (ml * (uint32_t)N + (uint32_t)(n + 8 * (gq >> 1))) * 2u : kOobOffset;
+        rq[i][p] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rrsrc, off, 0, 0));
+      }
+    }
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const bool nv = nw0 + j * 32 + g * 8 + g4 < N;
-            float rv[4], hv[4];
-            unpack_bf16x4(rr[g >> 1][g & 1], rv);
+    for (int i = 0; i < 8; ++i) {
+      const int ml = wm * 128 + i * 16 + (lane & 15);
+      const bool mv = m0 + ml < M;
+      float ss = 0.f, amax = 0.f;
+      uint32_t q8[8];  // e4m3 runs of subtiles 0..7
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              hv[v] = rv[v] + acc.v[j][i][g * 4 + v] * scale;
-              const float hm = nv ? hv[v] : 0.f;
-              ss = __builtin_fmaf(hm, hm, ss);
-              // max(amax, |hm|) in one instruction (fmaxf would first
-              // canonicalise both operands)
-              asm("v_max_f32_e64 %0, %1, |%2|" : "=v"(amax) : "v"(amax), "v"(hm));
-            }
-            hb[g] = pack_bf16x4(hv[0], hv[1], hv[2], hv[3]);
-            qb[g] = pack_e4m3x4_sat(hv[0] * inv_s8, hv[1] * inv_s8, hv[2] * inv_s8, hv[3] * inv_s8);
-          }
-#pragma unroll
-          for (int gp = 0; gp < 4; gp += 2) {  // h: runs gp (lane L) and gp + 1 (lane L + 32)
-            const int n = nw0 + j * 32 + (gp + (hi ? 1 : 0)) * 8;
-            const u32x2_t hs = hi ? hb[gp] : hb[gp + 1];
-            const u32x2_t hr = {(unsigned)__shfl_xor((int)hs.x, 32, 64),
-                                (unsigned)__shfl_xor((int)hs.y, 32, 64)};
-            store16(hrsrc,
-                    hi ? u32x4_t{hr.x, hr.y, hb[gp + 1].x, hb[gp + 1].y}
-                       : u32x4_t{hb[gp].x, hb[gp].y, hr.x, hr.y},
-                    (mv && n < N) ? (erow + (uint32_t)n) * 2u : kOobOffset);
-          }
-          if (h8) {  // lane L: features 0..15 of the block, lane L + 32: 16..31
-            const int n = nw0 + j * 32 + (hi ? 16 : 0);
-            const uint32_t q0 = hi ? qb[0] : qb[2], q1 = hi ? qb[1] : qb[3];
-            const uint32_t r0 = (unsigned)__shfl_xor((int)q0, 32, 64);
-            const uint32_t r1 = (unsigned)__shfl_xor((int)q1, 32, 64);
-            store16(qrsrc, hi ? u32x4_t{r0, qb[2], r1, qb[3]} : u32x4_t{qb[0], r0, qb[1], r1},
-                    (mv && n < N) ? erow + (uint32_t)n : kOobOffset);
-          }
+      for (int p = 0; p < 4; ++p) {
+        // this lane's residual runs of subtiles 2p (rr[0]) and 2p + 1 (rr[1])
+        u32x2_t rr[2];
+        {
+          const u32x4_t& v = rq[i][p];
+          const u32x2_t lo = {v.x, v.y}, hi = {v.z, v.w};
+          const u32x2_t sd = godd ? lo : hi;
+          const u32x2_t rx = {(unsigned)__shfl_xor((int)sd.x, 16, 64),
+                              (unsigned)__shfl_xor((int)sd.y, 16, 64)};
+          rr[0] = godd ? rx : lo;
+          rr[1] = godd ? hi : rx;
         }
-        ss += __shfl_xor(ss, 32, 64);
-        amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
-        if (mv && lane < 32 && nw0 < N) {
-          const size_t tt = (size_t)(nw0 / kRmsTileWidth);
-          psum[tt * M + m0 + ml] = ss;
-          if (pamax) pamax[tt * M + m0 + ml] = amax;
+        u32x2_t pk[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int j = 2 * p + u;
+          const bool nv = nw0 + 16 * j + 4 * gq < N;
+          float rv[4], hv[4];
+          unpack_bf16x4(rr[u], rv);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            hv[v] = rv[v] + acc.v[j][i][v] * scale;
+            const float hm = nv ? hv[v] : 0.f;
+            ss = __builtin_fmaf(hm, hm, ss);
+            asm("v_max_f32_e64 %0, %1, |%2|" : "=v"(amax) : "v"(amax), "v"(hm));
+          }
+          pk[u] = pack_bf16x4(hv[0], hv[1], hv[2], hv[3]);
+          q8[j] = pack_e4m3x4_sat(hv[0] * inv_s8, hv[1] * inv_s8, hv[2] * inv_s8, hv[3] * inv_s8);
         }
+        const int n = nw0 + 16 * (2 * p + (godd ? 1 : 0)) + 8 * (gq >> 1);
+        store16_exchanged(hrsrc, pk, godd,
+                          (mv && n < N) ? ((uint32_t)ml * (uint32_t)N + (uint32_t)n) * 2u
+                                        : kOobOffset);
+      }
+      if (h8) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {  // subtiles 4b .. 4b + 3
+          // step 1 (lanes 16 apart): runs of subtiles 4b + s (s = 0, 1 for even
+          // gq; s = 1 for odd) -> 8 bytes of subtile 4b + (gq & 1) and of
+          // 4b + 2 + (gq & 1), at features 8 (gq / 2) + 0..7
+          uint32_t e8[2][2];  // [subtile pair][run]
+#pragma unroll
+          for (int pr = 0; pr < 2; ++pr) {
+            const uint32_t a0 = q8[4 * b + 2 * pr], a1 = q8[4 * b + 2 * pr + 1];
+            const uint32_t sd = godd ? a0 : a1;
+            const uint32_t rx = (unsigned)__shfl_xor((int)sd, 16, 64);
+            e8[pr][0] = godd ? rx : a0;  // lower 4 features of the lane's 8
+            e8[pr][1] = godd ? a1 : rx;
+          }
+          // step 2 (lanes 32 apart): gq < 2 keeps pair 0 (features 0..7 of
+          // its subtile) and receives features 8..15 of it; gq >= 2 keeps
+          // pair 1 (features 8..15) and receives features 0..7
+          const uint32_t s0 = ghi ? e8[0][0] : e8[1][0], s1 = ghi ? e8[0][1] : e8[1][1];
+          const uint32_t x0 = (unsigned)__shfl_xor((int)s0, 32, 64);
+          const uint32_t x1 = (unsigned)__shfl_xor((int)s1, 32, 64);
+          const u32x4_t v = ghi ? u32x4_t{x0, x1, e8[1][0], e8[1][1]}
+                                : u32x4_t{e8[0][0], e8[0][1], x0, x1};
+          const int sub = 4 * b + (godd ? 1 : 0) + (ghi ? 2 : 0);
+          const int n = nw0 + 16 * sub;
+          store16(qrsrc, v, (mv && n < N) ? (uint32_t)ml * (uint32_t)N + (uint32_t)n : kOobOffset);
+        }
+      }
+      ss = sum_over_lane_groups(ss);
+      amax = max_over_lane_groups(amax);
+      if (mv && lane < 16 && nw0 < N) {
+        const size_t tt = (size_t)(nw0 / kRmsTileWidth);
+        psum[tt * M + m0 + ml] = ss;
+        if (pamax) pamax[tt * M + m0 + ml] = amax;
       }
     }
     prefetched = has_next;
@@ -175,6 +170,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_residual_partialrms_fp8(
 // ---------------------------------------------------------------------------
 constexpr int kSwigluStores8 = 16;  // 16-byte stores per lane per tile
 
+// Gate subtile j and up subtile j + 4 sit in the same lane and register (as
+// in the bf16 GEMM2); lanes 16 apart exchange one 4-feature run per 16-byte
+// store.
 __global__ __launch_bounds__(kThreads, 1) void k_rowscale_swiglu_fp8(
     const uint8_t* __restrict__ X, const float* __restrict__ x_scale,
     const uint8_t* __restrict__ Wg, const uint8_t* __restrict__ Wu,
@@ -185,6 +183,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_rowscale_swiglu_fp8(
   const float sgu = sg * (x_scale[0] * wu_scale[0]);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
+  const int gq = lane >> 4;
+  const bool godd = (gq & 1) != 0;
   const int nt = gm * gn;
   bool prefetched = false;
   for (int t = blockIdx.x; t < nt; t += gridDim.x) {
@@ -195,55 +195,43 @@ __global__ __launch_bounds__(kThreads, 1) void k_rowscale_swiglu_fp8(
     const bool has_next = t + (int)gridDim.x < nt;
     const TileCoord nc = has_next ? map_tile(t + gridDim.x, gm, gn, 8) : tc;
     ch.next = MainloopSrc{X, Wg, Wu, M, N, K, nc.tm * kBM, nc.tn * (kBN / 2)};
-    float rr[4];
+    float rr[8];
     auto pre = [&]() {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) rr[i] = r[min(m0 + wm * 128 + i * 32 + (lane & 31), M - 1)];
+      for (int i = 0; i < 8; ++i) rr[i] = r[min(m0 + wm * 128 + i * 16 + (lane & 15), M - 1)];
     };
-    Acc8 acc;
+    Acc acc;
     mainloop_fp8<true, kSwigluStores8>(acc, smem, MainloopSrc{X, Wg, Wu, M, N, K, m0, n0}, ch,
-                                       pre, [] {});
-
-    // 16 stores per lane (masked ones at an out-of-range offset of a buffer
-    // starting at row m0); lanes L and L + 32 exchange halves of their 4-run
-    // pairs so that each stores a whole 8-feature run (see GEMM1 above).
+                                          pre, [] {});
     const __amdgpu_buffer_rsrc_t orsrc =
         make_rsrc(out + (size_t)m0 * N, (uint32_t)min(kBM, M - m0) * (uint32_t)N * 2u);
     const int nw0 = n0 + wn * 64;
-    const bool hi = lane >= 32;
     const float kNegLog2e = -1.4426950408889634f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ml = wm * 128 + i * 32 + (lane & 31);
+    for (int i = 0; i < 8; ++i) {
+      const int ml = wm * 128 + i * 16 + (lane & 15);
       const bool mv = m0 + ml < M;
       // silu(g) u = (a b sx^2 sg su r^2) / (1 + 2^(-log2e sx sg r a))
       const float c1 = kNegLog2e * sg * rr[i], k = sgu * rr[i] * rr[i];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j0 = 0; j0 < 4; j0 += 2) {
+        u32x2_t pk[2];
 #pragma unroll
-        for (int gp = 0; gp < 4; gp += 2) {
-          u32x2_t ob[2];
+        for (int u = 0; u < 2; ++u) {
+          const int j = j0 + u;
+          float o[4];
 #pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int g = gp + u;
-            float o[4];
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              const float a = acc.v[j][i][g * 4 + v], b = acc.v[j + 2][i][g * 4 + v];
-              const float e = __builtin_amdgcn_exp2f(a * c1);
-              o[v] = (a * k) * b * __builtin_amdgcn_rcpf(1.0f + e);
-            }
-            ob[u] = pack_bf16x4(o[0], o[1], o[2], o[3]);
+          for (int v = 0; v < 4; ++v) {
+            const float a = acc.v[j][i][v], b = acc.v[j + 4][i][v];
+            const float e = __builtin_amdgcn_exp2f(a * c1);
+            o[v] = (a * k) * b * __builtin_amdgcn_rcpf(1.0f + e);
           }
-          const int n = nw0 + j * 32 + (gp + (hi ? 1 : 0)) * 8;
-          const u32x2_t os = hi ? ob[0] : ob[1];
-          const u32x2_t orx = {(unsigned)__shfl_xor((int)os.x, 32, 64),
-                               (unsigned)__shfl_xor((int)os.y, 32, 64)};
-          const uint32_t off = (mv && n < N) ? ((uint32_t)ml * (uint32_t)N + (uint32_t)n) * 2u
-                                             : kOobOffset;
-          store16(orsrc, hi ? u32x4_t{orx.x, orx.y, ob[1].x, ob[1].y}
-                            : u32x4_t{ob[0].x, ob[0].y, orx.x, orx.y}, off);
+          pk[u] = pack_bf16x4(o[0], o[1], o[2], o[3]);
         }
+        const int n = nw0 + 16 * (j0 + (godd ? 1 : 0)) + 8 * (gq >> 1);
+        store16_exchanged(orsrc, pk, godd,
+                          (mv && n < N) ? ((uint32_t)ml * (uint32_t)N + (uint32_t)n) * 2u
+                                        : kOobOffset);
       }
     }
     prefetched = has_next;
@@ -254,8 +242,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_rowscale_swiglu_fp8(
 // ---------------------------------------------------------------------------
 // Plain fp8 GEMM for the unfused baseline: C[m, n] = bf16(A[m,:] . W[n,:] *
 // sa * sw), C with row stride ldc (so two GEMMs with different weight scales
-// can fill the two halves of one [M, 2N] buffer).  Stores as in GEMM1: lanes
-// L and L + 32 exchange halves of their run pairs, 16 bytes per store.
+// can fill the two halves of one [M, 2N] buffer).  Stores as in the plain
+// bf16 GEMM (lanes 16 apart exchange a 4-feature run; 16 bytes per store).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_plain_fp8(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ W, const float* __restrict__ a_scale,
@@ -265,8 +253,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_plain_fp8(
   const float scale = a_scale[0] * w_scale[0];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
+  const int gq = lane >> 4;
+  const bool godd = (gq & 1) != 0;
   const int nt = gm * gn;
-  const bool hi = lane >= 32;
   bool prefetched = false;
   for (int t = blockIdx.x; t < nt; t += gridDim.x) {
     const TileCoord tc = map_tile(t, gm, gn, 8);
@@ -276,35 +265,28 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_plain_fp8(
     const bool has_next = t + (int)gridDim.x < nt;
     const TileCoord nc = has_next ? map_tile(t + gridDim.x, gm, gn, 8) : tc;
     ch.next = MainloopSrc{A, W, nullptr, M, N, K, nc.tm * kBM, nc.tn * kBN};
-    Acc8 acc;
-    mainloop_fp8<false>(acc, smem, MainloopSrc{A, W, nullptr, M, N, K, m0, n0}, ch, [] {}, [] {});
+    Acc acc;
+    mainloop_fp8<false, 32>(acc, smem, MainloopSrc{A, W, nullptr, M, N, K, m0, n0}, ch,
+                               [] {}, [] {});
+    const int nw0 = n0 + wn * 128;
     const __amdgpu_buffer_rsrc_t crsrc =
         make_rsrc(C + (size_t)m0 * ldc, (uint32_t)min(kBM, M - m0) * (uint32_t)ldc * 2u);
-    const int nw0 = n0 + wn * 128;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ml = wm * 128 + i * 32 + (lane & 31);
+    for (int i = 0; i < 8; ++i) {
+      const int ml = wm * 128 + i * 16 + (lane & 15);
       const bool mv = m0 + ml < M;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        u32x2_t pk[4];
+      for (int j0 = 0; j0 < 8; j0 += 2) {
+        u32x2_t pk[2];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x16_t& a = acc.v[j][i];
-          pk[g] = pack_bf16x4(a[g * 4] * scale, a[g * 4 + 1] * scale, a[g * 4 + 2] * scale,
-                              a[g * 4 + 3] * scale);
+        for (int u = 0; u < 2; ++u) {
+          const f32x4_t& a = acc.v[j0 + u][i];
+          pk[u] = pack_bf16x4(a[0] * scale, a[1] * scale, a[2] * scale, a[3] * scale);
         }
-#pragma unroll
-        for (int gp = 0; gp < 4; gp += 2) {
-          const int n = nw0 + j * 32 + (gp + (hi ? 1 : 0)) * 8;
-          const u32x2_t sd = hi ? pk[gp] : pk[gp + 1];
-          const u32x2_t rx = {(unsigned)__shfl_xor((int)sd.x, 32, 64),
-                              (unsigned)__shfl_xor((int)sd.y, 32, 64)};
-          store16(crsrc,
-                  hi ? u32x4_t{rx.x, rx.y, pk[gp + 1].x, pk[gp + 1].y}
-                     : u32x4_t{pk[gp].x, pk[gp].y, rx.x, rx.y},
-                  (mv && n < N) ? ((uint32_t)ml * (uint32_t)ldc + (uint32_t)n) * 2u : kOobOffset);
-        }
+        const int n = nw0 + 16 * (j0 + (godd ? 1 : 0)) + 8 * (gq >> 1);
+        store16_exchanged(crsrc, pk, godd,
+                          (mv && n < N) ? ((uint32_t)ml * (uint32_t)ldc + (uint32_t)n) * 2u
+                                        : kOobOffset);
       }
     }
     prefetched = has_next;
@@ -318,8 +300,8 @@ hipError_t launch_gemm_plain_fp8(const uint8_t* A, const uint8_t* W, const float
                                  const float* w_scale, uint16_t* C, int M, int N, int K, int ldc,
                                  hipStream_t stream) {
   const int gm = cdiv(M, kBM), gn = cdiv(N, kBN);
-  hipLaunchKernelGGL(k_gemm_plain_fp8, dim3(min(gm * gn, cu_count())), dim3(kThreads), 0, stream,
-                     A, W, a_scale, w_scale, C, M, N, K, ldc, gm, gn);
+  hipLaunchKernelGGL(k_gemm_plain_fp8, dim3(min(gm * gn, cu_count())), dim3(kThreads), 0,
+                     stream, A, W, a_scale, w_scale, C, M, N, K, ldc, gm, gn);
   return hipGetLastError();
 }
 
