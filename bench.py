@@ -169,6 +169,24 @@ def main():
     fused_steps = np.array([per[k].sum() for k in range(args.steps)])
     unf_steps = step_times(torch, stream, unfused_step, args.steps)
 
+    # context only: the same unfused block in eager PyTorch (torch.mm on hipBLASLt, torch
+    # elementwise and reduction kernels), the analogue of the vendor-BLAS + PyTorch baseline the
+    # page compares against; weights transposed once, outside the timed region
+    print("[bench] torch eager unfused sequence (context)", file=sys.stderr, flush=True)
+    w1_t, wgu_t = w1.t().contiguous(), wgu.t().contiguous()
+    g32 = gamma.to(torch.float32)
+
+    def torch_step():
+        hh = torch.mm(x, w1_t) + res
+        h32 = hh.float()
+        nn = (h32 * torch.rsqrt(h32.pow(2).mean(-1, keepdim=True) + eps) * g32).to(torch.bfloat16)
+        gu = torch.mm(nn, wgu_t)
+        return torch.nn.functional.silu(gu[:, :ffn]) * gu[:, ffn:]
+    for _ in range(max(3, args.warmup // 10)):
+        torch_step()
+    torch_ms = float(np.median(step_times(torch, stream, torch_step, args.steps)))
+    del w1_t, wgu_t
+
     cold = None
     if not args.no_cold:
         print("[bench] cold pass (1 GiB overwritten before every step)", file=sys.stderr,
@@ -220,6 +238,12 @@ def main():
         "pct_of_mfma_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "step_ms": pctl(fused_steps),
         "cold_cache": cold,
+        "torch_eager_unfused": {"ms_per_step": round(torch_ms, 4),
+                                "tflops": round(flops / (torch_ms * 1e-3) / 1e12, 2),
+                                "speedup_fused_vs_torch": round(torch_ms / ms_step, 3),
+                                "note": "context, not the baseline: median step of the same block "
+                                        "in eager PyTorch (torch.mm on hipBLASLt, bf16; RMSNorm "
+                                        "in fp32; SwiGLU)"},
         "unfused": {"ms_per_step": round(unf_ms_step, 4), "tflops": round(unf_tflops, 2),
                     "speedup_fused_vs_unfused": round(unf_ms_step / ms_step, 3),
                     "step_ms": pctl(unf_steps)},
