@@ -465,6 +465,24 @@ def _mlp_bwd_row(torch, ops, inputs, stream, steps, warmup, bf, name="mlp_1b_bwd
     ms_bu = _events_time(torch, stream, bwd_u, steps, warmup)
     kbu = _kernel_times(torch, stream, bwd_uk, steps)
     ms_tu = _events_time(torch, stream, train_u, steps, warmup)
+    # context only: the same backward chain in eager PyTorch (torch.mm on hipBLASLt with
+    # contiguous operands; the SwiGLU gradient on bf16 tensors as autograd would run it, the
+    # RMSNorm gradient in fp32), from the unfused forward's g|u
+    w2 = torch.cat([wg_f, wu_f], 0).contiguous()  # W' = [Wg; Wu] diag(gamma), [2 ffn, d]
+
+    def bwd_torch():
+        dout = torch.mm(dy, wd)
+        g, u = gu_u[:, :ffn], gu_u[:, ffn:]
+        sg = torch.sigmoid(g)
+        sl = g * sg
+        dzt = torch.cat([dout * u * (sg + sl * (1 - sg)), dout * sl], 1)
+        G = torch.mm(dzt, w2).float()
+        h32 = h_u.float()
+        rr = torch.rsqrt(h32.pow(2).mean(-1, keepdim=True) + eps)
+        dhh = rr * G - (rr.pow(3) / d) * (h32 * G).sum(-1, keepdim=True) * h32 + dy.float()
+        return torch.mm(dhh.to(torch.bfloat16), wo)
+    ms_bt = _events_time(torch, stream, bwd_torch, steps, warmup)
+    del w2
     fl_b = 2.0 * M * ffn * d + 2.0 * M * d * 2 * ffn + 2.0 * M * K1 * d
     fl_w = 2.0 * M * 2 * ffn * d + 2.0 * M * d * ffn + 2.0 * M * d * K1
     fl_t = fl_b + fl_w + 2.0 * M * d * K1 + 2.0 * M * 2 * ffn * d
@@ -484,7 +502,12 @@ def _mlp_bwd_row(torch, ops, inputs, stream, steps, warmup, bf, name="mlp_1b_bwd
                                                     "gemm_bf16_G", "rmsnorm_bwd",
                                                     "gemm_bf16_dx"), kbu)),
                         "train_step_ms": round(ms_tu, 4),
-                        "train_step_speedup_fused_vs_unfused": round(ms_tu / ms_t, 3)}}
+                        "train_step_speedup_fused_vs_unfused": round(ms_tu / ms_t, 3)},
+            "torch_eager_bwd": {"bwd_ms": round(ms_bt, 4),
+                                "bwd_speedup_fused_vs_torch": round(ms_bt / ms_b, 3),
+                                "note": "context, not the baseline: the same backward chain in "
+                                        "eager PyTorch (torch.mm on hipBLASLt; SwiGLU gradient "
+                                        "on bf16 tensors, RMSNorm gradient in fp32)"}}
 
 
 def _kernel_times(torch, stream, fns, steps):
