@@ -400,8 +400,11 @@ __device__ __forceinline__ void mainloop_bf16(Acc& acc, char* smem, const Mainlo
 // per stage, accumulators in the bf16 layout (struct Acc).  Under the power
 // limit this MFMA form keeps a higher clock than the 32x32x64 one.  A
 // fragment is 32 bytes of one row (two 16-byte chunks): lane L reads row
-// base + L % 16, logical chunks 2 (L / 16) and 2 (L / 16) + 1; both operands
-// use the same lane -> chunk map, so every product pairs equal k.
+// base + L % 16, logical chunks L / 16 and L / 16 + 4.  Each of the two
+// 16-byte reads then has the bf16 loop's pattern (the four lane groups read
+// four consecutive chunks), which is free of LDS bank conflicts; chunks 2 g
+// and 2 g + 1 instead conflict on about half the cycles.  Both operands use
+// the same lane -> chunk map, so every product pairs equal k.
 //
 // Registers: token fragments A[0..7] and weight fragments B[0..7] of one
 // stage (128 VGPRs).  Per stage kt (slot kt & 1), with A[0..3] and B of kt
@@ -434,7 +437,7 @@ __device__ __forceinline__ void mainloop_fp8(Acc& acc, char* smem, const Mainloo
   uint32_t xo[2], wo[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const uint32_t slot = (uint32_t)((2 * (lane >> 4) + h) ^ (lane & 7)) * 16u;
+    const uint32_t slot = (uint32_t)((4 * h + (lane >> 4)) ^ (lane & 7)) * 16u;
     xo[h] = (uint32_t)(wm * 128 + (lane & 15)) * kRowBytes + slot;
     wo[h] = (uint32_t)kXBytes + (uint32_t)(wave_wrow_base<kGated>(wn) + (lane & 15)) * kRowBytes + slot;
   }
