@@ -1,5 +1,5 @@
 // e4m3 (OCP E4M3FN) GEMM kernels with epilogue programs, on the fp8 mainloop
-// of gemm_core.hpp.
+// of gemm_core_fp8.hpp.
 //
 // Citations name sections of the news page "CODA: New Research Optimizes
 // Transformer Training with GEMM-Epilogue Programming" (KuCoin news flash).
@@ -7,14 +7,14 @@
 // the matrix products faster while the data movement around them does not
 // shrink, which is what fusing the epilogues removes.
 //
-// The mainloop is gemm_core.hpp's mainloop_fp8 (v_mfma_f32_16x16x128_f8f6f4),
+// The mainloop is gemm_core_fp8.hpp's mainloop_fp8 (v_mfma_f32_16x16x128_f8f6f4),
 // whose accumulators have the bf16 kernels' layout: lane L = 16 gq + r,
 // register v of the 16x16 tile (j, i) holds feature nbase + 16 j + 4 gq + v
 // of token mbase + 16 i + r.  A run of 4 consecutive features is 8 bytes of
 // bf16 or 4 bytes of e4m3, and a per-token sum over the wave's features is a
 // lane-local sum plus exchanges between lanes 16 and 32 apart.
 
-#include "gemm_core.hpp"
+#include "gemm_core_fp8.hpp"
 #include "launch.hpp"
 
 namespace coda {
