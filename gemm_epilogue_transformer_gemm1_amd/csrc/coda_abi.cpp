@@ -277,7 +277,12 @@ int coda_gemm_rope(const void* h, const void* Wqkv, const float* r, const float*
         !aligned(rope_cos, 16) || !aligned(rope_sin, 16) || !aligned(pos, 4))
       return CODA_ERR_ALIGN;
     if (int st = check_device()) return st;
-    return launched(coda::launch_rope_bf16(
+    // QKV widths that are a multiple of six heads (384) run on the 128 x 384
+    // block tile, which fills whole rounds of compute units where the
+    // 256 x 256 tile would leave the last round partly idle
+    const auto launch = (n_q_heads + 2 * n_kv_heads) % 6 == 0 ? coda::launch_rope_bf16_wide
+                                                               : coda::launch_rope_bf16;
+    return launched(launch(
         static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(Wqkv), r, rope_cos,
         rope_sin, pos, max_pos, static_cast<uint16_t*>(qkv), M, K, n_q_heads, n_kv_heads,
         as_stream(stream)));

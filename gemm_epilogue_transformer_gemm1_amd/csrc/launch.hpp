@@ -39,6 +39,11 @@ hipError_t launch_rmsnorm_bwd(const uint16_t* G, const uint16_t* h, const uint16
 hipError_t launch_rope_bf16(const uint16_t* X, const uint16_t* W, const float* r,
                             const float* rcos, const float* rsin, const int* pos, int max_pos,
                             uint16_t* out, int M, int K, int n_q, int n_kv, hipStream_t stream);
+// same operation on the 128 x 384 block tile (QKV width a multiple of 384)
+hipError_t launch_rope_bf16_wide(const uint16_t* X, const uint16_t* W, const float* r,
+                                 const float* rcos, const float* rsin, const int* pos, int max_pos,
+                                 uint16_t* out, int M, int K, int n_q, int n_kv,
+                                 hipStream_t stream);
 hipError_t launch_rope_tables(double theta, int max_pos, int head_dim, float* rcos, float* rsin,
                               hipStream_t stream);
 hipError_t launch_block_lse_bf16(const uint16_t* X, const uint16_t* W, const float* r,

@@ -63,6 +63,10 @@ def test_rope_tables_match_oracle():
 @pytest.mark.parametrize("M,d,K1,nq,nkv,seq", [
     (300, 256, 192, 4, 2, 100),    # ragged M, many positions
     (200, 384, 128, 3, 1, 64),     # 5 heads: the last wave tile holds one head
+    # head counts that are a multiple of 6 run on the 128 x 384 block tile
+    (200, 256, 128, 4, 1, 64),     # 6 heads: one tile column, ragged M, four stages
+    (300, 128, 128, 8, 2, 100),    # 12 heads: two tile columns, three row tiles, two stages
+    (130, 64, 64, 2, 2, 50),       # 6 heads, one stage per tile
 ])
 def test_rope_block_ragged(M, d, K1, nq, nkv, seq):
     w = inputs.make_attn(seed=7, M=M, d=d, K1=K1, n_q=nq, n_kv=nkv, head_dim=64, seq_len=seq)
@@ -78,11 +82,12 @@ def test_rope_block_ragged(M, d, K1, nq, nkv, seq):
     assert norm_err(q[:, vlo:], ref["qkv"][:, vlo:]) <= TOL_BF16
 
 
-def test_rope_position_zero_is_identity_on_gpu():
+@pytest.mark.parametrize("nq,nkv", [(2, 1), (4, 1)])  # 4 heads; 6 heads (128 x 384 tile)
+def test_rope_position_zero_is_identity_on_gpu(nq, nkv):
     """With every position 0 the rotation is the identity, so q|k|v equal the
     plain row-scaled projection (checked against the oracle with RoPE off)."""
-    w = inputs.make_attn(seed=8, M=128, d=256, K1=128, n_q=2, n_kv=1, head_dim=64, seq_len=1)
-    say("rope block, all positions 0")
+    w = inputs.make_attn(seed=8, M=128, d=256, K1=128, n_q=nq, n_kv=nkv, head_dim=64, seq_len=1)
+    say(f"rope block, all positions 0, nq={nq} nkv={nkv}")
     got = run_fused(w)
     ref = oracle_rows(w)
     n = oracle.rmsnorm(ref["h"], w.arrays["gamma"].astype(np.float64), EPS)
@@ -102,3 +107,17 @@ def test_attn_rope_full_sampled_rows():
     assert row_rel_err(f32_host(got["r"])[rows], ref["r"]) <= TOL_ROW
     assert norm_err(bf16_host(got["qkv"][rows.tolist()]), ref["qkv"]) <= TOL_BF16
     assert bool(torch.isfinite(got["qkv"].float()).all())
+
+
+def test_rope_wide_tile_chained_sampled_rows():
+    """18 heads (QKV width 1152, three 128 x 384 tile columns) at M = 16384:
+    384 tiles for the compute units, so workgroups chain into a second tile;
+    sampled rows vs the oracle."""
+    w = inputs.make_attn(seed=9, M=16384, d=128, K1=64, n_q=12, n_kv=3, head_dim=64,
+                         seq_len=2048)
+    say("rope block, 128 x 384 tiles chained (M=16384, 18 heads)")
+    got = run_fused(w)
+    rows = sample_rows(w.sizes["M"], n=48)
+    ref = oracle_rows(w, rows)
+    assert norm_err(bf16_host(got["h"][rows.tolist()]), ref["h"]) <= TOL_BF16
+    assert norm_err(bf16_host(got["qkv"][rows.tolist()]), ref["qkv"]) <= TOL_BF16
