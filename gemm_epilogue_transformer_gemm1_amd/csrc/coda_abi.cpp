@@ -351,10 +351,11 @@ int coda_gemm_bf16(const void* A, const void* W, void* C, int M, int N, int K, v
     if (int st = check_gemm_shape(M, N, K, 64)) return st;
     if (!aligned(A, 16) || !aligned(W, 16) || !aligned(C, 16)) return CODA_ERR_ALIGN;
     if (int st = check_device()) return st;
-    return launched(coda::launch_gemm_plain_bf16(static_cast<const uint16_t*>(A),
-                                                 static_cast<const uint16_t*>(W),
-                                                 static_cast<uint16_t*>(C), M, N, K,
-                                                 as_stream(stream)));
+    // the 128 x 384 tile where it fills the rounds of compute units better
+    const auto launch = coda::prefer_wide_tile(M, N) ? coda::launch_gemm_plain_bf16_wide
+                                                     : coda::launch_gemm_plain_bf16;
+    return launched(launch(static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(W),
+                           static_cast<uint16_t*>(C), M, N, K, as_stream(stream)));
   } catch (...) {
     return CODA_ERR_LAUNCH;
   }

@@ -39,6 +39,10 @@ hipError_t launch_rmsnorm_bwd(const uint16_t* G, const uint16_t* h, const uint16
 hipError_t launch_rope_bf16(const uint16_t* X, const uint16_t* W, const float* r,
                             const float* rcos, const float* rsin, const int* pos, int max_pos,
                             uint16_t* out, int M, int K, int n_q, int n_kv, hipStream_t stream);
+// plain bf16 GEMM on the 128 x 384 block tile, and whether a shape should use it
+hipError_t launch_gemm_plain_bf16_wide(const uint16_t* A, const uint16_t* W, uint16_t* C, int M,
+                                       int N, int K, hipStream_t stream);
+bool prefer_wide_tile(int M, int N);
 // same operation on the 128 x 384 block tile (QKV width a multiple of 384)
 hipError_t launch_rope_bf16_wide(const uint16_t* X, const uint16_t* W, const float* r,
                                  const float* rcos, const float* rsin, const int* pos, int max_pos,

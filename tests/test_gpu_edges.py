@@ -25,6 +25,10 @@ def _ints(rng, shape, lo, hi):
     (4096, 8192, 192),   # 512 tiles, three stages
     (1, 16, 64),         # a single row, a single 16-wide feature group
     (257, 272, 64),      # ragged everything, one stage
+    # shapes where the plain GEMM takes the 128 x 384 tile
+    (8192, 3072, 64),    # 512 wide tiles (chained), one stage
+    (8192, 3072, 192),   # 512 wide tiles, three stages
+    (300, 320, 128),     # ragged rows, one partial tile column, two stages
 ])
 def test_gemm1_and_plain_exact(M, N, K):
     rng = np.random.default_rng(M + N + K)
