@@ -304,6 +304,16 @@ def step_times_cold(torch, stream, fn, steps, scratch):
     return [e0.elapsed_time(e1) for e0, e1 in evs]
 
 
+def splitk_parts(M, N, K, cus):
+    """Reduction parts for an M x N output over K: doubled while the
+    256 x 256 tiles times the parts stay below the compute-unit count."""
+    tiles = -(-M // 256) * -(-N // 256)
+    p = 1
+    while tiles * p < cus and p < 16 and K % (128 * p) == 0:
+        p *= 2
+    return p
+
+
 def _events_time(torch, stream, fn, steps, warmup, min_ms=None):
     """Mean step time (ms) over back-to-back steps.  Warmup and timed region
     each cover at least `min_ms` of GPU work (the shader clock settles over
@@ -398,6 +408,16 @@ def _mlp_bwd_row(torch, ops, inputs, stream, steps, warmup, bf, name="mlp_1b_bwd
     dz_T, o_T = torch.empty(2 * ffn, M, **bf16), torch.empty(ffn, M, **bf16)
     dW2, dWd, dWo = (torch.empty(2 * ffn, d, **bf16), torch.empty(d, ffn, **bf16),
                      torch.empty(d, K1, **bf16))
+    # dWo (d x K1) has too few output tiles for the chip: split its reduction
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    parts_o = splitk_parts(d, K1, M, cus)
+    ws_o = torch.empty(parts_o, d, K1, dtype=torch.float32, device=dev)
+
+    def gemm_dwo():
+        if parts_o > 1:
+            ops.gemm_bf16_splitk(dh_T, x_T, dWo, ws_o)
+        else:
+            ops.gemm_bf16(dh_T, x_T, dWo)
 
     def dw():
         ops.transpose(h, h_T, row_scale=r)
@@ -408,7 +428,7 @@ def _mlp_bwd_row(torch, ops, inputs, stream, steps, warmup, bf, name="mlp_1b_bwd
         ops.transpose(x, x_T)
         ops.gemm_bf16(dz_T, h_T, dW2)
         ops.gemm_bf16(dy_T, o_T, dWd)
-        ops.gemm_bf16(dh_T, x_T, dWo)
+        gemm_dwo()
 
     def train():
         prep()
@@ -454,7 +474,7 @@ def _mlp_bwd_row(torch, ops, inputs, stream, steps, warmup, bf, name="mlp_1b_bwd
         ops.transpose(x, x_T)
         ops.gemm_bf16(dz_T, n_T, dW2)
         ops.gemm_bf16(dy_T, o_T, dWd)
-        ops.gemm_bf16(dh_T, x_T, dWo)
+        gemm_dwo()
 
     def train_u():
         prep()
@@ -493,7 +513,7 @@ def _mlp_bwd_row(torch, ops, inputs, stream, steps, warmup, bf, name="mlp_1b_bwd
             "bwd_pct_of_bf16_peak": round(100 * fl_b / ms_b / 1e9 / PEAK_BF16_TFLOPS, 2),
             "bwd_kernels_ms": dict(zip(("gemm_swiglu_bwd", "rms_bwd_reduce", "gemm_rmsnorm_bwd",
                                         "gemm_bf16_dx"), kb)),
-            "dw_ms": round(ms_w, 4), "dw_tflops": round(fl_w / ms_w / 1e9, 1),
+            "dw_ms": round(ms_w, 4), "dwo_reduction_parts": parts_o, "dw_tflops": round(fl_w / ms_w / 1e9, 1),
             "weight_prep_ms": round(ms_p, 4),
             "train_step_ms": round(ms_t, 4), "train_step_tflops": round(fl_t / ms_t / 1e9, 1),
             "unfused": {"bwd_ms": round(ms_bu, 4), "bwd_tflops": round(fl_b / ms_bu / 1e9, 1),

@@ -7,6 +7,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstring>
 
@@ -356,6 +357,25 @@ int coda_gemm_bf16(const void* A, const void* W, void* C, int M, int N, int K, v
                                                      : coda::launch_gemm_plain_bf16;
     return launched(launch(static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(W),
                            static_cast<uint16_t*>(C), M, N, K, as_stream(stream)));
+  } catch (...) {
+    return CODA_ERR_LAUNCH;
+  }
+}
+
+int coda_gemm_bf16_splitk(const void* A, const void* W, void* C, float* workspace, int M, int N,
+                          int K, int parts, void* stream) {
+  try {
+    if (!A || !W || !C || !workspace) return CODA_ERR_NULL;
+    if (parts < 1 || parts > 16) return CODA_ERR_SHAPE;
+    if (int st = check_gemm_shape(M, N, K, 64 * parts)) return st;
+    // one block's workspace rows (up to 256 x N fp32) stay below 2 GiB
+    if ((int64_t)std::min(M, 256) * N * 4 >= (int64_t(1) << 31)) return CODA_ERR_SHAPE;
+    if (!aligned(A, 16) || !aligned(W, 16) || !aligned(C, 16) || !aligned(workspace, 16))
+      return CODA_ERR_ALIGN;
+    if (int st = check_device()) return st;
+    return launched(coda::launch_gemm_splitk_bf16(
+        static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(W),
+        static_cast<uint16_t*>(C), workspace, M, N, K, parts, as_stream(stream)));
   } catch (...) {
     return CODA_ERR_LAUNCH;
   }

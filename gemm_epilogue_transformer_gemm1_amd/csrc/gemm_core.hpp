@@ -84,6 +84,9 @@ struct MainloopSrc {
   int K;           // reduction length in elements
   int m0;          // first token row of the block
   int n0;          // first weight row of the block (per weight matrix)
+  int ld = 0;      // row pitch of X and the weights in elements (0: K); a pitch
+                   // above K reads a column slice, e.g. one part of a split
+                   // reduction with X and the weights offset to its first column
 };
 
 // Persistent kernels walk several tiles per workgroup.  While a tile's last
@@ -126,10 +129,12 @@ struct LoadPlan {
 
   __device__ __forceinline__ LoadPlan(const MainloopSrc& s, char* smem, int wave, int lane,
                                       int esize) {
-    const uint32_t row_bytes = (uint32_t)s.K * (uint32_t)esize;
-    xr = make_rsrc(s.X, (uint32_t)s.M * row_bytes);
+    const uint32_t row_bytes = (uint32_t)(s.ld > 0 ? s.ld : s.K) * (uint32_t)esize;
+    // ranges end at the last row's K-th element (the whole matrix for ld = K)
+    const uint32_t tail = (uint32_t)s.K * (uint32_t)esize;
+    xr = make_rsrc(s.X, (uint32_t)(s.M - 1) * row_bytes + tail);
     const void* wsrc = (kGated && wave >= 2) ? s.W1 : s.W0;
-    wr = make_rsrc(wsrc, (uint32_t)s.Nw * row_bytes);
+    wr = make_rsrc(wsrc, (uint32_t)(s.Nw - 1) * row_bytes + tail);
     const int wrow_shift = (kGated && wave >= 2) ? 128 : 0;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {

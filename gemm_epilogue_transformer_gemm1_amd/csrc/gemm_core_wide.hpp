@@ -46,9 +46,10 @@ struct LoadPlanW {
   char* lds[16];
 
   __device__ __forceinline__ LoadPlanW(const MainloopSrc& s, char* smem, int wave, int lane) {
-    const uint32_t row_bytes = (uint32_t)s.K * 2u;
-    xr = make_rsrc(s.X, (uint32_t)s.M * row_bytes);
-    wr = make_rsrc(s.W0, (uint32_t)s.Nw * row_bytes);
+    const uint32_t row_bytes = (uint32_t)(s.ld > 0 ? s.ld : s.K) * 2u;
+    const uint32_t tail = (uint32_t)s.K * 2u;  // ranges end at the last row's K-th element
+    xr = make_rsrc(s.X, (uint32_t)(s.M - 1) * row_bytes + tail);
+    wr = make_rsrc(s.W0, (uint32_t)(s.Nw - 1) * row_bytes + tail);
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       const bool isx = q < 4;

@@ -43,6 +43,10 @@ hipError_t launch_rope_bf16(const uint16_t* X, const uint16_t* W, const float* r
 hipError_t launch_gemm_plain_bf16_wide(const uint16_t* A, const uint16_t* W, uint16_t* C, int M,
                                        int N, int K, hipStream_t stream);
 bool prefer_wide_tile(int M, int N);
+// Plain GEMM with the reduction split in `parts` ranges of K / parts columns:
+// fp32 partial products to ws [parts, M, N], then C = bf16 of their sum.
+hipError_t launch_gemm_splitk_bf16(const uint16_t* A, const uint16_t* W, uint16_t* C, float* ws,
+                                   int M, int N, int K, int parts, hipStream_t stream);
 // same operation on the 128 x 384 block tile (QKV width a multiple of 384)
 hipError_t launch_rope_bf16_wide(const uint16_t* X, const uint16_t* W, const float* r,
                                  const float* rcos, const float* rsin, const int* pos, int max_pos,

@@ -45,6 +45,7 @@ _SIGNATURES = {
     "coda_fold_gamma": ([_p, _p, _p, _c_int, _c_int, _p], _c_int),
     "coda_rope_tables": ([_c_double, _c_int, _c_int, _p, _p, _p], _c_int),
     "coda_gemm_bf16": ([_p, _p, _p, _c_int, _c_int, _c_int, _p], _c_int),
+    "coda_gemm_bf16_splitk": ([_p, _p, _p, _p, _c_int, _c_int, _c_int, _c_int, _p], _c_int),
     "coda_residual_add": ([_p, _p, _p, _i64, _p], _c_int),
     "coda_rmsnorm": ([_p, _p, _c_float, _p, _c_int, _c_int, _p], _c_int),
     "coda_swiglu": ([_p, _p, _c_int, _c_int, _p], _c_int),
@@ -351,6 +352,19 @@ def gemm_bf16(A, W, C, stream=None):
     _shape(C, (M, N), "C")
     _call("coda_gemm_bf16", _ptr(A, _BF16, "A"), _ptr(W, _BF16, "W"), _ptr(C, _BF16, "C"),
           M, N, K, _stream(stream))
+
+
+def gemm_bf16_splitk(A, W, C, workspace, stream=None):
+    """C = bf16(A W^T) with the reduction split in workspace.shape[0] parts
+    (fp32 partial products in workspace [parts, M, N], summed in part order)."""
+    M, K = A.shape
+    N = W.shape[0]
+    parts = workspace.shape[0]
+    _shape(W, (N, K), "W")
+    _shape(C, (M, N), "C")
+    _shape(workspace, (parts, M, N), "workspace")
+    _call("coda_gemm_bf16_splitk", _ptr(A, _BF16, "A"), _ptr(W, _BF16, "W"), _ptr(C, _BF16, "C"),
+          _ptr(workspace, _F32, "workspace"), M, N, K, parts, _stream(stream))
 
 
 def residual_add(y, res, h, stream=None):

@@ -195,7 +195,8 @@ int coda_gemm_block_lse(const void* X, const void* W, const float* r, const int3
  * and then dx = dh Wo is a plain GEMM with Wo^T (coda_gemm_bf16).  The weight
  * gradients reduce over the tokens and have no epilogue: token-major copies
  * (coda_transpose_bf16; the row scale r is applied while copying h) and plain
- * GEMMs (coda_gemm_bf16) give dWd = dY^T out, dW' = dz^T (r h) and dWo = dh^T x.
+ * GEMMs (coda_gemm_bf16, or coda_gemm_bf16_splitk where the output has too few
+ * tiles) give dWd = dY^T out, dW' = dz^T (r h) and dWo = dh^T x.
  */
 
 /* coda_gemm_rowscale_swiglu (bf16) that also stores the pre-activations for
@@ -258,6 +259,24 @@ int coda_fold_gamma(const void* W, const float* gamma, void* W_out, int N, int K
  * Sizes: rows, cols >= 1; rows * cols and cols * ld_dst below 2^31. */
 int coda_transpose_bf16(const void* src, const float* row_scale, int rows, int cols, void* dst,
                         int ld_dst, void* stream);
+
+/* The plain GEMM of coda_gemm_bf16 with its reduction split in `parts`
+ * ranges, for the weight gradients, whose outputs (d x d at d = 2048: 64
+ * tiles of 256 x 256) are too small to occupy every compute unit while the
+ * reduction runs over all tokens:
+ *   workspace[p, m, n] = sum over k in [p K/parts, (p+1) K/parts) of
+ *                        A[m,k] W[n,k]                         (fp32)
+ *   C[m, n] = bf16( ((workspace[0,m,n] + workspace[1,m,n]) + ...) )
+ * summed in part order for every element (deterministic; equal to
+ * coda_gemm_bf16 up to the rounding of the fp32 sums).  A [M,K], W [N,K],
+ * C [M,N] bf16; workspace [parts, M, N] fp32, owned by the caller, written
+ * whole before it is read (no clearing needed), left holding the partial
+ * products.  Two kernels on `stream`; calls that share a workspace must be
+ * ordered on one stream.  Sizes as coda_gemm_bf16 with 1 <= parts <= 16,
+ * K % (64 parts) == 0 and min(M, 256) * N * 4 below 2^31; 16-byte aligned
+ * pointers. */
+int coda_gemm_bf16_splitk(const void* A, const void* W, void* C, float* workspace, int M, int N,
+                          int K, int parts, void* stream);
 
 /* rope_cos/rope_sin[p*(hd/2)+i] = cos/sin(p * theta^(-2i/hd)), angles and
  * trigonometry in fp64, stored fp32.  Sizes: max_pos >= 1, head_dim even. */

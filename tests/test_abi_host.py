@@ -97,6 +97,7 @@ def test_valid_arguments_without_gpu_report_device_error(L):
     # fails cleanly on a machine without a gfx950 GPU.
     st = L.coda_gemm_bf16(A16, A16, A16, 64, 64, 64, None)
     assert st == ERR_DEVICE
+    assert L.coda_gemm_bf16_splitk(A16, A16, A16, A16, 64, 64, 256, 4, None) == ERR_DEVICE
 
 
 def test_backward_validation(L):
@@ -134,6 +135,15 @@ def test_backward_validation(L):
     assert L.coda_transpose_bf16(A16, None, 4, 8, A16, 3, None) == ERR_SHAPE    # ld_dst < rows
     assert L.coda_transpose_bf16(A16 + 1, None, 4, 8, A16, 4, None) == ERR_ALIGN
     assert L.coda_transpose_bf16(A16, A16 + 2, 4, 8, A16, 4, None) == ERR_ALIGN
+    # coda_gemm_bf16_splitk(A, W, C, workspace, M, N, K, parts, stream)
+    k = L.coda_gemm_bf16_splitk
+    assert k(A16, A16, A16, None, 64, 256, 512, 4, None) == ERR_NULL
+    assert k(A16, A16, A16, A16, 64, 256, 512, 0, None) == ERR_SHAPE     # parts >= 1
+    assert k(A16, A16, A16, A16, 64, 256, 512, 17, None) == ERR_SHAPE    # parts <= 16
+    assert k(A16, A16, A16, A16, 64, 256, 384, 4, None) == ERR_SHAPE     # K % (64 parts)
+    assert k(A16, A16, A16, A16, 64, 264, 512, 4, None) == ERR_SHAPE     # N % 16
+    assert k(A16, A16, A16, A16, 256, 1 << 21, 64, 1, None) == ERR_SHAPE  # 256 N fp32 rows
+    assert k(A16, A16, A16, A16 + 8, 64, 256, 512, 4, None) == ERR_ALIGN
 
 
 def test_binding_checks_backward_shapes():
