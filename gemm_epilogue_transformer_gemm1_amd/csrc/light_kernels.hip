@@ -172,53 +172,52 @@ __global__ __launch_bounds__(256) void k_transpose_bf16(const uint16_t* __restri
   }
 }
 
-// The same with 16-byte accesses on both sides, for rows % 8 == cols % 8 ==
-// ld_dst % 8 == 0 and 16-byte aligned pointers: a thread loads 8 consecutive
-// elements of a source row, and stores 8 consecutive elements of a
-// destination row gathered from a column of the LDS tile.  The 16-byte
-// chunks of tile row rr are rotated by rr / 8: the lanes gathering one column
-// read rows 8 apart, which would otherwise all fall in the same bank.
-__global__ __launch_bounds__(256) void k_transpose_bf16_v8(const uint16_t* __restrict__ src,
+// The same with 16-byte accesses on both sides and no LDS, for rows % 8 ==
+// cols % 8 == ld_dst % 8 == 0 and 16-byte aligned pointers.  A lane loads an
+// 8 x 8 block (8 source rows of 16 bytes), transposes it in registers and
+// stores 8 destination rows of 16 bytes.  Lane L of a wave takes row group
+// L / 8 and column chunk L % 8 of a 64 x 64 wave tile, so each load reads 8
+// runs of 128 bytes (8 lanes along a source row) and each store writes 8 runs
+// of 128 bytes (8 lanes along a destination row); the four waves of a block
+// cover 128 x 128.  Every block is either wholly inside or wholly outside
+// the matrix per lane (both sizes are multiples of 8).
+__global__ __launch_bounds__(256) void k_transpose_bf16_r8(const uint16_t* __restrict__ src,
                                                            const float* __restrict__ row_scale,
                                                            int rows, int cols,
                                                            uint16_t* __restrict__ dst,
                                                            int ld_dst) {
-  __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];  // 144-byte rows
-  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = blockIdx.y * 128 + (wave >> 1) * 64 + (lane >> 3) * 8;
+  const int c = blockIdx.x * 128 + (wave & 1) * 64 + (lane & 7) * 8;
+  if (r >= rows || c >= cols) return;
+  u32x4_t v[8];
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int q = (int)threadIdx.x + k * 256;  // 64 rows x 8 chunks of 8
-    const int rr = q >> 3, cc = (q & 7) * 8;
-    const int r = r0 + rr, c = c0 + cc;
-    i32x4_t v = {0, 0, 0, 0};
-    if (r < rows && c < cols) {
-      v = *(const i32x4_t*)(src + (size_t)r * cols + c);
-      if (row_scale) {
-        const float sc = row_scale[r];
-        float f[8];
-        unpack_bf16x4(u32x2_t{(unsigned)v.x, (unsigned)v.y}, f);
-        unpack_bf16x4(u32x2_t{(unsigned)v.z, (unsigned)v.w}, f + 4);
-        const u32x2_t lo = pack_bf16x4(f[0] * sc, f[1] * sc, f[2] * sc, f[3] * sc);
-        const u32x2_t hi = pack_bf16x4(f[4] * sc, f[5] * sc, f[6] * sc, f[7] * sc);
-        v = i32x4_t{(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
-      }
+  for (int i = 0; i < 8; ++i) v[i] = *(const u32x4_t*)(src + (size_t)(r + i) * cols + c);
+  if (row_scale) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float sc = row_scale[r + i];
+      float f[8];
+      unpack_bf16x4(u32x2_t{v[i].x, v[i].y}, f);
+      unpack_bf16x4(u32x2_t{v[i].z, v[i].w}, f + 4);
+      const u32x2_t lo = pack_bf16x4(f[0] * sc, f[1] * sc, f[2] * sc, f[3] * sc);
+      const u32x2_t hi = pack_bf16x4(f[4] * sc, f[5] * sc, f[6] * sc, f[7] * sc);
+      v[i] = u32x4_t{lo.x, lo.y, hi.x, hi.y};
     }
-    *(i32x4_t*)&tile[rr][(((cc >> 3) + (rr >> 3)) & 7) * 8] = v;
   }
-  __syncthreads();
+  // destination row c + j holds element j of source rows r .. r + 7: element
+  // j of row i is half j & 1 of word j / 2 of v[i]
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int q = (int)threadIdx.x + k * 256;  // 64 destination rows x 8 chunks of 8
-    const int oc = q >> 3, orr = (q & 7) * 8;
-    const int c = c0 + oc, r = r0 + orr;
-    if (c < cols && r < rows) {
-      const int pos = ((((oc >> 3) + (orr >> 3)) & 7) * 8) + (oc & 7);  // rows orr..orr+7
-      uint32_t w[4];
+  for (int j = 0; j < 8; ++j) {
+    uint32_t w[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        w[e] = (uint32_t)tile[orr + 2 * e][pos] | ((uint32_t)tile[orr + 2 * e + 1][pos] << 16);
-      *(i32x4_t*)(dst + (size_t)c * ld_dst + r) = i32x4_t{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
-    }
+    for (int i = 0; i < 8; ++i) w[i] = v[i][j >> 1];
+    uint32_t o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      o[e] = (j & 1) ? ((w[2 * e] >> 16) | (w[2 * e + 1] & 0xffff0000u))
+                     : ((w[2 * e] & 0xffffu) | (w[2 * e + 1] << 16));
+    *(u32x4_t*)(dst + (size_t)(c + j) * ld_dst + r) = u32x4_t{o[0], o[1], o[2], o[3]};
   }
 }
 
@@ -228,7 +227,7 @@ hipError_t launch_transpose_bf16(const uint16_t* src, const float* row_scale, in
                   (reinterpret_cast<uintptr_t>(src) & 15) == 0 &&
                   (reinterpret_cast<uintptr_t>(dst) & 15) == 0;
   if (v8)
-    hipLaunchKernelGGL(k_transpose_bf16_v8, dim3(cdiv(cols, 64), cdiv(rows, 64)), dim3(256), 0,
+    hipLaunchKernelGGL(k_transpose_bf16_r8, dim3(cdiv(cols, 128), cdiv(rows, 128)), dim3(256), 0,
                        stream, src, row_scale, rows, cols, dst, ld_dst);
   else
     hipLaunchKernelGGL(k_transpose_bf16, dim3(cdiv(cols, 64), cdiv(rows, 64)), dim3(256), 0,

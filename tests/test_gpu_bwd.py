@@ -109,7 +109,8 @@ def check_against_oracle(got, ref, rows=None, w=None):
 
 def test_transpose_exact():
     rng = np.random.default_rng(0)
-    for rows, cols in ((1, 1), (70, 130), (257, 64), (64, 1000), (136, 200), (8, 8)):
+    for rows, cols in ((1, 1), (70, 130), (257, 64), (64, 1000), (136, 200), (8, 8), (264, 392),
+                       (1032, 136)):
         say(f"transpose {rows}x{cols}")
         a = bf16_dev(inputs.to_bf16_bits(rng.standard_normal((rows, cols)).astype(np.float32)))
         dst = torch.zeros(cols, rows + 24, dtype=torch.bfloat16, device=DEV)
@@ -275,7 +276,11 @@ def run_weight_grads(w, fz):
                      torch.empty(d, K1, **bf))
     ops.gemm_bf16(dzT, hT, dW2)   # gradient of the folded [Wg'; Wu']
     ops.gemm_bf16(dyT, outT, dWd)
-    ops.gemm_bf16(dhT, xT, dWo)
+    # dWo (d x K1) has few output tiles: its reduction over the M tokens is
+    # split in parts (M a multiple of 64 * parts)
+    parts = 4 if M % 256 == 0 else 3 if M % 192 == 0 else 1
+    ws = torch.empty(parts, d, K1, dtype=torch.float32, device=DEV)
+    ops.gemm_bf16_splitk(dhT, xT, dWo, ws)
     torch.cuda.synchronize()
     return dict(dW2=dW2, dWd=dWd, dWo=dWo)
 
@@ -303,7 +308,7 @@ def test_weight_grads_ragged_features():
     check_weight_grads(w, run_weight_grads(w, fz), oracle_rows(w))
 
 
-@pytest.mark.parametrize("rows,cols", [(130, 70), (128, 72), (8, 1024)])
+@pytest.mark.parametrize("rows,cols", [(130, 70), (128, 72), (8, 1024), (264, 392)])
 def test_transpose_row_scale_exact(rows, cols):
     """The scaled transpose rounds src * scale once (RNE) per element (ragged
     sizes take the element-wise kernel, multiples of 8 the 16-byte one)."""
