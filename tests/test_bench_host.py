@@ -35,3 +35,18 @@ def test_records_follow_the_kernel_sources(bench, monkeypatch):
     assert bench.measured_traffic("gemm_rowscale_swiglu") is None
     assert bench.measured_clock_ghz("gemm_rowscale_swiglu") is None
     assert bench.measured_traffic("no_such_kernel") is None
+
+
+def test_split_reduction_parts(bench):
+    """Parts double while tiles x parts stays below the compute-unit count and
+    the reduction still divides into 64-element stages per part."""
+    assert bench.splitk_parts(2048, 2048, 8192, 256) == 4      # dWo: 64 tiles
+    assert bench.splitk_parts(2048, 8192, 8192, 256) == 1      # dWd: 256 tiles
+    assert bench.splitk_parts(16384, 2048, 8192, 256) == 1     # dW': 512 tiles
+    assert bench.splitk_parts(256, 256, 8192, 256) == 16       # one tile: capped at 16
+    assert bench.splitk_parts(2048, 2048, 192, 256) == 1       # 192 is not a multiple of 128
+    assert bench.splitk_parts(2048, 2048, 256, 256) == 4       # 4 parts of one stage each
+    assert bench.splitk_parts(2048, 2048, 384, 256) == 2       # 2 parts of 192 (not 4 of 96)
+    for M, N, K in ((2048, 2048, 8192), (300, 272, 4096), (1, 16, 65536)):
+        p = bench.splitk_parts(M, N, K, 256)
+        assert K % (64 * p) == 0 and 1 <= p <= 16
