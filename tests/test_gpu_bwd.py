@@ -120,6 +120,29 @@ def test_transpose_exact():
         assert not dst[:, :8].any().item() and not dst[:, 8 + rows:].any().item()
 
 
+def test_transpose_full_size_exact():
+    """The token-major copies at the 1B backward sizes: dz [8192, 16384] and
+    the row-scaled h [8192, 2048], bit for bit (the scaled copy against the
+    fp32 product rounded to bf16 with round-to-nearest-even, as the kernel
+    computes it; torch's float -> bfloat16 conversion rounds the same way)."""
+    g = torch.Generator(device=DEV).manual_seed(5)
+    say("transpose full size dz 8192x16384")
+    dz = torch.randn(8192, 16384, device=DEV, generator=g).to(torch.bfloat16)
+    dzT = torch.empty(16384, 8192, dtype=torch.bfloat16, device=DEV)
+    ops.transpose(dz, dzT)
+    torch.cuda.synchronize()
+    assert torch.equal(dzT.view(torch.int16), dz.t().contiguous().view(torch.int16))
+    del dz, dzT
+    say("scaled transpose full size h 8192x2048")
+    h = torch.randn(8192, 2048, device=DEV, generator=g).to(torch.bfloat16)
+    r = torch.rand(8192, device=DEV, generator=g) + 0.5
+    hT = torch.empty(2048, 8192, dtype=torch.bfloat16, device=DEV)
+    ops.transpose(h, hT, row_scale=r)
+    torch.cuda.synchronize()
+    ref = (h.float() * r[:, None]).to(torch.bfloat16).t().contiguous()
+    assert torch.equal(hT.view(torch.int16), ref.view(torch.int16))
+
+
 def test_forward_save_matches_forward():
     """The saving variant stores the same out bits as the plain GEMM2 and
     g, u of the oracle."""
