@@ -36,6 +36,7 @@ def _run(A, W, parts, ws=None):
 
 
 @pytest.mark.parametrize("M,N,K,parts", [
+    (2048, 2048, 8192, 4),   # the dWo launch of the 1B backward, bit for bit
     (2048, 2048, 1024, 4),   # 64 tiles x 4 parts: one work unit per compute unit
     (4096, 4096, 512, 2),    # 512 units: workgroups chain units of different parts
     (520, 2048, 8192, 16),   # 384 units of 512 columns, ragged last tile row
