@@ -31,13 +31,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_splitk_bf16(const uint16_t
   __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int tiles = gm * gn;
-  const int nt = tiles * parts;
+  const int nt = gm * gn * parts;
   const int kp = K / parts;
-  // unit t: part t / tiles, output tile t % tiles (tiles in the XCD-aware order)
+  // Units form a (parts * gm) x gn grid of tiles, part-major along the rows,
+  // walked in the XCD-aware order: each XCD's units then share one part's
+  // operand slabs through its L2 (dWo: one part and 8 x 4 tiles per XCD,
+  // 12 MiB of operands, instead of one tile column of every part, 36 MiB).
+  auto unit = [&](int t, int& p) {
+    const TileCoord c = map_tile(t, gm * parts, gn, 8);
+    p = c.tm / gm;
+    return TileCoord{c.tm - p * gm, c.tn};
+  };
   auto src = [&](int t) {
-    const int p = t / tiles;
-    const TileCoord c = map_tile(t - p * tiles, gm, gn, 8);
+    int p;
+    const TileCoord c = unit(t, p);
     return MainloopSrc{A + (size_t)p * kp, W + (size_t)p * kp, nullptr, M, N, kp,
                        c.tm * kBM, c.tn * kBN, K};
   };
@@ -54,7 +61,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_splitk_bf16(const uint16_t
     // lane L of a 16 x 16 subtile holds 4 consecutive features of one row:
     // each store writes 64 contiguous bytes of 16 rows
     const int m0 = cur.m0, n0 = cur.n0;
-    const int p = t / tiles;
+    int p;
+    unit(t, p);
     const int nw0 = n0 + wn * 128 + 4 * (lane >> 4);
     const __amdgpu_buffer_rsrc_t wsrc =
         make_rsrc(ws + ((size_t)p * M + m0) * N, (uint32_t)min(kBM, M - m0) * (uint32_t)N * 4u);
