@@ -35,6 +35,10 @@ def parse():
                    help="untimed steps (fused and unfused sequence each) before timing; the "
                         "shader clock settles over the first ~35 ms of sustained load, so the "
                         "default covers about 100 ms")
+    p.add_argument("--warmup-ms", type=float, default=200.0,
+                   help="GPU-time floor of the warm-up: after the --warmup steps, fused and "
+                        "unfused steps keep alternating until this much GPU time has passed, so "
+                        "the timed steps start on a settled shader clock")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-rows", action="store_true",
                    help="skip timing the attention-input, LM-head and fp8 workloads")
@@ -152,19 +156,43 @@ def main():
         print(f"[bench] copied {args.calibrate_copy} MiB x3", file=sys.stderr, flush=True)
         del src, dst
 
-    print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    print(f"[bench] warmup {args.warmup} steps (floor {args.warmup_ms:.0f} ms of GPU time)",
+          file=sys.stderr, flush=True)
+    w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0.record(stream)
     for _ in range(args.warmup):
         fused_step()
         unfused_step()
+    w1.record(stream)
     torch.cuda.synchronize()
+    warm_ms, warm_pairs = w0.elapsed_time(w1), args.warmup
+    while warm_ms < args.warmup_ms:
+        # one fused + unfused pair takes about 1 ms; top up in chunks
+        pair_ms = warm_ms / warm_pairs if warm_pairs else 1.0
+        extra = int(min(500, max(1, np.ceil((args.warmup_ms - warm_ms) / max(pair_ms, 0.05)))))
+        w0.record(stream)
+        for _ in range(extra):
+            fused_step()
+            unfused_step()
+        w1.record(stream)
+        torch.cuda.synchronize()
+        warm_ms += w0.elapsed_time(w1)
+        warm_pairs += extra
 
     print(f"[bench] timing {args.steps} fused steps", file=sys.stderr, flush=True)
-    # 1) whole-step throughput, no events between kernels
+    # 1) whole-step throughput, no events between kernels: the headline pass, right after
+    #    the warm-up
     fused_ms, fused_wall, _ = timed(fused_step, args.steps)
-    # 2) per-kernel durations with events on the launch stream
-    _, _, per = timed(fused_step, args.steps, per_kernel=True)
     print(f"[bench] timing {args.steps} unfused steps", file=sys.stderr, flush=True)
     unfused_ms, _, _ = timed(unfused_step, args.steps)
+    # the same two passes twice more, alternating, so that the fused/unfused ratio does not
+    # depend on which sequence ran first
+    fused_passes, unfused_passes = [fused_ms], [unfused_ms]
+    for _ in range(2):
+        fused_passes.append(timed(fused_step, args.steps)[0])
+        unfused_passes.append(timed(unfused_step, args.steps)[0])
+    # 2) per-kernel durations with events on the launch stream
+    _, _, per = timed(fused_step, args.steps, per_kernel=True)
     # per-step distribution (events before and after every step)
     fused_steps = np.array([per[k].sum() for k in range(args.steps)])
     unf_steps = step_times(torch, stream, unfused_step, args.steps)
@@ -246,7 +274,18 @@ def main():
                                         "in fp32; SwiGLU)"},
         "unfused": {"ms_per_step": round(unf_ms_step, 4), "tflops": round(unf_tflops, 2),
                     "speedup_fused_vs_unfused": round(unf_ms_step / ms_step, 3),
-                    "step_ms": pctl(unf_steps)},
+                    "step_ms": pctl(unf_steps),
+                    "alternating_passes": {
+                        "fused_ms_per_step": [round(v / args.steps, 4) for v in fused_passes],
+                        "unfused_ms_per_step": [round(v / args.steps, 4) for v in unfused_passes],
+                        "speedup_of_medians": round(float(np.median(unfused_passes)) /
+                                                    float(np.median(fused_passes)), 3),
+                        "note": "three passes of --steps steps each, fused and unfused in "
+                                "turn; the first fused pass is the headline"}},
+        "warmup_floor": {"min_gpu_ms": args.warmup_ms, "gpu_ms": round(warm_ms, 1),
+                         "fused_unfused_pairs_run": warm_pairs,
+                         "note": "the --warmup steps, extended until the warm-up has run this "
+                                 "much GPU time (fused and unfused alternating)"},
         "kernels_ms": {"gemm_residual_partialrms": round(g1_ms, 4),
                        "rms_reduce": round(red_ms, 4),
                        "gemm_rowscale_swiglu": round(g2_ms, 4)},

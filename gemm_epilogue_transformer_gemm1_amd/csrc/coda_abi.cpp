@@ -309,8 +309,8 @@ int coda_gemm_block_lse(const void* X, const void* W, const float* r, const int3
                                                    static_cast<const uint16_t*>(W), r, labels,
                                                    tile_max, tile_sumexp, label_logit, M, V, K, s))
       return launched(e);
-    return launched(coda::launch_lse_merge(tile_max, tile_sumexp, label_logit,
-                                           coda_lse_tiles(V), M, lse, loss, s));
+    return launched(coda::launch_lse_merge(tile_max, tile_sumexp, label_logit, labels,
+                                           coda_lse_tiles(V), M, V, lse, loss, s));
   } catch (...) {
     return CODA_ERR_LAUNCH;
   }

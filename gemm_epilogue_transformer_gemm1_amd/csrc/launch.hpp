@@ -57,8 +57,9 @@ hipError_t launch_rope_tables(double theta, int max_pos, int head_dim, float* rc
 hipError_t launch_block_lse_bf16(const uint16_t* X, const uint16_t* W, const float* r,
                                  const int* labels, float* tmax, float* tsum, float* label_logit,
                                  int M, int V, int K, hipStream_t stream);
-hipError_t launch_lse_merge(const float* tmax, const float* tsum, const float* label_logit, int T,
-                            int M, float* lse, float* loss, hipStream_t stream);
+hipError_t launch_lse_merge(const float* tmax, const float* tsum, const float* label_logit,
+                            const int* labels, int T, int M, int V, float* lse, float* loss,
+                            hipStream_t stream);
 hipError_t launch_gemm_plain_bf16(const uint16_t* A, const uint16_t* W, uint16_t* C, int M, int N,
                                   int K, hipStream_t stream);
 

@@ -4,6 +4,8 @@
 // Citations name sections of the news page "CODA: New Research Optimizes
 // Transformer Training with GEMM-Epilogue Programming" (KuCoin news flash).
 
+#include <algorithm>
+
 #include "coda_device.hpp"
 #include "launch.hpp"
 
@@ -246,10 +248,15 @@ hipError_t launch_fold_gamma(const uint16_t* W, const float* gamma, uint16_t* W_
 // ---------------------------------------------------------------------------
 // Log-sum-exp merge of the per-tile (max, sum-exp) pairs (section "Five
 // building blocks and a LEGO language": the running max / sum-exp statistics
-// of online normalisation).  A 256-thread block owns 64 token rows: lane l of
-// wave w merges tiles w, w+4, w+8, ... of row 64*block + l (coalesced 256 B
-// reads per wave), then the four partial pairs are merged through LDS.
-//   lse = Mx + ln sum_t s_t e^(m_t - Mx);  loss = lse - label_logit.
+// of online normalisation).  A 512-thread block owns 32 token rows and splits
+// each row's tiles over 16 lanes: lane l of wave w takes row 32*block + l%32
+// and tiles s, s+16, s+32, ... with s = 2w + l/32, so every load instruction
+// reads two 128-byte runs (32 consecutive rows of two tiles).  A lane merges
+// four tiles per step (one new max, five exponentials), the two halves of a
+// wave meet through one lane exchange and the eight waves through LDS.
+//   lse = Mx + ln sum_t s_t e^(m_t - Mx);  loss = lse - label_logit,
+// and loss = 0 for a label outside [0, V) (a row that carries no loss; its
+// label logit is never read).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void lse_combine(float& m, float& s, float m2, float s2) {
   const float nm = fmaxf(m, m2);
@@ -259,44 +266,62 @@ __device__ __forceinline__ void lse_combine(float& m, float& s, float m2, float 
   m = nm;
 }
 
-__global__ __launch_bounds__(256) void k_lse_merge(const float* __restrict__ tmax,
+constexpr int kMergeRows = 32;    // token rows per block
+constexpr int kMergeSlices = 16;  // lanes sharing one row
+
+__global__ __launch_bounds__(512) void k_lse_merge(const float* __restrict__ tmax,
                                                    const float* __restrict__ tsum,
-                                                   const float* __restrict__ label_logit, int T,
-                                                   int M, float* __restrict__ lse,
+                                                   const float* __restrict__ label_logit,
+                                                   const int* __restrict__ labels, int T, int M,
+                                                   int V, float* __restrict__ lse,
                                                    float* __restrict__ loss) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int m = blockIdx.x * 64 + lane;
+  const int row = lane & (kMergeRows - 1);
+  const int m = blockIdx.x * kMergeRows + row;
   const int mc = min(m, M - 1);
+  const float k = 1.4426950408889634f;
   float rm = -INFINITY, rs = 0.f;
-  int t = wave;
-  for (; t + 12 < T; t += 16) {  // four tiles in flight per lane
+  int t = wave * 2 + (lane >> 5);
+  for (; t + 3 * kMergeSlices < T; t += 4 * kMergeSlices) {
     float a[4], b[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      a[q] = tmax[(size_t)(t + 4 * q) * M + mc];
-      b[q] = tsum[(size_t)(t + 4 * q) * M + mc];
+      a[q] = tmax[(size_t)(t + q * kMergeSlices) * M + mc];
+      b[q] = tsum[(size_t)(t + q * kMergeSlices) * M + mc];
     }
+    const float nm = fmaxf(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])), rm);
+    if (nm != -INFINITY) {
+      float acc = rs * __builtin_amdgcn_exp2f((rm - nm) * k);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) lse_combine(rm, rs, a[q], b[q]);
+      for (int q = 0; q < 4; ++q) acc += b[q] * __builtin_amdgcn_exp2f((a[q] - nm) * k);
+      rs = acc;
+      rm = nm;
+    }
   }
-  for (; t < T; t += 4) lse_combine(rm, rs, tmax[(size_t)t * M + mc], tsum[(size_t)t * M + mc]);
-  __shared__ float pm[4][64], ps[4][64];
-  pm[wave][lane] = rm;
-  ps[wave][lane] = rs;
+  for (; t < T; t += kMergeSlices)
+    lse_combine(rm, rs, tmax[(size_t)t * M + mc], tsum[(size_t)t * M + mc]);
+  lse_combine(rm, rs, __shfl_xor(rm, 32, 64), __shfl_xor(rs, 32, 64));
+  __shared__ float pm[8][kMergeRows], ps[8][kMergeRows];
+  if (lane < kMergeRows) {
+    pm[wave][lane] = rm;
+    ps[wave][lane] = rs;
+  }
   __syncthreads();
-  if (wave == 0 && m < M) {
+  if (wave == 0 && lane < kMergeRows && m < M) {
 #pragma unroll
-    for (int w = 1; w < 4; ++w) lse_combine(rm, rs, pm[w][lane], ps[w][lane]);
+    for (int w = 1; w < 8; ++w) lse_combine(rm, rs, pm[w][lane], ps[w][lane]);
     const float l = rm + logf(rs);
     if (lse) lse[m] = l;
-    loss[m] = l - label_logit[m];
+    const int lab = labels[m];
+    loss[m] = (lab >= 0 && lab < V) ? l - label_logit[m] : 0.f;
   }
 }
 
-hipError_t launch_lse_merge(const float* tmax, const float* tsum, const float* label_logit, int T,
-                            int M, float* lse, float* loss, hipStream_t stream) {
-  hipLaunchKernelGGL(k_lse_merge, dim3(cdiv(M, 64)), dim3(256), 0, stream, tmax, tsum,
-                     label_logit, T, M, lse, loss);
+hipError_t launch_lse_merge(const float* tmax, const float* tsum, const float* label_logit,
+                            const int* labels, int T, int M, int V, float* lse, float* loss,
+                            hipStream_t stream) {
+  hipLaunchKernelGGL(k_lse_merge, dim3(cdiv(M, kMergeRows)), dim3(512), 0, stream, tmax, tsum,
+                     label_logit, labels, T, M, V, lse, loss);
   return hipGetLastError();
 }
 
@@ -558,7 +583,8 @@ hipError_t launch_rope_apply(uint16_t* qkv, const float* rcos, const float* rsin
 
 // loss[m] = logsumexp_n z[m, n] - z[m, label[m]] over stored bf16 logits
 // [M, V]: one block per row; each thread keeps a running (max, sum exp) over
-// its chunks of 8 logits, then the 256 pairs are merged.
+// its chunks of 8 logits, then the 256 pairs are merged.  A label outside
+// [0, V) gives loss 0, as in the fused merge.
 __global__ __launch_bounds__(256) void k_ce_rows(const uint16_t* __restrict__ z,
                                                  const int* __restrict__ labels,
                                                  float* __restrict__ lse, float* __restrict__ loss,
@@ -592,31 +618,55 @@ __global__ __launch_bounds__(256) void k_ce_rows(const uint16_t* __restrict__ z,
   if (threadIdx.x == 0) {
     for (int w = 1; w < 4; ++w) lse_combine(mx, se, pm[w], ps[w]);
     const float l = mx + logf(se);
-    const int lab = min(max(labels[m], 0), V - 1);
+    const int lab = labels[m];
     lse[m] = l;
-    loss[m] = l - bf16_to_f32(row[lab]);
+    loss[m] = (lab >= 0 && lab < V) ? l - bf16_to_f32(row[lab]) : 0.f;
   }
 }
 
 // e4m3 quantisation for the unfused fp8 baseline (delayed scaling):
 // out = E4M3_sat(x / s_in) with s_in the previous scale, and the amax of |x|
-// for the next one (one atomicMax per block on the non-negative float's bits).
+// for the next one.  A grid of a few blocks per compute unit walks the
+// tensor in 8-element groups (four groups in flight per lane), keeps the
+// lane's running amax in a register, and each block issues one atomicMax
+// (on the non-negative float's bit pattern, which orders like the float).
+__device__ __forceinline__ float quantize8(const uint16_t* __restrict__ x, uint8_t* __restrict__ out,
+                                           int64_t g, float inv, float mx) {
+  float f[8];
+  load8(x + g * 8, f);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) mx = fmaxf(mx, fabsf(f[q]));
+  const uint32_t lo = pack_e4m3x4_sat(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv);
+  const uint32_t hi = pack_e4m3x4_sat(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv);
+  *(u32x2_t*)(out + g * 8) = u32x2_t{lo, hi};
+  return mx;
+}
+
 __global__ __launch_bounds__(256) void k_quantize_e4m3(const uint16_t* __restrict__ x,
                                                        const float* __restrict__ s_in,
                                                        uint8_t* __restrict__ out, int64_t total8,
                                                        unsigned int* __restrict__ amax_bits) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const float inv = 1.0f / s_in[0];
   float mx = 0.f;
-  if (idx < total8) {
-    const float inv = 1.0f / s_in[0];
-    float f[8];
-    load8(x + idx * 8, f);
+  for (; g + 3 * stride < total8; g += 4 * stride) {
+    i32x4_t raw[4];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) mx = fmaxf(mx, fabsf(f[q]));
-    const uint32_t lo = pack_e4m3x4_sat(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv);
-    const uint32_t hi = pack_e4m3x4_sat(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv);
-    *(u32x2_t*)(out + idx * 8) = u32x2_t{lo, hi};
+    for (int u = 0; u < 4; ++u) raw[u] = *(const i32x4_t*)(x + (g + u * stride) * 8);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      float f[8];
+      unpack_bf16x4(u32x2_t{(unsigned)raw[u].x, (unsigned)raw[u].y}, f);
+      unpack_bf16x4(u32x2_t{(unsigned)raw[u].z, (unsigned)raw[u].w}, f + 4);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) mx = fmaxf(mx, fabsf(f[q]));
+      const uint32_t lo = pack_e4m3x4_sat(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv);
+      const uint32_t hi = pack_e4m3x4_sat(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv);
+      *(u32x2_t*)(out + (g + u * stride) * 8) = u32x2_t{lo, hi};
+    }
   }
+  for (; g < total8; g += stride) mx = quantize8(x, out, g, inv, mx);
   __shared__ float red[4];
   for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
@@ -629,9 +679,10 @@ hipError_t launch_quantize_e4m3(const uint16_t* x, const float* s_in, uint8_t* o
                                 float* amax, float* s_out, hipStream_t stream) {
   unsigned int* bits = reinterpret_cast<unsigned int*>(amax);
   const int64_t total8 = count / 8;
+  const int blocks = (int)std::min<int64_t>(cdiv(total8, 256), (int64_t)cu_count() * 8);
   hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(1), 0, stream, bits);
-  hipLaunchKernelGGL(k_quantize_e4m3, dim3(cdiv(total8, 256)), dim3(256), 0, stream, x, s_in, out,
-                     total8, bits);
+  hipLaunchKernelGGL(k_quantize_e4m3, dim3(blocks), dim3(256), 0, stream, x, s_in, out, total8,
+                     bits);
   hipLaunchKernelGGL(k_amax_to_scale, dim3(1), dim3(1), 0, stream, bits, amax, s_out);
   return hipGetLastError();
 }

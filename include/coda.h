@@ -26,9 +26,9 @@
  *     returns.  Results are visible after the caller synchronises the stream.
  *   - Return value: CODA_OK (0) or a negative coda_status.  Arguments are
  *     validated BEFORE any HIP runtime call, so a bad argument never launches
- *     anything.  Data-dependent problems (NaN / Inf inputs, labels outside
- *     [0, V)) are not detected: they propagate as NaN / garbage into the
- *     affected rows only.
+ *     anything.  NaN / Inf inputs are not detected: they propagate as NaN
+ *     into the affected rows only.  A label outside [0, V) marks a row that
+ *     carries no loss (loss 0) in both cross-entropy calls.
  *   - Matrix pointers must be 16-byte aligned, float / int vectors 4-byte
  *     aligned.  Outputs must not alias inputs.
  *   - Calls keep no global mutable state and are thread-safe; calls on
@@ -170,7 +170,10 @@ int coda_gemm_rope(const void* h, const void* Wqkv, const float* r, const float*
  *   label_logit[m] = z[m, labels[m]], from the fp32 accumulator
  *   lse[m]  = M_m + ln sum_t tile_sumexp * exp(tile_max - M_m), M_m = max_t tile_max
  *   loss[m] = lse[m] - label_logit[m]        (natural log, one value per row)
- * X [M,K] bf16, W [V,K] bf16, labels [M] int32 in [0,V) (not checked),
+ *   a label outside [0,V) (e.g. an ignore index such as -100) marks a row that
+ *   carries no loss: loss[m] = 0, lse[m] is still written and label_logit[m]
+ *   is neither written nor read
+ * X [M,K] bf16, W [V,K] bf16, labels [M] int32,
  * tile_max, tile_sumexp [T_v, M] fp32 workspace (T_v = coda_lse_tiles(V)),
  * label_logit, loss [M] fp32, lse [M] fp32 or NULL.
  * Sizes: M >= 1; V >= 16, V % 16 == 0; K % 64 == 0.
@@ -321,7 +324,8 @@ int coda_rope_apply(void* qkv, const float* rope_cos, const float* rope_sin, con
                     int max_pos, int M, int n_q_heads, int n_kv_heads, int head_dim, void* stream);
 /* Cross entropy of stored bf16 logits z [M,V] (as a plain GEMM writes them):
  *   lse[m] = ln sum_v exp z[m,v],  loss[m] = lse[m] - z[m, labels[m]]
- * labels [M] int32 in [0,V) (clamped, not checked); lse, loss [M] fp32; V % 8 == 0. */
+ * labels [M] int32; a label outside [0,V) gives loss[m] = 0 (as coda_gemm_block_lse);
+ * lse, loss [M] fp32; V % 8 == 0. */
 int coda_cross_entropy_rows(const void* logits, const int32_t* labels, float* lse, float* loss,
                             int M, int V, void* stream);
 

@@ -271,19 +271,26 @@ def lm_head_ce(x, wlm, labels, r=None, chunk=256):
     epilogue" lists cross-entropy among the re-parameterised ops).
 
     z = diag(r) x wlm^T (r optional), loss[m] = lse(z[m]) - z[m, label[m]].
+    Reading (the page is silent on it): a label outside [0, V), such as an
+    ignore index of -100, marks a row that carries no loss, so loss[m] = 0;
+    its lse is still defined and its label logit is NaN.
     Rows are processed in chunks so the float64 logits stay bounded."""
     x = np.asarray(x, dtype=np.float64)
     labels = np.asarray(labels)
     M = x.shape[0]
+    V = np.asarray(wlm).shape[0]
+    valid = (labels >= 0) & (labels < V)
     lse = np.empty(M)
-    zl = np.empty(M)
+    zl = np.full(M, np.nan)
     for m0 in range(0, M, chunk):
         z = gemm_nt(x[m0:m0 + chunk], wlm)
         if r is not None:
             z = np.asarray(r, dtype=np.float64)[m0:m0 + chunk, None] * z
         lse[m0:m0 + chunk] = logsumexp_rows(z)
-        zl[m0:m0 + chunk] = z[np.arange(z.shape[0]), labels[m0:m0 + chunk]]
-    return {"lse": lse, "label_logit": zl, "loss": lse - zl}
+        rows = np.nonzero(valid[m0:m0 + chunk])[0]
+        zl[m0 + rows] = z[rows, labels[m0 + rows]]
+    loss = np.where(valid, lse - np.where(valid, zl, 0.0), 0.0)
+    return {"lse": lse, "label_logit": zl, "loss": loss}
 
 
 # ---------------------------------------------------------------------------

@@ -81,3 +81,25 @@ def sample_rows(M, n=48, seed=0):
     rows = set(r for r in edges if 0 <= r < M)
     rows.update(int(x) for x in rng.integers(0, M, size=n))
     return np.array(sorted(rows))
+
+
+class MaxErr:
+    """max|err| / max|ref| of a whole tensor accumulated over row chunks."""
+
+    def __init__(self):
+        self.err = 0.0
+        self.ref = 0.0
+
+    def add(self, got, ref):
+        got = np.asarray(got, dtype=np.float64)
+        ref = np.asarray(ref, dtype=np.float64)
+        self.err = max(self.err, float(np.max(np.abs(got - ref))))
+        self.ref = max(self.ref, float(np.max(np.abs(ref))))
+
+    def value(self):
+        return self.err / max(self.ref, 1e-300)
+
+
+def row_chunks(M, chunk=2048):
+    """Consecutive row ranges covering [0, M), for oracle runs over every row."""
+    return [np.arange(m0, min(M, m0 + chunk)) for m0 in range(0, M, chunk)]

@@ -281,6 +281,31 @@ def pin_ce_zero_weights():
     return _ok(float(np.max(np.abs(o["loss"] - lnv))), 1e-12, "W = 0 gives ln V")
 
 
+def pin_ce_ignored_rows(seed=19):
+    """Rows whose label lies outside [0, V) carry no loss: torch's
+    cross_entropy with ignore_index = -100 (library routine) gives 0 there, and
+    the other rows keep their loss; a label of V or more is ignored the same
+    way, and every row's lse is the plain log-sum-exp."""
+    g = torch.Generator().manual_seed(seed)
+    V = 23
+    x = torch.randn(8, 6, generator=g, dtype=torch.float64)
+    w = torch.randn(V, 6, generator=g, dtype=torch.float64)
+    lab = torch.randint(0, V, (8,), generator=g)
+    lab[1] = -100
+    lab[4] = -100
+    ref = torch.nn.functional.cross_entropy(x @ w.T, lab, reduction="none", ignore_index=-100)
+    ref_lse = torch.logsumexp(x @ w.T, dim=1).numpy()
+    o = oracle.lm_head_ce(x.numpy(), w.numpy(), lab.numpy(), chunk=3)
+    err = max(float(np.max(np.abs(o["loss"] - ref.numpy()))), _rel(o["lse"], ref_lse))
+    lab2 = lab.numpy().copy()
+    lab2[[1, 4]] = [V, V + 7]
+    o2 = oracle.lm_head_ce(x.numpy(), w.numpy(), lab2, chunk=5)
+    err = max(err, float(np.max(np.abs(o2["loss"] - ref.numpy()))))
+    ok = bool(o["loss"][1] == 0.0 and o["loss"][4] == 0.0 and o2["loss"][1] == 0.0
+              and np.all(o["loss"][[0, 2, 3, 5, 6, 7]] > 0))
+    return _ok(err if ok else 1.0, 1e-13, "ce ignored rows")
+
+
 def pin_lse_merge(seed=11):
     rng = np.random.default_rng(seed)
     z = rng.standard_normal((5, 300)) * 20
@@ -518,7 +543,7 @@ ALL_PINS = [
     pin_mlp_bruteforce, pin_mlp_exact_example, pin_rmsnorm_torch, pin_rms_closed_forms,
     pin_unit_rms, pin_rowscale_commutes, pin_swiglu, pin_rope_closed_forms,
     pin_rope_torch_complex, pin_rope_relative, pin_attn_bruteforce, pin_ce_bruteforce,
-    pin_ce_torch, pin_ce_zero_weights, pin_lse_merge, pin_partial_sumsq, pin_fp8_block,
+    pin_ce_torch, pin_ce_zero_weights, pin_ce_ignored_rows, pin_lse_merge, pin_partial_sumsq, pin_fp8_block,
     pin_swiglu_grad, pin_layer_bwd_finite_differences, pin_layer_bwd_torch,
     pin_rmsnorm_bwd_scale_invariance, pin_bwd_row_coefficient,
 ]

@@ -14,15 +14,15 @@ from tests.gpu_util import (DEV, TOL_ROW, bf16_dev, dec_bf16, f32_dev, f32_host,
 pytestmark = pytest.mark.gpu
 
 
-def run_lse(w, r=None, W=None):
+def run_lse(w, r=None, W=None, labels=None):
     M, d, V = w.sizes["M"], w.sizes["d"], w.sizes["V"]
     x = bf16_dev(w.arrays["x"])
     wl = W if W is not None else bf16_dev(w.arrays["wlm"])
-    lab = i32_dev(w.arrays["labels"])
+    lab = i32_dev(w.arrays["labels"] if labels is None else labels)
     T = ops.lse_tiles(V)
     tmax = torch.empty(T, M, dtype=torch.float32, device=DEV)
     tsum = torch.empty_like(tmax)
-    zl = torch.empty(M, dtype=torch.float32, device=DEV)
+    zl = torch.full((M,), float("nan"), dtype=torch.float32, device=DEV)
     lse = torch.empty(M, dtype=torch.float32, device=DEV)
     loss = torch.empty(M, dtype=torch.float32, device=DEV)
     ops.gemm_block_lse(x, wl, lab, tmax, tsum, zl, loss, lse=lse,
@@ -32,11 +32,12 @@ def run_lse(w, r=None, W=None):
             "lse": f32_host(lse), "loss": f32_host(loss)}
 
 
-def oracle_rows(w, rows=None, r=None):
+def oracle_rows(w, rows=None, r=None, labels=None, chunk=256):
     sel = (lambda a: a) if rows is None else (lambda a: a[rows])
     rr = None if r is None else sel(r).astype(np.float64)
+    lab = w.arrays["labels"] if labels is None else labels
     return oracle.lm_head_ce(dec_bf16(sel(w.arrays["x"])), dec_bf16(w.arrays["wlm"]),
-                             sel(w.arrays["labels"]), r=rr)
+                             sel(lab), r=rr, chunk=chunk)
 
 
 def check_partials(w, got, rows):
@@ -88,15 +89,49 @@ def test_lse_zero_weights_gives_ln_v():
     assert float(np.max(np.abs(got["zl"]))) == 0.0
 
 
-def test_lm_head_full_sampled_rows():
-    """Full LM-head shape (M=8192, d=2048, V=128256); the oracle checks
-    sampled rows, the merge invariants run on a few of them."""
+def test_lse_ignored_labels():
+    """Labels outside [0, V) (an ignore index of -100, and V or more) mark rows
+    that carry no loss: loss 0 on those rows in the fused path and in the
+    unfused row cross entropy, lse still the row's log-sum-exp, every other
+    row unchanged (the label-logit buffer starts as NaN, so a read of an
+    unwritten entry would show)."""
+    w = inputs.make_lm(seed=14, M=300, d=192, V=1008)
+    lab = w.arrays["labels"].copy()
+    ign = np.array([0, 5, 17, 128, 255, 299])
+    lab[ign] = [-100, -1, 1008, 5000, -100, 2 ** 31 - 1]
+    say("block lse with ignored labels M=300 d=192 V=1008")
+    got = run_lse(w, labels=lab)
+    ref = oracle_rows(w, labels=lab)
+    keep = np.setdiff1d(np.arange(300), ign)
+    assert np.all(got["loss"][ign] == 0.0)
+    assert row_rel_err(got["loss"][keep], ref["loss"][keep]) <= TOL_ROW
+    assert row_rel_err(got["lse"], ref["lse"]) <= TOL_ROW
+    assert np.all(np.isnan(got["zl"][ign]))
+    # the unfused baseline: stored bf16 logits, then the row cross entropy
+    M, V = 300, 1008
+    x, wl = bf16_dev(w.arrays["x"]), bf16_dev(w.arrays["wlm"])
+    z = torch.empty(M, V, dtype=torch.bfloat16, device=DEV)
+    lse_u = torch.empty(M, dtype=torch.float32, device=DEV)
+    loss_u = torch.full((M,), float("nan"), dtype=torch.float32, device=DEV)
+    ops.gemm_bf16(x, wl, z)
+    ops.cross_entropy_rows(z, i32_dev(lab), lse_u, loss_u)
+    torch.cuda.synchronize()
+    lu = f32_host(loss_u)
+    assert np.all(lu[ign] == 0.0)
+    assert float(np.max(np.abs(lu[keep] - ref["loss"][keep]))) <= 0.05  # bf16 logits
+    assert float(np.max(np.abs(f32_host(lse_u) - ref["lse"]))) <= 0.05
+
+
+def test_lm_head_full_every_row():
+    """Full LM-head shape (M=8192, d=2048, V=128256) in the launch the
+    benchmark times: the loss and lse of every row against the oracle, and the
+    partial invariants on 64 rows."""
     w = inputs.make_workload("lm_head")
-    say("lm_head full size, sampled rows")
+    say("lm_head full size, every row")
     got = run_lse(w)
-    rows = sample_rows(w.sizes["M"], n=24)
-    ref = oracle_rows(w, rows)
-    assert row_rel_err(got["loss"][rows], ref["loss"]) <= TOL_ROW
-    assert row_rel_err(got["lse"][rows], ref["lse"]) <= TOL_ROW
-    assert np.all(np.isfinite(got["loss"]))
-    check_partials(w, got, rows[:4])
+    ref = oracle_rows(w, chunk=512)
+    assert row_rel_err(got["loss"], ref["loss"]) <= TOL_ROW
+    assert row_rel_err(got["lse"], ref["lse"]) <= TOL_ROW
+    assert float(np.max(np.abs(got["zl"] - ref["label_logit"]))) <= 1e-3
+    rows = sample_rows(w.sizes["M"], n=64)
+    check_partials(w, got, rows)

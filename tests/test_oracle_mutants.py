@@ -56,6 +56,19 @@ def _lse_merge_no_rescale(mx, se, order=None):
     return M + np.log(np.sum(se, axis=0))
 
 
+def _lm_head_ignored_keep_lse(x, wlm, labels, r=None, chunk=256):
+    o = _ORIG_LM(x, wlm, labels, r=r, chunk=chunk)
+    V = np.asarray(wlm).shape[0]
+    bad = (np.asarray(labels) < 0) | (np.asarray(labels) >= V)
+    o["loss"] = np.where(bad, o["lse"], o["loss"])
+    return o
+
+
+def _lm_head_ignored_clamped(x, wlm, labels, r=None, chunk=256):
+    V = np.asarray(wlm).shape[0]
+    return _ORIG_LM(x, wlm, np.clip(np.asarray(labels), 0, V - 1), r=r, chunk=chunk)
+
+
 def _lm_head_label_shift(x, wlm, labels, r=None, chunk=256):
     V = np.asarray(wlm).shape[0]
     return _ORIG_LM(x, wlm, (np.asarray(labels) + 1) % V, r=r, chunk=chunk)
@@ -120,6 +133,8 @@ MUTANTS = {
     "lse without max": ("logsumexp_rows", lambda z: np.log(np.sum(np.exp(np.asarray(z)), axis=1)) + 1e-3),
     "merge without rescale": ("lse_merge", _lse_merge_no_rescale),
     "label off by one": ("lm_head_ce", _lm_head_label_shift),
+    "ignored row keeps its lse as loss": ("lm_head_ce", _lm_head_ignored_keep_lse),
+    "out-of-range label clamped": ("lm_head_ce", _lm_head_ignored_clamped),
     "swiglu grad without the s(1-s) term": ("swiglu_grad", _swiglu_grad_no_curvature),
     "rmsnorm bwd correction dropped": ("rmsnorm_bwd", _rmsnorm_bwd_variant(sign=0.0)),
     "rmsnorm bwd correction sign": ("rmsnorm_bwd", _rmsnorm_bwd_variant(sign=1.0)),
