@@ -158,25 +158,25 @@ def main():
 
     print(f"[bench] warmup {args.warmup} steps (floor {args.warmup_ms:.0f} ms of GPU time)",
           file=sys.stderr, flush=True)
-    w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    w0.record(stream)
+    wa, wb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wa.record(stream)
     for _ in range(args.warmup):
         fused_step()
         unfused_step()
-    w1.record(stream)
+    wb.record(stream)
     torch.cuda.synchronize()
-    warm_ms, warm_pairs = w0.elapsed_time(w1), args.warmup
+    warm_ms, warm_pairs = wa.elapsed_time(wb), args.warmup
     while warm_ms < args.warmup_ms:
         # one fused + unfused pair takes about 1 ms; top up in chunks
         pair_ms = warm_ms / warm_pairs if warm_pairs else 1.0
         extra = int(min(500, max(1, np.ceil((args.warmup_ms - warm_ms) / max(pair_ms, 0.05)))))
-        w0.record(stream)
+        wa.record(stream)
         for _ in range(extra):
             fused_step()
             unfused_step()
-        w1.record(stream)
+        wb.record(stream)
         torch.cuda.synchronize()
-        warm_ms += w0.elapsed_time(w1)
+        warm_ms += wa.elapsed_time(wb)
         warm_pairs += extra
 
     print(f"[bench] timing {args.steps} fused steps", file=sys.stderr, flush=True)
@@ -458,6 +458,11 @@ def _mlp_bwd_row(torch, ops, inputs, stream, steps, warmup, bf, name="mlp_1b_bwd
         else:
             ops.gemm_bf16(dh_T, x_T, dWo)
 
+    # gradient of the RMSNorm gain: partial sums over 128-row slices of the
+    # gate|up weight gradient, then the light reduce
+    pdg = torch.empty(ops.dgamma_slices(2 * ffn), d, dtype=torch.float32, device=dev)
+    dgamma = torch.empty(d, dtype=torch.float32, device=dev)
+
     def dw():
         ops.transpose(h, h_T, row_scale=r)
         ops.transpose(dz, dz_T)
@@ -465,7 +470,9 @@ def _mlp_bwd_row(torch, ops, inputs, stream, steps, warmup, bf, name="mlp_1b_bwd
         ops.transpose(o, o_T)
         ops.transpose(dh, dh_T)
         ops.transpose(x, x_T)
-        ops.gemm_bf16(dz_T, h_T, dW2)
+        # dW = dW' diag(gamma) (unfolded gate|up) and the dgamma partials in its epilogue
+        ops.gemm_wgrad_gamma(dz_T, h_T, wgu, gamma, dW2, pdg)
+        ops.dgamma_reduce(pdg, dgamma)
         ops.gemm_bf16(dy_T, o_T, dWd)
         gemm_dwo()
 
@@ -504,6 +511,8 @@ def _mlp_bwd_row(torch, ops, inputs, stream, steps, warmup, bf, name="mlp_1b_bwd
 
     n_T = torch.empty(d, M, **bf16)
 
+    pdg_u = torch.empty_like(pdg)
+
     def dw_u():  # the same GEMMs; the normalised n (with gamma) is stored here
         ops.transpose(n_u, n_T)
         ops.transpose(dz_u, dz_T)
@@ -511,7 +520,10 @@ def _mlp_bwd_row(torch, ops, inputs, stream, steps, warmup, bf, name="mlp_1b_bwd
         ops.transpose(o_u, o_T)
         ops.transpose(dh_u, dh_T)
         ops.transpose(x, x_T)
-        ops.gemm_bf16(dz_T, n_T, dW2)
+        ops.gemm_bf16(dz_T, n_T, dW2)  # the unfolded gate|up gradient directly
+        # dgamma = sum_n dW * W / gamma: a column-dot pass over the stored gradient
+        ops.col_dot_partial(dW2, wgu, pdg_u)
+        ops.dgamma_reduce(pdg_u, dgamma, gamma_div=gamma)
         ops.gemm_bf16(dy_T, o_T, dWd)
         gemm_dwo()
 
@@ -523,6 +535,7 @@ def _mlp_bwd_row(torch, ops, inputs, stream, steps, warmup, bf, name="mlp_1b_bwd
     fwd_u()
     ms_bu = _events_time(torch, stream, bwd_u, steps, warmup)
     kbu = _kernel_times(torch, stream, bwd_uk, steps)
+    ms_wu = _events_time(torch, stream, dw_u, steps, warmup)
     ms_tu = _events_time(torch, stream, train_u, steps, warmup)
     # context only: the same backward chain in eager PyTorch (torch.mm on hipBLASLt with
     # contiguous operands; the SwiGLU gradient on bf16 tensors as autograd would run it, the
@@ -553,6 +566,9 @@ def _mlp_bwd_row(torch, ops, inputs, stream, steps, warmup, bf, name="mlp_1b_bwd
             "bwd_kernels_ms": dict(zip(("gemm_swiglu_bwd", "rms_bwd_reduce", "gemm_rmsnorm_bwd",
                                         "gemm_bf16_dx"), kb)),
             "dw_ms": round(ms_w, 4), "dwo_reduction_parts": parts_o, "dw_tflops": round(fl_w / ms_w / 1e9, 1),
+            "dw_note": "weight gradients of the unfolded weights (dWg|dWu = dW' diag(gamma) from "
+                       "the GEMM epilogue), dWd, dWo and dgamma (partial sums in the same "
+                       "epilogue + light reduce); the unfused sequence gives the same gradients",
             "weight_prep_ms": round(ms_p, 4),
             "train_step_ms": round(ms_t, 4), "train_step_tflops": round(fl_t / ms_t / 1e9, 1),
             "unfused": {"bwd_ms": round(ms_bu, 4), "bwd_tflops": round(fl_b / ms_bu / 1e9, 1),
@@ -560,6 +576,7 @@ def _mlp_bwd_row(torch, ops, inputs, stream, steps, warmup, bf, name="mlp_1b_bwd
                         "bwd_kernels_ms": dict(zip(("gemm_bf16_dout", "swiglu_bwd",
                                                     "gemm_bf16_G", "rmsnorm_bwd",
                                                     "gemm_bf16_dx"), kbu)),
+                        "dw_ms": round(ms_wu, 4),
                         "train_step_ms": round(ms_tu, 4),
                         "train_step_speedup_fused_vs_unfused": round(ms_tu / ms_t, 3)},
             "torch_eager_bwd": {"bwd_ms": round(ms_bt, 4),

@@ -215,6 +215,57 @@ int coda_gemm_swiglu_bwd(const void* dY, const void* WdT, const void* gu, void* 
   }
 }
 
+int coda_dgamma_slices(int M) { return M <= 0 ? 0 : (M + 127) / 128; }
+
+int coda_gemm_wgrad_gamma(const void* A, const void* B, const void* W, const float* gamma,
+                          void* dW, float* partial_dgamma, int M, int N, int K, void* stream) {
+  try {
+    if (!A || !B || !W || !gamma || !dW || !partial_dgamma) return CODA_ERR_NULL;
+    if (int st = check_gemm_shape(M, N, K, 64)) return st;
+    if (!small_enough(coda_dgamma_slices(M), N)) return CODA_ERR_SHAPE;
+    if (!aligned(A, 16) || !aligned(B, 16) || !aligned(W, 16) || !aligned(dW, 16) ||
+        !aligned(gamma, 16) || !aligned(partial_dgamma, 16))
+      return CODA_ERR_ALIGN;
+    if (int st = check_device()) return st;
+    return launched(coda::launch_gemm_wgrad_gamma_bf16(
+        static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B),
+        static_cast<const uint16_t*>(W), gamma, static_cast<uint16_t*>(dW), partial_dgamma, M, N,
+        K, as_stream(stream)));
+  } catch (...) {
+    return CODA_ERR_LAUNCH;
+  }
+}
+
+int coda_dgamma_reduce(const float* partial, int P, int N, const float* gamma_div, float* dgamma,
+                       void* stream) {
+  try {
+    if (!partial || !dgamma) return CODA_ERR_NULL;
+    if (P < 1 || N < 1 || !small_enough(P, N)) return CODA_ERR_SHAPE;
+    if (!aligned(partial, 4) || !aligned(dgamma, 4) || (gamma_div && !aligned(gamma_div, 4)))
+      return CODA_ERR_ALIGN;
+    if (int st = check_device()) return st;
+    return launched(coda::launch_dgamma_reduce(partial, P, N, gamma_div, dgamma,
+                                               as_stream(stream)));
+  } catch (...) {
+    return CODA_ERR_LAUNCH;
+  }
+}
+
+int coda_col_dot_partial(const void* X, const void* Y, int M, int N, float* partial,
+                         void* stream) {
+  try {
+    if (!X || !Y || !partial) return CODA_ERR_NULL;
+    if (M < 1 || N < 8 || N % 8 != 0 || !small_enough(M, N)) return CODA_ERR_SHAPE;
+    if (!aligned(X, 16) || !aligned(Y, 16) || !aligned(partial, 4)) return CODA_ERR_ALIGN;
+    if (int st = check_device()) return st;
+    return launched(coda::launch_col_dot_partial(static_cast<const uint16_t*>(X),
+                                                 static_cast<const uint16_t*>(Y), M, N, partial,
+                                                 as_stream(stream)));
+  } catch (...) {
+    return CODA_ERR_LAUNCH;
+  }
+}
+
 int coda_rms_bwd_reduce(const float* partial_dot, int T, int M, const float* r, int N, float* c,
                         void* stream) {
   try {

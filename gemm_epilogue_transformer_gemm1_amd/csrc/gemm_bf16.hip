@@ -445,7 +445,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_block_lse_bf16(
           }
       }
       se = sum_over_lane_groups(se);
-      const int loff = lab[i] - nw0;  // label's entry within this wave's window
+      // label's entry within this wave's window; labels at or past V (rows
+      // that carry no loss) match nothing, not even the padding of the last tile
+      const int loff = lab[i] < V ? lab[i] - nw0 : -1;
       if (__any((unsigned)loff < (unsigned)kLseTileWidth)) {
         float zl = 0.f;
         bool has = false;

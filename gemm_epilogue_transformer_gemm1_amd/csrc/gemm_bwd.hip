@@ -312,6 +312,161 @@ __global__ __launch_bounds__(kThreads, 1) void k_rmsnorm_bwd_bf16(RmsBwdArgs g, 
 }
 
 // ---------------------------------------------------------------------------
+// Weight gradient of the gamma-folded gate|up weight W' = W diag(gamma), with
+// the gradient of the RMSNorm gain as its epilogue (section "What CODA can
+// do": RMSNorm gradients; section "Five building blocks and a LEGO language":
+// block reduction).  The GEMM reduces over the tokens,
+//   G[n,k] = A[n,:] . B[k,:]    (A = dz^T [M, K], B = (r h)^T [N, K]; G = dW'),
+// and its epilogue reads the unfolded weight W [M, N] and gamma [N]:
+//   dW[n,k]   = bf16(G[n,k] gamma[k])                      (gradient of W)
+//   pdg[p, k] = sum over the 128 rows n of slice p of G[n,k] W[n,k]
+// so that dgamma[k] = sum_p pdg[p, k] (from W'[n,k] = W[n,k] gamma[k]).  A
+// wave's slice is its 128 rows; its 32 column sums per lane meet over the 16
+// rows of a lane group in four halving exchange steps, after which each lane
+// holds two adjacent columns.
+// ---------------------------------------------------------------------------
+struct WgradGammaArgs {
+  const uint16_t* A;      // [M, K]
+  const uint16_t* B;      // [N, K]
+  const uint16_t* W;      // [M, N]
+  const float* gamma;     // [N]
+  uint16_t* dW;           // [M, N]
+  float* pdg;             // [ceil(M / 128), N]
+  int M, N, K;
+};
+
+// One bf16 operand tile of the epilogue in the accumulator layout (a 4-feature
+// run per lane, 8-byte loads), loaded per token subtile as in EpiPairNarrow.
+struct EpiOne {
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t ld;
+  int nw0, N, wm, lane;
+  u32x2_t a[8][8];
+
+  __device__ __forceinline__ void load(int i) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int n = nw0 + 16 * j;
+      const uint32_t ml = (uint32_t)(wm * 128 + i * 16 + (lane & 15));
+      const uint32_t o = n < N ? (ml * ld + (uint32_t)(n + 4 * (lane >> 4))) * 2u : kOobOffset;
+      a[i][j] = __builtin_amdgcn_raw_buffer_load_b64(rs, o, 0, 0);
+    }
+  }
+};
+
+// Sum of v over the 16 lanes of each 16-lane group (lane bits 0..3), n values
+// per lane halving each step: on return lane L holds, in v[0] and v[1], the
+// sums of its group's values 2 (8 b3 + 4 b2 + 2 b1 + b0) + 0 and + 1, b_k the
+// bits of L.  All 64 lanes must take part.
+__device__ __forceinline__ void rows16_halving_sum(float (&v)[32], int lane) {
+#pragma unroll
+  for (int step = 0; step < 4; ++step) {
+    const int half = 16 >> step;      // values kept after this step
+    const int mask = 8 >> step;       // partner lane
+    const bool hi = (lane & mask) != 0;
+#pragma unroll
+    for (int c = 0; c < half; ++c) {
+      const float send = hi ? v[c] : v[c + half];
+      const float keep = hi ? v[c + half] : v[c];
+      v[c] = keep + __shfl_xor(send, mask, 64);
+    }
+  }
+}
+
+__device__ __forceinline__ void wgrad_gamma_tile(const WgradGammaArgs& g, char* smem, int m0,
+                                                 int n0, const TileChain& ch) {
+  const int tid = bwd_tile_tid();
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int gq = lane >> 4;
+  const int M = g.M, N = g.N;
+  const int nw0 = n0 + wn * 128;
+  const uint32_t rows_here = (uint32_t)min(kBM, M - m0);
+  EpiOne wt;
+  wt.rs = make_rsrc(g.W + (size_t)m0 * N, rows_here * (uint32_t)N * 2u);
+  wt.ld = (uint32_t)N;
+  wt.nw0 = nw0;
+  wt.N = N;
+  wt.wm = wm;
+  wt.lane = lane;
+  // gamma of the lane's 32 columns nw0 + 16 j + 4 gq + 0..3 (zero past N)
+  const __amdgpu_buffer_rsrc_t grs = make_rsrc(g.gamma, (uint32_t)N * 4u);
+  f32x4_t gm[8];
+  auto pre = [&] {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      gm[j] = __builtin_bit_cast(
+          f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                       grs, (uint32_t)(nw0 + 16 * j + 4 * gq) * 4u, 0, 0));
+    wt.load(0);
+  };
+  const __amdgpu_buffer_rsrc_t orsrc =
+      make_rsrc(g.dW + (size_t)m0 * N, rows_here * (uint32_t)N * 2u);
+  Acc acc;
+  mainloop_bf16<false, kBwdEpiVmem>(acc, smem, MainloopSrc{g.A, g.B, nullptr, M, N, g.K, m0, n0},
+                                    ch, pre, [&] { wt.load(1); wt.load(2); });
+
+  const bool godd = (gq & 1) != 0;
+  float ds[32];
+#pragma unroll
+  for (int c = 0; c < 32; ++c) ds[c] = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (i + 3 < 8) wt.load(i + 3);
+    const int ml = wm * 128 + i * 16 + (lane & 15);
+    const bool mv = m0 + ml < M;
+#pragma unroll
+    for (int j0 = 0; j0 < 8; j0 += 2) {
+      u32x2_t pk[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int j = j0 + u;
+        float wv[4], o[4];
+        unpack_bf16x4(wt.a[i][j], wv);  // zero past M or N
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float gv = acc.v[j][i][v];
+          ds[4 * j + v] = __builtin_fmaf(gv, wv[v], ds[4 * j + v]);
+          o[v] = gv * gm[j][v];
+        }
+        pk[u] = pack_bf16x4(o[0], o[1], o[2], o[3]);
+      }
+      const int n = nw0 + 16 * (j0 + (godd ? 1 : 0)) + 8 * (gq >> 1);
+      store16_exchanged(orsrc, pk, godd,
+                        (mv && n < N) ? ((uint32_t)ml * (uint32_t)N + (uint32_t)n) * 2u
+                                      : kOobOffset);
+    }
+  }
+  rows16_halving_sum(ds, lane);
+  // lane holds columns c0, c0 + 1 of its 4-wide runs: c = 2 (8 b3 + 4 b2 + 2 b1 + b0)
+  // indexes 4 j + v, so j = 4 b3 + 2 b2 + b1 and v = 2 b0
+  const int b = lane & 15;
+  const int col = nw0 + 16 * (b >> 1) + 4 * gq + 2 * (b & 1);
+  if (col < N && m0 + wm * 128 < M) {
+    const size_t p = (size_t)((m0 + wm * 128) / 128);
+    *(float2*)(g.pdg + p * N + col) = make_float2(ds[0], ds[1]);
+  }
+}
+
+__global__ __launch_bounds__(kThreads, 1) void k_gemm_wgrad_gamma_bf16(WgradGammaArgs g, int gm,
+                                                                        int gn) {
+  __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
+  const int nt = gm * gn;
+  bool prefetched = false;
+  for (int t = blockIdx.x; t < nt; t += gridDim.x) {
+    const TileCoord tc = map_tile(t, gm, gn, 8);
+    TileChain ch;
+    ch.prefetched = prefetched;
+    const bool has_next = t + (int)gridDim.x < nt;
+    const TileCoord nc = has_next ? map_tile(t + gridDim.x, gm, gn, 8) : tc;
+    ch.next = MainloopSrc{g.A, g.B, nullptr, g.M, g.N, g.K, nc.tm * kBM, nc.tn * kBN};
+    wgrad_gamma_tile(g, smem, tc.tm * kBM, tc.tn * kBN, ch);
+    prefetched = has_next;
+  }
+  wait_vm0();  // the last tile's unused prefetch into LDS lands before the block ends
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 static inline int cdiv_b(int a, int b) { return (a + b - 1) / b; }
@@ -331,6 +486,15 @@ hipError_t launch_rmsnorm_bwd_bf16(const uint16_t* dz, const uint16_t* W2T, cons
   const int gm = cdiv_b(M, kBM), gn = cdiv_b(N, kBN);
   hipLaunchKernelGGL(k_rmsnorm_bwd_bf16, dim3(min(gm * gn, cu_count())), dim3(kThreads), 0, stream,
                      RmsBwdArgs{dz, W2T, h, dY, r, c, dh, M, N, K}, gm, gn);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_wgrad_gamma_bf16(const uint16_t* A, const uint16_t* B, const uint16_t* W,
+                                       const float* gamma, uint16_t* dW, float* pdg, int M, int N,
+                                       int K, hipStream_t stream) {
+  const int gm = cdiv_b(M, kBM), gn = cdiv_b(N, kBN);
+  hipLaunchKernelGGL(k_gemm_wgrad_gamma_bf16, dim3(min(gm * gn, cu_count())), dim3(kThreads), 0,
+                     stream, WgradGammaArgs{A, B, W, gamma, dW, pdg, M, N, K}, gm, gn);
   return hipGetLastError();
 }
 

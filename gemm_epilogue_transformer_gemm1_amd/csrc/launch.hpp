@@ -30,6 +30,13 @@ hipError_t launch_swiglu_bwd_bf16(const uint16_t* dY, const uint16_t* WdT, const
 hipError_t launch_rmsnorm_bwd_bf16(const uint16_t* dz, const uint16_t* W2T, const uint16_t* h,
                                    const uint16_t* dY, const float* r, const float* c,
                                    uint16_t* dh, int M, int N, int K, hipStream_t stream);
+hipError_t launch_gemm_wgrad_gamma_bf16(const uint16_t* A, const uint16_t* B, const uint16_t* W,
+                                       const float* gamma, uint16_t* dW, float* pdg, int M, int N,
+                                       int K, hipStream_t stream);
+hipError_t launch_dgamma_reduce(const float* pdg, int P, int N, const float* gamma_div,
+                                float* dgamma, hipStream_t stream);
+hipError_t launch_col_dot_partial(const uint16_t* X, const uint16_t* Y, int M, int N, float* pdg,
+                                  hipStream_t stream);
 hipError_t launch_rms_bwd_reduce(const float* pdot, int T, int M, const float* r, int N, float* c,
                                  hipStream_t stream);
 hipError_t launch_swiglu_bwd(const uint16_t* dout, const uint16_t* gu, uint16_t* dz, int M, int N,

@@ -13,6 +13,20 @@ namespace coda {
 
 static inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
+// 8 bf16 (16 bytes) <-> 8 floats
+__device__ __forceinline__ void load8(const uint16_t* p, float* f) {
+  const i32x4_t raw = *(const i32x4_t*)p;
+  unpack_bf16x4(u32x2_t{(unsigned)raw.x, (unsigned)raw.y}, f);
+  unpack_bf16x4(u32x2_t{(unsigned)raw.z, (unsigned)raw.w}, f + 4);
+}
+
+__device__ __forceinline__ void store8(uint16_t* p, const float* f) {
+  const u32x2_t lo = pack_bf16x4(f[0], f[1], f[2], f[3]);
+  const u32x2_t hi = pack_bf16x4(f[4], f[5], f[6], f[7]);
+  *(i32x4_t*)p = i32x4_t{(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
+}
+
+
 // ---------------------------------------------------------------------------
 // The light reduction (section "CODA: the secret in the epilogue": a light
 // reduction kernel aggregates the partial RMS values).  Four lanes per token
@@ -95,6 +109,102 @@ hipError_t launch_rms_bwd_reduce(const float* pdot, int T, int M, const float* r
                                  hipStream_t stream) {
   hipLaunchKernelGGL(k_rms_bwd_reduce, dim3(cdiv(M, kReduceRowsPerBlock)), dim3(256), 0, stream,
                      pdot, T, M, r, 1.0f / (float)N, c);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Gradient of the RMSNorm gain.  The fused weight-gradient GEMM leaves partial
+// column sums pdg [P, N] (one row per 128-row slice of the gate|up weight);
+// the light reduction sums them in slice order (deterministic):
+//   dgamma[k] = sum_p pdg[p, k]          (divided by gamma[k] if gamma_div).
+// A 512-thread block owns 64 columns; wave w sums slices w, w + 8, ... with
+// four loads in flight, the eight partial sums meet in LDS.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(512) void k_dgamma_reduce(const float* __restrict__ pdg, int P,
+                                                       int N, const float* __restrict__ gamma_div,
+                                                       float* __restrict__ dgamma) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = blockIdx.x * 64 + lane;
+  const int cc = min(col, N - 1);
+  float s = 0.f;
+  int p = wave;
+  for (; p + 24 < P; p += 32) {
+    const float a0 = pdg[(size_t)p * N + cc], a1 = pdg[(size_t)(p + 8) * N + cc];
+    const float a2 = pdg[(size_t)(p + 16) * N + cc], a3 = pdg[(size_t)(p + 24) * N + cc];
+    s += (a0 + a1) + (a2 + a3);
+  }
+  for (; p < P; p += 8) s += pdg[(size_t)p * N + cc];
+  __shared__ float red[8][64];
+  red[wave][lane] = s;
+  __syncthreads();
+  if (wave == 0 && col < N) {
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) t += red[w][lane];
+    dgamma[col] = gamma_div ? t / gamma_div[col] : t;
+  }
+}
+
+hipError_t launch_dgamma_reduce(const float* pdg, int P, int N, const float* gamma_div,
+                                float* dgamma, hipStream_t stream) {
+  hipLaunchKernelGGL(k_dgamma_reduce, dim3(cdiv(N, 64)), dim3(512), 0, stream, pdg, P, N,
+                     gamma_div, dgamma);
+  return hipGetLastError();
+}
+
+// Unfused counterpart of the weight-gradient epilogue: per 128-row slice p,
+//   pdg[p, k] = sum over rows n of the slice of X[n, k] Y[n, k]   (bf16 in)
+// e.g. X = the stored unfolded-weight gradient dW, Y = W (then dgamma is that
+// sum divided by gamma).  A 256-thread block covers 512 columns of one slice:
+// each wave 32 of its rows, 8 columns per lane with 16-byte loads, the four
+// waves' sums meet in LDS.
+__global__ __launch_bounds__(256) void k_col_dot_partial(const uint16_t* __restrict__ X,
+                                                         const uint16_t* __restrict__ Y, int M,
+                                                         int N, float* __restrict__ pdg) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c0 = blockIdx.x * 512 + lane * 8;
+  const int r0 = blockIdx.y * 128 + wave * 32;
+  float acc[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+  if (c0 < N) {
+    const int rn = max(0, min(32, M - r0));
+    int k = 0;
+    for (; k + 4 <= rn; k += 4) {
+      float xv[4][8], yv[4][8];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        load8(X + (size_t)(r0 + k + u) * N + c0, xv[u]);
+        load8(Y + (size_t)(r0 + k + u) * N + c0, yv[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(xv[u][q], yv[u][q], acc[q]);
+    }
+    for (; k < rn; ++k) {
+      float xv[8], yv[8];
+      load8(X + (size_t)(r0 + k) * N + c0, xv);
+      load8(Y + (size_t)(r0 + k) * N + c0, yv);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(xv[q], yv[q], acc[q]);
+    }
+  }
+  __shared__ float red[4][512];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) red[wave][lane * 8 + q] = acc[q];
+  __syncthreads();
+  for (int c = threadIdx.x; c < 512; c += 256) {
+    const int col = blockIdx.x * 512 + c;
+    if (col < N)
+      pdg[(size_t)blockIdx.y * N + col] = (red[0][c] + red[1][c]) + (red[2][c] + red[3][c]);
+  }
+}
+
+hipError_t launch_col_dot_partial(const uint16_t* X, const uint16_t* Y, int M, int N, float* pdg,
+                                  hipStream_t stream) {
+  hipLaunchKernelGGL(k_col_dot_partial, dim3(cdiv(N, 512), cdiv(M, 128)), dim3(256), 0, stream, X,
+                     Y, M, N, pdg);
   return hipGetLastError();
 }
 
@@ -353,18 +463,6 @@ hipError_t launch_rope_tables(double theta, int max_pos, int head_dim, float* rc
 // back (section "The cost of laziness in large-model training": every
 // operator boundary is a write-back to GPU memory).  16 B per lane accesses.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void load8(const uint16_t* p, float* f) {
-  const i32x4_t raw = *(const i32x4_t*)p;
-  unpack_bf16x4(u32x2_t{(unsigned)raw.x, (unsigned)raw.y}, f);
-  unpack_bf16x4(u32x2_t{(unsigned)raw.z, (unsigned)raw.w}, f + 4);
-}
-
-__device__ __forceinline__ void store8(uint16_t* p, const float* f) {
-  const u32x2_t lo = pack_bf16x4(f[0], f[1], f[2], f[3]);
-  const u32x2_t hi = pack_bf16x4(f[4], f[5], f[6], f[7]);
-  *(i32x4_t*)p = i32x4_t{(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
-}
-
 __global__ __launch_bounds__(256) void k_residual_add(const uint16_t* __restrict__ y,
                                                       const uint16_t* __restrict__ res,
                                                       uint16_t* __restrict__ h, int64_t total8) {

@@ -61,6 +61,10 @@ _SIGNATURES = {
     "coda_swiglu_bwd": ([_p, _p, _p, _c_int, _c_int, _p], _c_int),
     "coda_transpose_bf16": ([_p, _p, _c_int, _c_int, _p, _c_int, _p], _c_int),
     "coda_rmsnorm_bwd": ([_p, _p, _p, _c_float, _p, _c_int, _c_int, _p], _c_int),
+    "coda_dgamma_slices": ([_c_int], _c_int),
+    "coda_gemm_wgrad_gamma": ([_p, _p, _p, _p, _p, _p, _c_int, _c_int, _c_int, _p], _c_int),
+    "coda_dgamma_reduce": ([_p, _c_int, _c_int, _p, _p, _p], _c_int),
+    "coda_col_dot_partial": ([_p, _p, _c_int, _c_int, _p, _p], _c_int),
 }
 
 
@@ -243,6 +247,46 @@ def rms_bwd_reduce(partial_dot, N, r, c, stream=None):
     _shape(c, (M,), "c")
     _call("coda_rms_bwd_reduce", _ptr(partial_dot, _F32, "partial_dot"), T, M, _ptr(r, _F32, "r"),
           int(N), _ptr(c, _F32, "c"), _stream(stream))
+
+
+def dgamma_slices(M):
+    """Number of 128-row slices of the dgamma partial sums for M weight rows."""
+    return lib().coda_dgamma_slices(int(M))
+
+
+def gemm_wgrad_gamma(A, B, W, gamma, dW, partial_dgamma, stream=None):
+    """dW = bf16((A B^T) * gamma) with A = dz^T, B = (r h)^T, and the partial
+    sums partial_dgamma[p, k] = sum over 128-row slice p of (A B^T)[n,k] W[n,k]."""
+    M, K = A.shape
+    N = B.shape[0]
+    for t, shp, what in ((B, (N, K), "B"), (W, (M, N), "W"), (gamma, (N,), "gamma"),
+                         (dW, (M, N), "dW"), (partial_dgamma, (dgamma_slices(M), N),
+                                              "partial_dgamma")):
+        _shape(t, shp, what)
+    _call("coda_gemm_wgrad_gamma", _ptr(A, _BF16, "A"), _ptr(B, _BF16, "B"), _ptr(W, _BF16, "W"),
+          _ptr(gamma, _F32, "gamma"), _ptr(dW, _BF16, "dW"),
+          _ptr(partial_dgamma, _F32, "partial_dgamma"), M, N, K, _stream(stream))
+
+
+def dgamma_reduce(partial, dgamma, gamma_div=None, stream=None):
+    """dgamma[k] = sum_p partial[p, k] (divided by gamma_div[k] if given)."""
+    P, N = partial.shape
+    _shape(dgamma, (N,), "dgamma")
+    gd = None
+    if gamma_div is not None:
+        _shape(gamma_div, (N,), "gamma_div")
+        gd = _ptr(gamma_div, _F32, "gamma_div")
+    _call("coda_dgamma_reduce", _ptr(partial, _F32, "partial"), P, N, gd,
+          _ptr(dgamma, _F32, "dgamma"), _stream(stream))
+
+
+def col_dot_partial(X, Y, partial, stream=None):
+    """partial[p, k] = sum over 128-row slice p of X[n,k] Y[n,k] (bf16 inputs)."""
+    M, N = X.shape
+    _shape(Y, (M, N), "Y")
+    _shape(partial, (dgamma_slices(M), N), "partial")
+    _call("coda_col_dot_partial", _ptr(X, _BF16, "X"), _ptr(Y, _BF16, "Y"), M, N,
+          _ptr(partial, _F32, "partial"), _stream(stream))
 
 
 def gemm_rmsnorm_bwd(dz, W2T, h, dY, r, c, dh, stream=None):

@@ -243,6 +243,31 @@ int coda_gemm_rmsnorm_bwd(const void* dz, const void* W2T, const void* h, const 
                           const float* r, const float* c, void* dh, int M, int N, int K,
                           void* stream);
 
+/* Weight gradient of the gamma-folded gate|up weight W' = W diag(gamma), with
+ * the gradient of the RMSNorm gain as its epilogue (section "What CODA can
+ * do": RMSNorm gradients; section "Five building blocks and a LEGO language":
+ * block reduction).  The GEMM reduces over the tokens:
+ *   G[n,k] = A[n,:] . B[k,:]            (fp32, never stored; G = dW' = dz^T (r h))
+ *   dW[n,k] = bf16( G[n,k] * gamma[k] )  (the gradient of the unfolded W)
+ *   partial_dgamma[p*N + k] = sum over n in [128 p, 128 p + 128) of G[n,k] W[n,k]
+ * A [M,K] bf16 = dz^T (M = 2 ffn rows, K = tokens), B [N,K] bf16 = (r h)^T
+ * (N = d), W [M,N] bf16 = the unfolded [Wg; Wu], gamma [N] fp32, dW [M,N]
+ * bf16, partial_dgamma [P,N] fp32 with P = coda_dgamma_slices(M).  Then
+ * coda_dgamma_reduce(partial_dgamma, P, N, NULL, dgamma) gives
+ * dgamma[k] = sum_n G[n,k] W[n,k] (W'[n,k] = W[n,k] gamma[k]).
+ * Sizes as coda_gemm_bf16; partial_dgamma 16-byte aligned. */
+int coda_dgamma_slices(int M);
+int coda_gemm_wgrad_gamma(const void* A, const void* B, const void* W, const float* gamma,
+                          void* dW, float* partial_dgamma, int M, int N, int K, void* stream);
+
+/* dgamma[k] = sum_{p < P} partial[p*N + k], summed in slice order
+ * (deterministic), divided by gamma_div[k] when gamma_div is not NULL (the
+ * unfused form, whose partial sums hold dW * W with dW = dW' gamma; gamma_div
+ * must then have no zero entry).  partial [P,N], dgamma, gamma_div [N] fp32.
+ * Sizes: P, N >= 1. */
+int coda_dgamma_reduce(const float* partial, int P, int N, const float* gamma_div, float* dgamma,
+                       void* stream);
+
 /* ---- weight preparation (run once per weight update, not per token) ---- */
 
 /* W_out[n,k] = bf16( W[n,k] * gamma[k] ): folds the RMSNorm gain, which lies
@@ -291,6 +316,11 @@ int coda_rope_tables(double theta, int max_pos, int head_dim, float* rope_cos, f
 /* C[m,n] = bf16( A[m,:] . W[n,:] ) -- the same mainloop, plain store.
  * Sizes as coda_gemm_residual_partialrms (bf16). */
 int coda_gemm_bf16(const void* A, const void* W, void* C, int M, int N, int K, void* stream);
+/* partial[p*N + k] = sum over rows n in [128 p, 128 p + 128) of X[n,k] Y[n,k]
+ * (fp32 sums of bf16 products), P = coda_dgamma_slices(M) slices: the
+ * unfused counterpart of the coda_gemm_wgrad_gamma epilogue (X = a stored
+ * weight gradient, Y = the weight).  X, Y [M,N] bf16; N % 8 == 0. */
+int coda_col_dot_partial(const void* X, const void* Y, int M, int N, float* partial, void* stream);
 /* h = bf16(y + res), all [count] bf16; count % 8 == 0. */
 int coda_residual_add(const void* y, const void* res, void* h, int64_t count, void* stream);
 /* out[m,n] = bf16( h[m,n] * r_m * gamma[n] ), r_m = 1/sqrt(mean_n h^2 + eps).

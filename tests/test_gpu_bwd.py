@@ -298,6 +298,28 @@ def run_weight_grads(w, fz):
     dW2, dWd, dWo = (torch.empty(2 * ffn, d, **bf), torch.empty(d, ffn, **bf),
                      torch.empty(d, K1, **bf))
     ops.gemm_bf16(dzT, hT, dW2)   # gradient of the folded [Wg'; Wu']
+    # the same GEMM with the RMSNorm-gain epilogue: the unfolded gradient
+    # dW = dW' diag(gamma) and the partial sums of dW' * W for dgamma
+    wgu = torch.cat([bf16_dev(w.arrays["wg"]), bf16_dev(w.arrays["wu"])], 0).contiguous()
+    gamma = f32_dev(w.arrays["gamma"])
+    dWu = torch.full((2 * ffn, d), float("nan"), **bf)
+    pdg = torch.full((ops.dgamma_slices(2 * ffn), d), float("nan"), dtype=torch.float32,
+                     device=DEV)
+    dgamma = torch.empty(d, dtype=torch.float32, device=DEV)
+    ops.gemm_wgrad_gamma(dzT, hT, wgu, gamma, dWu, pdg)
+    ops.dgamma_reduce(pdg, dgamma)
+    # unfused: the unfolded gradient from the stored normalised n, then the
+    # column-dot pass and the reduce divided by gamma
+    n_u = torch.empty(M, d, **bf)
+    ops.rmsnorm(fz["h"], gamma, EPS, n_u)
+    nT = torch.empty(d, M, **bf)
+    ops.transpose(n_u, nT)
+    dWn = torch.empty(2 * ffn, d, **bf)
+    ops.gemm_bf16(dzT, nT, dWn)
+    pdg_u = torch.full_like(pdg, float("nan"))
+    dgamma_u = torch.empty_like(dgamma)
+    ops.col_dot_partial(dWn, wgu, pdg_u)
+    ops.dgamma_reduce(pdg_u, dgamma_u, gamma_div=gamma)
     ops.gemm_bf16(dyT, outT, dWd)
     # dWo (d x K1) has few output tiles: its reduction over the M tokens is
     # split in parts (M a multiple of 64 * parts)
@@ -305,7 +327,7 @@ def run_weight_grads(w, fz):
     ws = torch.empty(parts, d, K1, dtype=torch.float32, device=DEV)
     ops.gemm_bf16_splitk(dhT, xT, dWo, ws)
     torch.cuda.synchronize()
-    return dict(dW2=dW2, dWd=dWd, dWo=dWo)
+    return dict(dW2=dW2, dWd=dWd, dWo=dWo, dWu=dWu, dgamma=dgamma, dWn=dWn, dgamma_u=dgamma_u)
 
 
 def check_weight_grads(w, wg_, ref):
@@ -317,6 +339,13 @@ def check_weight_grads(w, wg_, ref):
             "dwu": norm_err(dW2[ffn:] * gamma, ref["dwu"]),
             "dwd": norm_err(bf16_host(wg_["dWd"]), ref["dwd"]),
             "dwo": norm_err(bf16_host(wg_["dWo"]), ref["dwo"])}
+    # the unfolded gradient and dgamma from the epilogue, and from the unfused passes
+    dWu, dWn = bf16_host(wg_["dWu"]), bf16_host(wg_["dWn"])
+    errs.update({"dwg_epilogue": norm_err(dWu[:ffn], ref["dwg"]),
+                 "dwu_epilogue": norm_err(dWu[ffn:], ref["dwu"]),
+                 "dgamma": norm_err(f32_host(wg_["dgamma"]), ref["dgamma"]),
+                 "dwg_unfused": norm_err(dWn[:ffn], ref["dwg"]),
+                 "dgamma_unfused": norm_err(f32_host(wg_["dgamma_u"]), ref["dgamma"])})
     say(f"weight gradient errors {errs}")
     for k, e in errs.items():
         assert e <= TOL_BF16, (k, e)
@@ -329,6 +358,41 @@ def test_weight_grads_ragged_features():
     say("weight gradients M=576 d=448 K1=320 ffn=1056")
     fz = run_fused(w)
     check_weight_grads(w, run_weight_grads(w, fz), oracle_rows(w))
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 272, 128), (512, 256, 64), (1040, 528, 192)])
+def test_wgrad_gamma_exact(M, N, K):
+    """Integer operands make every sum exact: G = A B^T has |G| <= K, gamma in
+    {1/2, 1, 2, -1} keeps G gamma exact in bf16 (|G gamma| <= 256 with at most
+    8 significant bits), W in [-3, 3] keeps every partial sum an integer below
+    2^24.  dW, the partial sums and dgamma must equal the oracle bit for bit
+    (ragged rows and columns, one and several tiles, 128-row slices that end
+    inside a tile)."""
+    rng = np.random.default_rng(M + N + K)
+    a, b = _ints(rng, (M, K), -1, 1), _ints(rng, (N, K), -1, 1)
+    wt = _ints(rng, (M, N), -3, 3)
+    gam = rng.choice(np.array([0.5, 1.0, 2.0, -1.0], dtype=np.float32), size=N)
+    if K > 128:  # keep |G gamma| <= 256
+        gam = np.where(np.abs(gam) > 1, 1.0, gam).astype(np.float32)
+    say(f"wgrad gamma epilogue exact M={M} N={N} K={K}")
+    A, B, W = (bf16_dev(bf16_encode_few(v)) for v in (a, b, wt))
+    dW = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+    P = ops.dgamma_slices(M)
+    pdg = torch.full((P, N), float("nan"), dtype=torch.float32, device=DEV)
+    dg = torch.empty(N, dtype=torch.float32, device=DEV)
+    ops.gemm_wgrad_gamma(A, B, W, f32_dev(gam), dW, pdg)
+    ops.dgamma_reduce(pdg, dg)
+    pdg_u = torch.full((P, N), float("nan"), dtype=torch.float32, device=DEV)
+    ops.col_dot_partial(W, W, pdg_u)
+    torch.cuda.synchronize()
+    G = oracle.gemm_nt(a, b)
+    assert np.array_equal(bf16_host(dW), G * gam.astype(np.float64)[None, :])
+    ref_p = np.stack([np.sum(G[p * 128:(p + 1) * 128] * wt[p * 128:(p + 1) * 128], axis=0)
+                      for p in range(P)])
+    assert np.array_equal(f32_host(pdg), ref_p)
+    assert np.array_equal(f32_host(dg), np.sum(G * wt, axis=0))
+    ref_u = np.stack([np.sum(wt[p * 128:(p + 1) * 128] ** 2, axis=0) for p in range(P)])
+    assert np.array_equal(f32_host(pdg_u), ref_u)
 
 
 @pytest.mark.parametrize("rows,cols", [(130, 70), (128, 72), (8, 1024), (264, 392)])
