@@ -48,6 +48,36 @@ int check_device() {
 
 int launched(hipError_t e) { return e == hipSuccess ? CODA_OK : CODA_ERR_LAUNCH; }
 
+// Scratch of the entry point that allocates nothing (coda_gemm_block_lse_noalloc).
+// Host code never uses the array's name as an address: each device's copy is
+// located once with hipGetSymbolAddress and that pointer is used.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::atomic<int> g_scratch_state[kMaxDevices];  // 0 unknown, 1 ready, 2 failed
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+// This device's scratch pointer (the current device has passed check_device).
+void* device_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  int st = g_scratch_state[dev].load(std::memory_order_acquire);
+  if (st == 0) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e == hipSuccess && ptr) g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+    st = (e == hipSuccess && ptr) ? 1 : 2;
+    g_scratch_state[dev].store(st, std::memory_order_release);
+  }
+  return st == 1 ? g_scratch_ptr[dev].load(std::memory_order_acquire) : nullptr;
+}
+
+size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
+
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 int check_gemm_shape(int M, int N, int K, int kmul) {
@@ -362,6 +392,37 @@ int coda_gemm_block_lse(const void* X, const void* W, const float* r, const int3
       return launched(e);
     return launched(coda::launch_lse_merge(tile_max, tile_sumexp, label_logit, labels,
                                            coda_lse_tiles(V), M, V, lse, loss, s));
+  } catch (...) {
+    return CODA_ERR_LAUNCH;
+  }
+}
+
+size_t coda_lse_noalloc_max_bytes(void) { return kScratchBytes; }
+
+int coda_gemm_block_lse_noalloc(const void* X, const void* W, const float* r,
+                                const int32_t* labels, float* lse, float* loss, int M, int V,
+                                int K, void* stream) {
+  try {
+    if (!X || !W || !labels || !loss) return CODA_ERR_NULL;
+    if (int st = check_gemm_shape(M, V, K, 64)) return st;
+    const size_t T = (size_t)coda_lse_tiles(V);
+    const size_t part = round256(T * (size_t)M * 4);
+    if (2 * part + round256((size_t)M * 4) > kScratchBytes) return CODA_ERR_SHAPE;
+    if (!aligned(X, 16) || !aligned(W, 16) || !aligned(labels, 4) || !aligned(loss, 4) ||
+        (r && !aligned(r, 4)) || (lse && !aligned(lse, 4)))
+      return CODA_ERR_ALIGN;
+    if (int st = check_device()) return st;
+    char* base = static_cast<char*>(device_scratch());
+    if (!base) return CODA_ERR_DEVICE;
+    float* tmax = reinterpret_cast<float*>(base);
+    float* tsum = reinterpret_cast<float*>(base + part);
+    float* zl = reinterpret_cast<float*>(base + 2 * part);
+    hipStream_t s = as_stream(stream);
+    if (hipError_t e = coda::launch_block_lse_bf16(static_cast<const uint16_t*>(X),
+                                                   static_cast<const uint16_t*>(W), r, labels,
+                                                   tmax, tsum, zl, M, V, K, s))
+      return launched(e);
+    return launched(coda::launch_lse_merge(tmax, tsum, zl, labels, (int)T, M, V, lse, loss, s));
   } catch (...) {
     return CODA_ERR_LAUNCH;
   }

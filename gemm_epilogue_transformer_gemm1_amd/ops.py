@@ -62,6 +62,9 @@ _SIGNATURES = {
     "coda_transpose_bf16": ([_p, _p, _c_int, _c_int, _p, _c_int, _p], _c_int),
     "coda_rmsnorm_bwd": ([_p, _p, _p, _c_float, _p, _c_int, _c_int, _p], _c_int),
     "coda_dgamma_slices": ([_c_int], _c_int),
+    "coda_lse_noalloc_max_bytes": ([], ctypes.c_size_t),
+    "coda_gemm_block_lse_noalloc": ([_p, _p, _p, _p, _p, _p, _c_int, _c_int, _c_int, _p],
+                                    _c_int),
     "coda_gemm_wgrad_gamma": ([_p, _p, _p, _p, _p, _p, _c_int, _c_int, _c_int, _p], _c_int),
     "coda_dgamma_reduce": ([_p, _c_int, _c_int, _p, _p, _p], _c_int),
     "coda_col_dot_partial": ([_p, _p, _c_int, _c_int, _p, _p], _c_int),
@@ -366,6 +369,24 @@ def gemm_block_lse(X, W, labels, tile_max, tile_sumexp, label_logit, loss, lse=N
           _ptr(labels, _I32, "labels"), _ptr(tile_max, _F32, "tile_max"),
           _ptr(tile_sumexp, _F32, "tile_sumexp"), _ptr(label_logit, _F32, "label_logit"),
           _ptr(lse, _F32, "lse"), _ptr(loss, _F32, "loss"), M, V, K, _stream(stream))
+
+
+def gemm_block_lse_noalloc(X, W, labels, loss, lse=None, r=None, stream=None):
+    """coda_gemm_block_lse with the partials in the library's static scratch
+    (no allocation; calls on one GPU must not overlap)."""
+    M, K = X.shape
+    V = W.shape[0]
+    _shape(W, (V, K), "W")
+    for t, shp, what in ((labels, (M,), "labels"), (loss, (M,), "loss"), (lse, (M,), "lse"),
+                         (r, (M,), "r")):
+        _want(t, shp, what)
+    _call("coda_gemm_block_lse_noalloc", _ptr(X, _BF16, "X"), _ptr(W, _BF16, "W"),
+          _ptr(r, _F32, "r"), _ptr(labels, _I32, "labels"), _ptr(lse, _F32, "lse"),
+          _ptr(loss, _F32, "loss"), M, V, K, _stream(stream))
+
+
+def lse_noalloc_max_bytes():
+    return int(lib().coda_lse_noalloc_max_bytes())
 
 
 def fold_gamma(W, gamma, W_out, stream=None):

@@ -37,6 +37,7 @@
 #ifndef CODA_H
 #define CODA_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -181,6 +182,24 @@ int coda_gemm_rope(const void* h, const void* Wqkv, const float* r, const float*
 int coda_gemm_block_lse(const void* X, const void* W, const float* r, const int32_t* labels,
                         float* tile_max, float* tile_sumexp, float* label_logit, float* lse,
                         float* loss, int M, int V, int K, void* stream);
+
+/* coda_gemm_block_lse for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * kernels and results (lse, loss), with the per-tile (max, sum-exp) partials
+ * and the label logits kept in a scratch array of the library instead of
+ * caller workspace.  The array is a static device global of
+ * coda_lse_noalloc_max_bytes() bytes (64 MiB) that each GPU the library runs
+ * on holds until the process ends; the call allocates and frees nothing.
+ * Needs 2 * round256(4 T_v M) + round256(4 M) bytes of it (T_v =
+ * coda_lse_tiles(V)); larger sizes return CODA_ERR_SHAPE (M = 8192 at
+ * V = 128256 fits).  Nothing in the scratch needs clearing: every entry a
+ * call reads is written by that call.  All calls on one GPU share its
+ * scratch, so calls that overlap on one GPU (e.g. on two streams) race;
+ * order them on one stream.  Other arguments as coda_gemm_block_lse. */
+size_t coda_lse_noalloc_max_bytes(void);
+int coda_gemm_block_lse_noalloc(const void* X, const void* W, const float* r,
+                                const int32_t* labels, float* lse, float* loss, int M, int V,
+                                int K, void* stream);
 
 /* ---- backward of the MLP sub-layer ----
  *

@@ -18,7 +18,8 @@ A16 = 0x10000  # a fake 16-byte-aligned address, never dereferenced by these cal
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(coda_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(coda_\w+)\s*\(", text,
+                                 re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -144,6 +145,20 @@ def test_backward_validation(L):
     assert k(A16, A16, A16, A16, 64, 264, 512, 4, None) == ERR_SHAPE     # N % 16
     assert k(A16, A16, A16, A16, 256, 1 << 21, 64, 1, None) == ERR_SHAPE  # 256 N fp32 rows
     assert k(A16, A16, A16, A16 + 8, 64, 256, 512, 4, None) == ERR_ALIGN
+
+
+def test_noalloc_lse_validation(L):
+    """The LM head that allocates nothing rejects, before any HIP call, sizes
+    whose partials exceed its static scratch, and the usual bad arguments."""
+    f = L.coda_gemm_block_lse_noalloc
+    assert L.coda_lse_noalloc_max_bytes() == 64 << 20
+    # M = 16384 at V = 128256 needs 2 x 1002 x 16384 x 4 bytes: past 64 MiB
+    assert f(A16, A16, None, A16, None, A16, 16384, 128256, 2048, None) == ERR_SHAPE
+    assert f(None, A16, None, A16, None, A16, 64, 1024, 64, None) == ERR_NULL
+    assert f(A16, A16, None, A16, None, A16, 64, 1000, 64, None) == ERR_SHAPE   # V % 16
+    assert f(A16 + 2, A16, None, A16, None, A16, 64, 1024, 64, None) == ERR_ALIGN
+    # the full LM-head size fits: validation passes and only the device check remains
+    assert f(A16, A16, None, A16, None, A16, 8192, 128256, 2048, None) == ERR_DEVICE
 
 
 def test_binding_checks_backward_shapes():
