@@ -22,6 +22,7 @@
 // output feature nbase + 16 j + 4 (L / 16) + v of token mbase + 16 i + L % 16.
 
 #include "gemm_core.hpp"
+#include "gemm_core8.hpp"
 #include "launch.hpp"
 
 namespace coda {
@@ -39,57 +40,13 @@ __device__ __forceinline__ int bwd_tile_tid() {
 // above 47, so the next tile's first wait is vmcnt(63).
 constexpr int kBwdEpiVmem = 47;
 
-// Two bf16 operand tiles of the epilogue, [M, ld] each (buffers rs_a / rs_b
-// at column offsets col_a / col_b), loaded per token subtile i.  The
-// accumulator layout wants 4-feature runs (8 bytes) per lane; instead each
-// lane loads 16 bytes, 8 features of one row: for the feature subtile pair
-// (2 jp, 2 jp + 1), lanes of even 16-lane groups g read subtile 2 jp at
-// features 8 (g / 2) .. + 7 (their own run and that of group g + 1), lanes of
-// odd groups subtile 2 jp + 1 (the run of group g - 1 and their own), and
-// `runs` swaps the foreign halves between lanes 16 apart.  That halves the
-// vector memory instructions per subtile (8 instead of 16), so the operands
-// of three subtiles ahead and the stores between them stay within the 63
-// operations the wait counter can track and a wait for a subtile's operands
-// does not also wait for older stores.  Subtiles 0..2 are loaded during the
-// last two stages of the mainloop, subtile i + 3 while subtile i is processed.
-// Feature runs at or past N read at an out-of-range offset (zeros); rows past
-// M lie beyond the buffers, which start at the tile's first row.
-struct EpiPair {
-  __amdgpu_buffer_rsrc_t rs_a, rs_b;
-  uint32_t ld, col_a, col_b;
-  int nw0, N, wm, lane;
-  u32x4_t a[8][4], b[8][4];
-
-  __device__ __forceinline__ uint32_t off(int i, int jp, uint32_t col) const {
-    const int gq = lane >> 4;
-    const int n = nw0 + 16 * (2 * jp + (gq & 1));
-    const uint32_t ml = (uint32_t)(wm * 128 + i * 16 + (lane & 15));
-    return n < N ? (ml * ld + col + (uint32_t)(n + 8 * (gq >> 1))) * 2u : kOobOffset;
-  }
-  __device__ __forceinline__ void load(int i) {
-#pragma unroll
-    for (int jp = 0; jp < 4; ++jp) {
-      a[i][jp] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_a, off(i, jp, col_a), 0, 0));
-      b[i][jp] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_b, off(i, jp, col_b), 0, 0));
-    }
-  }
-  // This lane's runs of subtiles 2 jp (out[0]) and 2 jp + 1 (out[1]) from the
-  // 16 bytes it loaded; all 64 lanes must take part (lane shuffle).
-  __device__ __forceinline__ static void runs(const u32x4_t& v, bool godd, u32x2_t (&out)[2]) {
-    const u32x2_t lo = {v.x, v.y}, hi = {v.z, v.w};
-    const u32x2_t sd = godd ? lo : hi;
-    const u32x2_t rx = {(unsigned)__shfl_xor((int)sd.x, 16, 64),
-                        (unsigned)__shfl_xor((int)sd.y, 16, 64)};
-    out[0] = godd ? rx : lo;
-    out[1] = godd ? hi : rx;
-  }
-};
-
-// The RMSNorm-backward epilogue keeps 8-byte operand loads (one 4-feature run
-// per lane, the accumulator layout itself): with the 16-byte form its extra
-// exchange temporaries push the kernel past the register file.  Its epilogue
-// is small next to its mainloop (K = 2 ffn).  Same subtile schedule as
-// EpiPair; rows past M lie beyond the buffers.
+// The RMSNorm-backward epilogue's two operand tiles (h and dY, [M, ld] each),
+// loaded with 8-byte loads (one 4-feature run per lane, the accumulator layout
+// itself; a 16-byte form with a lane exchange needs temporaries that push
+// this kernel past the register file).  Its epilogue is small next to its
+// mainloop (K = 2 ffn).  Token subtiles 0..2 are loaded during the last two
+// stages of the mainloop, subtile i + 3 while subtile i is processed; rows
+// past M lie beyond the buffers, which start at the tile's first row.
 struct EpiPairNarrow {
   __amdgpu_buffer_rsrc_t rs_a, rs_b;
   uint32_t ld;
@@ -118,6 +75,20 @@ struct EpiPairNarrow {
 //   s = sigmoid(g), du = dout silu(g), dg = dout u (s + silu(g) (1 - s)),
 // stores dz = [dg | du] and the partial sums  sum (dg g + du u)  over each
 // wave's 128 features (T = ceil(N / 128) tiles, [T, M]).
+//
+// This GEMM runs on the two-waves-per-SIMD mainloop (gemm_core8.hpp): its
+// epilogue reads 256 KiB (g | u) and writes 256 KiB (dz) per 256 x 256 tile
+// and is bound by the loads the waves keep in flight, which eight waves
+// double; the mainloop itself is not faster with eight waves.  Each lane
+// loads its operands 16 bytes at a time (8 features of one row): for the
+// feature subtile pair (2 jp, 2 jp + 1), lanes of even 16-lane groups g read
+// subtile 2 jp at features 8 (g / 2) .. + 7 (their own 4-feature run and that
+// of group g + 1), odd groups subtile 2 jp + 1, and `runs` swaps the foreign
+// halves between lanes 16 apart.  Subtile 0 is loaded in the last stage of
+// the mainloop, subtile i + 1 while subtile i is processed (more ahead would
+// not fit the 128 registers a wave has beside its accumulators).  Feature
+// runs at or past N read at an out-of-range offset (zeros); rows past M lie
+// beyond the buffer, which starts at the tile's first row.
 // ---------------------------------------------------------------------------
 struct SwigluBwdArgs {
   const uint16_t* dY;   // [M, K]
@@ -126,6 +97,43 @@ struct SwigluBwdArgs {
   uint16_t* dz;         // [M, 2N]
   float* pdot;          // [T, M]
   int M, N, K;
+};
+
+// vector memory operations per lane the epilogue issues after the next
+// tile's loads: at least 3 x 8 operand loads and 4 x 8 stores
+constexpr int kSwigluBwdEpiVmem = 47;
+
+struct EpiGU {
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t ld, col_b;
+  int nw0, N, wm, lane;
+  u32x4_t a[4][4], b[4][4];
+
+  __device__ __forceinline__ uint32_t off(int i, int jp, uint32_t col) const {
+    const int gq = lane >> 4;
+    const int n = nw0 + 16 * (2 * jp + (gq & 1));
+    const uint32_t ml = (uint32_t)(wm * 64 + i * 16 + (lane & 15));
+    return n < N ? (ml * ld + col + (uint32_t)(n + 8 * (gq >> 1))) * 2u : kOobOffset;
+  }
+  __device__ __forceinline__ void load(int i) {
+#pragma unroll
+    for (int jp = 0; jp < 4; ++jp) {
+      a[i][jp] = __builtin_bit_cast(
+          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off(i, jp, 0), 0, 0));
+      b[i][jp] = __builtin_bit_cast(
+          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off(i, jp, col_b), 0, 0));
+    }
+  }
+  // This lane's runs of subtiles 2 jp (out[0]) and 2 jp + 1 (out[1]) from the
+  // 16 bytes it loaded; all 64 lanes must take part (lane shuffle).
+  __device__ __forceinline__ static void runs(const u32x4_t& v, bool godd, u32x2_t (&out)[2]) {
+    const u32x2_t lo = {v.x, v.y}, hi = {v.z, v.w};
+    const u32x2_t sd = godd ? lo : hi;
+    const u32x2_t rx = {(unsigned)__shfl_xor((int)sd.x, 16, 64),
+                        (unsigned)__shfl_xor((int)sd.y, 16, 64)};
+    out[0] = godd ? rx : lo;
+    out[1] = godd ? hi : rx;
+  }
 };
 
 __device__ __forceinline__ void swiglu_bwd_tile(const SwigluBwdArgs& g, char* smem, int m0, int n0,
@@ -138,34 +146,33 @@ __device__ __forceinline__ void swiglu_bwd_tile(const SwigluBwdArgs& g, char* sm
   const uint32_t ld = 2u * (uint32_t)N;
   const int nw0 = n0 + wn * 128;
   const uint32_t rows_here = (uint32_t)min(kBM, M - m0);
-  EpiPair z;
-  z.rs_a = make_rsrc(g.gu + (size_t)m0 * ld, rows_here * ld * 2u);
-  z.rs_b = z.rs_a;
+  EpiGU z;
+  z.rs = make_rsrc(g.gu + (size_t)m0 * ld, rows_here * ld * 2u);
   z.ld = ld;
-  z.col_a = 0;
   z.col_b = (uint32_t)N;
   z.nw0 = nw0;
   z.N = N;
   z.wm = wm;
   z.lane = lane;
   const __amdgpu_buffer_rsrc_t drsrc = make_rsrc(g.dz + (size_t)m0 * ld, rows_here * ld * 2u);
-  Acc acc;
-  mainloop_bf16<false, kBwdEpiVmem>(acc, smem, MainloopSrc{g.dY, g.WdT, nullptr, M, N, g.K, m0, n0},
-                                    ch, [&] { z.load(0); }, [&] { z.load(1); z.load(2); });
+  Acc8 acc;
+  mainloop8_bf16<false, kSwigluBwdEpiVmem>(
+      acc, smem, MainloopSrc{g.dY, g.WdT, nullptr, M, N, g.K, m0, n0}, ch, [] {},
+      [&] { z.load(0); });
 
   const bool godd = (gq & 1) != 0;
   const float kNegLog2e = -1.4426950408889634f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    if (i + 3 < 8) z.load(i + 3);
-    const int ml = wm * 128 + i * 16 + (lane & 15);
+  for (int i = 0; i < 4; ++i) {
+    if (i + 1 < 4) z.load(i + 1);
+    const int ml = wm * 64 + i * 16 + (lane & 15);
     const bool mv = m0 + ml < M;
     float ps = 0.f;
 #pragma unroll
     for (int j0 = 0; j0 < 8; j0 += 2) {
       u32x2_t pg[2], pu[2], ga[2], ub[2];
-      EpiPair::runs(z.a[i][j0 / 2], godd, ga);
-      EpiPair::runs(z.b[i][j0 / 2], godd, ub);
+      EpiGU::runs(z.a[i][j0 / 2], godd, ga);
+      EpiGU::runs(z.b[i][j0 / 2], godd, ub);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int j = j0 + u;
@@ -197,7 +204,7 @@ __device__ __forceinline__ void swiglu_bwd_tile(const SwigluBwdArgs& g, char* sm
   }
 }
 
-__global__ __launch_bounds__(kThreads, 1) void k_swiglu_bwd_bf16(SwigluBwdArgs g, int gm, int gn) {
+__global__ __launch_bounds__(kThreads8, 1) void k_swiglu_bwd_bf16(SwigluBwdArgs g, int gm, int gn) {
   __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
   const int nt = gm * gn;
   bool prefetched = false;
@@ -475,8 +482,8 @@ hipError_t launch_swiglu_bwd_bf16(const uint16_t* dY, const uint16_t* WdT, const
                                   uint16_t* dz, float* pdot, int M, int N, int K,
                                   hipStream_t stream) {
   const int gm = cdiv_b(M, kBM), gn = cdiv_b(N, kBN);
-  hipLaunchKernelGGL(k_swiglu_bwd_bf16, dim3(min(gm * gn, cu_count())), dim3(kThreads), 0, stream,
-                     SwigluBwdArgs{dY, WdT, gu, dz, pdot, M, N, K}, gm, gn);
+  hipLaunchKernelGGL(k_swiglu_bwd_bf16, dim3(min(gm * gn, cu_count())), dim3(kThreads8), 0,
+                     stream, SwigluBwdArgs{dY, WdT, gu, dz, pdot, M, N, K}, gm, gn);
   return hipGetLastError();
 }
 
