@@ -358,12 +358,14 @@ hipError_t launch_fold_gamma(const uint16_t* W, const float* gamma, uint16_t* W_
 // ---------------------------------------------------------------------------
 // Log-sum-exp merge of the per-tile (max, sum-exp) pairs (section "Five
 // building blocks and a LEGO language": the running max / sum-exp statistics
-// of online normalisation).  A 512-thread block owns 32 token rows and splits
-// each row's tiles over 16 lanes: lane l of wave w takes row 32*block + l%32
-// and tiles s, s+16, s+32, ... with s = 2w + l/32, so every load instruction
-// reads two 128-byte runs (32 consecutive rows of two tiles).  A lane merges
-// four tiles per step (one new max, five exponentials), the two halves of a
-// wave meet through one lane exchange and the eight waves through LDS.
+// of online normalisation).  A 1024-thread block owns 32 token rows and
+// splits each row's tiles over 32 lanes: lane l of wave w takes row
+// 32*block + l%32 and tiles s, s+32, s+64, ... with s = 2w + l/32, so every
+// load instruction reads two 128-byte runs (32 consecutive rows of two
+// tiles).  A lane merges four tiles per step (one new max, five exponentials)
+// and issues the next step's eight loads before it merges the current four,
+// so each lane keeps up to sixteen loads in flight; the two halves of a wave
+// meet through one lane exchange and the sixteen waves through LDS.
 //   lse = Mx + ln sum_t s_t e^(m_t - Mx);  loss = lse - label_logit,
 // and loss = 0 for a label outside [0, V) (a row that carries no loss; its
 // label logit is never read).
@@ -377,28 +379,38 @@ __device__ __forceinline__ void lse_combine(float& m, float& s, float m2, float 
 }
 
 constexpr int kMergeRows = 32;    // token rows per block
-constexpr int kMergeSlices = 16;  // lanes sharing one row
+constexpr int kMergeSlices = 32;  // lanes sharing one row (16 waves x 2 halves)
+constexpr int kMergeWaves = 16;
 
-__global__ __launch_bounds__(512) void k_lse_merge(const float* __restrict__ tmax,
-                                                   const float* __restrict__ tsum,
-                                                   const float* __restrict__ label_logit,
-                                                   const int* __restrict__ labels, int T, int M,
-                                                   int V, float* __restrict__ lse,
-                                                   float* __restrict__ loss) {
+__global__ __launch_bounds__(1024) void k_lse_merge(const float* __restrict__ tmax,
+                                                    const float* __restrict__ tsum,
+                                                    const float* __restrict__ label_logit,
+                                                    const int* __restrict__ labels, int T, int M,
+                                                    int V, float* __restrict__ lse,
+                                                    float* __restrict__ loss) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = lane & (kMergeRows - 1);
   const int m = blockIdx.x * kMergeRows + row;
-  const int mc = min(m, M - 1);
+  const size_t mc = (size_t)min(m, M - 1);
   const float k = 1.4426950408889634f;
+  constexpr int S = kMergeSlices;
   float rm = -INFINITY, rs = 0.f;
   int t = wave * 2 + (lane >> 5);
-  for (; t + 3 * kMergeSlices < T; t += 4 * kMergeSlices) {
-    float a[4], b[4];
+  auto load4 = [&](int t0, float (&a)[4], float (&b)[4]) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      a[q] = tmax[(size_t)(t + q * kMergeSlices) * M + mc];
-      b[q] = tsum[(size_t)(t + q * kMergeSlices) * M + mc];
+      a[q] = tmax[(size_t)(t0 + q * S) * M + mc];
+      b[q] = tsum[(size_t)(t0 + q * S) * M + mc];
     }
+  };
+  float a[4], b[4];
+  bool have = t + 3 * S < T;
+  if (have) load4(t, a, b);
+  while (have) {
+    const int tn = t + 4 * S;
+    const bool nhave = tn + 3 * S < T;
+    float na[4], nb[4];
+    if (nhave) load4(tn, na, nb);  // in flight while this step merges
     const float nm = fmaxf(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])), rm);
     if (nm != -INFINITY) {
       float acc = rs * __builtin_amdgcn_exp2f((rm - nm) * k);
@@ -407,11 +419,17 @@ __global__ __launch_bounds__(512) void k_lse_merge(const float* __restrict__ tma
       rs = acc;
       rm = nm;
     }
+    t = tn;
+    have = nhave;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      a[q] = na[q];
+      b[q] = nb[q];
+    }
   }
-  for (; t < T; t += kMergeSlices)
-    lse_combine(rm, rs, tmax[(size_t)t * M + mc], tsum[(size_t)t * M + mc]);
+  for (; t < T; t += S) lse_combine(rm, rs, tmax[(size_t)t * M + mc], tsum[(size_t)t * M + mc]);
   lse_combine(rm, rs, __shfl_xor(rm, 32, 64), __shfl_xor(rs, 32, 64));
-  __shared__ float pm[8][kMergeRows], ps[8][kMergeRows];
+  __shared__ float pm[kMergeWaves][kMergeRows], ps[kMergeWaves][kMergeRows];
   if (lane < kMergeRows) {
     pm[wave][lane] = rm;
     ps[wave][lane] = rs;
@@ -419,7 +437,7 @@ __global__ __launch_bounds__(512) void k_lse_merge(const float* __restrict__ tma
   __syncthreads();
   if (wave == 0 && lane < kMergeRows && m < M) {
 #pragma unroll
-    for (int w = 1; w < 8; ++w) lse_combine(rm, rs, pm[w][lane], ps[w][lane]);
+    for (int w = 1; w < kMergeWaves; ++w) lse_combine(rm, rs, pm[w][lane], ps[w][lane]);
     const float l = rm + logf(rs);
     if (lse) lse[m] = l;
     const int lab = labels[m];
@@ -430,8 +448,8 @@ __global__ __launch_bounds__(512) void k_lse_merge(const float* __restrict__ tma
 hipError_t launch_lse_merge(const float* tmax, const float* tsum, const float* label_logit,
                             const int* labels, int T, int M, int V, float* lse, float* loss,
                             hipStream_t stream) {
-  hipLaunchKernelGGL(k_lse_merge, dim3(cdiv(M, kMergeRows)), dim3(512), 0, stream, tmax, tsum,
-                     label_logit, labels, T, M, V, lse, loss);
+  hipLaunchKernelGGL(k_lse_merge, dim3(cdiv(M, kMergeRows)), dim3(64 * kMergeWaves), 0, stream,
+                     tmax, tsum, label_logit, labels, T, M, V, lse, loss);
   return hipGetLastError();
 }
 
