@@ -21,6 +21,8 @@
 // Accumulator layout: lane L, register v of the 16x16 tile (j, i) holds
 // output feature nbase + 16 j + 4 (L / 16) + v of token mbase + 16 i + L % 16.
 
+#include <type_traits>
+
 #include "gemm_core.hpp"
 #include "gemm_core8.hpp"
 #include "launch.hpp"
@@ -361,23 +363,38 @@ struct EpiOne {
   }
 };
 
-// Sum of v over the 16 lanes of each 16-lane group (lane bits 0..3), n values
-// per lane halving each step: on return lane L holds, in v[0] and v[1], the
-// sums of its group's values 2 (8 b3 + 4 b2 + 2 b1 + b0) + 0 and + 1, b_k the
-// bits of L.  All 64 lanes must take part.
+// Value of the lane given by a DPP row pattern (all lanes take part).
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, false));
+}
+
+// Sum of v over the 16 lanes of each 16-lane group (lane bits 0..3), the
+// values kept per lane halving each step: on return lane L holds, in v[0] and
+// v[1], the sums of its group's values 2 (8 b3 + 4 b2 + 2 b1 + b0) + 0 and + 1,
+// b_k the bits of L.  Step s pairs each lane with a partner that differs in
+// bit 3 - s and agrees in the bits decided before (partners L ^ 8, L ^ 7,
+// L ^ 2, L ^ 1: a row rotation by 8, the half-row mirror and two quad
+// permutations, all DPP moves rather than LDS-crossbar shuffles); the lane
+// with that bit set keeps the upper half of the values.
 __device__ __forceinline__ void rows16_halving_sum(float (&v)[32], int lane) {
+  auto step = [&](auto ctrl_tag, int half, int bit) {
+    constexpr int kCtrl = decltype(ctrl_tag)::value;
+    const bool hi = (lane & bit) != 0;
 #pragma unroll
-  for (int step = 0; step < 4; ++step) {
-    const int half = 16 >> step;      // values kept after this step
-    const int mask = 8 >> step;       // partner lane
-    const bool hi = (lane & mask) != 0;
-#pragma unroll
-    for (int c = 0; c < half; ++c) {
-      const float send = hi ? v[c] : v[c + half];
-      const float keep = hi ? v[c + half] : v[c];
-      v[c] = keep + __shfl_xor(send, mask, 64);
+    for (int c = 0; c < 16; ++c) {
+      if (c < half) {
+        const float send = hi ? v[c] : v[c + half];
+        const float keep = hi ? v[c + half] : v[c];
+        v[c] = keep + dpp_f32<kCtrl>(send);
+      }
     }
-  }
+  };
+  step(std::integral_constant<int, 0x128>{}, 16, 8);  // row_ror:8        (L ^ 8)
+  step(std::integral_constant<int, 0x141>{}, 8, 4);   // row_half_mirror  (L ^ 7)
+  step(std::integral_constant<int, 0x4E>{}, 4, 2);    // quad_perm 2,3,0,1 (L ^ 2)
+  step(std::integral_constant<int, 0xB1>{}, 2, 1);    // quad_perm 1,0,3,2 (L ^ 1)
 }
 
 __device__ __forceinline__ void wgrad_gamma_tile(const WgradGammaArgs& g, char* smem, int m0,
