@@ -19,13 +19,18 @@
 //     SIMD loop, but with two waves per SIMD the LDS serves them faster
 //     (measured on gfx950: ~183 B/clk per CU with 8 waves issuing 16-byte
 //     reads against ~110 with 4), and while one wave of a SIMD waits for its
-//     fragments, a barrier or its epilogue, the other one can issue MFMAs;
+//     fragments, a barrier or its epilogue operands, the other one can issue
+//     MFMAs.  Measured, the mainloop itself is no faster than
+//     mainloop_bf16's (equal at K = 2048, slower at K = 8192); what gains is
+//     an epilogue bound by memory operations in flight;
 //   * pipeline per stage kt (slot kt & 1; fa = the step-0 fragments, already
 //     in registers):
-//       R1: the 12 step-1 fragment reads (fb) within the first 3 groups of 4
-//           MFMAs on fa, one more group, then B1 (reads drained + barrier:
-//           slot kt & 1 is free everywhere), then fa's last 4 groups with the
-//           8 loads of stage kt+2 into that slot;
+//       R1: 8 groups of 4 MFMAs on fa; the 12 step-1 fragment reads (fb)
+//           within the first kRdGroups groups (default 3), B1 after group
+//           kB1 - 1 (default 4: reads drained + barrier, slot kt & 1 is free
+//           everywhere), the 8 loads of stage kt+2 into that slot in the
+//           groups after it (later barriers and other read spreads measured
+//           equal or slower);
 //       R2: 8 groups of 2 MFMAs on fb (weight subtiles 0..3);
 //       B2: this wave's stage kt+1 loads landed (kt+2 stays in flight), barrier;
 //       R3: 16 single MFMAs on fb (weight subtiles 4..7), the 12 step-0
