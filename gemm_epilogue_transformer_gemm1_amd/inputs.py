@@ -22,6 +22,10 @@ The shapes and distributions follow the LLaMA-3-shaped workloads:
   mlp_7b     M=8192,  d=4096, K1=4096, ffn=11008 (bf16)
   mlp_70b    M=8192,  d=8192, K1=8192, ffn=28672 (bf16)
   mlp_1b_bwd as mlp_1b, plus down projection wd and output gradient dy
+  layer_1b   one transformer layer at the 1B shape: the attn_rope block (the
+             previous MLP's down projection, K1=8192, then QKV + RoPE), causal
+             grouped-query attention over 4 sequences of 2048, then the mlp_1b
+             block with the attention output projection wo as its GEMM1
 Activations and residuals ~ N(0, 1); weights ~ N(0, 1/fan_in of the layer
 they feed, i.e. 1/d for the d-wide layers); gamma = 1 + 0.1 N(0, 1).
 """
@@ -48,10 +52,13 @@ WORKLOADS = {
     # forward + backward of the 1B-shaped MLP sub-layer (adds the down
     # projection and the gradient arriving at the sub-layer's output)
     "mlp_1b_bwd": (7, "mlp_bwd", dict(M=8192, d=2048, K1=2048, ffn=8192)),
+    # one transformer layer (attention input block -> attention -> MLP block)
+    "layer_1b": (8, "layer", dict(M=8192, d=2048, K1=8192, ffn=8192, n_q=32, n_kv=8,
+                                  head_dim=64, theta=500000.0, seq_len=2048)),
 }
 
 _TENSOR_IDS = {"x": 0, "res": 1, "w1": 2, "wg": 3, "wu": 4, "gamma": 5, "wqkv": 6,
-               "wlm": 7, "labels": 8, "wd": 9, "dy": 10}
+               "wlm": 7, "labels": 8, "wd": 9, "dy": 10, "wo": 11, "gamma2": 12}
 
 
 def _rng(seed, workload_id, tensor):
@@ -166,6 +173,25 @@ def make_mlp_fp8(seed=0, M=64, d=256, K1=256, ffn=512, workload_id=4, name="mlp_
     return w
 
 
+def make_layer(seed=0, M=64, d=256, K1=512, ffn=512, n_q=4, n_kv=2, head_dim=64,
+               theta=500000.0, seq_len=32, workload_id=8, name="layer"):
+    """One transformer layer in the periodic form of the hot path: the inputs
+    of make_attn (x = the previous MLP activation [M,K1], res [M,d], w1 = its
+    down projection [d,K1], wqkv, gamma, positions m mod seq_len) plus the
+    attention output projection wo [d, n_q hd] ~ N(0, 1/(n_q hd)), the gate and
+    up weights wg/wu [ffn,d] ~ N(0, 1/d) and the second RMSNorm gain gamma2."""
+    w = make_attn(seed, M, d, K1, n_q, n_kv, head_dim, theta, seq_len, workload_id, name)
+    w.kind = "layer"
+    w.sizes["ffn"] = ffn
+    w.arrays["wo"] = to_bf16_bits(normal_f32(seed, workload_id, "wo", (d, n_q * head_dim),
+                                             (n_q * head_dim) ** -0.5))
+    w.arrays["wg"] = to_bf16_bits(normal_f32(seed, workload_id, "wg", (ffn, d), d ** -0.5))
+    w.arrays["wu"] = to_bf16_bits(normal_f32(seed, workload_id, "wu", (ffn, d), d ** -0.5))
+    g = normal_f32(seed, workload_id, "gamma2", (d,), 1.0)
+    w.arrays["gamma2"] = (np.float32(1.0) + np.float32(0.1) * g).astype(np.float32)
+    return w
+
+
 def make_workload(name, seed=0, **overrides):
     """Build a named workload at its full sizes (or with sizes overridden)."""
     wid, kind, sizes = WORKLOADS[name]
@@ -181,4 +207,6 @@ def make_workload(name, seed=0, **overrides):
         return make_mlp_bwd(seed, workload_id=wid, name=name, **sizes)
     if kind == "mlp_fp8":
         return make_mlp_fp8(seed, workload_id=wid, name=name, **sizes)
+    if kind == "layer":
+        return make_layer(seed, workload_id=wid, name=name, **sizes)
     raise KeyError(name)

@@ -23,6 +23,12 @@ tests/test_oracle_*.py.  Parity status per function:
                             torch rms_norm/silu, commutation identity)
   attn_in_block, rope_*     pinned (brute force, rotation closed forms,
                             relative-position invariant, torch complex mult.)
+  attention_causal_gqa      pinned (brute force with math.fsum, torch
+                            scaled_dot_product_attention, first-query and
+                            equal-key closed forms)
+  layer_forward             pinned (torch float64 layer from rms_norm,
+                            complex rotation, scaled_dot_product_attention,
+                            silu)
   lm_head_ce, lse_*         pinned (brute force with math.fsum, torch
                             cross_entropy, W=0 closed form, merge order)
   partial_sumsq, tile_lse   pinned (sum identities with the row results)
@@ -50,6 +56,8 @@ from .reference import (  # noqa: F401
     rope_tables,
     apply_rope,
     attn_in_block,
+    attention_causal_gqa,
+    layer_forward,
     logsumexp_rows,
     lm_head_ce,
     partial_sumsq,

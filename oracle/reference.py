@@ -256,6 +256,60 @@ def attn_in_block(a, res, w1, wqkv, gamma, eps, pos, n_q, n_kv, head_dim, theta,
 
 
 # ---------------------------------------------------------------------------
+# attention core and the full layer (section "What CODA can do": every
+# operator of the layer except attention and the embedding is re-parameterised;
+# attention itself is the plain definition here, needed for the layer forward)
+# ---------------------------------------------------------------------------
+
+def attention_causal_gqa(qkv, seq_len, n_q, n_kv, head_dim):
+    """Causal grouped-query softmax attention.
+
+    qkv [M, (n_q + 2 n_kv) hd] laid out q | k | v, hd features per head; rows
+    [s L, (s+1) L) form sequence s (L = seq_len).  Reading (the page gives no
+    attention formula; this is the standard causal form): q head h attends
+    with kv head h // (n_q / n_kv); the score of query i and key j is
+    q_i . k_j / sqrt(hd); key j is visible to query i iff both lie in the same
+    sequence and j <= i; o_i = sum_j softmax_j(score_ij) v_j.
+    Returns o [M, n_q hd]."""
+    qkv = np.asarray(qkv, dtype=np.float64)
+    M = qkv.shape[0]
+    hd = head_dim
+    group = n_q // n_kv
+    o = np.empty((M, n_q * hd))
+    visible = np.tril(np.ones((seq_len, seq_len), dtype=bool))
+    for s0 in range(0, M, seq_len):
+        rows = slice(s0, s0 + seq_len)
+        for h in range(n_q):
+            g = h // group
+            q = qkv[rows, h * hd:(h + 1) * hd]
+            k = qkv[rows, (n_q + g) * hd:(n_q + g + 1) * hd]
+            v = qkv[rows, (n_q + n_kv + g) * hd:(n_q + n_kv + g + 1) * hd]
+            sc = np.where(visible, (q @ k.T) / np.sqrt(hd), -np.inf)
+            p = np.exp(sc - np.max(sc, axis=1, keepdims=True))
+            o[rows, h * hd:(h + 1) * hd] = (p / np.sum(p, axis=1, keepdims=True)) @ v
+    return o
+
+
+def layer_forward(a, res, w_down, wqkv, gamma1, wo, wg, wu, gamma2, eps, pos, n_q, n_kv,
+                  head_dim, theta, seq_len):
+    """One pre-norm transformer layer, in the periodic form of the hot path
+    (each GEMM output that feeds an RMSNorm is a residual add):
+      h1  = res + a w_down^T             (the previous MLP's down projection)
+      qkv = RoPE(RMSNorm(h1; gamma1) wqkv^T) on the q and k heads
+      o   = attention_causal_gqa(qkv)
+      h2  = h1 + o wo^T                  (attention output projection)
+      out = SwiGLU(RMSNorm(h2; gamma2) wg^T, RMSNorm(h2; gamma2) wu^T)
+    out is what the layer's own down projection reads next.
+    Returns dict(h1, r1, qkv, o, h2, r2, out)."""
+    f1 = attn_in_block(a, res, w_down, wqkv, gamma1, eps, pos, n_q, n_kv, head_dim, theta,
+                       seq_len)
+    o = attention_causal_gqa(f1["qkv"], seq_len, n_q, n_kv, head_dim)
+    f2 = mlp_block(o, f1["h"], wo, wg, wu, gamma2, eps)
+    return {"h1": f1["h"], "r1": f1["r"], "qkv": f1["qkv"], "o": o, "h2": f2["h"],
+            "r2": f2["r"], "out": f2["out"]}
+
+
+# ---------------------------------------------------------------------------
 # LM head cross entropy via log-sum-exp
 # ---------------------------------------------------------------------------
 

@@ -241,6 +241,127 @@ def pin_attn_bruteforce(seed=8):
 
 
 # ---------------------------------------------------------------------------
+# attention core and the full layer
+# ---------------------------------------------------------------------------
+
+def _qkv_random(rng, M, n_q, n_kv, hd, scale=1.0):
+    return rng.standard_normal((M, (n_q + 2 * n_kv) * hd)) * scale
+
+
+def pin_attention_bruteforce(seed=20):
+    """Pure-Python causal grouped-query attention (math.exp, math.fsum) on two
+    sequences of 5 rows, 4 q heads over 2 kv heads of 4 features."""
+    rng = np.random.default_rng(seed)
+    L, n_seq, n_q, n_kv, hd = 5, 2, 4, 2, 4
+    M = L * n_seq
+    qkv = _qkv_random(rng, M, n_q, n_kv, hd, 1.5)
+    o = R.attention_causal_gqa(qkv, L, n_q, n_kv, hd)
+    err = 0.0
+    for m in range(M):
+        s0 = (m // L) * L
+        for h in range(n_q):
+            g = h // (n_q // n_kv)
+            q = qkv[m, h * hd:(h + 1) * hd]
+            sc = []
+            for j in range(s0, m + 1):
+                k = qkv[j, (n_q + g) * hd:(n_q + g + 1) * hd]
+                sc.append(math.fsum(float(q[e]) * float(k[e]) for e in range(hd)) / math.sqrt(hd))
+            mx = max(sc)
+            w = [math.exp(x - mx) for x in sc]
+            z = math.fsum(w)
+            for e in range(hd):
+                vcol = (n_q + n_kv + g) * hd + e
+                ref = math.fsum(w[t] * float(qkv[s0 + t, vcol]) for t in range(len(w))) / z
+                err = max(err, abs(o[m, h * hd + e] - ref))
+    return _ok(err, 1e-12, "attention brute force")
+
+
+def pin_attention_torch(seed=21):
+    """torch's scaled_dot_product_attention (CPU, float64, is_causal) with the
+    kv heads repeated for their q-head groups."""
+    rng = np.random.default_rng(seed)
+    L, n_seq, n_q, n_kv, hd = 17, 3, 6, 2, 8
+    M = L * n_seq
+    qkv = _qkv_random(rng, M, n_q, n_kv, hd)
+    o = R.attention_causal_gqa(qkv, L, n_q, n_kv, hd)
+    t = torch.from_numpy(qkv).view(n_seq, L, n_q + 2 * n_kv, hd).permute(0, 2, 1, 3)
+    q, k, v = t[:, :n_q], t[:, n_q:n_q + n_kv], t[:, n_q + n_kv:]
+    rep = n_q // n_kv
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        q, k.repeat_interleave(rep, dim=1), v.repeat_interleave(rep, dim=1), is_causal=True)
+    ref = ref.permute(0, 2, 1, 3).reshape(M, n_q * hd).numpy()
+    return _ok(_rel(o, ref), 1e-13, "attention vs torch sdpa")
+
+
+def pin_attention_closed_forms(seed=22):
+    """The first query of each sequence sees only its own key, so its output
+    is that key's v row; with every key of a kv head equal, the softmax over
+    the visible keys is uniform, so query i gets the mean of v over the keys
+    0..i of its sequence."""
+    rng = np.random.default_rng(seed)
+    L, n_seq, n_q, n_kv, hd = 9, 2, 4, 1, 8
+    M = L * n_seq
+    qkv = _qkv_random(rng, M, n_q, n_kv, hd)
+    o = R.attention_causal_gqa(qkv, L, n_q, n_kv, hd)
+    vlo = (n_q + n_kv) * hd
+    e = 0.0
+    for s0 in (0, L):
+        for h in range(n_q):
+            e = max(e, float(np.max(np.abs(o[s0, h * hd:(h + 1) * hd] - qkv[s0, vlo:vlo + hd]))))
+    qkv2 = qkv.copy()
+    qkv2[:, n_q * hd:(n_q + 1) * hd] = rng.standard_normal(hd)[None, :]  # one key for all rows
+    o2 = R.attention_causal_gqa(qkv2, L, n_q, n_kv, hd)
+    for m in range(M):
+        s0 = (m // L) * L
+        mean = np.mean(qkv2[s0:m + 1, vlo:vlo + hd], axis=0)
+        for h in range(n_q):
+            e = max(e, float(np.max(np.abs(o2[m, h * hd:(h + 1) * hd] - mean))))
+    return _ok(e, 1e-13, "attention closed forms")
+
+
+def pin_layer_torch(seed=23):
+    """The whole layer in torch float64 from library routines: rms_norm,
+    rotation as complex multiplication, scaled_dot_product_attention with the
+    kv heads repeated, silu."""
+    rng = np.random.default_rng(seed)
+    L, n_seq, d, K1, ffn, n_q, n_kv, hd = 6, 2, 16, 12, 20, 4, 2, 4
+    M, theta, eps = L * n_seq, 500000.0, 1e-5
+    a = rng.standard_normal((M, K1))
+    res = rng.standard_normal((M, d))
+    w_down = rng.standard_normal((d, K1)) / math.sqrt(K1)
+    wqkv = rng.standard_normal(((n_q + 2 * n_kv) * hd, d)) / math.sqrt(d)
+    wo = rng.standard_normal((d, n_q * hd)) / math.sqrt(n_q * hd)
+    wg, wu = (rng.standard_normal((ffn, d)) / math.sqrt(d) for _ in range(2))
+    g1, g2 = 1 + 0.1 * rng.standard_normal(d), 1 + 0.1 * rng.standard_normal(d)
+    pos = np.arange(M) % L
+    o = R.layer_forward(a, res, w_down, wqkv, g1, wo, wg, wu, g2, eps, pos, n_q, n_kv, hd,
+                        theta, L)
+    T = lambda x: torch.from_numpy(np.asarray(x, dtype=np.float64))
+    h1 = T(res) + T(a) @ T(w_down).T
+    n1 = torch.nn.functional.rms_norm(h1, (d,), weight=T(g1), eps=eps)
+    y = (n1 @ T(wqkv).T).view(M, n_q + 2 * n_kv, 2, hd // 2)
+    inv = theta ** (-torch.arange(hd // 2, dtype=torch.float64) * 2 / hd)
+    ang = T(pos)[:, None] * inv[None, :]
+    z = torch.complex(y[:, :, 0], y[:, :, 1])
+    rot = z * torch.polar(torch.ones_like(ang), ang)[:, None, :]
+    nr = n_q + n_kv
+    yr = torch.cat([torch.stack([rot.real, rot.imag], dim=2)[:, :nr], y[:, nr:]], dim=1)
+    qkv = yr.reshape(M, (n_q + 2 * n_kv) * hd)
+    t = qkv.view(n_seq, L, n_q + 2 * n_kv, hd).permute(0, 2, 1, 3)
+    rep = n_q // n_kv
+    att = torch.nn.functional.scaled_dot_product_attention(
+        t[:, :n_q], t[:, n_q:nr].repeat_interleave(rep, dim=1),
+        t[:, nr:].repeat_interleave(rep, dim=1), is_causal=True)
+    att = att.permute(0, 2, 1, 3).reshape(M, n_q * hd)
+    h2 = h1 + att @ T(wo).T
+    n2 = torch.nn.functional.rms_norm(h2, (d,), weight=T(g2), eps=eps)
+    out = torch.nn.functional.silu(n2 @ T(wg).T) * (n2 @ T(wu).T)
+    err = max(_rel(o["qkv"], qkv.numpy()), _rel(o["o"], att.numpy()), _rel(o["h2"], h2.numpy()),
+              _rel(o["out"], out.numpy()))
+    return _ok(err, 1e-12, "layer vs torch")
+
+
+# ---------------------------------------------------------------------------
 # LSE / cross entropy
 # ---------------------------------------------------------------------------
 
@@ -542,7 +663,8 @@ def pin_bwd_row_coefficient(seed=18):
 ALL_PINS = [
     pin_mlp_bruteforce, pin_mlp_exact_example, pin_rmsnorm_torch, pin_rms_closed_forms,
     pin_unit_rms, pin_rowscale_commutes, pin_swiglu, pin_rope_closed_forms,
-    pin_rope_torch_complex, pin_rope_relative, pin_attn_bruteforce, pin_ce_bruteforce,
+    pin_rope_torch_complex, pin_rope_relative, pin_attn_bruteforce, pin_attention_bruteforce,
+    pin_attention_torch, pin_attention_closed_forms, pin_layer_torch, pin_ce_bruteforce,
     pin_ce_torch, pin_ce_zero_weights, pin_ce_ignored_rows, pin_lse_merge, pin_partial_sumsq, pin_fp8_block,
     pin_swiglu_grad, pin_layer_bwd_finite_differences, pin_layer_bwd_torch,
     pin_rmsnorm_bwd_scale_invariance, pin_bwd_row_coefficient,

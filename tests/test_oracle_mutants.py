@@ -11,6 +11,7 @@ from tests import oracle_pins
 _ORIG_ROPE = R.apply_rope
 _ORIG_LM = R.lm_head_ce
 _ORIG_DEC = codecs.e4m3_decode
+_ORIG_ATT = R.attention_causal_gqa
 
 
 def _mlp_block_no_gamma(x, res, wo, wg, wu, gamma, eps):
@@ -118,6 +119,29 @@ def _layer_bwd_up_gate_swapped(x, res, wo, wg, wu, gamma, eps, wd, dy):
     return _ORIG_LAYER_BWD(x, res, wo, wu, wg, gamma, eps, wd, dy)
 
 
+def _attention_variant(mask="causal", group="div", scale="sqrt", cross_seq=False):
+    def att(qkv, seq_len, n_q, n_kv, head_dim):
+        qkv = np.asarray(qkv, dtype=np.float64)
+        M, hd = qkv.shape[0], head_dim
+        L = M if cross_seq else seq_len
+        o = np.empty((M, n_q * hd))
+        tri = {"causal": np.tril(np.ones((L, L), bool)), "none": np.ones((L, L), bool),
+               "strict": np.tril(np.ones((L, L), bool), -1) | (np.arange(L)[:, None] == 0)}[mask]
+        for s0 in range(0, M, L):
+            rows = slice(s0, s0 + L)
+            for h in range(n_q):
+                g = h // (n_q // n_kv) if group == "div" else h % n_kv
+                q = qkv[rows, h * hd:(h + 1) * hd]
+                k = qkv[rows, (n_q + g) * hd:(n_q + g + 1) * hd]
+                v = qkv[rows, (n_q + n_kv + g) * hd:(n_q + n_kv + g + 1) * hd]
+                sc = (q @ k.T) / (np.sqrt(hd) if scale == "sqrt" else hd)
+                sc = np.where(tri, sc, -np.inf)
+                p = np.exp(sc - np.max(sc, axis=1, keepdims=True))
+                o[rows, h * hd:(h + 1) * hd] = (p / np.sum(p, axis=1, keepdims=True)) @ v
+        return o
+    return att
+
+
 MUTANTS = {
     "eps outside sqrt": ("rms_scale", lambda h, eps: 1.0 / np.sqrt(np.mean(np.asarray(h) ** 2, axis=1)) + eps),
     "sum instead of mean": ("rms_scale", lambda h, eps: 1.0 / np.sqrt(np.sum(np.asarray(h) ** 2, axis=1) + eps)),
@@ -144,6 +168,11 @@ MUTANTS = {
     "gate and up swapped in backward": ("mlp_layer_bwd", _layer_bwd_up_gate_swapped),
     "weight gradient without the row scale": ("mlp_layer_bwd", _layer_bwd_dw_without_row_scale),
     "down-projection gradient with permuted features": ("mlp_layer_bwd", _layer_bwd_dwd_transposed_operands),
+    "attention without the causal mask": ("attention_causal_gqa", _attention_variant(mask="none")),
+    "attention excludes the query's own key": ("attention_causal_gqa", _attention_variant(mask="strict")),
+    "kv head chosen as h mod n_kv": ("attention_causal_gqa", _attention_variant(group="mod")),
+    "attention scaled by 1/hd": ("attention_causal_gqa", _attention_variant(scale="hd")),
+    "attention across sequence boundaries": ("attention_causal_gqa", _attention_variant(cross_seq=True)),
     "abs instead of square": ("partial_sumsq", lambda h, w: np.stack([np.sum(np.abs(np.asarray(h)[:, t * w:(t + 1) * w]), axis=1) for t in range((np.asarray(h).shape[1] + w - 1) // w)])),
 }
 
