@@ -19,10 +19,10 @@ BUILD_DIR = os.path.join(HERE, "_build")
 ARCH = "gfx950"
 
 SOURCES = ["coda_abi.cpp", "gemm_bf16.hip", "gemm_bwd.hip", "gemm_fp8.hip", "gemm_wide.hip",
-           "gemm_splitk.hip", "light_kernels.hip"]
+           "gemm_splitk.hip", "light_kernels.hip", "attention.hip"]
 # sources whose kernels run inline-asm MFMAs: their assembly is hazard-checked
 MFMA_SOURCES = ["gemm_bf16.hip", "gemm_bwd.hip", "gemm_fp8.hip", "gemm_wide.hip",
-                "gemm_splitk.hip"]
+                "gemm_splitk.hip", "attention.hip"]
 
 # Packed fp32 VALU forms are kept out of generated code on purpose.
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -1,0 +1,219 @@
+// Causal grouped-query attention forward: the attention core of the full
+// transformer-layer forward.  The page's method re-parameterises every
+// operator of the layer except attention (section "What CODA can do"); this
+// kernel is the plain attention between the QKV+RoPE GEMM and the output
+// projection GEMM, written for gfx950.  Its running statistics are the
+// page's stateful max / sum-exp transform (section "Five building blocks and
+// a LEGO language"), the same ones as the LM head's block log-sum-exp.
+//
+//   o_i = sum_{j <= i} softmax_j(q_i . k_j / sqrt(64)) v_j   per q head,
+//   keys and values of kv head h / (n_q / n_kv), within one sequence.
+//
+// Design (one 256-thread workgroup per (sequence, q head, 128 queries)):
+//   * wave w owns queries 32 w .. 32 w + 31 of the block (two 16-query
+//     subtiles); its q fragments (64 features) stay in registers;
+//   * key steps of 64: the block's K rows go to LDS row-major with the 16-byte
+//     chunk swizzle of the GEMMs (chunk c of row r at slot c ^ (r & 7)), its
+//     V rows to LDS transposed (V^T[d][key], rows padded to 136 bytes); the
+//     next step's K and V rows are loaded into registers while the current
+//     step computes;
+//   * S^T = K Q^T on v_mfma_f32_16x16x32_bf16 with K as the first operand:
+//     lane L holds the scores of keys 4 (L / 16) + r of query L % 16, so a
+//     query's row max is a lane-local max and two lane exchanges;
+//   * P V as O^T = V^T P^T: lane L's eight P values (keys 4 g .. 4 g + 3 and
+//     16 + 4 g .. 16 + 4 g + 3 of a 32-key chunk, g = L / 16) are exactly the
+//     second operand of the MFMA for its query, so P never leaves the lane;
+//     the V^T fragment is read from LDS in the same key order;
+//   * online softmax in base 2: u = s log2(e) / 8, running max m and the
+//     lane's share of the running sum; per step O and the sums are rescaled by
+//     2^(m_old - m_new); at the end the four lane groups' sums meet and O is
+//     divided by the total;
+//   * causal: a wave skips key steps wholly after its last query; the steps
+//     that straddle its queries mask keys past each query to -inf;
+//   * workgroups are launched longest first (the query blocks with the most
+//     key steps), all heads and sequences of a block position together.
+#include "coda_device.hpp"
+#include "launch.hpp"
+
+namespace coda {
+
+constexpr int kAttnQB = 128;        // queries per workgroup
+constexpr int kAttnKB = 64;         // keys per step
+constexpr int kAttnHd = 64;         // head dimension
+constexpr int kVtPitch = 136;       // bytes per row of V^T in LDS (64 keys + 8 bytes)
+
+struct AttnArgs {
+  const uint16_t* qkv;  // [M, C], C = (n_q + 2 n_kv) 64, q | k | v
+  uint16_t* o;          // [M, n_q 64]
+  int M, L, nq, nkv;
+};
+
+__global__ __launch_bounds__(256, 2) void k_attention_fwd(AttnArgs a) {
+  __shared__ __attribute__((aligned(1024))) char ks[kAttnKB * 128];
+  __shared__ __attribute__((aligned(16))) char vt[kAttnHd * kVtPitch];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int g4 = lane >> 4, r16 = lane & 15;
+  const int nqb = a.L / kAttnQB;
+  const int heads_seqs = a.nq * (a.M / a.L);
+  // longest first: all (head, sequence) pairs of the last query block, then
+  // the next-to-last, ...
+  const int qb = nqb - 1 - (int)blockIdx.x / heads_seqs;
+  const int hs = (int)blockIdx.x % heads_seqs;
+  const int h = hs % a.nq, seq = hs / a.nq;
+  const int kvh = h / (a.nq / a.nkv);
+  const int C = (a.nq + 2 * a.nkv) * kAttnHd;
+  const size_t row0 = (size_t)seq * a.L;  // first row of the sequence
+  const int q0 = qb * kAttnQB;            // first query of the block (sequence position)
+  const int qmin = q0 + 32 * wave;        // this wave's first query
+  const uint16_t* kbase = a.qkv + (size_t)(a.nq + kvh) * kAttnHd;
+  const uint16_t* vbase = a.qkv + (size_t)(a.nq + a.nkv + kvh) * kAttnHd;
+
+  // q fragments: subtile qs, 32-feature chunk c: query qmin + 16 qs + L % 16,
+  // features 32 c + 8 (L / 16) .. + 7
+  bf16x8_t qf[2][2];
+#pragma unroll
+  for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+      qf[qs][c] = *(const bf16x8_t*)(a.qkv + (row0 + qmin + 16 * qs + r16) * C +
+                                     (size_t)h * kAttnHd + 32 * c + 8 * g4);
+
+  // K / V rows of one key step: thread t moves 16-byte chunks i = t and
+  // t + 256 of the 64 x 128-byte block: row i / 8, chunk i % 8
+  i32x4_t kreg[2], vreg[2];
+  auto fetch = [&](int kb) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = tid + 256 * u;
+      const size_t row = row0 + (size_t)kb * kAttnKB + (i >> 3);
+      kreg[u] = *(const i32x4_t*)(kbase + row * C + 8 * (i & 7));
+      vreg[u] = *(const i32x4_t*)(vbase + row * C + 8 * (i & 7));
+    }
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = tid + 256 * u;
+      const int row = i >> 3, c = i & 7;
+      *(i32x4_t*)(ks + row * 128 + ((c ^ (row & 7)) << 4)) = kreg[u];
+      // V^T[8 c + e][row]
+      const uint32_t w[4] = {(uint32_t)vreg[u].x, (uint32_t)vreg[u].y, (uint32_t)vreg[u].z,
+                             (uint32_t)vreg[u].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        *(uint16_t*)(vt + (8 * c + e) * kVtPitch + 2 * row) =
+            (uint16_t)(e & 1 ? w[e >> 1] >> 16 : w[e >> 1] & 0xffffu);
+    }
+  };
+
+  const float kC0 = 1.4426950408889634f * 0.125f;  // log2(e) / sqrt(64)
+  float mrun[2] = {-INFINITY, -INFINITY};  // running max (base-2 units) per query subtile
+  float lrun[2] = {0.f, 0.f};              // this lane's share of the running sum
+  f32x4_t ot[4][2];                        // O^T: feature subtile dt, query subtile qs
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) ot[dt][qs] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int nkb = (q0 + kAttnQB) / kAttnKB;  // key steps up to the block's last query
+  fetch(0);
+  for (int kb = 0; kb < nkb; ++kb) {
+    __syncthreads();  // the previous step's LDS reads are done
+    stage();
+    __syncthreads();
+    if (kb + 1 < nkb) fetch(kb + 1);  // in flight while this step computes
+    const int k0 = kb * kAttnKB;
+    if (k0 > qmin + 31) continue;  // every key after every query of this wave
+    // S^T = K Q^T: st[ks][qs] lane L, register r: key k0 + 16 ks + 4 g + r,
+    // query qmin + 16 qs + L % 16
+    f32x4_t st[4][2];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const int row = 16 * kt + r16;
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs) st[kt][qs] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const bf16x8_t kf = *(const bf16x8_t*)(ks + row * 128 + (((4 * c + g4) ^ (row & 7)) << 4));
+#pragma unroll
+        for (int qs = 0; qs < 2; ++qs) st[kt][qs] = mfma16x16x32(kf, qf[qs][c], st[kt][qs]);
+      }
+    }
+    const bool diag = k0 + kAttnKB - 1 > qmin;  // some key after some query of the wave
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+      const int qpos = qmin + 16 * qs + r16;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float u = st[kt][qs][r] * kC0;
+          if (diag && k0 + 16 * kt + 4 * g4 + r > qpos) u = -INFINITY;
+          st[kt][qs][r] = u;
+          mx = fmaxf(mx, u);
+        }
+      mx = max_over_lane_groups(mx);
+      const float mnew = fmaxf(mrun[qs], mx);  // finite: key 0 is visible to every query
+      const float alpha = __builtin_amdgcn_exp2f(mrun[qs] - mnew);
+      mrun[qs] = mnew;
+      float ls = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = __builtin_amdgcn_exp2f(st[kt][qs][r] - mnew);
+          st[kt][qs][r] = p;
+          ls += p;
+        }
+      lrun[qs] = lrun[qs] * alpha + ls;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) ot[dt][qs] *= alpha;
+    }
+    // O^T += V^T P^T over two 32-key chunks
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      bf16x8_t pf[2];
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs) {
+        const f32x4_t& lo = st[2 * c][qs];
+        const f32x4_t& hi = st[2 * c + 1][qs];
+        pf[qs] = bf16x8_t{(__bf16)lo[0], (__bf16)lo[1], (__bf16)lo[2], (__bf16)lo[3],
+                          (__bf16)hi[0], (__bf16)hi[1], (__bf16)hi[2], (__bf16)hi[3]};
+      }
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const char* vrow = vt + (16 * dt + r16) * kVtPitch;
+        const u32x2_t va = *(const u32x2_t*)(vrow + 2 * (32 * c + 4 * g4));
+        const u32x2_t vb = *(const u32x2_t*)(vrow + 2 * (32 * c + 16 + 4 * g4));
+        const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, u32x4_t{va.x, va.y, vb.x, vb.y});
+#pragma unroll
+        for (int qs = 0; qs < 2; ++qs) ot[dt][qs] = mfma16x16x32(vf, pf[qs], ot[dt][qs]);
+      }
+    }
+  }
+
+  // o[query][h 64 + 16 dt + 4 g + r] = O^T / sum
+#pragma unroll
+  for (int qs = 0; qs < 2; ++qs) {
+    const float inv = 1.0f / sum_over_lane_groups(lrun[qs]);
+    uint16_t* orow = a.o + (row0 + qmin + 16 * qs + r16) * (size_t)(a.nq * kAttnHd) +
+                     (size_t)h * kAttnHd + 4 * g4;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const f32x4_t& v = ot[dt][qs];
+      *(u32x2_t*)(orow + 16 * dt) = pack_bf16x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+    }
+  }
+}
+
+hipError_t launch_attention_fwd(const uint16_t* qkv, uint16_t* o, int M, int L, int nq, int nkv,
+                                hipStream_t stream) {
+  const int blocks = (L / kAttnQB) * nq * (M / L);
+  hipLaunchKernelGGL(k_attention_fwd, dim3(blocks), dim3(256), 0, stream,
+                     AttnArgs{qkv, o, M, L, nq, nkv});
+  return hipGetLastError();
+}
+
+}  // namespace coda

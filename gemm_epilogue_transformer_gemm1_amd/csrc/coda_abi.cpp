@@ -397,6 +397,27 @@ int coda_gemm_block_lse(const void* X, const void* W, const float* r, const int3
   }
 }
 
+int coda_attention_fwd(const void* qkv, void* o, int M, int seq_len, int n_q_heads,
+                       int n_kv_heads, int head_dim, void* stream) {
+  try {
+    if (!qkv || !o) return CODA_ERR_NULL;
+    if (head_dim != 64 || n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads != 0)
+      return CODA_ERR_SHAPE;
+    if (seq_len < 128 || seq_len % 128 != 0 || M < seq_len || M % seq_len != 0)
+      return CODA_ERR_SHAPE;
+    const int64_t C = (int64_t)(n_q_heads + 2 * n_kv_heads) * head_dim;
+    if (!small_enough(M, C) || !small_enough(M, (int64_t)n_q_heads * head_dim))
+      return CODA_ERR_SHAPE;
+    if (!aligned(qkv, 16) || !aligned(o, 16)) return CODA_ERR_ALIGN;
+    if (int st = check_device()) return st;
+    return launched(coda::launch_attention_fwd(static_cast<const uint16_t*>(qkv),
+                                               static_cast<uint16_t*>(o), M, seq_len, n_q_heads,
+                                               n_kv_heads, as_stream(stream)));
+  } catch (...) {
+    return CODA_ERR_LAUNCH;
+  }
+}
+
 size_t coda_lse_noalloc_max_bytes(void) { return kScratchBytes; }
 
 int coda_gemm_block_lse_noalloc(const void* X, const void* W, const float* r,

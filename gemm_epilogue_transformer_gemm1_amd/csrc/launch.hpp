@@ -61,6 +61,8 @@ hipError_t launch_rope_bf16_wide(const uint16_t* X, const uint16_t* W, const flo
                                  hipStream_t stream);
 hipError_t launch_rope_tables(double theta, int max_pos, int head_dim, float* rcos, float* rsin,
                               hipStream_t stream);
+hipError_t launch_attention_fwd(const uint16_t* qkv, uint16_t* o, int M, int L, int nq, int nkv,
+                                hipStream_t stream);
 hipError_t launch_block_lse_bf16(const uint16_t* X, const uint16_t* W, const float* r,
                                  const int* labels, float* tmax, float* tsum, float* label_logit,
                                  int M, int V, int K, hipStream_t stream);

@@ -62,6 +62,7 @@ _SIGNATURES = {
     "coda_transpose_bf16": ([_p, _p, _c_int, _c_int, _p, _c_int, _p], _c_int),
     "coda_rmsnorm_bwd": ([_p, _p, _p, _c_float, _p, _c_int, _c_int, _p], _c_int),
     "coda_dgamma_slices": ([_c_int], _c_int),
+    "coda_attention_fwd": ([_p, _p, _c_int, _c_int, _c_int, _c_int, _c_int, _p], _c_int),
     "coda_lse_noalloc_max_bytes": ([], ctypes.c_size_t),
     "coda_gemm_block_lse_noalloc": ([_p, _p, _p, _p, _p, _p, _c_int, _c_int, _c_int, _p],
                                     _c_int),
@@ -369,6 +370,16 @@ def gemm_block_lse(X, W, labels, tile_max, tile_sumexp, label_logit, loss, lse=N
           _ptr(labels, _I32, "labels"), _ptr(tile_max, _F32, "tile_max"),
           _ptr(tile_sumexp, _F32, "tile_sumexp"), _ptr(label_logit, _F32, "label_logit"),
           _ptr(lse, _F32, "lse"), _ptr(loss, _F32, "loss"), M, V, K, _stream(stream))
+
+
+def attention_fwd(qkv, o, seq_len, n_q_heads, n_kv_heads, head_dim=64, stream=None):
+    """Causal grouped-query attention over sequences of seq_len rows of qkv
+    (q | k | v) into o [M, n_q_heads * head_dim]."""
+    M = qkv.shape[0]
+    _shape(qkv, (M, (n_q_heads + 2 * n_kv_heads) * head_dim), "qkv")
+    _shape(o, (M, n_q_heads * head_dim), "o")
+    _call("coda_attention_fwd", _ptr(qkv, _BF16, "qkv"), _ptr(o, _BF16, "o"), M, int(seq_len),
+          int(n_q_heads), int(n_kv_heads), int(head_dim), _stream(stream))
 
 
 def gemm_block_lse_noalloc(X, W, labels, loss, lse=None, r=None, stream=None):

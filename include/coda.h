@@ -201,6 +201,20 @@ int coda_gemm_block_lse_noalloc(const void* X, const void* W, const float* r,
                                 const int32_t* labels, float* lse, float* loss, int M, int V,
                                 int K, void* stream);
 
+/* Causal grouped-query attention forward, the attention core between the
+ * QKV+RoPE GEMM and the output-projection GEMM of a full layer (page section
+ * "What CODA can do": the method re-parameterises every operator but
+ * attention; this is the plain attention the layer needs):
+ *   o[m, h hd + e] = sum_{j <= i} softmax_j( q_i . k_j / sqrt(hd) ) v_j[e]
+ * for query m = s L + i of sequence s (rows [s L, (s+1) L) form a sequence),
+ * q = qkv[m, h hd ..], k, v of kv head h / (n_q / n_kv) from the k and v
+ * parts of qkv (the layout coda_gemm_rope writes: q | k | v).  fp32 scores
+ * and statistics, P rounded to bf16 for the P V product, bf16 output.
+ * qkv [M, (n_q + 2 n_kv) hd] bf16, o [M, n_q hd] bf16, 16-byte aligned.
+ * Sizes: head_dim == 64; n_q % n_kv == 0; seq_len % 128 == 0; M % seq_len == 0. */
+int coda_attention_fwd(const void* qkv, void* o, int M, int seq_len, int n_q_heads,
+                       int n_kv_heads, int head_dim, void* stream);
+
 /* ---- backward of the MLP sub-layer ----
  *
  * Page section "CODA: the secret in the epilogue": when the forward tail is
