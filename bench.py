@@ -688,6 +688,9 @@ def time_other_rows(torch, ops, inputs, stream, steps, warmup):
                                       round(float((loss_u - loss).abs().max().item()), 6)}}
     del x, wl, tmax, tsum, w, logits, lse_u, loss_u
 
+    # one whole layer at the 1B shape: attention-input block, attention, MLP block
+    out["layer_1b"] = _layer_row(torch, ops, inputs, stream, steps, warmup, bf)
+
     # the bf16 MLP block at the 7B and 70B hidden sizes
     for name in ("mlp_7b", "mlp_70b"):
         out[name] = _mlp_row(torch, ops, inputs, stream, name, steps, warmup, bf)
@@ -753,6 +756,97 @@ def time_other_rows(torch, ops, inputs, stream, steps, warmup):
                                      "tflops": round(fl / ms_u / 1e9, 1),
                                      "speedup_fused_vs_unfused": round(ms_u / ms, 3)}}
     return out
+
+
+def attention_flops(M, L, nq, hd):
+    """Algorithmic FLOPs of causal attention: q.k and p.v, 2 hd each, for every
+    (query, visible key) pair, L (L + 1) / 2 pairs per sequence and head."""
+    return 4.0 * hd * nq * (M // L) * L * (L + 1) / 2
+
+
+def _layer_row(torch, ops, inputs, stream, steps, warmup, bf):
+    """Forward of one transformer layer at the 1B shape (M=8192 as 4 sequences
+    of 2048, d=2048, previous-MLP width 8192, ffn=8192, 32 q / 8 kv heads of
+    64): the fused chain of seven launches against the unfused sequence with
+    the same attention kernel, plus per-launch times of the fused chain."""
+    print("[bench] layer_1b", file=sys.stderr, flush=True)
+    dev = "cuda:0"
+    eps = 1e-5
+    w = inputs.make_workload("layer_1b")
+    sz = w.sizes
+    M, d, K1, ffn = sz["M"], sz["d"], sz["K1"], sz["ffn"]
+    nq, nkv, hd, L = sz["n_q"], sz["n_kv"], sz["head_dim"], sz["seq_len"]
+    x, res, wdn, wqkv, wo, wg, wu = (bf(w.arrays[k])
+                                     for k in ("x", "res", "w1", "wqkv", "wo", "wg", "wu"))
+    g1, g2 = (torch.from_numpy(w.arrays[k]).to(dev) for k in ("gamma", "gamma2"))
+    wqkv_f, wg_f, wu_f = torch.empty_like(wqkv), torch.empty_like(wg), torch.empty_like(wu)
+    ops.fold_gamma(wqkv, g1, wqkv_f)
+    ops.fold_gamma(wg, g2, wg_f)
+    ops.fold_gamma(wu, g2, wu_f)
+    cos = torch.empty(L, hd // 2, dtype=torch.float32, device=dev)
+    sin = torch.empty_like(cos)
+    ops.rope_tables(sz["theta"], L, hd, cos, sin)
+    pos = torch.from_numpy(w.arrays["pos"]).to(dev)
+    e = dict(dtype=torch.bfloat16, device=dev)
+    h1, h2 = torch.empty(M, d, **e), torch.empty(M, d, **e)
+    T = ops.rms_tiles(d)
+    P1, P2 = (torch.empty(T, M, dtype=torch.float32, device=dev) for _ in range(2))
+    r1, r2 = (torch.empty(M, dtype=torch.float32, device=dev) for _ in range(2))
+    qkv = torch.empty(M, (nq + 2 * nkv) * hd, **e)
+    o = torch.empty(M, nq * hd, **e)
+    act = torch.empty(M, ffn, **e)
+    fused = [lambda: ops.gemm_residual_partialrms(x, wdn, res, h1, P1),
+             lambda: ops.rms_reduce(P1, d, eps, r1),
+             lambda: ops.gemm_rope(h1, wqkv_f, r1, cos, sin, pos, qkv, nq, nkv, hd),
+             lambda: ops.attention_fwd(qkv, o, L, nq, nkv),
+             lambda: ops.gemm_residual_partialrms(o, wo, h1, h2, P2),
+             lambda: ops.rms_reduce(P2, d, eps, r2),
+             lambda: ops.gemm_rowscale_swiglu(h2, wg_f, wu_f, r2, act)]
+    names = ["gemm1_down_residual_partialrms", "rms_reduce", "qkv_rope", "attention",
+             "gemm1_o_residual_partialrms", "rms_reduce", "gemm2_rowscale_swiglu"]
+
+    def layer():
+        for f in fused:
+            f()
+    ms = _events_time(torch, stream, layer, steps, warmup)
+    per = _kernel_times(torch, stream, fused, steps)
+    # unfused: every GEMM plain, residual add, RMSNorm, RoPE in place and
+    # SwiGLU as their own launches; the same attention kernel
+    y, hu1, nu, hu2 = (torch.empty(M, d, **e) for _ in range(4))
+    qkv_u, o_u = torch.empty_like(qkv), torch.empty_like(o)
+    gu = torch.empty(M, 2 * ffn, **e)
+    wgu = torch.cat([wg, wu], 0)  # gate rows then up rows: one GEMM writes g | u
+    act_u = torch.empty_like(act)
+
+    def layer_u():
+        ops.gemm_bf16(x, wdn, y)
+        ops.residual_add(y, res, hu1)
+        ops.rmsnorm(hu1, g1, eps, nu)
+        ops.gemm_bf16(nu, wqkv, qkv_u)
+        ops.rope_apply(qkv_u, cos, sin, pos, nq, nkv, hd)
+        ops.attention_fwd(qkv_u, o_u, L, nq, nkv)
+        ops.gemm_bf16(o_u, wo, y)
+        ops.residual_add(y, hu1, hu2)
+        ops.rmsnorm(hu2, g2, eps, nu)
+        ops.gemm_bf16(nu, wgu, gu)
+        ops.swiglu(gu, act_u)
+    ms_u = _events_time(torch, stream, layer_u, steps, warmup)
+    fl_att = attention_flops(M, L, nq, hd)
+    fl = (2.0 * M * d * K1 + 2.0 * M * (nq + 2 * nkv) * hd * d + fl_att
+          + 2.0 * M * d * nq * hd + 2.0 * M * 2 * ffn * d)
+    att_ms = per[3]
+    return {"workload": "M=8192 (4 sequences of 2048), d=2048, previous-MLP width 8192, "
+                        "ffn=8192, 32 q / 8 kv heads of 64, causal attention, RoPE theta=5e5",
+            "ms_per_step": round(ms, 4), "tflops": round(fl / ms / 1e9, 1),
+            "pct_of_bf16_peak": round(100 * fl / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
+            "flops_note": "GEMM FLOPs 2MNK each; attention 4 hd per causal (query, key) pair",
+            "kernels_ms": dict(zip([f"{i}_{n}" for i, n in enumerate(names)], per)),
+            "attention": {"ms": att_ms, "gflop": round(fl_att / 1e9, 2),
+                          "tflops": round(fl_att / att_ms / 1e9, 1),
+                          "pct_of_bf16_peak": round(100 * fl_att / att_ms / 1e9
+                                                    / PEAK_BF16_TFLOPS, 2)},
+            "unfused": {"ms_per_step": round(ms_u, 4), "tflops": round(fl / ms_u / 1e9, 1),
+                        "speedup_fused_vs_unfused": round(ms_u / ms, 3)}}
 
 
 def _mlp_row(torch, ops, inputs, stream, name, steps, warmup, bf, **sizes):
