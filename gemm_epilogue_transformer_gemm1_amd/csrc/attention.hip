@@ -12,24 +12,27 @@
 // Design (one 256-thread workgroup per (sequence, q head, 128 queries)):
 //   * wave w owns queries 32 w .. 32 w + 31 of the block (two 16-query
 //     subtiles); its q fragments (64 features) stay in registers;
-//   * key steps of 64: the block's K rows go to LDS row-major with the 16-byte
-//     chunk swizzle of the GEMMs (chunk c of row r at slot c ^ (r & 7)), its
-//     V rows to LDS transposed (V^T[d][key], rows padded to 136 bytes); the
-//     next step's K and V rows are loaded into registers while the current
-//     step computes;
+//   * key steps of 64: the step's K and V rows go to LDS row-major with the
+//     16-byte chunk swizzle of the GEMMs (chunk c of row r at slot c ^ (r & 7));
+//     the next step's rows are loaded into registers while the current step
+//     computes;
 //   * S^T = K Q^T on v_mfma_f32_16x16x32_bf16 with K as the first operand:
 //     lane L holds the scores of keys 4 (L / 16) + r of query L % 16, so a
-//     query's row max is a lane-local max and two lane exchanges;
+//     query's row max is a lane-local max and two lane-group exchanges
+//     (v_permlane32_swap, v_permlane16_swap);
 //   * P V as O^T = V^T P^T: lane L's eight P values (keys 4 g .. 4 g + 3 and
 //     16 + 4 g .. 16 + 4 g + 3 of a 32-key chunk, g = L / 16) are exactly the
 //     second operand of the MFMA for its query, so P never leaves the lane;
-//     the V^T fragment is read from LDS in the same key order;
-//   * online softmax in base 2: u = s log2(e) / 8, running max m and the
-//     lane's share of the running sum; per step O and the sums are rescaled by
-//     2^(m_old - m_new); at the end the four lane groups' sums meet and O is
-//     divided by the total;
-//   * causal: a wave skips key steps wholly after its last query; the steps
-//     that straddle its queries mask keys past each query to -inf;
+//     the V^T operand comes from the row-major V rows through the transposing
+//     LDS read ds_read_b64_tr_b16 (per 16-lane group, result lane i, element j
+//     is element i % 4 of source lane 4 j + i / 4), in the same key order;
+//   * online softmax in base 2 with the scale folded into one FMA:
+//     p = 2^(s log2(e) / 8 - m).  The reference m is raised only when a row's
+//     max exceeds it by more than 2^8 (one wave-uniform test per step), so the
+//     rescale of O and of the sums by 2^(m_old - m_new) is rare; p stays below
+//     2^8, well inside bf16 and fp32 range, and O / sum does not depend on m;
+//   * causal: a wave skips key steps wholly after its last query; only the
+//     steps that straddle its queries mask keys past each query to -inf;
 //   * workgroups are launched longest first (the query blocks with the most
 //     key steps), all heads and sequences of a block position together.
 #include "coda_device.hpp"
@@ -40,7 +43,10 @@ namespace coda {
 constexpr int kAttnQB = 128;        // queries per workgroup
 constexpr int kAttnKB = 64;         // keys per step
 constexpr int kAttnHd = 64;         // head dimension
-constexpr int kVtPitch = 136;       // bytes per row of V^T in LDS (64 keys + 8 bytes)
+constexpr float kLazyGrow = 8.0f;   // log2 headroom before the reference max is raised
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 struct AttnArgs {
   const uint16_t* qkv;  // [M, C], C = (n_q + 2 n_kv) 64, q | k | v
@@ -48,9 +54,19 @@ struct AttnArgs {
   int M, L, nq, nkv;
 };
 
+// max over lanes l, l ^ 16, l ^ 32, l ^ 48
+__device__ __forceinline__ float max_lane_groups(float v) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, v);
+  const auto x = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+  v = fmaxf(__builtin_bit_cast(float, x[0]), __builtin_bit_cast(float, x[1]));
+  const uint32_t c = __builtin_bit_cast(uint32_t, v);
+  const auto y = __builtin_amdgcn_permlane16_swap(c, c, false, false);
+  return fmaxf(__builtin_bit_cast(float, y[0]), __builtin_bit_cast(float, y[1]));
+}
+
 __global__ __launch_bounds__(256, 2) void k_attention_fwd(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char ks[kAttnKB * 128];
-  __shared__ __attribute__((aligned(16))) char vt[kAttnHd * kVtPitch];
+  __shared__ __attribute__((aligned(1024))) char vs[kAttnKB * 128];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int g4 = lane >> 4, r16 = lane & 15;
@@ -80,7 +96,7 @@ __global__ __launch_bounds__(256, 2) void k_attention_fwd(AttnArgs a) {
                                      (size_t)h * kAttnHd + 32 * c + 8 * g4);
 
   // K / V rows of one key step: thread t moves 16-byte chunks i = t and
-  // t + 256 of the 64 x 128-byte block: row i / 8, chunk i % 8
+  // t + 256 of each 64 x 128-byte block: row i / 8, chunk i % 8
   i32x4_t kreg[2], vreg[2];
   auto fetch = [&](int kb) {
 #pragma unroll
@@ -96,19 +112,24 @@ __global__ __launch_bounds__(256, 2) void k_attention_fwd(AttnArgs a) {
     for (int u = 0; u < 2; ++u) {
       const int i = tid + 256 * u;
       const int row = i >> 3, c = i & 7;
-      *(i32x4_t*)(ks + row * 128 + ((c ^ (row & 7)) << 4)) = kreg[u];
-      // V^T[8 c + e][row]
-      const uint32_t w[4] = {(uint32_t)vreg[u].x, (uint32_t)vreg[u].y, (uint32_t)vreg[u].z,
-                             (uint32_t)vreg[u].w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        *(uint16_t*)(vt + (8 * c + e) * kVtPitch + 2 * row) =
-            (uint16_t)(e & 1 ? w[e >> 1] >> 16 : w[e >> 1] & 0xffffu);
+      const int off = row * 128 + ((c ^ (row & 7)) << 4);
+      *(i32x4_t*)(ks + off) = kreg[u];
+      *(i32x4_t*)(vs + off) = vreg[u];
     }
   };
+  // transposing-read addresses (bytes into vs) of this lane for feature
+  // subtile dt and 32-key chunk c, half hf (keys +0 / +16): source lane
+  // 4 j + q of group g points at row 32 c + 16 hf + 4 g + j, features
+  // 16 dt + 4 q .. + 3
+  const int tr_j = r16 >> 2, tr_q = lane & 3;
+  auto tr_off = [&](int dt, int c, int hf) {
+    const int row = 32 * c + 16 * hf + 4 * g4 + tr_j;
+    const int byte = 32 * dt + 8 * tr_q;
+    return row * 128 + ((((byte >> 4) ^ (row & 7)) << 4) | (byte & 15));
+  };
 
-  const float kC0 = 1.4426950408889634f * 0.125f;  // log2(e) / sqrt(64)
-  float mrun[2] = {-INFINITY, -INFINITY};  // running max (base-2 units) per query subtile
+  const float kC = 1.4426950408889634f * 0.125f;  // log2(e) / sqrt(64)
+  float mref[2] = {-INFINITY, -INFINITY};  // reference max (base-2 units) per query subtile
   float lrun[2] = {0.f, 0.f};              // this lane's share of the running sum
   f32x4_t ot[4][2];                        // O^T: feature subtile dt, query subtile qs
 #pragma unroll
@@ -125,8 +146,8 @@ __global__ __launch_bounds__(256, 2) void k_attention_fwd(AttnArgs a) {
     if (kb + 1 < nkb) fetch(kb + 1);  // in flight while this step computes
     const int k0 = kb * kAttnKB;
     if (k0 > qmin + 31) continue;  // every key after every query of this wave
-    // S^T = K Q^T: st[ks][qs] lane L, register r: key k0 + 16 ks + 4 g + r,
-    // query qmin + 16 qs + L % 16
+    // S^T = K Q^T: st[kt][qs] lane L, register r: key k0 + 16 kt + 4 g + r,
+    // query qmin + 16 qs + L % 16 (raw scores)
     f32x4_t st[4][2];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
@@ -140,36 +161,53 @@ __global__ __launch_bounds__(256, 2) void k_attention_fwd(AttnArgs a) {
         for (int qs = 0; qs < 2; ++qs) st[kt][qs] = mfma16x16x32(kf, qf[qs][c], st[kt][qs]);
       }
     }
-    const bool diag = k0 + kAttnKB - 1 > qmin;  // some key after some query of the wave
+    if (k0 + kAttnKB - 1 > qmin) {  // the step straddles the wave's queries
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs) {
+        const int rel = qmin + 16 * qs + r16 - k0 - 4 * g4;  // key offset limit in this lane
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (16 * kt + r > rel) st[kt][qs][r] = -INFINITY;
+      }
+    }
+    float mnew[2];
+    bool grow = false;
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) {
-      const int qpos = qmin + 16 * qs + r16;
       float mx = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float u = st[kt][qs][r] * kC0;
-          if (diag && k0 + 16 * kt + 4 * g4 + r > qpos) u = -INFINITY;
-          st[kt][qs][r] = u;
-          mx = fmaxf(mx, u);
-        }
-      mx = max_over_lane_groups(mx);
-      const float mnew = fmaxf(mrun[qs], mx);  // finite: key 0 is visible to every query
-      const float alpha = __builtin_amdgcn_exp2f(mrun[qs] - mnew);
-      mrun[qs] = mnew;
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, st[kt][qs][r]);
+      mnew[qs] = max_lane_groups(mx) * kC;
+      grow |= mnew[qs] > mref[qs] + kLazyGrow;
+    }
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wave-uniform: raise the reference
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs) {
+        const float m = fmaxf(mref[qs], mnew[qs]);
+        const float alpha = __builtin_amdgcn_exp2f(mref[qs] - m);
+        mref[qs] = m;
+        lrun[qs] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) ot[dt][qs] *= alpha;
+      }
+    }
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+      const float nm = -mref[qs];
       float ls = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float p = __builtin_amdgcn_exp2f(st[kt][qs][r] - mnew);
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kt][qs][r], kC, nm));
           st[kt][qs][r] = p;
           ls += p;
         }
-      lrun[qs] = lrun[qs] * alpha + ls;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) ot[dt][qs] *= alpha;
+      lrun[qs] += ls;
     }
     // O^T += V^T P^T over two 32-key chunks
 #pragma unroll
@@ -184,10 +222,13 @@ __global__ __launch_bounds__(256, 2) void k_attention_fwd(AttnArgs a) {
       }
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        const char* vrow = vt + (16 * dt + r16) * kVtPitch;
-        const u32x2_t va = *(const u32x2_t*)(vrow + 2 * (32 * c + 4 * g4));
-        const u32x2_t vb = *(const u32x2_t*)(vrow + 2 * (32 * c + 16 + 4 * g4));
-        const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, u32x4_t{va.x, va.y, vb.x, vb.y});
+        const i16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4_t*)((__attribute__((address_space(3))) char*)vs + tr_off(dt, c, 0)));
+        const i16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4_t*)((__attribute__((address_space(3))) char*)vs + tr_off(dt, c, 1)));
+        const bf16x8_t vf = __builtin_bit_cast(
+            bf16x8_t, u32x4_t{__builtin_bit_cast(u32x2_t, va).x, __builtin_bit_cast(u32x2_t, va).y,
+                              __builtin_bit_cast(u32x2_t, vb).x, __builtin_bit_cast(u32x2_t, vb).y});
 #pragma unroll
         for (int qs = 0; qs < 2; ++qs) ot[dt][qs] = mfma16x16x32(vf, pf[qs], ot[dt][qs]);
       }

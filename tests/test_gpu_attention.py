@@ -77,6 +77,25 @@ def test_attention_peaked_scores():
     assert norm_err(got, ref) <= TOL_BF16
 
 
+def test_attention_rising_scores():
+    """Scores that rise along the keys (by about 0.09 in log2 units per key,
+    plus noise): the running max keeps growing, so the reference max is both
+    held while p climbs towards its 2^8 headroom and raised many times."""
+    L, n_seq, nq, nkv = 1024, 2, 4, 2
+    M = L * n_seq
+    rng = np.random.default_rng(8)
+    a = (0.3 * rng.standard_normal((M, (nq + 2 * nkv) * 64))).astype(np.float32)
+    a[:, :nq * 64:64] = 8.0                                   # q feature 0 of every head
+    ramp = 0.06 * np.tile(np.arange(L), n_seq).astype(np.float32)
+    for kh in range(nkv):
+        a[:, (nq + kh) * 64] = ramp                           # k feature 0 grows with the key
+    bits = inputs.to_bf16_bits(a)
+    say("attention with rising scores")
+    got = run_attention(bits, L, nq, nkv)
+    ref = oracle.attention_causal_gqa(dec_bf16(bits), L, nq, nkv, 64)
+    assert norm_err(got, ref) <= TOL_BF16
+
+
 def test_attention_layer_shape_every_row():
     """The layer's attention at full size (4 sequences of 2048, 32 q / 8 kv
     heads of 64) on the QKV the 1B-shaped layer produces, every row."""
