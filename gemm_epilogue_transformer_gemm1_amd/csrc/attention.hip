@@ -9,13 +9,15 @@
 //   o_i = sum_{j <= i} softmax_j(q_i . k_j / sqrt(64)) v_j   per q head,
 //   keys and values of kv head h / (n_q / n_kv), within one sequence.
 //
-// Design (one 256-thread workgroup per (sequence, q head, 128 queries)):
-//   * wave w owns queries 32 w .. 32 w + 31 of the block (two 16-query
-//     subtiles); its q fragments (64 features) stay in registers;
-//   * key steps of 64: the step's K and V rows go to LDS row-major with the
-//     16-byte chunk swizzle of the GEMMs (chunk c of row r at slot c ^ (r & 7));
-//     the next step's rows are loaded into registers while the current step
-//     computes;
+// Design (one 128-thread workgroup per (sequence, q head, 128 queries)):
+//   * wave w owns queries 64 w .. 64 w + 63 of the block (four 16-query
+//     subtiles); its q fragments (64 features) stay in registers, so every K
+//     and V fragment read from LDS feeds four MFMAs;
+//   * key steps of 64 through two LDS stages: the K and V rows of a step are
+//     loaded straight into LDS (buffer_load ... lds, no register staging),
+//     row-major with the 16-byte chunk swizzle of the GEMMs (chunk c of row r
+//     at slot c ^ (r & 7)); the step after next is in flight while a step
+//     computes, with one barrier per step;
 //   * S^T = K Q^T on v_mfma_f32_16x16x32_bf16 with K as the first operand:
 //     lane L holds the scores of keys 4 (L / 16) + r of query L % 16, so a
 //     query's row max is a lane-local max and two lane-group exchanges
@@ -31,8 +33,8 @@
 //     max exceeds it by more than 2^8 (one wave-uniform test per step), so the
 //     rescale of O and of the sums by 2^(m_old - m_new) is rare; p stays below
 //     2^8, well inside bf16 and fp32 range, and O / sum does not depend on m;
-//   * causal: a wave skips key steps wholly after its last query; only the
-//     steps that straddle its queries mask keys past each query to -inf;
+//   * causal: a wave skips the key step after its queries; the one step that
+//     holds its queries masks keys past each query to -inf;
 //   * workgroups are launched longest first (the query blocks with the most
 //     key steps), all heads and sequences of a block position together.
 #include "coda_device.hpp"
@@ -40,10 +42,11 @@
 
 namespace coda {
 
-constexpr int kAttnQB = 128;        // queries per workgroup
-constexpr int kAttnKB = 64;         // keys per step
-constexpr int kAttnHd = 64;         // head dimension
-constexpr float kLazyGrow = 8.0f;   // log2 headroom before the reference max is raised
+constexpr int kAttnQB = 128;              // queries per workgroup
+constexpr int kAttnKB = 64;               // keys per step
+constexpr int kAttnHd = 64;               // head dimension
+constexpr int kAttnStage = 2 * kAttnKB * 128;  // K rows then V rows of one step (16 KiB)
+constexpr float kLazyGrow = 8.0f;         // log2 headroom before the reference max is raised
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
@@ -64,9 +67,24 @@ __device__ __forceinline__ float max_lane_groups(float v) {
   return fmaxf(__builtin_bit_cast(float, y[0]), __builtin_bit_cast(float, y[1]));
 }
 
-__global__ __launch_bounds__(256, 2) void k_attention_fwd(AttnArgs a) {
-  __shared__ __attribute__((aligned(1024))) char ks[kAttnKB * 128];
-  __shared__ __attribute__((aligned(1024))) char vs[kAttnKB * 128];
+// s_waitcnt vmcnt(n), expcnt and lgkmcnt not waited for
+template <int N>
+__device__ __forceinline__ void attn_wait_vm() {
+  static_assert(N >= 0 && N < 16, "small counts only");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
+// Barrier without the release fence of __syncthreads, which would also wait
+// for the loads of the step after next; the signal fences keep the compiler
+// from moving LDS accesses across it.
+__device__ __forceinline__ void attn_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+__global__ __launch_bounds__(128, 2) void k_attention_fwd(AttnArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kAttnStage];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int g4 = lane >> 4, r16 = lane & 15;
@@ -81,43 +99,40 @@ __global__ __launch_bounds__(256, 2) void k_attention_fwd(AttnArgs a) {
   const int C = (a.nq + 2 * a.nkv) * kAttnHd;
   const size_t row0 = (size_t)seq * a.L;  // first row of the sequence
   const int q0 = qb * kAttnQB;            // first query of the block (sequence position)
-  const int qmin = q0 + 32 * wave;        // this wave's first query
-  const uint16_t* kbase = a.qkv + (size_t)(a.nq + kvh) * kAttnHd;
-  const uint16_t* vbase = a.qkv + (size_t)(a.nq + a.nkv + kvh) * kAttnHd;
+  const int qmin = q0 + 64 * wave;        // this wave's first query
 
   // q fragments: subtile qs, 32-feature chunk c: query qmin + 16 qs + L % 16,
   // features 32 c + 8 (L / 16) .. + 7
-  bf16x8_t qf[2][2];
+  bf16x8_t qf[4][2];
 #pragma unroll
-  for (int qs = 0; qs < 2; ++qs)
+  for (int qs = 0; qs < 4; ++qs)
 #pragma unroll
     for (int c = 0; c < 2; ++c)
       qf[qs][c] = *(const bf16x8_t*)(a.qkv + (row0 + qmin + 16 * qs + r16) * C +
                                      (size_t)h * kAttnHd + 32 * c + 8 * g4);
 
-  // K / V rows of one key step: thread t moves 16-byte chunks i = t and
-  // t + 256 of each 64 x 128-byte block: row i / 8, chunk i % 8
-  i32x4_t kreg[2], vreg[2];
-  auto fetch = [&](int kb) {
+  // loads of one step: wave w fills rows 32 w .. 32 w + 31 of the K and of the
+  // V block, 8 rows (1 KiB) per instruction; the lane writing LDS slot s of
+  // row r fetches chunk s ^ (r & 7) of that row
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.qkv + row0 * C, (uint32_t)a.L * C * 2u);
+  uint32_t koff[4], voff[4];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int i = tid + 256 * u;
-      const size_t row = row0 + (size_t)kb * kAttnKB + (i >> 3);
-      kreg[u] = *(const i32x4_t*)(kbase + row * C + 8 * (i & 7));
-      vreg[u] = *(const i32x4_t*)(vbase + row * C + 8 * (i & 7));
+  for (int q = 0; q < 4; ++q) {
+    const int lr = 32 * wave + 8 * q + (lane >> 3);
+    const int c = (lane & 7) ^ (lr & 7);
+    koff[q] = (uint32_t)(lr * C + (a.nq + kvh) * kAttnHd) * 2u + 16u * c;
+    voff[q] = (uint32_t)(lr * C + (a.nq + a.nkv + kvh) * kAttnHd) * 2u + 16u * c;
+  }
+  auto issue = [&](int slot, int kb) {
+    const uint32_t soff = (uint32_t)kb * kAttnKB * C * 2u;
+    char* kl = smem + slot * kAttnStage + wave * 32 * 128;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      load16_to_lds(rs, kl + q * 1024, koff[q], soff);
+      load16_to_lds(rs, kl + kAttnKB * 128 + q * 1024, voff[q], soff);
     }
   };
-  auto stage = [&]() {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int i = tid + 256 * u;
-      const int row = i >> 3, c = i & 7;
-      const int off = row * 128 + ((c ^ (row & 7)) << 4);
-      *(i32x4_t*)(ks + off) = kreg[u];
-      *(i32x4_t*)(vs + off) = vreg[u];
-    }
-  };
-  // transposing-read addresses (bytes into vs) of this lane for feature
+  // transposing-read address (bytes into a V block) of this lane for feature
   // subtile dt and 32-key chunk c, half hf (keys +0 / +16): source lane
   // 4 j + q of group g points at row 32 c + 16 hf + 4 g + j, features
   // 16 dt + 4 q .. + 3
@@ -129,115 +144,125 @@ __global__ __launch_bounds__(256, 2) void k_attention_fwd(AttnArgs a) {
   };
 
   const float kC = 1.4426950408889634f * 0.125f;  // log2(e) / sqrt(64)
-  float mref[2] = {-INFINITY, -INFINITY};  // reference max (base-2 units) per query subtile
-  float lrun[2] = {0.f, 0.f};              // this lane's share of the running sum
-  f32x4_t ot[4][2];                        // O^T: feature subtile dt, query subtile qs
+  float mref[4], lrun[4];  // reference max (base-2 units), this lane's share of the sum
+  f32x4_t ot[4][4];        // O^T: feature subtile dt, query subtile qs
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
+  for (int qs = 0; qs < 4; ++qs) {
+    mref[qs] = -INFINITY;
+    lrun[qs] = 0.f;
 #pragma unroll
-    for (int qs = 0; qs < 2; ++qs) ot[dt][qs] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < 4; ++dt) ot[dt][qs] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
 
   const int nkb = (q0 + kAttnQB) / kAttnKB;  // key steps up to the block's last query
-  fetch(0);
+  issue(0, 0);
+  if (nkb > 1) {
+    issue(1, 1);
+    attn_wait_vm<8>();
+  } else {
+    attn_wait_vm<0>();
+  }
+  attn_barrier();
   for (int kb = 0; kb < nkb; ++kb) {
-    __syncthreads();  // the previous step's LDS reads are done
-    stage();
-    __syncthreads();
-    if (kb + 1 < nkb) fetch(kb + 1);  // in flight while this step computes
     const int k0 = kb * kAttnKB;
-    if (k0 > qmin + 31) continue;  // every key after every query of this wave
-    // S^T = K Q^T: st[kt][qs] lane L, register r: key k0 + 16 kt + 4 g + r,
-    // query qmin + 16 qs + L % 16 (raw scores)
-    f32x4_t st[4][2];
+    if (k0 <= qmin) {  // wave-uniform: the step after the wave's queries is skipped
+      const char* ks = smem + (kb & 1) * kAttnStage;
+      __attribute__((address_space(3))) char* vs =
+          (__attribute__((address_space(3))) char*)(ks + kAttnKB * 128);
+      // S^T = K Q^T: st[kt][qs] lane L, register r: key k0 + 16 kt + 4 g + r,
+      // query qmin + 16 qs + L % 16 (raw scores)
+      f32x4_t st[4][4];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      const int row = 16 * kt + r16;
+      for (int kt = 0; kt < 4; ++kt) {
+        const int row = 16 * kt + r16;
 #pragma unroll
-      for (int qs = 0; qs < 2; ++qs) st[kt][qs] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int qs = 0; qs < 4; ++qs) st[kt][qs] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const bf16x8_t kf = *(const bf16x8_t*)(ks + row * 128 + (((4 * c + g4) ^ (row & 7)) << 4));
+        for (int c = 0; c < 2; ++c) {
+          const bf16x8_t kf =
+              *(const bf16x8_t*)(ks + row * 128 + (((4 * c + g4) ^ (row & 7)) << 4));
 #pragma unroll
-        for (int qs = 0; qs < 2; ++qs) st[kt][qs] = mfma16x16x32(kf, qf[qs][c], st[kt][qs]);
+          for (int qs = 0; qs < 4; ++qs) st[kt][qs] = mfma16x16x32(kf, qf[qs][c], st[kt][qs]);
+        }
       }
-    }
-    if (k0 + kAttnKB - 1 > qmin) {  // the step straddles the wave's queries
+      if (k0 == qmin) {  // the step that holds the wave's queries: mask later keys
 #pragma unroll
-      for (int qs = 0; qs < 2; ++qs) {
-        const int rel = qmin + 16 * qs + r16 - k0 - 4 * g4;  // key offset limit in this lane
+        for (int qs = 0; qs < 4; ++qs) {
+          const int rel = 16 * qs + r16 - 4 * g4;  // key offset limit in this lane
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (16 * kt + r > rel) st[kt][qs][r] = -INFINITY;
+        }
+      }
+      float mnew[4];
+      bool grow = false;
+#pragma unroll
+      for (int qs = 0; qs < 4; ++qs) {
+        float mx = -INFINITY;
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (16 * kt + r > rel) st[kt][qs][r] = -INFINITY;
+          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, st[kt][qs][r]);
+        mnew[qs] = max_lane_groups(mx) * kC;
+        grow |= mnew[qs] > mref[qs] + kLazyGrow;
       }
-    }
-    float mnew[2];
-    bool grow = false;
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wave-uniform: raise the reference
 #pragma unroll
-    for (int qs = 0; qs < 2; ++qs) {
-      float mx = -INFINITY;
+        for (int qs = 0; qs < 4; ++qs) {
+          const float m = fmaxf(mref[qs], mnew[qs]);
+          const float alpha = __builtin_amdgcn_exp2f(mref[qs] - m);
+          mref[qs] = m;
+          lrun[qs] *= alpha;
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, st[kt][qs][r]);
-      mnew[qs] = max_lane_groups(mx) * kC;
-      grow |= mnew[qs] > mref[qs] + kLazyGrow;
-    }
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wave-uniform: raise the reference
-#pragma unroll
-      for (int qs = 0; qs < 2; ++qs) {
-        const float m = fmaxf(mref[qs], mnew[qs]);
-        const float alpha = __builtin_amdgcn_exp2f(mref[qs] - m);
-        mref[qs] = m;
-        lrun[qs] *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) ot[dt][qs] *= alpha;
-      }
-    }
-#pragma unroll
-    for (int qs = 0; qs < 2; ++qs) {
-      const float nm = -mref[qs];
-      float ls = 0.f;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kt][qs][r], kC, nm));
-          st[kt][qs][r] = p;
-          ls += p;
+          for (int dt = 0; dt < 4; ++dt) ot[dt][qs] *= alpha;
         }
-      lrun[qs] += ls;
-    }
-    // O^T += V^T P^T over two 32-key chunks
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      bf16x8_t pf[2];
-#pragma unroll
-      for (int qs = 0; qs < 2; ++qs) {
-        const f32x4_t& lo = st[2 * c][qs];
-        const f32x4_t& hi = st[2 * c + 1][qs];
-        pf[qs] = bf16x8_t{(__bf16)lo[0], (__bf16)lo[1], (__bf16)lo[2], (__bf16)lo[3],
-                          (__bf16)hi[0], (__bf16)hi[1], (__bf16)hi[2], (__bf16)hi[3]};
       }
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const i16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4_t*)((__attribute__((address_space(3))) char*)vs + tr_off(dt, c, 0)));
-        const i16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4_t*)((__attribute__((address_space(3))) char*)vs + tr_off(dt, c, 1)));
-        const bf16x8_t vf = __builtin_bit_cast(
-            bf16x8_t, u32x4_t{__builtin_bit_cast(u32x2_t, va).x, __builtin_bit_cast(u32x2_t, va).y,
-                              __builtin_bit_cast(u32x2_t, vb).x, __builtin_bit_cast(u32x2_t, vb).y});
+      for (int qs = 0; qs < 4; ++qs) {
+        const float nm = -mref[qs];
+        float ls = 0.f;
 #pragma unroll
-        for (int qs = 0; qs < 2; ++qs) ot[dt][qs] = mfma16x16x32(vf, pf[qs], ot[dt][qs]);
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kt][qs][r], kC, nm));
+            st[kt][qs][r] = p;
+            ls += p;
+          }
+        lrun[qs] += ls;
+      }
+      // O^T += V^T P^T over two 32-key chunks
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        bf16x8_t pf[4];
+#pragma unroll
+        for (int qs = 0; qs < 4; ++qs) {
+          const f32x4_t& lo = st[2 * c][qs];
+          const f32x4_t& hi = st[2 * c + 1][qs];
+          pf[qs] = bf16x8_t{(__bf16)lo[0], (__bf16)lo[1], (__bf16)lo[2], (__bf16)lo[3],
+                            (__bf16)hi[0], (__bf16)hi[1], (__bf16)hi[2], (__bf16)hi[3]};
+        }
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const i16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vs + tr_off(dt, c, 0)));
+          const i16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vs + tr_off(dt, c, 1)));
+          const u32x2_t wa = __builtin_bit_cast(u32x2_t, va), wb = __builtin_bit_cast(u32x2_t, vb);
+          const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, u32x4_t{wa.x, wa.y, wb.x, wb.y});
+#pragma unroll
+          for (int qs = 0; qs < 4; ++qs) ot[dt][qs] = mfma16x16x32(vf, pf[qs], ot[dt][qs]);
+        }
       }
     }
+    if (kb + 1 < nkb) attn_wait_vm<0>();  // this wave's part of the next step has landed
+    attn_barrier();                       // ... every wave's, and this step's slot is free
+    if (kb + 2 < nkb) issue(kb & 1, kb + 2);
   }
 
   // o[query][h 64 + 16 dt + 4 g + r] = O^T / sum
 #pragma unroll
-  for (int qs = 0; qs < 2; ++qs) {
+  for (int qs = 0; qs < 4; ++qs) {
     const float inv = 1.0f / sum_over_lane_groups(lrun[qs]);
     uint16_t* orow = a.o + (row0 + qmin + 16 * qs + r16) * (size_t)(a.nq * kAttnHd) +
                      (size_t)h * kAttnHd + 4 * g4;
@@ -252,7 +277,7 @@ __global__ __launch_bounds__(256, 2) void k_attention_fwd(AttnArgs a) {
 hipError_t launch_attention_fwd(const uint16_t* qkv, uint16_t* o, int M, int L, int nq, int nkv,
                                 hipStream_t stream) {
   const int blocks = (L / kAttnQB) * nq * (M / L);
-  hipLaunchKernelGGL(k_attention_fwd, dim3(blocks), dim3(256), 0, stream,
+  hipLaunchKernelGGL(k_attention_fwd, dim3(blocks), dim3(128), 0, stream,
                      AttnArgs{qkv, o, M, L, nq, nkv});
   return hipGetLastError();
 }
