@@ -161,6 +161,30 @@ def test_noalloc_lse_validation(L):
     assert f(A16, A16, None, A16, None, A16, 8192, 128256, 2048, None) == ERR_DEVICE
 
 
+def test_attention_validation(L):
+    """coda_attention_fwd(qkv, o, M, seq_len, n_q, n_kv, head_dim, stream)
+    rejects bad arguments before any HIP call."""
+    f = L.coda_attention_fwd
+    assert f(None, A16, 4096, 2048, 32, 8, 64, None) == ERR_NULL
+    assert f(A16, None, 4096, 2048, 32, 8, 64, None) == ERR_NULL
+    assert f(A16, A16, 4096, 2048, 32, 8, 128, None) == ERR_SHAPE    # head size 64 only
+    assert f(A16, A16, 4096, 2048, 32, 6, 64, None) == ERR_SHAPE     # n_q % n_kv
+    assert f(A16, A16, 4096, 2048, 0, 8, 64, None) == ERR_SHAPE
+    assert f(A16, A16, 4096, 2048, 32, 0, 64, None) == ERR_SHAPE
+    assert f(A16, A16, 4096, 2000, 32, 8, 64, None) == ERR_SHAPE     # seq_len % 128
+    assert f(A16, A16, 4096, 0, 32, 8, 64, None) == ERR_SHAPE
+    assert f(A16, A16, 6144, 4096, 32, 8, 64, None) == ERR_SHAPE     # M % seq_len
+    assert f(A16, A16, 1024, 2048, 32, 8, 64, None) == ERR_SHAPE     # M < seq_len
+    assert f(A16, A16, 1 << 20, 2048, 64, 8, 64, None) == ERR_SHAPE  # element count limit
+    assert f(A16 + 8, A16, 4096, 2048, 32, 8, 64, None) == ERR_ALIGN
+    assert f(A16, A16 + 2, 4096, 2048, 32, 8, 64, None) == ERR_ALIGN
+    if not torch.cuda.is_available():
+        assert f(A16, A16, 8192, 2048, 32, 8, 64, None) == ERR_DEVICE
+    with pytest.raises(ValueError, match="shape"):   # o of another width
+        ops.attention_fwd(torch.zeros(256, 6 * 64, dtype=torch.bfloat16),
+                          torch.zeros(256, 3 * 64, dtype=torch.bfloat16), 128, 4, 1)
+
+
 def test_binding_checks_backward_shapes():
     """The Python binding refuses output tensors of the wrong shape before any
     call (CPU tensors are rejected for not being on the device, which needs
