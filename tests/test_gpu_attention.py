@@ -29,10 +29,11 @@ def run_attention(bits, L, nq, nkv):
 
 
 @pytest.mark.parametrize("L,n_seq,nq,nkv", [(128, 2, 4, 2), (256, 3, 6, 2), (384, 1, 2, 2),
-                                             (128, 1, 1, 1), (512, 2, 8, 1)])
+                                             (128, 1, 1, 1), (512, 2, 8, 1), (4096, 1, 2, 1)])
 def test_attention_small(L, n_seq, nq, nkv):
     """Several query blocks and key steps per sequence, sequence boundaries,
-    grouped (and ungrouped) kv heads."""
+    grouped (and ungrouped) kv heads, and one long sequence (64 key steps for
+    its last query block)."""
     M = L * n_seq
     bits = _qkv_bits(L + nq + nkv, M, nq, nkv)
     say(f"attention L={L} seqs={n_seq} nq={nq} nkv={nkv}")
