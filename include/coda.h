@@ -32,7 +32,9 @@
  *   - Matrix pointers must be 16-byte aligned, float / int vectors 4-byte
  *     aligned.  Outputs must not alias inputs.
  *   - Calls keep no global mutable state and are thread-safe; calls on
- *     different streams may overlap.
+ *     different streams may overlap.  The one exception is
+ *     coda_gemm_block_lse_noalloc, whose partials live in a static scratch
+ *     array that every call on one GPU shares: such calls must not overlap.
  */
 #ifndef CODA_H
 #define CODA_H
