@@ -351,7 +351,8 @@ int coda_gemm_rope(const void* h, const void* Wqkv, const float* r, const float*
                    int n_q_heads, int n_kv_heads, int head_dim, void* stream) {
   try {
     if (!h || !Wqkv || !r || !rope_cos || !rope_sin || !pos || !qkv) return CODA_ERR_NULL;
-    if (head_dim != 64 || n_q_heads < 1 || n_kv_heads < 1 || max_pos < 1) return CODA_ERR_SHAPE;
+    if ((head_dim != 64 && head_dim != 128) || n_q_heads < 1 || n_kv_heads < 1 || max_pos < 1)
+      return CODA_ERR_SHAPE;
     const int64_t N = (int64_t)(n_q_heads + 2 * n_kv_heads) * head_dim;
     if (N > (int64_t(1) << 24)) return CODA_ERR_SHAPE;
     if (int st = check_gemm_shape(M, (int)N, K, 64)) return st;
@@ -359,15 +360,18 @@ int coda_gemm_rope(const void* h, const void* Wqkv, const float* r, const float*
         !aligned(rope_cos, 16) || !aligned(rope_sin, 16) || !aligned(pos, 4))
       return CODA_ERR_ALIGN;
     if (int st = check_device()) return st;
-    // QKV widths that are a multiple of six heads (384) run on the 128 x 384
-    // block tile, which fills whole rounds of compute units where the
-    // 256 x 256 tile would leave the last round partly idle
-    const auto launch = (n_q_heads + 2 * n_kv_heads) % 6 == 0 ? coda::launch_rope_bf16_wide
-                                                               : coda::launch_rope_bf16;
-    return launched(launch(
-        static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(Wqkv), r, rope_cos,
-        rope_sin, pos, max_pos, static_cast<uint16_t*>(qkv), M, K, n_q_heads, n_kv_heads,
-        as_stream(stream)));
+    const uint16_t* hx = static_cast<const uint16_t*>(h);
+    const uint16_t* wx = static_cast<const uint16_t*>(Wqkv);
+    uint16_t* out = static_cast<uint16_t*>(qkv);
+    // 64-wide heads whose count is a multiple of six (384 columns) run on the
+    // 128 x 384 block tile, which fills whole rounds of compute units where
+    // the 256 x 256 tile would leave the last round partly idle
+    if (head_dim == 64 && (n_q_heads + 2 * n_kv_heads) % 6 == 0)
+      return launched(coda::launch_rope_bf16_wide(hx, wx, r, rope_cos, rope_sin, pos, max_pos, out,
+                                                  M, K, n_q_heads, n_kv_heads,
+                                                  as_stream(stream)));
+    return launched(coda::launch_rope_bf16(hx, wx, r, rope_cos, rope_sin, pos, max_pos, out, M, K,
+                                           n_q_heads, n_kv_heads, head_dim, as_stream(stream)));
   } catch (...) {
     return CODA_ERR_LAUNCH;
   }
@@ -401,7 +405,8 @@ int coda_attention_fwd(const void* qkv, void* o, int M, int seq_len, int n_q_hea
                        int n_kv_heads, int head_dim, void* stream) {
   try {
     if (!qkv || !o) return CODA_ERR_NULL;
-    if (head_dim != 64 || n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads != 0)
+    if ((head_dim != 64 && head_dim != 128) || n_q_heads < 1 || n_kv_heads < 1 ||
+        n_q_heads % n_kv_heads != 0)
       return CODA_ERR_SHAPE;
     if (seq_len < 128 || seq_len % 128 != 0 || M < seq_len || M % seq_len != 0)
       return CODA_ERR_SHAPE;
@@ -412,7 +417,7 @@ int coda_attention_fwd(const void* qkv, void* o, int M, int seq_len, int n_q_hea
     if (int st = check_device()) return st;
     return launched(coda::launch_attention_fwd(static_cast<const uint16_t*>(qkv),
                                                static_cast<uint16_t*>(o), M, seq_len, n_q_heads,
-                                               n_kv_heads, as_stream(stream)));
+                                               n_kv_heads, head_dim, as_stream(stream)));
   } catch (...) {
     return CODA_ERR_LAUNCH;
   }
@@ -628,7 +633,8 @@ int coda_rope_apply(void* qkv, const float* rope_cos, const float* rope_sin, con
                     int max_pos, int M, int n_q_heads, int n_kv_heads, int head_dim, void* stream) {
   try {
     if (!qkv || !rope_cos || !rope_sin || !pos) return CODA_ERR_NULL;
-    if (head_dim != 64 || n_q_heads < 1 || n_kv_heads < 1 || max_pos < 1 || M < 1)
+    if ((head_dim != 64 && head_dim != 128) || n_q_heads < 1 || n_kv_heads < 1 || max_pos < 1 ||
+        M < 1)
       return CODA_ERR_SHAPE;
     const int64_t N = (int64_t)(n_q_heads + 2 * n_kv_heads) * head_dim;
     if (N > (int64_t(1) << 24) || !small_enough(M, N)) return CODA_ERR_SHAPE;
@@ -636,7 +642,8 @@ int coda_rope_apply(void* qkv, const float* rope_cos, const float* rope_sin, con
       return CODA_ERR_ALIGN;
     if (int st = check_device()) return st;
     return launched(coda::launch_rope_apply(static_cast<uint16_t*>(qkv), rope_cos, rope_sin, pos,
-                                            max_pos, M, n_q_heads, n_kv_heads, as_stream(stream)));
+                                            max_pos, M, n_q_heads, n_kv_heads, head_dim,
+                                            as_stream(stream)));
   } catch (...) {
     return CODA_ERR_LAUNCH;
   }

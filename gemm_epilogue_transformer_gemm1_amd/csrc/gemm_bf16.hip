@@ -267,15 +267,21 @@ __global__ __launch_bounds__(kThreads, 1) void k_rowscale_swiglu_bf16(Gemm2Args 
 // in the epilogue": RoPE re-parameterised into the epilogue; section "Five
 // building blocks and a LEGO language": RoPE is an elementwise transform and
 // the cos/sin rows are vector loads).  Output tile 256 tokens x 256 features;
-// a wave's 128 features are two whole 64-wide heads, and the rotate-half
-// partner of feature c (< 32) of a head, c + 32, is subtile j + 2 in the same
-// lane and register, so the rotation needs no data exchange.
+// a wave's 128 features are whole heads (two of 64, or one of 128), and the
+// rotate-half partner of feature c < kHd / 2 of a head, c + kHd / 2, is
+// subtile j + kHd / 32 in the same lane and register, so the rotation needs
+// no data exchange.
 // ---------------------------------------------------------------------------
+template <int kHd>
 __global__ __launch_bounds__(kThreads, 1) void k_rope_bf16(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, const float* __restrict__ r,
     const float* __restrict__ rcos, const float* __restrict__ rsin, const int* __restrict__ pos,
     int max_pos, uint16_t* __restrict__ out, int M, int N, int K, int rot_features, int gm,
     int gn) {
+  static_assert(kHd == 64 || kHd == 128, "head size");
+  constexpr int kHalf = kHd / 2;          // rotate-half pair distance
+  constexpr int kSub = kHalf / 16;        // subtiles per half head (2 or 4)
+  constexpr int kHeads = 128 / kHd;       // heads per wave (2 or 1)
   __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -303,41 +309,54 @@ __global__ __launch_bounds__(kThreads, 1) void k_rope_bf16(
     Acc acc;
     mainloop_bf16<false>(acc, smem, MainloopSrc{X, W, nullptr, M, N, K, m0, n0}, ch, pre, [] {});
 
-    const int nw0 = n0 + wn * 128;  // multiple of 128: two whole heads of 64
-    // cos/sin of the 8 token subtiles, all loaded before the first use (one
-    // latency instead of eight); the fragment registers are free by now.
-    // Positions outside the table are clamped into it (memory safety).
-    // Angle index of subtile jj (0, 1) of a head: 16 jj + 4 gq + v.
-    f32x4_t ct[8][2], st[8][2];
+    const int nw0 = n0 + wn * 128;  // multiple of 128: whole heads
+    // cos/sin rows: angle index of subtile jj (< kSub) of a half head is
+    // 16 jj + 4 gq + v.  Positions outside the table are clamped into it
+    // (memory safety).  With 64-wide heads the rows of all 8 token subtiles
+    // are loaded before the first use (one latency instead of eight); with
+    // 128-wide heads (twice the registers) token subtile i + 1's rows are
+    // loaded while subtile i is processed.
+    constexpr int kPre = kHd == 64 ? 8 : 2;
+    f32x4_t ct[kPre][kSub], st[kPre][kSub];
+    auto load_cs = [&](int i, int slot) {
+      const size_t p = (size_t)min(max(pp[i], 0), max_pos - 1) * kHalf + 4 * gq;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const size_t p = (size_t)min(max(pp[i], 0), max_pos - 1) * 32 + 4 * gq;
-      ct[i][0] = *(const f32x4_t*)(rcos + p);
-      ct[i][1] = *(const f32x4_t*)(rcos + p + 16);
-      st[i][0] = *(const f32x4_t*)(rsin + p);
-      st[i][1] = *(const f32x4_t*)(rsin + p + 16);
+      for (int jj = 0; jj < kSub; ++jj) {
+        ct[slot][jj] = *(const f32x4_t*)(rcos + p + 16 * jj);
+        st[slot][jj] = *(const f32x4_t*)(rsin + p + 16 * jj);
+      }
+    };
+    if constexpr (kHd == 64) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) load_cs(i, i);
+    } else {
+      load_cs(0, 0);
     }
     // Stores as in GEMM2: lanes gq and gq ^ 1 exchange one run of each pair of
-    // subtiles (jj = 0, 1 of a half-head), so each 16-byte store writes 64
-    // contiguous bytes of 16 rows; masked lanes store out of range of a
-    // buffer that starts at the tile's first row.
+    // subtiles of a half head, so each 16-byte store writes 64 contiguous
+    // bytes of 16 rows; masked lanes store out of range of a buffer that
+    // starts at the tile's first row.
     const __amdgpu_buffer_rsrc_t orsrc =
         make_rsrc(out + (size_t)m0 * N, (uint32_t)min(kBM, M - m0) * (uint32_t)N * 2u);
     const bool godd = (gq & 1) != 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
+      const int cur = kHd == 64 ? i : (i & 1);
+      if constexpr (kHd != 64) {
+        if (i + 1 < 8) load_cs(i + 1, (i + 1) & 1);
+      }
       const int ml = wm * 128 + i * 16 + (lane & 15);  // row within the tile
       const bool mv = m0 + ml < M;
       const float rr_i = rr[i];
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int hbase = nw0 + hh * 64;
+      for (int hh = 0; hh < kHeads; ++hh) {
+        const int hbase = nw0 + hh * kHd;
         const bool rot = hbase < rot_features;
-        u32x2_t plo[2], phi[2];
+        u32x2_t plo[kSub], phi[kSub];
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          const int ja = hh * 4 + jj, jb = ja + 2;
-          const f32x4_t cs = ct[i][jj], sn = st[i][jj];
+        for (int jj = 0; jj < kSub; ++jj) {
+          const int ja = hh * 2 * kSub + jj, jb = ja + kSub;
+          const f32x4_t cs = ct[cur][jj], sn = st[cur][jj];
           float lo[4], hi[4];
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
@@ -349,16 +368,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_rope_bf16(
           phi[jj] = pack_bf16x4(hi[0], hi[1], hi[2], hi[3]);
         }
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {  // features [0,32) and [32,64) of the head
-          const u32x2_t* pk = half ? phi : plo;
-          const u32x2_t sd = godd ? pk[0] : pk[1];
-          const u32x2_t rx = {(unsigned)__shfl_xor((int)sd.x, 16, 64),
-                              (unsigned)__shfl_xor((int)sd.y, 16, 64)};
-          const int n = hbase + 32 * half + 16 * (godd ? 1 : 0) + 8 * (gq >> 1);
-          const uint32_t off = (mv && n < N) ? ((uint32_t)ml * (uint32_t)N + (uint32_t)n) * 2u
-                                             : kOobOffset;
-          store16(orsrc, godd ? u32x4_t{rx.x, rx.y, pk[1].x, pk[1].y}
-                              : u32x4_t{pk[0].x, pk[0].y, rx.x, rx.y}, off);
+        for (int half = 0; half < 2; ++half) {  // features [0, kHalf) and [kHalf, kHd) of the head
+#pragma unroll
+          for (int jp = 0; jp < kSub / 2; ++jp) {  // subtile pairs (2 jp, 2 jp + 1)
+            const u32x2_t* pk = (half ? phi : plo) + 2 * jp;
+            const u32x2_t sd = godd ? pk[0] : pk[1];
+            const u32x2_t rx = {(unsigned)__shfl_xor((int)sd.x, 16, 64),
+                                (unsigned)__shfl_xor((int)sd.y, 16, 64)};
+            const int n = hbase + kHalf * half + 16 * (2 * jp + (godd ? 1 : 0)) + 8 * (gq >> 1);
+            const uint32_t off = (mv && n < N) ? ((uint32_t)ml * (uint32_t)N + (uint32_t)n) * 2u
+                                               : kOobOffset;
+            store16(orsrc, godd ? u32x4_t{rx.x, rx.y, pk[1].x, pk[1].y}
+                                : u32x4_t{pk[0].x, pk[0].y, rx.x, rx.y}, off);
+          }
         }
       }
     }
@@ -565,11 +587,13 @@ hipError_t launch_rowscale_swiglu_save_bf16(const uint16_t* X, const uint16_t* W
 
 hipError_t launch_rope_bf16(const uint16_t* X, const uint16_t* W, const float* r,
                             const float* rcos, const float* rsin, const int* pos, int max_pos,
-                            uint16_t* out, int M, int K, int n_q, int n_kv, hipStream_t stream) {
-  const int N = (n_q + 2 * n_kv) * 64;
+                            uint16_t* out, int M, int K, int n_q, int n_kv, int head_dim,
+                            hipStream_t stream) {
+  const int N = (n_q + 2 * n_kv) * head_dim;
   const int gm = cdiv(M, kBM), gn = cdiv(N, kBN);
-  hipLaunchKernelGGL(k_rope_bf16, dim3(min(gm * gn, cu_count())), dim3(kThreads), 0, stream, X, W, r, rcos, rsin,
-                     pos, max_pos, out, M, N, K, (n_q + n_kv) * 64, gm, gn);
+  const auto kern = head_dim == 128 ? k_rope_bf16<128> : k_rope_bf16<64>;
+  hipLaunchKernelGGL(kern, dim3(min(gm * gn, cu_count())), dim3(kThreads), 0, stream, X, W, r,
+                     rcos, rsin, pos, max_pos, out, M, N, K, (n_q + n_kv) * head_dim, gm, gn);
   return hipGetLastError();
 }
 

@@ -45,7 +45,8 @@ hipError_t launch_rmsnorm_bwd(const uint16_t* G, const uint16_t* h, const uint16
                               uint16_t* dh, int M, int N, hipStream_t stream);
 hipError_t launch_rope_bf16(const uint16_t* X, const uint16_t* W, const float* r,
                             const float* rcos, const float* rsin, const int* pos, int max_pos,
-                            uint16_t* out, int M, int K, int n_q, int n_kv, hipStream_t stream);
+                            uint16_t* out, int M, int K, int n_q, int n_kv, int head_dim,
+                            hipStream_t stream);
 // plain bf16 GEMM on the 128 x 384 block tile, and whether a shape should use it
 hipError_t launch_gemm_plain_bf16_wide(const uint16_t* A, const uint16_t* W, uint16_t* C, int M,
                                        int N, int K, hipStream_t stream);
@@ -62,7 +63,7 @@ hipError_t launch_rope_bf16_wide(const uint16_t* X, const uint16_t* W, const flo
 hipError_t launch_rope_tables(double theta, int max_pos, int head_dim, float* rcos, float* rsin,
                               hipStream_t stream);
 hipError_t launch_attention_fwd(const uint16_t* qkv, uint16_t* o, int M, int L, int nq, int nkv,
-                                hipStream_t stream);
+                                int head_dim, hipStream_t stream);
 hipError_t launch_block_lse_bf16(const uint16_t* X, const uint16_t* W, const float* r,
                                  const int* labels, float* tmax, float* tsum, float* label_logit,
                                  int M, int V, int K, hipStream_t stream);
@@ -93,7 +94,8 @@ hipError_t launch_rmsnorm(const uint16_t* h, const float* gamma, float eps, uint
                           int N, hipStream_t stream);
 hipError_t launch_swiglu(const uint16_t* gu, uint16_t* out, int M, int N, hipStream_t stream);
 hipError_t launch_rope_apply(uint16_t* qkv, const float* rcos, const float* rsin, const int* pos,
-                             int max_pos, int M, int n_q, int n_kv, hipStream_t stream);
+                             int max_pos, int M, int n_q, int n_kv, int head_dim,
+                             hipStream_t stream);
 hipError_t launch_gemm_plain_fp8(const uint8_t* A, const uint8_t* W, const float* a_scale,
                                  const float* w_scale, uint16_t* C, int M, int N, int K, int ldc,
                                  hipStream_t stream);

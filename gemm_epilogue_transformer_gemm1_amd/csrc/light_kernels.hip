@@ -661,39 +661,42 @@ hipError_t launch_rmsnorm_bwd(const uint16_t* G, const uint16_t* h, const uint16
 // ---------------------------------------------------------------------------
 
 // In-place rotate-half RoPE on the first n_rot heads (q, then k) of a stored
-// qkv tensor [M, N], heads of 64: one thread per (row, head, 4 pairs).
-// Positions outside the table are clamped into it, as in the fused kernel.
+// qkv tensor [M, N], heads of hd (64 or 128): one thread per (row, head, 4
+// pairs).  Positions outside the table are clamped into it, as in the fused
+// kernel.
 __global__ __launch_bounds__(256) void k_rope_apply(uint16_t* __restrict__ qkv,
                                                     const float* __restrict__ rcos,
                                                     const float* __restrict__ rsin,
                                                     const int* __restrict__ pos, int max_pos,
-                                                    int M, int N, int n_rot) {
+                                                    int M, int N, int n_rot, int hd) {
+  const int half = hd / 2, quads = half / 4;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t per_row = (int64_t)n_rot * 8;
+  const int64_t per_row = (int64_t)n_rot * quads;
   if (idx >= (int64_t)M * per_row) return;
   const int64_t m = idx / per_row;
   const int rem = (int)(idx - m * per_row);
-  const int q4 = (rem & 7) * 4;
-  uint16_t* base = qkv + m * N + (rem >> 3) * 64;
-  const size_t p = (size_t)min(max(pos[m], 0), max_pos - 1) * 32 + q4;
+  const int q4 = (rem % quads) * 4;
+  uint16_t* base = qkv + m * N + (int64_t)(rem / quads) * hd;
+  const size_t p = (size_t)min(max(pos[m], 0), max_pos - 1) * half + q4;
   const f32x4_t c = *(const f32x4_t*)(rcos + p), sn = *(const f32x4_t*)(rsin + p);
   float a[4], b[4], ra[4], rb[4];
   unpack_bf16x4(*(const u32x2_t*)(base + q4), a);
-  unpack_bf16x4(*(const u32x2_t*)(base + 32 + q4), b);
+  unpack_bf16x4(*(const u32x2_t*)(base + half + q4), b);
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     ra[v] = a[v] * c[v] - b[v] * sn[v];
     rb[v] = b[v] * c[v] + a[v] * sn[v];
   }
   *(u32x2_t*)(base + q4) = pack_bf16x4(ra[0], ra[1], ra[2], ra[3]);
-  *(u32x2_t*)(base + 32 + q4) = pack_bf16x4(rb[0], rb[1], rb[2], rb[3]);
+  *(u32x2_t*)(base + half + q4) = pack_bf16x4(rb[0], rb[1], rb[2], rb[3]);
 }
 
 hipError_t launch_rope_apply(uint16_t* qkv, const float* rcos, const float* rsin, const int* pos,
-                             int max_pos, int M, int n_q, int n_kv, hipStream_t stream) {
-  const int N = (n_q + 2 * n_kv) * 64, n_rot = n_q + n_kv;
-  hipLaunchKernelGGL(k_rope_apply, dim3(cdiv((int64_t)M * n_rot * 8, 256)), dim3(256), 0, stream,
-                     qkv, rcos, rsin, pos, max_pos, M, N, n_rot);
+                             int max_pos, int M, int n_q, int n_kv, int head_dim,
+                             hipStream_t stream) {
+  const int N = (n_q + 2 * n_kv) * head_dim, n_rot = n_q + n_kv;
+  hipLaunchKernelGGL(k_rope_apply, dim3(cdiv((int64_t)M * n_rot * (head_dim / 8), 256)),
+                     dim3(256), 0, stream, qkv, rcos, rsin, pos, max_pos, M, N, n_rot, head_dim);
   return hipGetLastError();
 }
 

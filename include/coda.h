@@ -154,7 +154,7 @@ int coda_gemm_rowscale_swiglu(int dtype, const void* X, const float* x_scale, co
  * rope_cos / rope_sin [max_pos, hd/2] fp32 (coda_rope_tables; 16-byte aligned),
  * pos [M] int32 in [0, max_pos) (a position outside is clamped into the table),
  * qkv [M, (nq+2nkv)hd] bf16.
- * Sizes: head_dim == 64; nq, nkv >= 1; K % 64 == 0; M >= 1.
+ * Sizes: head_dim 64 or 128; nq, nkv >= 1; K % 64 == 0; M >= 1.
  */
 int coda_gemm_rope(const void* h, const void* Wqkv, const float* r, const float* rope_cos,
                    const float* rope_sin, const int32_t* pos, int max_pos, void* qkv, int M,
@@ -213,7 +213,8 @@ int coda_gemm_block_lse_noalloc(const void* X, const void* W, const float* r,
  * parts of qkv (the layout coda_gemm_rope writes: q | k | v).  fp32 scores
  * and statistics, P rounded to bf16 for the P V product, bf16 output.
  * qkv [M, (n_q + 2 n_kv) hd] bf16, o [M, n_q hd] bf16, 16-byte aligned.
- * Sizes: head_dim == 64; n_q % n_kv == 0; seq_len % 128 == 0; M % seq_len == 0. */
+ * Sizes: head_dim 64 or 128; n_q % n_kv == 0; seq_len % 128 == 0;
+ * M % seq_len == 0. */
 int coda_attention_fwd(const void* qkv, void* o, int M, int seq_len, int n_q_heads,
                        int n_kv_heads, int head_dim, void* stream);
 
@@ -384,7 +385,7 @@ int coda_quantize_e4m3(const void* x, int64_t count, const float* s_in, void* ou
                        float* s_out, void* stream);
 /* In place on a stored qkv [M, (nq+2nkv)*hd] bf16 (as a plain GEMM writes it): the
  * rotate-half RoPE of coda_gemm_rope on the q and k heads, each pair rounded to bf16
- * again.  Tables, positions and sizes as coda_gemm_rope (head_dim 64). */
+ * again.  Tables, positions and sizes as coda_gemm_rope (head_dim 64 or 128). */
 int coda_rope_apply(void* qkv, const float* rope_cos, const float* rope_sin, const int32_t* pos,
                     int max_pos, int M, int n_q_heads, int n_kv_heads, int head_dim, void* stream);
 /* Cross entropy of stored bf16 logits z [M,V] (as a plain GEMM writes them):

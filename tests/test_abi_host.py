@@ -167,7 +167,8 @@ def test_attention_validation(L):
     f = L.coda_attention_fwd
     assert f(None, A16, 4096, 2048, 32, 8, 64, None) == ERR_NULL
     assert f(A16, None, 4096, 2048, 32, 8, 64, None) == ERR_NULL
-    assert f(A16, A16, 4096, 2048, 32, 8, 128, None) == ERR_SHAPE    # head size 64 only
+    assert f(A16, A16, 4096, 2048, 32, 8, 96, None) == ERR_SHAPE     # head size 64 or 128
+    assert f(A16, A16, 4096, 2048, 32, 8, 256, None) == ERR_SHAPE
     assert f(A16, A16, 4096, 2048, 32, 6, 64, None) == ERR_SHAPE     # n_q % n_kv
     assert f(A16, A16, 4096, 2048, 0, 8, 64, None) == ERR_SHAPE
     assert f(A16, A16, 4096, 2048, 32, 0, 64, None) == ERR_SHAPE
@@ -180,9 +181,24 @@ def test_attention_validation(L):
     assert f(A16, A16 + 2, 4096, 2048, 32, 8, 64, None) == ERR_ALIGN
     if not torch.cuda.is_available():
         assert f(A16, A16, 8192, 2048, 32, 8, 64, None) == ERR_DEVICE
+        assert f(A16, A16, 8192, 2048, 64, 8, 128, None) == ERR_DEVICE
     with pytest.raises(ValueError, match="shape"):   # o of another width
         ops.attention_fwd(torch.zeros(256, 6 * 64, dtype=torch.bfloat16),
                           torch.zeros(256, 3 * 64, dtype=torch.bfloat16), 128, 4, 1)
+
+
+def test_rope_head_sizes(L):
+    """The RoPE calls take heads of 64 or 128 and reject other sizes before
+    any HIP call."""
+    g = L.coda_gemm_rope
+    # (h, Wqkv, r, cos, sin, pos, max_pos, qkv, M, K, n_q, n_kv, head_dim, stream)
+    for hd in (32, 96, 256):
+        assert g(A16, A16, A16, A16, A16, A16, 64, A16, 64, 64, 4, 2, hd, None) == ERR_SHAPE
+        assert L.coda_rope_apply(A16, A16, A16, A16, 64, 64, 4, 2, hd, None) == ERR_SHAPE
+    if not torch.cuda.is_available():
+        for hd in (64, 128):
+            assert g(A16, A16, A16, A16, A16, A16, 64, A16, 64, 64, 4, 2, hd, None) == ERR_DEVICE
+            assert L.coda_rope_apply(A16, A16, A16, A16, 64, 64, 4, 2, hd, None) == ERR_DEVICE
 
 
 def test_binding_checks_backward_shapes():

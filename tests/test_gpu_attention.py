@@ -14,16 +14,16 @@ pytestmark = pytest.mark.gpu
 EPS = 1e-5
 
 
-def _qkv_bits(seed, M, nq, nkv, scale=1.0):
+def _qkv_bits(seed, M, nq, nkv, scale=1.0, hd=64):
     rng = np.random.default_rng(seed)
-    a = (rng.standard_normal((M, (nq + 2 * nkv) * 64)) * scale).astype(np.float32)
+    a = (rng.standard_normal((M, (nq + 2 * nkv) * hd)) * scale).astype(np.float32)
     return inputs.to_bf16_bits(a)
 
 
-def run_attention(bits, L, nq, nkv):
+def run_attention(bits, L, nq, nkv, hd=64):
     M = bits.shape[0]
-    o = torch.full((M, nq * 64), float("nan"), dtype=torch.bfloat16, device=DEV)
-    ops.attention_fwd(bf16_dev(bits), o, L, nq, nkv)
+    o = torch.full((M, nq * hd), float("nan"), dtype=torch.bfloat16, device=DEV)
+    ops.attention_fwd(bf16_dev(bits), o, L, nq, nkv, hd)
     torch.cuda.synchronize()
     return bf16_host(o)
 
@@ -40,6 +40,41 @@ def test_attention_small(L, n_seq, nq, nkv):
     got = run_attention(bits, L, nq, nkv)
     ref = oracle.attention_causal_gqa(dec_bf16(bits), L, nq, nkv, 64)
     assert norm_err(got, ref) <= TOL_BF16
+
+
+@pytest.mark.parametrize("L,n_seq,nq,nkv", [(128, 2, 4, 2), (256, 3, 6, 2), (384, 1, 2, 2),
+                                             (128, 1, 1, 1), (512, 2, 8, 1), (2048, 1, 2, 2)])
+def test_attention_head128(L, n_seq, nq, nkv):
+    """Heads of 128 (the 7B / 70B shapes): 32 queries per wave, four waves per
+    workgroup, 256-byte K and V rows."""
+    M = L * n_seq
+    bits = _qkv_bits(L + nq + 3 * nkv, M, nq, nkv, hd=128)
+    say(f"attention hd=128 L={L} seqs={n_seq} nq={nq} nkv={nkv}")
+    got = run_attention(bits, L, nq, nkv, hd=128)
+    ref = oracle.attention_causal_gqa(dec_bf16(bits), L, nq, nkv, 128)
+    assert norm_err(got, ref) <= TOL_BF16
+
+
+def test_attention_head128_closed_forms_and_peaks():
+    """Heads of 128: the first query of a sequence returns its own v row;
+    with scores of magnitude ~100 the lazy reference max is raised often."""
+    L, n_seq, nq, nkv, hd = 256, 2, 4, 2, 128
+    M = L * n_seq
+    rng = np.random.default_rng(15)
+    a = rng.standard_normal((M, (nq + 2 * nkv) * hd)).astype(np.float32)
+    a[:, :nq * hd] *= 10.0
+    bits = inputs.to_bf16_bits(a)
+    say("attention hd=128 closed forms and peaked scores")
+    got = run_attention(bits, L, nq, nkv, hd=hd)
+    x = dec_bf16(bits)
+    ref = oracle.attention_causal_gqa(x, L, nq, nkv, hd)
+    assert norm_err(got, ref) <= TOL_BF16
+    for s0 in (0, L):
+        for h in range(nq):
+            g = h // (nq // nkv)
+            v = x[s0, (nq + nkv + g) * hd:(nq + nkv + g + 1) * hd]
+            o = got[s0, h * hd:(h + 1) * hd]
+            assert float(np.max(np.abs(o - v))) <= 2 ** -7 * max(1.0, float(np.max(np.abs(v))))
 
 
 def test_attention_closed_forms():

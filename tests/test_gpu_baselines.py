@@ -13,15 +13,16 @@ from tests.gpu_util import (DEV, TOL_BF16, TOL_ROW, bf16_dev, bf16_host, dec_bf1
 pytestmark = pytest.mark.gpu
 
 
-def test_rope_apply_vs_oracle():
-    M, nq, nkv, hd, max_pos = 300, 4, 2, 64, 64
+@pytest.mark.parametrize("hd", [64, 128])
+def test_rope_apply_vs_oracle(hd):
+    M, nq, nkv, max_pos = 300, 4, 2, 64
     N = (nq + 2 * nkv) * hd
     rng = np.random.default_rng(5)
     y = rng.standard_normal((M, N)).astype(np.float32)
     bits = inputs.to_bf16_bits(y)
     pos = (np.arange(M) * 7 % max_pos).astype(np.int32)
     cos, sin = oracle.rope_tables(max_pos, hd, 10000.0)
-    say(f"rope_apply M={M} heads {nq}+{nkv}+{nkv}")
+    say(f"rope_apply M={M} heads {nq}+{nkv}+{nkv} of {hd}")
     qkv = bf16_dev(bits)
     ops.rope_apply(qkv, f32_dev(cos), f32_dev(sin), i32_dev(pos), nq, nkv, hd)
     torch.cuda.synchronize()

@@ -82,6 +82,54 @@ def test_rope_block_ragged(M, d, K1, nq, nkv, seq):
     assert norm_err(q[:, vlo:], ref["qkv"][:, vlo:]) <= TOL_BF16
 
 
+@pytest.mark.parametrize("M,d,K1,nq,nkv,seq", [
+    (300, 256, 192, 4, 2, 100),    # 8 heads of 128: four tile columns, ragged M
+    (200, 256, 128, 3, 1, 64),     # 5 heads: the last tile column holds one head
+    (130, 128, 64, 8, 8, 50),      # 24 heads (no grouping), one stage per tile
+])
+def test_rope_block_head128(M, d, K1, nq, nkv, seq):
+    """Heads of 128 (the 7B / 70B shapes): a wave's 128 features are one head
+    and the rotate-half partner of feature c is c + 64."""
+    w = inputs.make_attn(seed=11, M=M, d=d, K1=K1, n_q=nq, n_kv=nkv, head_dim=128, seq_len=seq)
+    say(f"rope block hd=128 M={M} d={d} K1={K1} nq={nq} nkv={nkv} seq={seq}")
+    got = run_fused(w)
+    ref = oracle_rows(w)
+    assert row_rel_err(f32_host(got["r"]), ref["r"]) <= TOL_ROW
+    q = bf16_host(got["qkv"])
+    assert norm_err(q, ref["qkv"]) <= TOL_BF16
+    vlo = (nq + nkv) * 128
+    assert norm_err(q[:, vlo:], ref["qkv"][:, vlo:]) <= TOL_BF16
+    # rotated half of every q and k head on its own (a swapped pair would
+    # still leave the unrotated half right)
+    for hh in range(nq + nkv):
+        c0 = hh * 128
+        assert norm_err(q[:, c0 + 64:c0 + 128], ref["qkv"][:, c0 + 64:c0 + 128]) <= TOL_BF16
+
+
+def test_rope_head128_chained_sampled_rows():
+    """Heads of 128 at M = 16384 with 10 heads (5 tile columns): 320 tiles, so
+    workgroups chain into a second tile; sampled rows vs the oracle."""
+    w = inputs.make_attn(seed=12, M=16384, d=128, K1=64, n_q=8, n_kv=1, head_dim=128,
+                         seq_len=2048)
+    say("rope block hd=128, chained tiles (M=16384, 10 heads)")
+    got = run_fused(w)
+    rows = sample_rows(w.sizes["M"], n=48)
+    ref = oracle_rows(w, rows)
+    assert norm_err(bf16_host(got["qkv"][rows.tolist()]), ref["qkv"]) <= TOL_BF16
+
+
+@pytest.mark.parametrize("hd", [64, 128])
+def test_rope_position_zero_identity_any_head(hd):
+    """Positions all 0 with heads of 64 and 128 on the 256 x 256 tile."""
+    w = inputs.make_attn(seed=13, M=96, d=128, K1=64, n_q=2, n_kv=1, head_dim=hd, seq_len=1)
+    say(f"rope block, all positions 0, hd={hd}")
+    got = run_fused(w)
+    ref = oracle_rows(w)
+    n = oracle.rmsnorm(ref["h"], w.arrays["gamma"].astype(np.float64), EPS)
+    plain = oracle.gemm_nt(n, dec_bf16(w.arrays["wqkv"]))
+    assert norm_err(bf16_host(got["qkv"]), plain) <= TOL_BF16
+
+
 @pytest.mark.parametrize("nq,nkv", [(2, 1), (4, 1)])  # 4 heads; 6 heads (128 x 384 tile)
 def test_rope_position_zero_is_identity_on_gpu(nq, nkv):
     """With every position 0 the rotation is the identity, so q|k|v equal the
