@@ -689,7 +689,8 @@ def time_other_rows(torch, ops, inputs, stream, steps, warmup):
     del x, wl, tmax, tsum, w, logits, lse_u, loss_u
 
     # one whole layer at the 1B shape: attention-input block, attention, MLP block
-    out["layer_1b"] = _layer_row(torch, ops, inputs, stream, steps, warmup, bf)
+    for name in ("layer_1b", "layer_7b", "layer_70b"):
+        out[name] = _layer_row(torch, ops, inputs, stream, steps, warmup, bf, name)
 
     # the bf16 MLP block at the 7B and 70B hidden sizes
     for name in ("mlp_7b", "mlp_70b"):
@@ -764,15 +765,16 @@ def attention_flops(M, L, nq, hd):
     return 4.0 * hd * nq * (M // L) * L * (L + 1) / 2
 
 
-def _layer_row(torch, ops, inputs, stream, steps, warmup, bf):
-    """Forward of one transformer layer at the 1B shape (M=8192 as 4 sequences
-    of 2048, d=2048, previous-MLP width 8192, ffn=8192, 32 q / 8 kv heads of
-    64): the fused chain of seven launches against the unfused sequence with
-    the same attention kernel, plus per-launch times of the fused chain."""
-    print("[bench] layer_1b", file=sys.stderr, flush=True)
+def _layer_row(torch, ops, inputs, stream, steps, warmup, bf, name="layer_1b"):
+    """Forward of one transformer layer (layer_1b: M=8192 as 4 sequences of
+    2048, d=2048, previous-MLP width 8192, ffn=8192, 32 q / 8 kv heads of 64;
+    layer_7b and layer_70b: the 7B and 70B hidden sizes with heads of 128):
+    the fused chain of seven launches against the unfused sequence with the
+    same attention kernel, plus per-launch times of the fused chain."""
+    print(f"[bench] {name}", file=sys.stderr, flush=True)
     dev = "cuda:0"
     eps = 1e-5
-    w = inputs.make_workload("layer_1b")
+    w = inputs.make_workload(name)
     sz = w.sizes
     M, d, K1, ffn = sz["M"], sz["d"], sz["K1"], sz["ffn"]
     nq, nkv, hd, L = sz["n_q"], sz["n_kv"], sz["head_dim"], sz["seq_len"]
@@ -798,7 +800,7 @@ def _layer_row(torch, ops, inputs, stream, steps, warmup, bf):
     fused = [lambda: ops.gemm_residual_partialrms(x, wdn, res, h1, P1),
              lambda: ops.rms_reduce(P1, d, eps, r1),
              lambda: ops.gemm_rope(h1, wqkv_f, r1, cos, sin, pos, qkv, nq, nkv, hd),
-             lambda: ops.attention_fwd(qkv, o, L, nq, nkv),
+             lambda: ops.attention_fwd(qkv, o, L, nq, nkv, hd),
              lambda: ops.gemm_residual_partialrms(o, wo, h1, h2, P2),
              lambda: ops.rms_reduce(P2, d, eps, r2),
              lambda: ops.gemm_rowscale_swiglu(h2, wg_f, wu_f, r2, act)]
@@ -824,7 +826,7 @@ def _layer_row(torch, ops, inputs, stream, steps, warmup, bf):
         ops.rmsnorm(hu1, g1, eps, nu)
         ops.gemm_bf16(nu, wqkv, qkv_u)
         ops.rope_apply(qkv_u, cos, sin, pos, nq, nkv, hd)
-        ops.attention_fwd(qkv_u, o_u, L, nq, nkv)
+        ops.attention_fwd(qkv_u, o_u, L, nq, nkv, hd)
         ops.gemm_bf16(o_u, wo, y)
         ops.residual_add(y, hu1, hu2)
         ops.rmsnorm(hu2, g2, eps, nu)
@@ -835,8 +837,9 @@ def _layer_row(torch, ops, inputs, stream, steps, warmup, bf):
     fl = (2.0 * M * d * K1 + 2.0 * M * (nq + 2 * nkv) * hd * d + fl_att
           + 2.0 * M * d * nq * hd + 2.0 * M * 2 * ffn * d)
     att_ms = per[3]
-    return {"workload": "M=8192 (4 sequences of 2048), d=2048, previous-MLP width 8192, "
-                        "ffn=8192, 32 q / 8 kv heads of 64, causal attention, RoPE theta=5e5",
+    return {"workload": f"M={M} ({M // L} sequences of {L}), d={d}, previous-MLP width {K1}, "
+                        f"ffn={ffn}, {nq} q / {nkv} kv heads of {hd}, causal attention, "
+                        f"RoPE theta={sz['theta']:g}",
             "ms_per_step": round(ms, 4), "tflops": round(fl / ms / 1e9, 1),
             "pct_of_bf16_peak": round(100 * fl / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
             "flops_note": "GEMM FLOPs 2MNK each; attention 4 hd per causal (query, key) pair",

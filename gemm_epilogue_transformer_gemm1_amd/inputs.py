@@ -5,10 +5,11 @@ numbers and rounds them to the storage formats the kernels read (bf16, OCP
 E4M3FN with one fp32 scale per tensor).  Both the HIP path and the CPU oracle
 receive the arrays built here; neither builds its own.
 
-Every tensor has its own stream:
-    numpy.random.Generator(PCG64(SeedSequence(seed, spawn_key=(workload, tensor))))
-so tensors are reproducible independently of each other and of generation
-order.  Normals are drawn in float32 and scaled by their standard deviation,
+Every tensor has its own streams, one per chunk of about 2^20 elements (whole
+rows):
+    numpy.random.Generator(PCG64(SeedSequence(seed, spawn_key=(workload, tensor, chunk))))
+so tensors are reproducible independently of each other, of generation order
+and of the number of threads that draw the chunks.  Normals are drawn in float32 and scaled by their standard deviation,
 then rounded to bf16 (round to nearest even, via torch's CPU cast) or
 quantised to e4m3 with scale = amax / 448 (torch's CPU cast after clamping, so
 that the code saturates instead of overflowing to NaN).
@@ -26,10 +27,14 @@ The shapes and distributions follow the LLaMA-3-shaped workloads:
              previous MLP's down projection, K1=8192, then QKV + RoPE), causal
              grouped-query attention over 4 sequences of 2048, then the mlp_1b
              block with the attention output projection wo as its GEMM1
+  layer_7b   the layer at d=4096, K1=ffn=11008, 32 q / 32 kv heads of 128
+  layer_70b  the layer at d=8192, K1=ffn=28672, 64 q / 8 kv heads of 128
 Activations and residuals ~ N(0, 1); weights ~ N(0, 1/fan_in of the layer
 they feed, i.e. 1/d for the d-wide layers); gamma = 1 + 0.1 N(0, 1).
 """
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -55,28 +60,48 @@ WORKLOADS = {
     # one transformer layer (attention input block -> attention -> MLP block)
     "layer_1b": (8, "layer", dict(M=8192, d=2048, K1=8192, ffn=8192, n_q=32, n_kv=8,
                                   head_dim=64, theta=500000.0, seq_len=2048)),
+    # the same layer at the 7B and 70B hidden sizes: LLaMA-2-7B (32 heads of
+    # 128, no grouping, RoPE theta 1e4, ffn 11008) and LLaMA-3-70B (64 q / 8 kv
+    # heads of 128, theta 5e5, ffn 28672); the previous MLP's width is ffn
+    "layer_7b": (9, "layer", dict(M=8192, d=4096, K1=11008, ffn=11008, n_q=32, n_kv=32,
+                                  head_dim=128, theta=10000.0, seq_len=2048)),
+    "layer_70b": (10, "layer", dict(M=8192, d=8192, K1=28672, ffn=28672, n_q=64, n_kv=8,
+                                    head_dim=128, theta=500000.0, seq_len=2048)),
 }
 
 _TENSOR_IDS = {"x": 0, "res": 1, "w1": 2, "wg": 3, "wu": 4, "gamma": 5, "wqkv": 6,
                "wlm": 7, "labels": 8, "wd": 9, "dy": 10, "wo": 11, "gamma2": 12}
 
 
-def _rng(seed, workload_id, tensor):
-    ss = np.random.SeedSequence(seed, spawn_key=(workload_id, _TENSOR_IDS[tensor]))
+def _rng(seed, workload_id, tensor, chunk=None):
+    key = (workload_id, _TENSOR_IDS[tensor]) + (() if chunk is None else (chunk,))
+    ss = np.random.SeedSequence(seed, spawn_key=key)
     return np.random.Generator(np.random.PCG64(ss))
 
 
-def normal_f32(seed, workload_id, tensor, shape, std, chunk_rows=4096):
-    """float32 N(0, std^2) array, drawn row-chunk by row-chunk."""
-    g = _rng(seed, workload_id, tensor)
+_CHUNK_ELEMS = 1 << 20
+_POOL = ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1))
+
+
+def normal_f32(seed, workload_id, tensor, shape, std):
+    """float32 N(0, std^2) array.  Rows are drawn in chunks of about 2^20
+    elements (R = max(1, 2^20 // row length) rows); chunk c (rows
+    [R c, R c + R)) has its own stream (spawn key (workload, tensor, c)), so
+    the chunks are drawn in parallel threads and the values do not depend on
+    the thread count."""
     out = np.empty(shape, dtype=np.float32)
     rows = shape[0]
-    for r0 in range(0, rows, chunk_rows):
-        r1 = min(rows, r0 + chunk_rows)
-        blk = g.standard_normal(size=(r1 - r0,) + tuple(shape[1:]), dtype=np.float32)
+    row_elems = int(np.prod(shape[1:], dtype=np.int64)) if len(shape) > 1 else 1
+    chunk_rows = max(1, _CHUNK_ELEMS // row_elems)
+
+    def fill(c):
+        r0, r1 = c * chunk_rows, min(rows, (c + 1) * chunk_rows)
+        blk = out[r0:r1]
+        _rng(seed, workload_id, tensor, c).standard_normal(out=blk, dtype=np.float32)
         if std != 1.0:
             blk *= np.float32(std)
-        out[r0:r1] = blk
+
+    list(_POOL.map(fill, range((rows + chunk_rows - 1) // chunk_rows)))
     return out
 
 
@@ -153,8 +178,7 @@ def make_lm(seed=0, M=64, d=256, V=1000, workload_id=3, name="lm"):
     """LM-head inputs: x [M,d] bf16, wlm [V,d] bf16, labels [M] int32 in [0,V)."""
     w = Workload(name, "lm", dict(M=M, d=d, V=V), seed)
     w.arrays["x"] = to_bf16_bits(normal_f32(seed, workload_id, "x", (M, d), 1.0))
-    w.arrays["wlm"] = to_bf16_bits(normal_f32(seed, workload_id, "wlm", (V, d), d ** -0.5,
-                                              chunk_rows=8192))
+    w.arrays["wlm"] = to_bf16_bits(normal_f32(seed, workload_id, "wlm", (V, d), d ** -0.5))
     w.arrays["labels"] = _rng(seed, workload_id, "labels").integers(0, V, size=M, dtype=np.int32)
     return w
 

@@ -152,7 +152,7 @@ def run_layer(w):
     partial RMS) -> reduce -> GEMM2 (row scale, SwiGLU)."""
     sz = w.sizes
     M, d, K1, ffn = sz["M"], sz["d"], sz["K1"], sz["ffn"]
-    nq, nkv, L = sz["n_q"], sz["n_kv"], sz["seq_len"]
+    nq, nkv, L, hd = sz["n_q"], sz["n_kv"], sz["seq_len"], sz["head_dim"]
     bf = dict(dtype=torch.bfloat16, device=DEV)
     x, res, wdn, wqkv = (bf16_dev(w.arrays[k]) for k in ("x", "res", "w1", "wqkv"))
     wo, wg, wu = (bf16_dev(w.arrays[k]) for k in ("wo", "wg", "wu"))
@@ -161,21 +161,21 @@ def run_layer(w):
     ops.fold_gamma(wqkv, g1, wqkv_f)
     ops.fold_gamma(wg, g2, wg_f)
     ops.fold_gamma(wu, g2, wu_f)
-    cos = torch.empty(L, 32, dtype=torch.float32, device=DEV)
+    cos = torch.empty(L, hd // 2, dtype=torch.float32, device=DEV)
     sin = torch.empty_like(cos)
-    ops.rope_tables(sz["theta"], L, 64, cos, sin)
+    ops.rope_tables(sz["theta"], L, hd, cos, sin)
     pos = i32_dev(w.arrays["pos"])
     T = ops.rms_tiles(d)
     h1, h2 = torch.empty(M, d, **bf), torch.empty(M, d, **bf)
     P1, P2 = (torch.empty(T, M, dtype=torch.float32, device=DEV) for _ in range(2))
     r1, r2 = (torch.empty(M, dtype=torch.float32, device=DEV) for _ in range(2))
-    qkv = torch.empty(M, (nq + 2 * nkv) * 64, **bf)
-    o = torch.empty(M, nq * 64, **bf)
+    qkv = torch.empty(M, (nq + 2 * nkv) * hd, **bf)
+    o = torch.empty(M, nq * hd, **bf)
     out = torch.empty(M, ffn, **bf)
     ops.gemm_residual_partialrms(x, wdn, res, h1, P1)
     ops.rms_reduce(P1, d, EPS, r1)
-    ops.gemm_rope(h1, wqkv_f, r1, cos, sin, pos, qkv, nq, nkv, 64)
-    ops.attention_fwd(qkv, o, L, nq, nkv)
+    ops.gemm_rope(h1, wqkv_f, r1, cos, sin, pos, qkv, nq, nkv, hd)
+    ops.attention_fwd(qkv, o, L, nq, nkv, hd)
     ops.gemm_residual_partialrms(o, wo, h1, h2, P2)
     ops.rms_reduce(P2, d, EPS, r2)
     ops.gemm_rowscale_swiglu(h2, wg_f, wu_f, r2, out)
@@ -190,8 +190,8 @@ def oracle_layer(w):
         dec_bf16(w.arrays["x"]), dec_bf16(w.arrays["res"]), dec_bf16(w.arrays["w1"]),
         dec_bf16(w.arrays["wqkv"]), w.arrays["gamma"].astype(np.float64),
         dec_bf16(w.arrays["wo"]), dec_bf16(w.arrays["wg"]), dec_bf16(w.arrays["wu"]),
-        w.arrays["gamma2"].astype(np.float64), EPS, w.arrays["pos"], sz["n_q"], sz["n_kv"], 64,
-        sz["theta"], sz["seq_len"])
+        w.arrays["gamma2"].astype(np.float64), EPS, w.arrays["pos"], sz["n_q"], sz["n_kv"],
+        sz["head_dim"], sz["theta"], sz["seq_len"])
 
 
 def _row_norm_rel(got, ref):
@@ -215,8 +215,8 @@ def check_layer(w, got):
     takes r2 from h2 before the bf16 rounding of its store (relative 2^-9 of
     the row norm), so |dr2 / r2| <= ||h2_gpu - h2_ref|| / ||h2_ref|| + 2^-9 + TOL_ROW."""
     sz = w.sizes
-    nq, nkv, L = sz["n_q"], sz["n_kv"], sz["seq_len"]
-    stage = {"o": oracle.attention_causal_gqa(got["qkv"], L, nq, nkv, 64)}
+    nq, nkv, L, hd = sz["n_q"], sz["n_kv"], sz["seq_len"], sz["head_dim"]
+    stage = {"o": oracle.attention_causal_gqa(got["qkv"], L, nq, nkv, hd)}
     f2 = oracle.mlp_block(got["o"], got["h1"], dec_bf16(w.arrays["wo"]), dec_bf16(w.arrays["wg"]),
                           dec_bf16(w.arrays["wu"]), w.arrays["gamma2"].astype(np.float64), EPS)
     stage.update({"h2": f2["h"], "r2": f2["r"], "out": f2["out"]})
@@ -252,4 +252,14 @@ def test_layer_1b_every_row():
     row of every stage against the oracle."""
     w = inputs.make_workload("layer_1b")
     say("layer_1b full size, every row")
+    check_layer(w, run_layer(w))
+
+
+@pytest.mark.parametrize("name", ["layer_7b", "layer_70b"])
+def test_layer_7b_70b_one_sequence_every_row(name):
+    """The layer at the 7B (32 heads of 128, no grouping, ffn 11008) and 70B
+    (64 q / 8 kv heads of 128, ffn 28672) shapes on one sequence of 2048
+    tokens, every row of every stage."""
+    w = inputs.make_workload(name, M=2048)
+    say(f"{name} at M=2048 (one sequence), every row")
     check_layer(w, run_layer(w))
