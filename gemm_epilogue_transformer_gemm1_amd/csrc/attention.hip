@@ -39,7 +39,8 @@
 //   * causal: a wave skips the key steps after its queries; the step that
 //     holds them masks keys past each query to -inf;
 //   * workgroups are launched longest first (the query blocks with the most
-//     key steps), all heads and sequences of a block position together.
+//     key steps), all heads and sequences of a block position together, the
+//     q heads that share a kv head on one XCD.
 #include "coda_device.hpp"
 #include "launch.hpp"
 
@@ -112,13 +113,26 @@ __global__ __launch_bounds__(64 * AttnShape<kHd>::kWaves, 2) void k_attention_fw
   const int lane = tid & 63, wave = tid >> 6;
   const int g4 = lane >> 4, r16 = lane & 15;
   const int nqb = a.L / kAttnQB;
-  const int heads_seqs = a.nq * (a.M / a.L);
-  // longest first: all (head, sequence) pairs of the last query block, then
-  // the next-to-last, ...
-  const int qb = nqb - 1 - (int)blockIdx.x / heads_seqs;
-  const int hs = (int)blockIdx.x % heads_seqs;
-  const int h = hs % a.nq, seq = hs / a.nq;
-  const int kvh = h / (a.nq / a.nkv);
+  const int grp = a.nq / a.nkv;             // q heads per kv head
+  const int npairs = a.nkv * (a.M / a.L);   // (kv head, sequence) pairs
+  const int units = npairs * grp;           // workgroups per query-block position
+  // longest first: every (q head, sequence) of the last query block, then
+  // the next-to-last, ...  When the pairs split evenly over the 8 XCDs
+  // (workgroup i runs on XCD i % 8), XCD x takes the pairs p = x mod 8 with
+  // all their q heads at every block position, so the K and V rows of a pair
+  // are read through one L2.
+  const int qb = nqb - 1 - (int)blockIdx.x / units;
+  const int t = (int)blockIdx.x % units;
+  int pair, gi;
+  if (npairs % 8 == 0) {
+    pair = ((t >> 3) / grp) * 8 + (t & 7);
+    gi = (t >> 3) % grp;
+  } else {
+    pair = t / grp;
+    gi = t % grp;
+  }
+  const int kvh = pair % a.nkv, seq = pair / a.nkv;
+  const int h = kvh * grp + gi;
   const int C = (a.nq + 2 * a.nkv) * kHd;
   const size_t row0 = (size_t)seq * a.L;  // first row of the sequence
   const int q0 = qb * kAttnQB;            // first query of the block (sequence position)
