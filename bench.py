@@ -41,7 +41,8 @@ def parse():
                         "the timed steps start on a settled shader clock")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-rows", action="store_true",
-                   help="skip timing the attention-input, LM-head and fp8 workloads")
+                   help="skip the other_rows workloads (attention input, LM head, the layer "
+                        "at 1B / 7B / 70B, the 7B and 70B MLP blocks, the backward, fp8)")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="before timing, copy a buffer of this many MiB three times (a plain "
                         "copy kernel of known size, to scale HBM byte counters)")
