@@ -277,20 +277,23 @@ def pin_attention_bruteforce(seed=20):
 
 
 def pin_attention_torch(seed=21):
-    """torch's scaled_dot_product_attention (CPU, float64, is_causal) with the
-    kv heads repeated for their q-head groups."""
+    """torch's scaled_dot_product_attention (CPU, float64, is_causal, default
+    scale 1/sqrt(hd)) with the kv heads repeated for their q-head groups, at a
+    small head and at the heads of 64 and 128 the kernels take."""
     rng = np.random.default_rng(seed)
-    L, n_seq, n_q, n_kv, hd = 17, 3, 6, 2, 8
-    M = L * n_seq
-    qkv = _qkv_random(rng, M, n_q, n_kv, hd)
-    o = R.attention_causal_gqa(qkv, L, n_q, n_kv, hd)
-    t = torch.from_numpy(qkv).view(n_seq, L, n_q + 2 * n_kv, hd).permute(0, 2, 1, 3)
-    q, k, v = t[:, :n_q], t[:, n_q:n_q + n_kv], t[:, n_q + n_kv:]
-    rep = n_q // n_kv
-    ref = torch.nn.functional.scaled_dot_product_attention(
-        q, k.repeat_interleave(rep, dim=1), v.repeat_interleave(rep, dim=1), is_causal=True)
-    ref = ref.permute(0, 2, 1, 3).reshape(M, n_q * hd).numpy()
-    return _ok(_rel(o, ref), 1e-13, "attention vs torch sdpa")
+    worst = 0.0
+    for (L, n_seq, n_q, n_kv, hd) in ((17, 3, 6, 2, 8), (9, 2, 4, 1, 64), (7, 2, 2, 2, 128)):
+        M = L * n_seq
+        qkv = _qkv_random(rng, M, n_q, n_kv, hd)
+        o = R.attention_causal_gqa(qkv, L, n_q, n_kv, hd)
+        t = torch.from_numpy(qkv).view(n_seq, L, n_q + 2 * n_kv, hd).permute(0, 2, 1, 3)
+        q, k, v = t[:, :n_q], t[:, n_q:n_q + n_kv], t[:, n_q + n_kv:]
+        rep = n_q // n_kv
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            q, k.repeat_interleave(rep, dim=1), v.repeat_interleave(rep, dim=1), is_causal=True)
+        ref = ref.permute(0, 2, 1, 3).reshape(M, n_q * hd).numpy()
+        worst = max(worst, _rel(o, ref))
+    return _ok(worst, 1e-13, "attention vs torch sdpa (hd 8, 64, 128)")
 
 
 def pin_attention_closed_forms(seed=22):
