@@ -181,21 +181,24 @@ def pin_rope_closed_forms():
 
 
 def pin_rope_torch_complex(seed=6):
-    """RoPE as complex multiplication: (a + ib) * e^{i angle}."""
+    """RoPE as complex multiplication: (a + ib) * e^{i angle}, at a small head
+    and at the heads of 64 and 128 the kernels take (theta 5e5 and 1e4)."""
     rng = np.random.default_rng(seed)
-    M, hd, nh, theta = 11, 8, 3, 500000.0
-    y = rng.standard_normal((M, nh * hd))
-    pos = rng.integers(0, 50, size=M)
-    cos, sin = R.rope_tables(64, hd, theta)
-    out = R.apply_rope(y, pos, 2, hd, cos, sin)
-    yt = torch.from_numpy(y).view(M, nh, 2, hd // 2)
-    z = torch.complex(yt[:, :, 0], yt[:, :, 1])
-    inv = theta ** (-torch.arange(hd // 2, dtype=torch.float64) * 2 / hd)
-    ang = torch.from_numpy(pos).double()[:, None] * inv[None, :]
-    rot = z * torch.polar(torch.ones_like(ang), ang)[:, None, :]
-    ref = torch.stack([rot.real, rot.imag], dim=2).reshape(M, nh * hd).numpy()
-    ref[:, 2 * hd:] = y[:, 2 * hd:]  # third head not rotated
-    return _ok(_rel(out, ref), 1e-13, "rope vs torch complex")
+    worst = 0.0
+    for (M, hd, nh, theta) in ((11, 8, 3, 500000.0), (7, 64, 3, 500000.0), (5, 128, 3, 10000.0)):
+        y = rng.standard_normal((M, nh * hd))
+        pos = rng.integers(0, 2048, size=M)
+        cos, sin = R.rope_tables(2048, hd, theta)
+        out = R.apply_rope(y, pos, 2, hd, cos, sin)
+        yt = torch.from_numpy(y).view(M, nh, 2, hd // 2)
+        z = torch.complex(yt[:, :, 0], yt[:, :, 1])
+        inv = theta ** (-torch.arange(hd // 2, dtype=torch.float64) * 2 / hd)
+        ang = torch.from_numpy(pos).double()[:, None] * inv[None, :]
+        rot = z * torch.polar(torch.ones_like(ang), ang)[:, None, :]
+        ref = torch.stack([rot.real, rot.imag], dim=2).reshape(M, nh * hd).numpy()
+        ref[:, 2 * hd:] = y[:, 2 * hd:]  # third head not rotated
+        worst = max(worst, _rel(out, ref))
+    return _ok(worst, 1e-12, "rope vs torch complex (hd 8, 64, 128)")
 
 
 def pin_rope_relative(seed=7):
