@@ -246,6 +246,16 @@ def test_layer_small():
     check_layer(w, run_layer(w))
 
 
+def test_layer_small_head128_ragged():
+    """A whole layer with heads of 128 at small ragged widths: two sequences of
+    128, 4 q / 2 kv heads, d = 384 (one and a half GEMM tiles), previous-MLP
+    width 320, ffn = 704."""
+    w = inputs.make_layer(seed=4, M=256, d=384, K1=320, ffn=704, n_q=4, n_kv=2, head_dim=128,
+                          theta=10000.0, seq_len=128)
+    say("layer small hd=128 M=256 d=384 K1=320 ffn=704 4/2 heads L=128")
+    check_layer(w, run_layer(w))
+
+
 def test_layer_1b_every_row():
     """The 1B-shaped layer (M=8192 as 4 sequences of 2048, d=2048, ffn=8192,
     32 q / 8 kv heads) in the launch configuration the benchmark times; every
